@@ -1,0 +1,278 @@
+"""CPU oracle for importance-matrix-weighted row quantization.
+
+TEST INFRASTRUCTURE ONLY. This package loads ``liborc_qrow.so`` (a plain C
+implementation compiled with gcc, see ``qrow_oracle.c``) through ctypes and
+exposes it on numpy arrays. Only the test-suite, the package smoke check and
+the benchmark's CPU-baseline leg may import it; the GPU library never does.
+
+Every function here only marshals arguments: all arithmetic of the method is
+in the C file.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "qrow_oracle.c")
+LIB = os.path.join(HERE, "liborc_qrow.so")
+
+Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128 = range(6)
+TYPE_NAMES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1,
+              "q4_k": Q4_K, "q8_k128": Q8_K128}
+
+_lib = None
+_lock = threading.Lock()
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liborc_qrow.so with gcc (float contraction off)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"], check=True,
+                       cwd=HERE)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB):
+                build(force=True)
+            L = C.CDLL(LIB)
+            f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+            u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+            i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
+            i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+            vp = C.c_void_p
+            i64 = C.c_int64
+            L.orc_solver_constants.argtypes = [i32p]
+            L.orc_block_bytes.argtypes = [C.c_int]
+            L.orc_block_bytes.restype = C.c_size_t
+            L.orc_block_elems.argtypes = [C.c_int]
+            L.orc_row_bytes.argtypes = [C.c_int, i64]
+            L.orc_row_bytes.restype = C.c_size_t
+            L.orc_row_sigma2.argtypes = [f32p, i64]
+            L.orc_row_sigma2.restype = C.c_float
+            L.orc_row_sigma2_f64.argtypes = [f32p, i64]
+            L.orc_row_sigma2_f64.restype = C.c_double
+            L.orc_row_weights.argtypes = [f32p, vp, i64, C.c_float, f32p]
+            L.orc_solve_sym.argtypes = [C.c_int, f32p, f32p, C.c_int, C.c_int,
+                                        C.c_int, i8p, f32p, i32p]
+            L.orc_solve_asym.argtypes = [C.c_int, f32p, f32p, C.c_int, C.c_int,
+                                         C.c_int, C.c_int, u8p, f32p, f32p,
+                                         i32p]
+            L.orc_quantize_rows.argtypes = [C.c_int, vp, vp, i64, i64, vp]
+            L.orc_quantize_rows_grouped.argtypes = [C.c_int, vp, vp, i64, i64,
+                                                    i64, vp]
+            L.orc_quantize_row_sigma2.argtypes = [C.c_int, f32p, vp, i64,
+                                                  C.c_float, u8p]
+            L.orc_quantize_q8k128.argtypes = [vp, i64, i64, vp]
+            L.orc_dequantize_rows.argtypes = [C.c_int, vp, i64, i64, vp]
+            L.orc_f32_to_f16.argtypes = [C.c_float]
+            L.orc_f32_to_f16.restype = C.c_uint16
+            L.orc_f16_to_f32.argtypes = [C.c_uint16]
+            L.orc_f16_to_f32.restype = C.c_float
+            _lib = L
+    return _lib
+
+
+def _tid(t) -> int:
+    return TYPE_NAMES[t] if isinstance(t, str) else int(t)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def solver_constants() -> dict:
+    c = np.zeros(6, np.int32)
+    lib().orc_solver_constants(c)
+    return {"cand_step_x4": int(c[0]), "sym_cand": int(c[1]),
+            "sym_flip_passes": int(c[2]), "asym_cand": int(c[3]),
+            "asym_flip_passes": int(c[4]), "max_block": int(c[5])}
+
+
+def block_elems(t) -> int:
+    return lib().orc_block_elems(_tid(t))
+
+
+def block_bytes(t) -> int:
+    return lib().orc_block_bytes(_tid(t))
+
+
+def row_bytes(t, n_per_row: int) -> int:
+    return lib().orc_row_bytes(_tid(t), n_per_row)
+
+
+def row_sigma2(x) -> np.float32:
+    x = _f32(x)
+    return np.float32(lib().orc_row_sigma2(x, x.size))
+
+
+def row_sigma2_f64(x) -> float:
+    x = _f32(x)
+    return float(lib().orc_row_sigma2_f64(x, x.size))
+
+
+def row_weights(x, q, sigma2) -> np.ndarray:
+    x = _f32(x)
+    qq = None if q is None else _f32(q)
+    w = np.empty_like(x)
+    lib().orc_row_weights(x, _ptr(qq), x.size, np.float32(sigma2), w)
+    return w
+
+
+def solve_sym(x, w, nmax, K=None, F=None):
+    """Returns (levels int8 in [-nmax, nmax-1], d, info)."""
+    c = solver_constants()
+    K = c["sym_cand"] if K is None else K
+    F = c["sym_flip_passes"] if F is None else F
+    x, w = _f32(x), _f32(w)
+    l = np.zeros(x.size, np.int8)
+    d = np.zeros(1, np.float32)
+    info = np.zeros(4, np.int32)
+    rc = lib().orc_solve_sym(x.size, x, w, nmax, K, F, l, d, info)
+    if rc != 0:
+        raise ValueError("orc_solve_sym: invalid arguments")
+    return l, d[0], info
+
+
+def solve_asym(x, w, nmax, K=None, F=None, k4=False):
+    """Returns (levels uint8 in [0, nmax], d, m, info)."""
+    c = solver_constants()
+    K = c["asym_cand"] if K is None else K
+    F = c["asym_flip_passes"] if F is None else F
+    x, w = _f32(x), _f32(w)
+    l = np.zeros(x.size, np.uint8)
+    d = np.zeros(1, np.float32)
+    m = np.zeros(1, np.float32)
+    info = np.zeros(4, np.int32)
+    rc = lib().orc_solve_asym(x.size, x, w, nmax, K, F, int(k4), l, d, m, info)
+    if rc != 0:
+        raise ValueError("orc_solve_asym: invalid arguments")
+    return l, d[0], m[0], info
+
+
+def _rows_parallel(n_rows, fn, threads):
+    """Runs fn(r0, r1) over contiguous row ranges on `threads` threads
+    (ctypes releases the GIL during each foreign call)."""
+    threads = max(1, min(threads, n_rows)) if n_rows else 1
+    bounds = np.linspace(0, n_rows, threads + 1).astype(np.int64)
+    if threads == 1:
+        fn(0, n_rows)
+        return
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda i: fn(int(bounds[i]), int(bounds[i + 1])),
+                    range(threads)))
+
+
+def quantize_rows(t, x, imatrix=None, threads: int = 1) -> np.ndarray:
+    """x: [n_rows, n_per_row] float32. Returns uint8 [n_rows, row_bytes]."""
+    t = _tid(t)
+    x = _f32(x)
+    n_rows, n = x.shape
+    rb = row_bytes(t, n)
+    if rb == 0:
+        raise ValueError("n_per_row is not a multiple of the block length")
+    q = None if imatrix is None else _f32(imatrix)
+    out = np.zeros((n_rows, rb), np.uint8)
+
+    def run(r0, r1):
+        if r1 > r0:
+            rc = lib().orc_quantize_rows(t, _ptr(x[r0:r1]), _ptr(q), r1 - r0,
+                                         n, _ptr(out[r0:r1]))
+            if rc != 0:
+                raise ValueError("orc_quantize_rows failed")
+
+    _rows_parallel(n_rows, run, threads)
+    return out
+
+
+def quantize_rows_grouped(t, x, imatrix, rows_per_group: int,
+                          threads: int = 1) -> np.ndarray:
+    """x: [n_groups*rows_per_group, n] float32; imatrix: [n_groups, n]."""
+    t = _tid(t)
+    x = _f32(x)
+    q = _f32(imatrix)
+    n_rows, n = x.shape
+    rb = row_bytes(t, n)
+    out = np.zeros((n_rows, rb), np.uint8)
+
+    def run(r0, r1):
+        # rows [r0, r1) split at group boundaries
+        r = r0
+        while r < r1:
+            g = r // rows_per_group
+            e = min(r1, (g + 1) * rows_per_group)
+            rc = lib().orc_quantize_rows(t, _ptr(x[r:e]), _ptr(q[g]), e - r, n,
+                                         _ptr(out[r:e]))
+            if rc != 0:
+                raise ValueError("orc_quantize_rows failed")
+            r = e
+
+    _rows_parallel(n_rows, run, threads)
+    return out
+
+
+def quantize_row_sigma2(t, x, q, sigma2) -> np.ndarray:
+    t = _tid(t)
+    x = _f32(x).ravel()
+    qq = None if q is None else _f32(q)
+    out = np.zeros(row_bytes(t, x.size), np.uint8)
+    rc = lib().orc_quantize_row_sigma2(t, x, _ptr(qq), x.size,
+                                       np.float32(sigma2), out)
+    if rc != 0:
+        raise ValueError("orc_quantize_row_sigma2 failed")
+    return out
+
+
+def quantize_q8k128(x, threads: int = 1) -> np.ndarray:
+    x = _f32(x)
+    n_rows, n = x.shape
+    rb = row_bytes(Q8_K128, n)
+    if rb == 0:
+        raise ValueError("n_per_row is not a multiple of 128")
+    out = np.zeros((n_rows, rb), np.uint8)
+
+    def run(r0, r1):
+        if r1 > r0:
+            lib().orc_quantize_q8k128(_ptr(x[r0:r1]), r1 - r0, n,
+                                      _ptr(out[r0:r1]))
+
+    _rows_parallel(n_rows, run, threads)
+    return out
+
+
+def dequantize_rows(t, packed, n_rows: int, n_per_row: int) -> np.ndarray:
+    t = _tid(t)
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    if p.size != n_rows * row_bytes(t, n_per_row):
+        raise ValueError("packed buffer has the wrong size")
+    out = np.zeros((n_rows, n_per_row), np.float32)
+    rc = lib().orc_dequantize_rows(t, _ptr(p), n_rows, n_per_row, _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_dequantize_rows failed")
+    return out
+
+
+def f32_to_f16_bits(v: float) -> int:
+    return int(lib().orc_f32_to_f16(np.float32(v)))
+
+
+def f16_bits_to_f32(h: int) -> float:
+    return float(lib().orc_f16_to_f32(int(h)))

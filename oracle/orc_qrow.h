@@ -1,0 +1,104 @@
+/*
+ * orc_qrow.h -- declarations of the CPU oracle (test infrastructure only).
+ *
+ * The oracle is a plain, slow, single-threaded C implementation of
+ * importance-matrix-weighted row quantization. It exists to check the GPU
+ * library. Only the test-suite, the package smoke check and the benchmark's
+ * CPU-baseline leg may load it; the GPU library never does, and the two share
+ * no code, headers or tables. Every constant below is the oracle's own copy.
+ *
+ * Floating-point contract: compiled with -ffp-contract=off and without
+ * -ffast-math, so every float operation is one IEEE-754 binary32 operation
+ * rounded to nearest-even, and fused multiply-adds appear only where fmaf()
+ * is written.
+ */
+#ifndef ORC_QROW_H
+#define ORC_QROW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Output formats (values fixed; the GPU library's enum must match). */
+enum {
+    ORC_Q4_0 = 0,    /* 32 weights, levels -8..7, fp32 scale              20 B */
+    ORC_Q4_1 = 1,    /* 32 weights, levels 0..15, fp32 scale + fp32 min   24 B */
+    ORC_Q5_0 = 2,    /* 32 weights, levels -16..15, fp32 scale            24 B */
+    ORC_Q5_1 = 3,    /* 32 weights, levels 0..31, fp32 scale + fp32 min   28 B */
+    ORC_Q4_K = 4,    /* 256 weights, 8x32 sub-blocks, 6-bit sc/mn, fp16 d 144 B */
+    ORC_Q8_K128 = 5  /* 128 activations, fp32 d, int8, int16 sums/32     140 B */
+};
+
+/* Solver constants (the oracle's own copy). */
+#define ORC_CAND_STEP       0.25f /* spacing of the trial scales, in levels   */
+#define ORC_SYM_CAND        5     /* trial scales, symmetric blocks           */
+#define ORC_SYM_FLIP_PASSES 2     /* greedy flip passes, symmetric blocks     */
+#define ORC_ASYM_CAND       3     /* trial scales, asymmetric blocks          */
+#define ORC_ASYM_FLIP_PASSES 1    /* greedy flip passes, asymmetric blocks    */
+
+/* Return codes. */
+#define ORC_OK       0
+#define ORC_EINVAL  -1
+
+/* Fills c[0..5] = {step*4 (as int), sym cand, sym passes, asym cand,
+ * asym passes, max block length}; lets a test compare the two copies. */
+void orc_solver_constants(int32_t *c);
+
+size_t orc_block_bytes(int type);
+int    orc_block_elems(int type);
+size_t orc_row_bytes(int type, int64_t n_per_row);   /* 0 if invalid */
+
+/* Row statistic: sigma2 = (sum of x^2 in double) / n, rounded once to float.
+ * orc_row_sigma2_f64 returns the value before that last rounding. */
+float  orc_row_sigma2(const float *x, int64_t n);
+double orc_row_sigma2_f64(const float *x, int64_t n);
+
+/* Element importances w_j = q_j * sqrtf(fmaf(x_j, x_j, sigma2)); q == NULL
+ * means q_j = 1. */
+void orc_row_weights(const float *x, const float *q, int64_t n, float sigma2,
+                     float *w);
+
+/* Block solvers on n <= 256 elements with explicit weights w.
+ * info[0] = index of the winning trial scale (-1: zero block),
+ * info[1] = flips accepted, info[2] = passes run,
+ * info[3] = 1 if the last pass run accepted nothing (converged).
+ * Symmetric: levels l in [-nmax, nmax-1] returned in l_out (signed).
+ * Asymmetric: levels in [0, nmax]; k4 != 0 selects the Q4_K sub-block rules
+ * (range widened to include 0, offset m <= 0). */
+int orc_solve_sym(int n, const float *x, const float *w, int nmax, int K, int F,
+                  int8_t *l_out, float *d_out, int32_t *info);
+int orc_solve_asym(int n, const float *x, const float *w, int nmax, int K,
+                   int F, int k4, uint8_t *l_out, float *d_out, float *m_out,
+                   int32_t *info);
+
+/* Weight-row quantizers: x is [n_rows, n_per_row] fp32 row-major; imatrix
+ * is [n_per_row] (or NULL); out holds n_rows * orc_row_bytes() bytes. */
+int orc_quantize_rows(int type, const float *x, const float *imatrix,
+                      int64_t n_rows, int64_t n_per_row, uint8_t *out);
+/* Grouped: imatrix is [n_groups, n_per_row]; row r uses group r / rpg. */
+int orc_quantize_rows_grouped(int type, const float *x, const float *imatrix,
+                              int64_t n_groups, int64_t rows_per_group,
+                              int64_t n_per_row, uint8_t *out);
+/* One row with the row statistic supplied by the caller. */
+int orc_quantize_row_sigma2(int type, const float *x, const float *q,
+                            int64_t n_per_row, float sigma2, uint8_t *out);
+
+/* Q8_K_128 activation quantizer. */
+int orc_quantize_q8k128(const float *x, int64_t n_rows, int64_t n_per_row,
+                        uint8_t *out);
+
+/* Decoder for every format above. */
+int orc_dequantize_rows(int type, const uint8_t *in, int64_t n_rows,
+                        int64_t n_per_row, float *out);
+
+/* IEEE-754 binary16 conversions (round to nearest-even, subnormals kept). */
+uint16_t orc_f32_to_f16(float f);
+float    orc_f16_to_f32(uint16_t h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
