@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Benchmark of the importance-weighted row quantizer on one MI355X.
+
+Headline workload: Q4_K quantization of an 11008 x 4096 fp32 FFN weight matrix
+(x = s_r * 0.015*N(0,1), per-row scale s_r ~ LogNormal(0, 0.3), per-column
+importance LogNormal(0, 1.5); synthetic, seeded). One step = one call of
+qr_quantize_rows over the whole matrix: load, row statistic, importances,
+trial scales, least squares, flips, super-block scales, packing.
+
+Protocol: W untimed warm-up steps, then K timed steps. Before every step a
+1 GiB buffer is overwritten (outside the timed interval) so that neither L2
+nor the 256 MB Infinity Cache holds the input. Each step is bracketed by HIP
+events recorded on the stream the kernel is launched on; ms_per_step is
+their mean. The whole loop is bracketed by torch.cuda.synchronize().
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "Gweights/s quantized (Q4_0, Q4_K) + achieved HBM GB/s fraction"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed_steps(fn, steps, warmup, flush):
+    import torch
+    for _ in range(warmup):
+        flush.fill_(1.0)
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush.fill_(float(i))
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(ms) / len(ms), min(ms), wall
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the secondary workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
+              "is not supported (rows are independent, see the sharding notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from post_weight_quantization_row_amd import qrow, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    qrow.load_library()
+    dev = torch.device("cuda:0")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+
+    # ---- headline: Q4_K, 11008 x 4096 fp32
+    n_rows, n = 11008, 4096
+    x, q = synth.torch_q4_k_matrix(dev, n_rows, n)
+    rb = qrow.qr_row_bytes("q4_k", n)
+    out = torch.empty((n_rows, rb), dtype=torch.uint8, device=dev)
+    step = lambda: qrow.qr_quantize_rows("q4_k", x, q, out=out)
+    log(f"q4_k {n_rows}x{n}: warmup {args.warmup}, steps {args.steps}")
+    ms, ms_min, wall = timed_steps(step, args.steps, args.warmup, flush)
+    weights = n_rows * n
+    alg_bytes = weights * 4 + n * 4 + n_rows * rb
+    gws = weights / (ms * 1e-3) / 1e9
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    torch.cuda.synchronize()
+    # back-to-back (input may stay in the Infinity Cache), for context only
+    t = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_b2b = (time.perf_counter() - t) * 1e3 / args.steps
+
+    result = {
+        "metric": METRIC,
+        "value": round(gws, 3),
+        "unit": "Gweights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "q4_k_11008x4096", "type": "q4_k",
+                   "n_rows": n_rows, "n_per_row": n, "src": "f32",
+                   "imatrix": "LogNormal(0,1.5) per column",
+                   "cache_flush_between_steps": "1 GiB"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "k_quantize_rows<Q4_K,f32>",
+                     "bytes_per_launch": alg_bytes},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "ms_per_step_min": round(ms_min, 5),
+        "ms_per_step_back_to_back": round(ms_b2b, 5),
+        "wall_s_timed_loop": round(wall, 4),
+    }
+
+    # ---- CPU baseline: the oracle on the same matrix (it also checks parity)
+    if not args.no_cpu_baseline:
+        import oracle
+        xh = x.cpu().numpy()
+        qh = q.cpu().numpy()
+        threads = min(16, os.cpu_count() or 1)
+        log(f"cpu baseline: oracle on the full matrix, {threads} threads")
+        t = time.perf_counter()
+        ref = oracle.quantize_rows("q4_k", xh, qh, threads=threads)
+        dt = time.perf_counter() - t
+        same = np.array_equal(ref, out.cpu().numpy())
+        result["cpu_baseline"] = {
+            "value": round(weights / dt / 1e9, 5), "unit": "Gweights/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "the full 11008x4096 matrix, one pass",
+            "seconds": round(dt, 3)}
+        result["parity_vs_oracle"] = "bit-identical" if same else "DIFFERS"
+
+    # ---- secondary workloads (one line of numbers each)
+    if not args.no_extra:
+        extra = {}
+        x0, q0 = synth.q4_0_matrix()
+        x0d, q0d = torch.from_numpy(x0).to(dev), torch.from_numpy(q0).to(dev)
+        o0 = torch.empty((2048, qrow.qr_row_bytes("q4_0", 2048)), dtype=torch.uint8, device=dev)
+        m0, _, _ = timed_steps(lambda: qrow.qr_quantize_rows("q4_0", x0d, q0d, out=o0), 10, 2, flush)
+        b0 = 2048 * 2048 * 4 + 2048 * 4 + o0.numel()
+        extra["q4_0_2048x2048"] = {"ms": round(m0, 5), "Gweights/s": round(2048 * 2048 / m0 / 1e6, 3),
+                                   "hbm_frac": round(b0 / (m0 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        xa, _ = synth.q8_k128_activations()
+        xad = torch.from_numpy(xa).to(dev)
+        oa = torch.empty((8192, qrow.qr_row_bytes("q8_k128", 7168)), dtype=torch.uint8, device=dev)
+        ma, _, _ = timed_steps(lambda: qrow.qr_quantize_activations_q8k128(xad, out=oa), 10, 2, flush)
+        ba = xa.nbytes + oa.numel()
+        extra["q8_k128_8192x7168"] = {"ms": round(ma, 5), "Gvalues/s": round(xa.size / ma / 1e6, 3),
+                                      "hbm_frac": round(ba / (ma * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        y = torch.empty((n_rows, n), dtype=torch.float32, device=dev)
+        md, _, _ = timed_steps(lambda: qrow.qr_dequantize_rows("q4_k", out, n_rows, n, out=y), 10, 2, flush)
+        bd = out.numel() + y.numel() * 4
+        extra["dequantize_q4_k_11008x4096"] = {"ms": round(md, 5),
+                                               "hbm_frac": round(bd / (md * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        result["extra"] = extra
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * qrow.h -- C-ABI of libqrow.so: importance-matrix-weighted row quantization
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages (cited by title and section):
+ *  [WT] "ik_llama.cpp 量化权重之谜：weight[j] = qw[j] * sqrtf(sigma2 + xb[j]*xb[j])
+ *       的由来与原理", section 一: per row, sigma2 is the mean of x^2; each element
+ *       gets the importance w = qw * sqrt(sigma2 + x^2), qw being the imatrix
+ *       (diagonal Hessian estimate) entry of its column; each block's scale is
+ *       the weighted least-squares value sumlx/suml2, refined by greedy level
+ *       flips along g = scale*w*(x - scale*l).
+ *  [KQ] "3.2 K-quants 与重要性矩阵：量化兵器谱", section 一: the Q4_K super-block.
+ *  [LQ] "从零理解 LLM 量化 PTQ、QAT 与 ik_llama.cpp 量化体系的源码级导学",
+ *       section 2.1: the legacy 32-weight blocks Q4_0, Q4_1, Q5_0, Q5_1.
+ *  [Q8] "ik_llama.cpp 量化精度修复实录：用 Q8_K_128 替代 Q8_1 …", section 修复方案:
+ *       the Q8_K_128 activation block; the row length must be a multiple of
+ *       128.
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are caller-owned DEVICE pointers (HIP device memory or
+ *    managed memory visible to the current device), 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL: the default stream). Every call only
+ *    enqueues work on that stream and returns; the caller synchronizes.
+ *  - The library allocates no device memory and keeps no state between
+ *    calls, except the thread-local error string.
+ *  - Rows are stored contiguously (row-major, no padding); the packed output
+ *    of a row is qr_row_bytes(type, n_per_row) bytes and row r starts at
+ *    byte r * qr_row_bytes(type, n_per_row).
+ *  - Return value 0 on success, a negative QR_E* code on failure. On failure
+ *    nothing is launched and qr_last_error() describes the problem.
+ *  - n_rows == 0 is a successful no-op.
+ *  - Inputs must be finite. Importances must be finite and >= 0 (they are
+ *    sums of squared activations); this is not checked on the device.
+ *
+ * Packed block layouts (little-endian; the pages give bit widths, these byte
+ * layouts are this library's):
+ *  Q4_0  20 B: f32 d | u8 qs[16]            levels l in -8..7,  code u = l+8
+ *  Q4_1  24 B: f32 d | f32 m | u8 qs[16]    levels 0..15,       x ~ d*u + m
+ *  Q5_0  24 B: f32 d | u32 qh | u8 qs[16]   levels -16..15,     u = l+16
+ *  Q5_1  28 B: f32 d | f32 m | u32 qh | u8 qs[16]   levels 0..31
+ *     qs[i] holds u_i (low nibble) and u_{i+16} (high nibble); bit i of qh
+ *     is bit 4 of u_i.
+ *  Q4_K 144 B per 256: f16 d | f16 dmin | sc[8] as 6-bit fields in 6 B |
+ *     mn[8] as 6-bit fields in 6 B | u8 qs[128]; field j sits at bit 6j;
+ *     sub-block j (32 weights) uses qs[16j .. 16j+15] as above and decodes
+ *     to (d*sc_j)*u - dmin*mn_j.
+ *  Q8_K128 140 B per 128: f32 d | i8 q[128] | i16 bsum[4]; bsum[g] is the
+ *     plain sum of q[32g .. 32g+31], not multiplied by d.
+ */
+#ifndef QROW_H
+#define QROW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QR_Q4_0 = 0,
+    QR_Q4_1 = 1,
+    QR_Q5_0 = 2,
+    QR_Q5_1 = 3,
+    QR_Q4_K = 4,
+    QR_Q8_K128 = 5
+} qr_type;
+
+typedef enum { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
+
+#define QR_OK            0
+#define QR_EINVAL_TYPE  -1  /* unknown type, or a type the call does not take */
+#define QR_EINVAL_SHAPE -2  /* n_per_row not a positive multiple of the block
+                               length (32, 256 or 128), above the supported
+                               maximum, or a negative count                   */
+#define QR_EINVAL_PTR   -3  /* NULL or misaligned pointer with n_rows > 0    */
+#define QR_EOVERFLOW    -4  /* a size computation overflows                  */
+#define QR_EDEVICE      -5  /* the HIP runtime reported an error            */
+
+/* Largest supported row: the row is staged on chip while its blocks are
+ * solved. */
+#define QR_MAX_ROW_F32   32768
+#define QR_MAX_ROW_BF16  65536
+
+/*
+ * qr_quantize_rows -- importance-weighted quantization of weight rows [WT 一],
+ * [KQ 一], [LQ 2.1].
+ *  t        QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1 or QR_Q4_K (else EINVAL_TYPE).
+ *  src      QR_F32 or QR_BF16: element type of x.
+ *  x        [n_rows, n_per_row] weights, row-major.
+ *  imatrix  [n_per_row] fp32 importances shared by all rows, or NULL for
+ *           unit importances.
+ *  out      n_rows * qr_row_bytes(t, n_per_row) bytes, written completely.
+ * Per row: sigma2 = (sum x^2, accumulated in double) / n_per_row rounded to
+ * float; w_j = imatrix[j] * sqrtf(fmaf(x_j, x_j, sigma2)); a 32-weight group
+ * whose w are all zero uses imatrix = 1 instead. Each 32-weight block (Q4_K:
+ * sub-block) is fitted by a trial-scale search, the weighted least-squares
+ * scale (and offset), and greedy flip passes; Q4_K then quantizes the eight
+ * sub-scales and offsets to 6 bits under fp16 super-scales and re-rounds the
+ * levels. The results are bit-identical to the CPU oracle of this project.
+ */
+int qr_quantize_rows(int t, int src, const void *x, const float *imatrix,
+                     int64_t n_rows, int64_t n_per_row, void *out,
+                     void *stream);
+
+/*
+ * qr_quantize_rows_grouped -- as qr_quantize_rows for a stack of matrices
+ * that share a shape but not an imatrix (e.g. the experts of an MoE layer),
+ * in one launch. x is [n_groups * rows_per_group, n_per_row]; imatrix is
+ * [n_groups, n_per_row] (or NULL); row r uses imatrix row r / rows_per_group.
+ */
+int qr_quantize_rows_grouped(int t, int src, const void *x,
+                             const float *imatrix, int64_t n_groups,
+                             int64_t rows_per_group, int64_t n_per_row,
+                             void *out, void *stream);
+
+/*
+ * qr_quantize_activations_q8k128 -- the Q8_K_128 activation quantizer
+ * [Q8 修复方案]. Per 128 values: amax = max |x|; codes q = rint(x * (127/amax))
+ * in -127..127; d = amax / 127 stored as f32; bsum[g] = sum of 32 codes as
+ * int16, not multiplied by d. An all-zero block (or one whose 127/amax is
+ * not finite) stores d = 0 and zero codes. n_per_row must be a multiple of
+ * 128. x is fp32 or bf16 [n_rows, n_per_row]; out holds
+ * n_rows * qr_row_bytes(QR_Q8_K128, n_per_row) bytes.
+ */
+int qr_quantize_activations_q8k128(int src, const void *x, int64_t n_rows,
+                                   int64_t n_per_row, void *out, void *stream);
+
+/*
+ * qr_dequantize_rows -- decoder for every type above. in is the packed
+ * [n_rows, qr_row_bytes(t, n_per_row)] buffer; out is fp32
+ * [n_rows, n_per_row]. Symmetric blocks decode to d*(u - nmax), asymmetric
+ * ones to fmaf(d, u, m), Q4_K to fmaf(f32(d)*sc, u, -(f32(dmin)*mn)), Q8_K128
+ * to d*q.
+ */
+int qr_dequantize_rows(int t, const void *in, int64_t n_rows,
+                       int64_t n_per_row, float *out, void *stream);
+
+/* Packed bytes of one row; 0 if t is unknown or n_per_row is not a
+ * non-negative multiple of the block length. */
+size_t qr_row_bytes(int t, int64_t n_per_row);
+
+/* Elements per block: 32, 256 or 128; 0 for an unknown type. */
+int qr_block_elems(int t);
+
+/* Fills c[0..5] = {4 * trial-scale step, symmetric trials, symmetric flip
+ * passes, asymmetric trials, asymmetric flip passes, 32}: the solver
+ * constants compiled into the library. */
+void qr_solver_constants(int32_t *c);
+
+/* Message for the last failing call on this thread ("" if none). Valid
+ * until the next call on the same thread. */
+const char *qr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -352,9 +352,14 @@ int orc_solve_asym(int n, const float *x, const float *w, int nmax, int K,
     const float lo_level = 0.0f, hi_level = (float)nmax;
     int32_t inf_local[4] = {-1, 0, 0, 1};
 
+    /* Range of the block. Comparisons (not fminf/fmaxf) keep the first of two
+     * equal values, so the sign of a zero bound is fixed. */
     float lo = x[0], hi = x[0];
-    for (int i = 1; i < n; ++i) { lo = fminf(lo, x[i]); hi = fmaxf(hi, x[i]); }
-    if (k4) lo = fminf(lo, 0.0f);   /* Q4_K stores the offset as -dmin*mn, mn >= 0 */
+    for (int i = 1; i < n; ++i) {
+        lo = (x[i] < lo) ? x[i] : lo;
+        hi = (x[i] > hi) ? x[i] : hi;
+    }
+    if (k4) lo = (0.0f < lo) ? 0.0f : lo;  /* Q4_K stores the offset as -dmin*mn, mn >= 0 */
 
     float Sw = 0.0f, Sx = 0.0f;
     for (int i = 0; i < n; ++i) {
@@ -506,8 +511,8 @@ static void quantize_q4k(const float *x, const float *w, uint8_t *out)
         float d, m;
         orc_solve_asym(32, x + 32 * j, w + 32 * j, 15, ORC_ASYM_CAND,
                        ORC_ASYM_FLIP_PASSES, 1, l, &d, &m, NULL);
-        a[j] = fmaxf(d, 0.0f);
-        b[j] = fmaxf(-m, 0.0f);
+        a[j] = d > 0.0f ? d : 0.0f;
+        b[j] = -m > 0.0f ? -m : 0.0f;
     }
     float amx = a[0], bmx = b[0];
     for (int j = 1; j < 8; ++j) { amx = fmaxf(amx, a[j]); bmx = fmaxf(bmx, b[j]); }

@@ -1,0 +1,878 @@
+// qrow.hip -- gfx950 kernels and the C-ABI of libqrow.so.
+//
+// Importance-matrix-weighted row quantization, following these pages (cited
+// by title and section):
+//  [WT] "ik_llama.cpp 量化权重之谜：weight[j] = qw[j] * sqrtf(sigma2 + xb[j]*xb[j])
+//       的由来与原理", section 一: row statistic sigma2, element importance
+//       qw*sqrt(sigma2 + x^2), least-squares block scale sumlx/suml2 and
+//       greedy level flips along g = scale*w*(x - scale*l).
+//  [KQ] "3.2 K-quants 与重要性矩阵：量化兵器谱", section 一: Q4_K super-block.
+//  [LQ] "从零理解 LLM 量化 PTQ、QAT 与 ik_llama.cpp 量化体系的源码级导学", 2.1:
+//       legacy 32-weight blocks.
+//  [Q8] "ik_llama.cpp 量化精度修复实录：用 Q8_K_128 替代 Q8_1 …", 修复方案:
+//       Q8_K_128 activation blocks.
+//
+// Execution model (gfx950, wave64):
+//  * Weight rows: one workgroup of one wave per row. The wave streams the
+//    row from HBM once with coalesced 16-byte loads into LDS (32-element
+//    groups padded to a 16-byte multiple so that per-lane group reads are
+//    bank-conflict free) while accumulating sum x^2 in double; a wave
+//    reduction gives sigma2. Each lane then owns one 32-element group at a
+//    time and solves it entirely in VGPRs: importances, trial scales,
+//    least-squares sums, the sequential flip passes (sequential within a
+//    lane, parallel across the 64 lanes), packing. For Q4_K, eight
+//    consecutive lanes hold the eight sub-blocks of one super-block and
+//    combine their scales with cross-lane shuffles.
+//  * Activations (Q8_K_128) and the decoders are streaming kernels: 32 lanes
+//    per 128-value block (one float4 each), several blocks in flight per
+//    wave.
+//
+// Numerics: every float operation that decides a code is written out
+// explicitly (fmaf where fused, no contraction: built with
+// -ffp-contract=off), divisions and square roots are correctly rounded, and
+// sums run in ascending element order inside one lane, so the outputs are
+// bit-identical to a sequential single-precision evaluation of the same
+// steps. The row sum of x^2 is accumulated in double; only the order of its
+// additions differs from a sequential sum, which can move sigma2 by one ulp
+// when the double sum lies within a few units of its last place of a float
+// rounding boundary.
+
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "qrow.h"
+
+namespace {
+
+// native vector types (usable with the nontemporal builtins)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+constexpr int QK = 32;                  // weights per fitted group
+constexpr int LDS_F32_STRIDE = 36;      // floats per staged group (32 + pad)
+constexpr int LDS_BF16_STRIDE = 40;     // bf16 per staged group (32 + pad)
+
+// Solver constants: trial-scale spacing and counts, flip passes.
+constexpr float CAND_STEP = 0.25f;
+constexpr int SYM_CAND = 5;
+constexpr int SYM_FLIP_PASSES = 2;
+constexpr int ASYM_CAND = 3;
+constexpr int ASYM_FLIP_PASSES = 1;
+
+// Trial k uses (nmax + CAND_STEP * offset(k)): 0, -1, +1, -2, +2.
+__host__ __device__ constexpr int cand_offset(int k) {
+  return k == 0 ? 0 : ((k & 1) ? -((k + 1) / 2) : k / 2);
+}
+
+__device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ float rne(float v) { return __builtin_rintf(v); }
+__device__ __forceinline__ float med3(float v, float lo, float hi) {
+  return __builtin_amdgcn_fmed3f(v, lo, hi);
+}
+__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Correctly rounded square root for t in [2^-96, FLT_MAX]: the hardware
+// square root (within one ulp) is corrected to the nearest float by testing
+// the residuals against its two neighbours (Tuckerman's test, exact with
+// fused multiply-adds). Outside that range the library sqrtf is used.
+__device__ __forceinline__ float sqrt_cr(float t, bool normal_range) {
+  if (!normal_range) return sqrtf(t);
+  float s = __builtin_amdgcn_sqrtf(t);
+  float sdn = __builtin_bit_cast(float, __builtin_bit_cast(int32_t, s) - 1);
+  float sup = __builtin_bit_cast(float, __builtin_bit_cast(int32_t, s) + 1);
+  float rdn = fma_(-sdn, s, t);
+  float rup = fma_(-sup, s, t);
+  s = (rdn <= 0.0f) ? sdn : s;
+  s = (rup > 0.0f) ? sup : s;
+  return s;
+}
+
+// -------------------------------------------------------------------------
+// row staging and the row statistic [WT 一]
+
+template <bool BF16>
+__device__ __forceinline__ double stage_row(const void* __restrict__ xrow, int n, void* lds, int lane) {
+  double acc = 0.0;
+  if (!BF16) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(xrow);
+    float* dst = reinterpret_cast<float*>(lds);
+    const int n4 = n >> 2;
+#pragma unroll 4
+    for (int i = lane; i < n4; i += WAVE) {
+      f32x4 v = __builtin_nontemporal_load(src + i);
+      const int e = i << 2;
+      *reinterpret_cast<f32x4*>(dst + (e >> 5) * LDS_F32_STRIDE + (e & 31)) = v;
+      acc = __builtin_fma((double)v.x, (double)v.x, acc);
+      acc = __builtin_fma((double)v.y, (double)v.y, acc);
+      acc = __builtin_fma((double)v.z, (double)v.z, acc);
+      acc = __builtin_fma((double)v.w, (double)v.w, acc);
+    }
+  } else {
+    const u32x4* src = reinterpret_cast<const u32x4*>(xrow);
+    uint16_t* dst = reinterpret_cast<uint16_t*>(lds);
+    const int n8 = n >> 3;
+#pragma unroll 4
+    for (int i = lane; i < n8; i += WAVE) {
+      u32x4 v = __builtin_nontemporal_load(src + i);
+      const int e = i << 3;
+      *reinterpret_cast<u32x4*>(dst + (e >> 5) * LDS_BF16_STRIDE + (e & 31)) = v;
+      const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double a = (double)__builtin_bit_cast(float, p[k] << 16);
+        const double b = (double)__builtin_bit_cast(float, p[k] & 0xffff0000u);
+        acc = __builtin_fma(a, a, acc);
+        acc = __builtin_fma(b, b, acc);
+      }
+    }
+  }
+  // wave reduction of the double partial sums
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, WAVE);
+  return acc;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load_group(const void* lds, int g, float (&x)[QK]) {
+  if (!BF16) {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(lds) + g * LDS_F32_STRIDE);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float4 v = p[k];
+      x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(lds) + g * LDS_BF16_STRIDE);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint4 v = p[k];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        x[8 * k + 2 * h] = __builtin_bit_cast(float, w4[h] << 16);
+        x[8 * k + 2 * h + 1] = __builtin_bit_cast(float, w4[h] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// Importances of one 32-weight group [WT 一]: w = q * sqrt(fma(x, x, sigma2)),
+// q taken from the element's own column; a group whose importances are all
+// zero uses q = 1.
+__device__ __forceinline__ void group_weights(const float (&x)[QK], const float* __restrict__ q,
+                                              float sigma2, bool normal_range, float (&w)[QK]) {
+  float s[QK];
+#pragma unroll
+  for (int i = 0; i < QK; ++i) s[i] = sqrt_cr(fma_(x[i], x[i], sigma2), normal_range);
+  if (q) {
+    const float4* q4 = reinterpret_cast<const float4*>(q);
+    uint32_t any = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float4 v = q4[k];
+      w[4 * k] = v.x * s[4 * k];
+      w[4 * k + 1] = v.y * s[4 * k + 1];
+      w[4 * k + 2] = v.z * s[4 * k + 2];
+      w[4 * k + 3] = v.w * s[4 * k + 3];
+    }
+#pragma unroll
+    for (int i = 0; i < QK; ++i) any |= fbits(w[i]) & 0x7fffffffu;
+    if (any == 0) {
+#pragma unroll
+      for (int i = 0; i < QK; ++i) w[i] = s[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < QK; ++i) w[i] = s[i];
+  }
+}
+
+// -------------------------------------------------------------------------
+// greedy flip passes [WT 一]
+//
+// Fit y ~ d*l with d = A/B, A = sum w y l, B = sum w l^2. Element j moves one
+// level along s = sign(A) * sign(y_j*B - l_j*A) (the sign of the pages'
+// gradient); the move is kept iff A'^2 * B > A^2 * B' and B' > 0, with
+// A' = A + s*w_j*y_j and B' = B + w_j*(2*s*l_j + 1). A pass that keeps no
+// move ends the loop for the wave; lanes that kept none repeat a pass whose
+// every decision is unchanged, so their result is the same.
+template <int F>
+__device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&w)[QK], const float (&wy)[QK],
+                                            float lo, float hi, float (&L)[QK], float& A_io, float& B_io) {
+  float A = A_io, B = B_io;
+#pragma unroll 1
+  for (int p = 0; p < F; ++p) {
+    bool changed = false;
+#pragma unroll
+    for (int j = 0; j < QK; ++j) {
+      const float t = L[j] * A;
+      const float e = fma_(y[j], B, -t);
+      const float s = ((fbits(A) ^ fbits(e)) & 0x80000000u) ? -1.0f : 1.0f;
+      const float lp = L[j] + s;
+      const float A1 = fma_(s, wy[j], A);
+      const float B1 = fma_(w[j], fma_(2.0f * s, L[j], 1.0f), B);
+      const bool keep = ((A1 * A1) * B > (A * A) * B1) && (B1 > 0.0f) && (lp >= lo) && (lp <= hi);
+      A = keep ? A1 : A;
+      B = keep ? B1 : B;
+      L[j] = keep ? lp : L[j];
+      changed |= keep;
+    }
+    if (!__any(changed)) break;
+  }
+  A_io = A;
+  B_io = B;
+}
+
+// -------------------------------------------------------------------------
+// symmetric group: levels -NMAX .. NMAX-1, one scale
+
+template <int NMAX>
+__device__ __forceinline__ float solve_sym(const float (&x)[QK], const float (&w)[QK], float (&L)[QK]) {
+  constexpr float LO = (float)-NMAX, HI = (float)(NMAX - 1);
+  // element of largest magnitude, first one on ties
+  float amax = fabsf(x[0]), xm = x[0];
+#pragma unroll
+  for (int i = 1; i < QK; ++i) {
+    const float a = fabsf(x[i]);
+    const bool g = a > amax;
+    amax = g ? a : amax;
+    xm = g ? x[i] : xm;
+  }
+  float wx[QK];
+#pragma unroll
+  for (int i = 0; i < QK; ++i) wx[i] = w[i] * x[i];
+
+  // Trial scales: the largest element maps to -(NMAX + step*k); each trial
+  // is scored by sumlx^2/suml2, compared by cross multiplication in double.
+  bool have = false;
+  float bS1 = 0.0f, bS2 = 0.0f, bis = 0.0f;
+  if (amax > 0.0f) {
+#pragma unroll
+    for (int k = 0; k < SYM_CAND; ++k) {
+      const float c = (float)NMAX + CAND_STEP * (float)cand_offset(k);
+      const float is = -c / xm;
+      float S1 = 0.0f, S2 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < QK; ++i) {
+        const float l = med3(rne(x[i] * is), LO, HI);
+        S1 = fma_(wx[i], l, S1);
+        S2 = fma_(w[i] * l, l, S2);
+      }
+      const bool ok = __builtin_isfinite(is) && (S2 > 0.0f);
+      const bool better = ok && (!have || ((double)S1 * (double)S1) * (double)bS2 >
+                                              ((double)bS1 * (double)bS1) * (double)S2);
+      if (better) { have = true; bS1 = S1; bS2 = S2; bis = is; }
+    }
+  }
+  if (!have) {
+#pragma unroll
+    for (int i = 0; i < QK; ++i) L[i] = 0.0f;
+    return 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < QK; ++i) L[i] = med3(rne(x[i] * bis), LO, HI);
+  float A = bS1, B = bS2;
+  flip_passes<SYM_FLIP_PASSES>(x, w, wx, LO, HI, L, A, B);
+  return A / B;
+}
+
+// -------------------------------------------------------------------------
+// asymmetric group: levels 0 .. NMAX, x ~ d*l + m
+
+// Two-parameter weighted least squares in double from the five float sums;
+// returns the score sum w x^2 - error. Codes with weighted spread below
+// 2^-16 of sum w l^2 count as constant; K4 forbids a positive offset.
+template <bool K4>
+__device__ __forceinline__ void fit_dm(float Sw_, float Sx_, float Sl_, float Sll_, float Slx_,
+                                       double& d, double& m, double& score) {
+  const double Sw = Sw_, Sx = Sx_, Sl = Sl_, Sll = Sll_, Slx = Slx_;
+  const double D = Sw * Sll - Sl * Sl;
+  double dd, mm;
+  if (D > Sw * Sll * 0x1p-16) {
+    const double r = 1.0 / D;
+    dd = (Sw * Slx - Sl * Sx) * r;
+    mm = (Sll * Sx - Sl * Slx) * r;
+  } else {
+    dd = 0.0;
+    mm = Sx / Sw;
+  }
+  if (K4 && mm > 0.0) {
+    mm = 0.0;
+    dd = Sll > 0.0 ? Slx / Sll : 0.0;
+  }
+  d = dd;
+  m = mm;
+  score = dd * Slx + mm * Sx;
+}
+
+__device__ __forceinline__ void asym_sums(const float (&w)[QK], const float (&wx)[QK], const float (&L)[QK],
+                                          float& Sl, float& Sll, float& Slx) {
+  float a = 0.0f, b = 0.0f, c = 0.0f;
+#pragma unroll
+  for (int i = 0; i < QK; ++i) {
+    const float wl = w[i] * L[i];
+    a = a + wl;
+    b = fma_(wl, L[i], b);
+    c = fma_(wx[i], L[i], c);
+  }
+  Sl = a; Sll = b; Slx = c;
+}
+
+template <int NMAX, bool K4>
+__device__ __forceinline__ void solve_asym(const float (&x)[QK], const float (&w)[QK], float (&L)[QK],
+                                           float& d_out, float& m_out) {
+  constexpr float HI = (float)NMAX;
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int i = 1; i < QK; ++i) {
+    lo = (x[i] < lo) ? x[i] : lo;
+    hi = (x[i] > hi) ? x[i] : hi;
+  }
+  if (K4) lo = (0.0f < lo) ? 0.0f : lo;
+
+  float wx[QK], xs[QK];
+  float Sw = 0.0f, Sx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < QK; ++i) {
+    wx[i] = w[i] * x[i];
+    xs[i] = x[i] - lo;
+    Sw = Sw + w[i];
+    Sx = Sx + wx[i];
+  }
+  if (hi == lo || !(Sw > 0.0f)) {
+#pragma unroll
+    for (int i = 0; i < QK; ++i) L[i] = 0.0f;
+    d_out = 0.0f;
+    m_out = lo;
+    return;
+  }
+  const float range = hi - lo;
+  bool have = false;
+  float bis = 0.0f;
+  double bm = 0.0, bscore = 0.0;
+#pragma unroll
+  for (int k = 0; k < ASYM_CAND; ++k) {
+    const float is = ((float)NMAX + CAND_STEP * (float)cand_offset(k)) / range;
+#pragma unroll
+    for (int i = 0; i < QK; ++i) L[i] = med3(rne(xs[i] * is), 0.0f, HI);
+    float Sl, Sll, Slx;
+    asym_sums(w, wx, L, Sl, Sll, Slx);
+    double d, m, score;
+    fit_dm<K4>(Sw, Sx, Sl, Sll, Slx, d, m, score);
+    const bool ok = __builtin_isfinite(is);
+    if (ok && (!have || score > bscore)) { have = true; bis = is; bm = m; bscore = score; }
+  }
+  if (!have) {
+#pragma unroll
+    for (int i = 0; i < QK; ++i) L[i] = 0.0f;
+    d_out = 0.0f;
+    m_out = lo;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < QK; ++i) L[i] = med3(rne(xs[i] * bis), 0.0f, HI);
+
+  // flips with the offset of the winning trial held fixed, then a joint refit
+  const float mf = (float)bm;
+  float y[QK], wy[QK];
+  float A = 0.0f, B = 0.0f;
+#pragma unroll
+  for (int i = 0; i < QK; ++i) {
+    y[i] = x[i] - mf;
+    wy[i] = w[i] * y[i];
+    A = fma_(wy[i], L[i], A);
+    B = fma_(w[i] * L[i], L[i], B);
+  }
+  flip_passes<ASYM_FLIP_PASSES>(y, w, wy, 0.0f, HI, L, A, B);
+
+  float Sl, Sll, Slx;
+  asym_sums(w, wx, L, Sl, Sll, Slx);
+  double d, m, score;
+  fit_dm<K4>(Sw, Sx, Sl, Sll, Slx, d, m, score);
+  d_out = (float)d;
+  m_out = (float)m;
+}
+
+// -------------------------------------------------------------------------
+// packers
+
+// 32 codes in [0, 15] -> 16 bytes: byte i = u_i | u_{i+16} << 4.
+__device__ __forceinline__ uint4 pack_nibbles(const uint32_t (&u)[QK]) {
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = 4 * k + b;
+      v |= ((u[i] & 15u) | ((u[i + 16] & 15u) << 4)) << (8 * b);
+    }
+    o[k] = v;
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ uint32_t pack_high_bits(const uint32_t (&u)[QK]) {
+  uint32_t qh = 0;
+#pragma unroll
+  for (int i = 0; i < QK; ++i) qh |= ((u[i] >> 4) & 1u) << i;
+  return qh;
+}
+
+__device__ __forceinline__ void store_u32(uint8_t* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
+
+// -------------------------------------------------------------------------
+// weight-row kernel
+
+template <int TYPE, bool BF16>
+__global__ __launch_bounds__(WAVE) void k_quantize_rows(const void* __restrict__ x, const float* __restrict__ imatrix,
+                                                        int n_per_row, int64_t rows_per_group,
+                                                        uint8_t* __restrict__ out, int64_t row_bytes) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int n_groups = n_per_row / QK;
+  const size_t elem = BF16 ? 2 : 4;
+
+  const void* xrow = reinterpret_cast<const unsigned char*>(x) + (size_t)row * n_per_row * elem;
+  const double ss = stage_row<BF16>(xrow, n_per_row, lds_raw, lane);
+  const float sigma2 = (float)(ss / (double)n_per_row);
+  const bool normal_range = sigma2 >= 0x1p-96f && sigma2 <= 3.0e38f;
+  __syncthreads();
+
+  const float* q = imatrix ? imatrix + (row / rows_per_group) * (int64_t)n_per_row : nullptr;
+  uint8_t* orow = out + row * row_bytes;
+
+  for (int base = 0; base < n_groups; base += WAVE) {
+    const int g = base + lane;
+    if (g >= n_groups) continue;
+    float xv[QK], w[QK], L[QK];
+    load_group<BF16>(lds_raw, g, xv);
+    group_weights(xv, q ? q + g * QK : nullptr, sigma2, normal_range, w);
+
+    if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
+      constexpr int NMAX = TYPE == QR_Q4_0 ? 8 : 16;
+      const float d = solve_sym<NMAX>(xv, w, L);
+      uint32_t u[QK];
+#pragma unroll
+      for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + (float)NMAX);
+      const uint4 qs = pack_nibbles(u);
+      if constexpr (TYPE == QR_Q4_0) {
+        uint8_t* p = orow + (size_t)g * 20;
+        store_u32(p, fbits(d));
+        store_u32(p + 4, qs.x); store_u32(p + 8, qs.y); store_u32(p + 12, qs.z); store_u32(p + 16, qs.w);
+      } else {
+        uint8_t* p = orow + (size_t)g * 24;
+        store_u32(p, fbits(d));
+        store_u32(p + 4, pack_high_bits(u));
+        store_u32(p + 8, qs.x); store_u32(p + 12, qs.y); store_u32(p + 16, qs.z); store_u32(p + 20, qs.w);
+      }
+    } else if constexpr (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
+      constexpr int NMAX = TYPE == QR_Q4_1 ? 15 : 31;
+      float d, m;
+      solve_asym<NMAX, false>(xv, w, L, d, m);
+      uint32_t u[QK];
+#pragma unroll
+      for (int i = 0; i < QK; ++i) u[i] = (uint32_t)L[i];
+      const uint4 qs = pack_nibbles(u);
+      if constexpr (TYPE == QR_Q4_1) {
+        uint8_t* p = orow + (size_t)g * 24;
+        store_u32(p, fbits(d)); store_u32(p + 4, fbits(m));
+        store_u32(p + 8, qs.x); store_u32(p + 12, qs.y); store_u32(p + 16, qs.z); store_u32(p + 20, qs.w);
+      } else {
+        uint8_t* p = orow + (size_t)g * 28;
+        store_u32(p, fbits(d)); store_u32(p + 4, fbits(m));
+        store_u32(p + 8, pack_high_bits(u));
+        store_u32(p + 12, qs.x); store_u32(p + 16, qs.y); store_u32(p + 20, qs.z); store_u32(p + 24, qs.w);
+      }
+    } else {  // QR_Q4_K: lanes 8s .. 8s+7 hold the sub-blocks of one super-block [KQ 一]
+      float d, m;
+      solve_asym<15, true>(xv, w, L, d, m);
+      const float a = d > 0.0f ? d : 0.0f;
+      const float b = -m > 0.0f ? -m : 0.0f;
+      float A = a, Bm = b;
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) {
+        A = fmaxf(A, __shfl_xor(A, off, 8));
+        Bm = fmaxf(Bm, __shfl_xor(Bm, off, 8));
+      }
+      const _Float16 d16 = (_Float16)(A / 63.0f);
+      const _Float16 m16 = (_Float16)(Bm / 63.0f);
+      const float dA = (float)d16, dB = (float)m16;
+      const float sc = dA > 0.0f ? med3(rne(a / dA), 0.0f, 63.0f) : 0.0f;
+      const float mn = dB > 0.0f ? med3(rne(b / dB), 0.0f, 63.0f) : 0.0f;
+      const float ds = dA * sc, dm = dB * mn;
+      uint32_t u[QK];
+      if (ds == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < QK; ++i) u[i] = 0;
+      } else {
+        const float id = 1.0f / ds;
+#pragma unroll
+        for (int i = 0; i < QK; ++i) u[i] = (uint32_t)med3(rne((xv[i] + dm) * id), 0.0f, 15.0f);
+      }
+      const uint4 qs = pack_nibbles(u);
+      const int j = g & 7;
+      uint64_t scb = (uint64_t)(uint32_t)sc << (6 * j);
+      uint64_t mnb = (uint64_t)(uint32_t)mn << (6 * j);
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) {
+        scb |= __shfl_xor(scb, off, 8);
+        mnb |= __shfl_xor(mnb, off, 8);
+      }
+      uint8_t* p = orow + (size_t)(g >> 3) * 144;
+      *reinterpret_cast<uint4*>(p + 16 + 16 * j) = qs;
+      if (j == 0) {
+        const uint32_t h0 = (uint32_t)__builtin_bit_cast(uint16_t, d16) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, m16) << 16);
+        const uint32_t h1 = (uint32_t)scb;
+        const uint32_t h2 = (uint32_t)(scb >> 32) | ((uint32_t)mnb << 16);
+        const uint32_t h3 = (uint32_t)(mnb >> 16);
+        *reinterpret_cast<uint4*>(p) = make_uint4(h0, h1, h2, h3);
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// Q8_K_128 activation kernel [Q8 修复方案]
+//
+// 32 lanes per 128-value block, one 4-value vector each; a wave covers two
+// blocks per step and keeps UNROLL steps of loads in flight.
+
+constexpr int Q8_UNROLL = 4;
+
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void* __restrict__ x, int64_t e) {
+  if (!BF16) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + e));
+    return make_float4(v.x, v.y, v.z, v.w);
+  }
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(x) + e));
+  return make_float4(__builtin_bit_cast(float, v.x << 16), __builtin_bit_cast(float, v.x & 0xffff0000u),
+                     __builtin_bit_cast(float, v.y << 16), __builtin_bit_cast(float, v.y & 0xffff0000u));
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_quantize_q8k128(const void* __restrict__ x, int64_t n_blocks,
+                                                         int blocks_per_row, uint8_t* __restrict__ out,
+                                                         int64_t row_bytes) {
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;            // which of the two blocks of a step
+  const int l32 = lane & 31;             // 4-value slot inside the block
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t steps = (n_blocks + 1) >> 1;
+
+  for (int64_t s0 = wave * Q8_UNROLL; s0 < steps; s0 += n_waves * Q8_UNROLL) {
+    float4 v[Q8_UNROLL];
+#pragma unroll
+    for (int u = 0; u < Q8_UNROLL; ++u) {
+      const int64_t blk = 2 * (s0 + u) + half;
+      v[u] = blk < n_blocks ? load4<BF16>(x, blk * 128 + 4 * l32) : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < Q8_UNROLL; ++u) {
+      const int64_t blk = 2 * (s0 + u) + half;
+      float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+      const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+      const bool zero = !(amax > 0.0f) || !__builtin_isfinite(id);
+      const float d = zero ? 0.0f : amax / 127.0f;
+      int32_t q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+      if (!zero) {
+        q0 = (int32_t)med3(rne(v[u].x * id), -127.0f, 127.0f);
+        q1 = (int32_t)med3(rne(v[u].y * id), -127.0f, 127.0f);
+        q2 = (int32_t)med3(rne(v[u].z * id), -127.0f, 127.0f);
+        q3 = (int32_t)med3(rne(v[u].w * id), -127.0f, 127.0f);
+      }
+      int32_t sum = q0 + q1 + q2 + q3;
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) sum += __shfl_xor(sum, off, 8);
+      // sums of groups 0..3 sit on lanes 0, 8, 16, 24 of the block
+      const int32_t s1 = __shfl_down(sum, 8, 32);
+      if (blk < n_blocks) {
+        const int64_t r = blk / blocks_per_row, b = blk - r * blocks_per_row;
+        uint8_t* p = out + r * row_bytes + b * 140;
+        const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
+                                ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+        store_u32(p + 4 + 4 * l32, packed);
+        if (l32 == 0) store_u32(p, fbits(d));
+        if (l32 == 0 || l32 == 16)
+          store_u32(p + 132 + (l32 >> 2), (uint32_t)(sum & 0xffff) | ((uint32_t)(s1 & 0xffff) << 16));
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// decoders: 8 lanes per 32-weight group, one float4 of output each
+
+template <int TYPE>
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ in, int64_t n_units,
+                                                    int units_per_row, int64_t row_bytes, float* __restrict__ out,
+                                                    int n_per_row) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = tid; t < n_units * 8; t += nthreads) {
+    const int64_t unit = t >> 3;
+    const int k = (int)(t & 7);            // output elements 4k .. 4k+3 of the group
+    const int64_t r = unit / units_per_row;
+    const int gi = (int)(unit - r * units_per_row);
+    const uint8_t* row = in + r * row_bytes;
+    float o[4];
+    if constexpr (TYPE == QR_Q8_K128) {
+      const uint8_t* p = row + (size_t)(gi >> 2) * 140;
+      const float d = __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p));
+      const uint32_t qv = *reinterpret_cast<const uint32_t*>(p + 4 + 32 * (gi & 3) + 4 * k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = d * (float)(int8_t)(qv >> (8 * i));
+    } else {
+      const uint8_t* qs;
+      float scale, offset;   // x = scale * u + offset  (symmetric: d*(u - nmax))
+      uint32_t qh = 0;
+      int nmax = 0;
+      bool fused = true;
+      if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
+        const uint8_t* p = row + (size_t)gi * (TYPE == QR_Q4_0 ? 20 : 24);
+        scale = __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p));
+        offset = 0.0f;
+        nmax = TYPE == QR_Q4_0 ? 8 : 16;
+        fused = false;
+        if (TYPE == QR_Q5_0) qh = *reinterpret_cast<const uint32_t*>(p + 4);
+        qs = p + (TYPE == QR_Q4_0 ? 4 : 8);
+      } else if constexpr (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
+        const uint8_t* p = row + (size_t)gi * (TYPE == QR_Q4_1 ? 24 : 28);
+        scale = __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p));
+        offset = __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p + 4));
+        if (TYPE == QR_Q5_1) qh = *reinterpret_cast<const uint32_t*>(p + 8);
+        qs = p + (TYPE == QR_Q4_1 ? 8 : 12);
+      } else {  // Q4_K
+        const uint8_t* p = row + (size_t)(gi >> 3) * 144;
+        const int j = gi & 7;
+        const uint32_t h0 = *reinterpret_cast<const uint32_t*>(p);
+        const uint32_t h1 = *reinterpret_cast<const uint32_t*>(p + 4);
+        const uint32_t h2 = *reinterpret_cast<const uint32_t*>(p + 8);
+        const uint32_t h3 = *reinterpret_cast<const uint32_t*>(p + 12);
+        const uint64_t scb = (uint64_t)h1 | ((uint64_t)(h2 & 0xffffu) << 32);
+        const uint64_t mnb = (uint64_t)(h2 >> 16) | ((uint64_t)h3 << 16);
+        const float dA = (float)__builtin_bit_cast(_Float16, (uint16_t)(h0 & 0xffffu));
+        const float dB = (float)__builtin_bit_cast(_Float16, (uint16_t)(h0 >> 16));
+        scale = dA * (float)(uint32_t)((scb >> (6 * j)) & 63u);
+        offset = -(dB * (float)(uint32_t)((mnb >> (6 * j)) & 63u));
+        qs = p + 16 + 16 * j;
+      }
+      // elements 4k..4k+3: low nibbles of bytes 4k.. (k < 4) or high nibbles of bytes 4(k-4)..
+      const uint32_t bytes = *reinterpret_cast<const uint32_t*>(qs + 4 * (k & 3));
+      const int sh = (k >> 2) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t u = (bytes >> (8 * i + sh)) & 15u;
+        if (TYPE == QR_Q5_0 || TYPE == QR_Q5_1) u |= ((qh >> (4 * k + i)) & 1u) << 4;
+        o[i] = fused ? fma_(scale, (float)u, offset) : scale * (float)((int32_t)u - nmax);
+      }
+    }
+    float* dst = out + r * (int64_t)n_per_row + (int64_t)gi * QK + 4 * k;
+    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// -------------------------------------------------------------------------
+// host side
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int block_elems(int t) {
+  switch (t) {
+    case QR_Q4_0: case QR_Q4_1: case QR_Q5_0: case QR_Q5_1: return 32;
+    case QR_Q4_K: return 256;
+    case QR_Q8_K128: return 128;
+    default: return 0;
+  }
+}
+
+size_t block_bytes(int t) {
+  switch (t) {
+    case QR_Q4_0: return 20;
+    case QR_Q4_1: return 24;
+    case QR_Q5_0: return 24;
+    case QR_Q5_1: return 28;
+    case QR_Q4_K: return 144;
+    case QR_Q8_K128: return 140;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QR_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return QR_OK;
+}
+
+template <int TYPE, bool BF16>
+int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_row, int64_t rows_per_group,
+                void* out, size_t row_bytes, hipStream_t stream) {
+  auto kern = k_quantize_rows<TYPE, BF16>;
+  const size_t lds = (size_t)(n_per_row / QK) * (BF16 ? LDS_BF16_STRIDE * 2 : LDS_F32_STRIDE * 4);
+  static bool attr_set = false;
+  if (lds > 65536 && !attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+    if (e != hipSuccess) return fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE), lds, stream, x, imatrix, n_per_row,
+                     rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes);
+  return check_launch("k_quantize_rows");
+}
+
+template <bool BF16>
+int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, int n_per_row,
+                  int64_t rows_per_group, void* out, size_t row_bytes, hipStream_t s) {
+  switch (t) {
+    case QR_Q4_0: return launch_rows<QR_Q4_0, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
+    case QR_Q4_1: return launch_rows<QR_Q4_1, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
+    case QR_Q5_0: return launch_rows<QR_Q5_0, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
+    case QR_Q5_1: return launch_rows<QR_Q5_1, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
+    case QR_Q4_K: return launch_rows<QR_Q4_K, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
+    default: return fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
+  }
+}
+
+int grid_for(int64_t work_items, int per_block) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  const int64_t cap = 256 * 32;   // enough workgroups to fill 256 CUs many times
+  if (g > cap) g = cap;
+  return g < 1 ? 1 : (int)g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qr_last_error(void) { return g_err; }
+
+int qr_block_elems(int t) { return block_elems(t); }
+
+size_t qr_row_bytes(int t, int64_t n_per_row) {
+  const int be = block_elems(t);
+  if (be == 0 || n_per_row < 0 || n_per_row % be != 0) return 0;
+  return (size_t)(n_per_row / be) * block_bytes(t);
+}
+
+void qr_solver_constants(int32_t* c) {
+  c[0] = (int32_t)(CAND_STEP * 4.0f);
+  c[1] = SYM_CAND;
+  c[2] = SYM_FLIP_PASSES;
+  c[3] = ASYM_CAND;
+  c[4] = ASYM_FLIP_PASSES;
+  c[5] = QK;
+}
+
+int qr_quantize_rows_grouped(int t, int src, const void* x, const float* imatrix, int64_t n_groups,
+                             int64_t rows_per_group, int64_t n_per_row, void* out, void* stream) {
+  g_err[0] = 0;
+  if (t < QR_Q4_0 || t > QR_Q4_K) return fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
+  if (src != QR_F32 && src != QR_BF16) return fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
+  if (n_groups < 0 || rows_per_group < 0) return fail(QR_EINVAL_SHAPE, "negative row count");
+  const int be = block_elems(t);
+  const int64_t max_row = src == QR_F32 ? QR_MAX_ROW_F32 : QR_MAX_ROW_BF16;
+  if (n_per_row <= 0 || n_per_row % be != 0 || n_per_row > max_row)
+    return fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d and at most %lld",
+                (long long)n_per_row, be, (long long)max_row);
+  if (rows_per_group != 0 && n_groups > INT64_MAX / rows_per_group)
+    return fail(QR_EOVERFLOW, "n_groups * rows_per_group overflows");
+  const int64_t n_rows = n_groups * rows_per_group;
+  if (n_rows == 0) return QR_OK;
+  if (n_rows > (int64_t)UINT32_MAX) return fail(QR_EOVERFLOW, "n_rows=%lld exceeds 2^32-1", (long long)n_rows);
+  const size_t rb = qr_row_bytes(t, n_per_row);
+  if ((uint64_t)n_rows > SIZE_MAX / rb || (uint64_t)n_rows > SIZE_MAX / ((uint64_t)n_per_row * 4))
+    return fail(QR_EOVERFLOW, "buffer size overflows");
+  if (!x || !out) return fail(QR_EINVAL_PTR, "x and out must be non-NULL");
+  if (!aligned16(x) || !aligned16(out) || (imatrix && !aligned16(imatrix)))
+    return fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return src == QR_F32
+             ? dispatch_rows<false>(t, x, imatrix, n_rows, (int)n_per_row, rows_per_group, out, rb, s)
+             : dispatch_rows<true>(t, x, imatrix, n_rows, (int)n_per_row, rows_per_group, out, rb, s);
+}
+
+int qr_quantize_rows(int t, int src, const void* x, const float* imatrix, int64_t n_rows, int64_t n_per_row,
+                     void* out, void* stream) {
+  if (n_rows < 0) {
+    g_err[0] = 0;
+    return fail(QR_EINVAL_SHAPE, "negative row count");
+  }
+  return qr_quantize_rows_grouped(t, src, x, imatrix, 1, n_rows, n_per_row, out, stream);
+}
+
+int qr_quantize_activations_q8k128(int src, const void* x, int64_t n_rows, int64_t n_per_row, void* out,
+                                   void* stream) {
+  g_err[0] = 0;
+  if (src != QR_F32 && src != QR_BF16) return fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
+  if (n_rows < 0 || n_per_row <= 0 || n_per_row % 128 != 0)
+    return fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of 128", (long long)n_per_row);
+  if (n_rows == 0) return QR_OK;
+  if (n_per_row / 128 > INT32_MAX) return fail(QR_EOVERFLOW, "row too long");
+  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return fail(QR_EOVERFLOW, "size overflows");
+  if (!x || !out) return fail(QR_EINVAL_PTR, "x and out must be non-NULL");
+  if (!aligned16(x) || !aligned16(out)) return fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+  const int64_t n_blocks = n_rows * (n_per_row / 128);
+  const int64_t steps = (n_blocks + 1) / 2;
+  const int grid = grid_for((steps + Q8_UNROLL - 1) / Q8_UNROLL, 4);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t rb = (int64_t)qr_row_bytes(QR_Q8_K128, n_per_row);
+  if (src == QR_F32)
+    hipLaunchKernelGGL(k_quantize_q8k128<false>, dim3(grid), dim3(256), 0, s, x, n_blocks, (int)(n_per_row / 128),
+                       reinterpret_cast<uint8_t*>(out), rb);
+  else
+    hipLaunchKernelGGL(k_quantize_q8k128<true>, dim3(grid), dim3(256), 0, s, x, n_blocks, (int)(n_per_row / 128),
+                       reinterpret_cast<uint8_t*>(out), rb);
+  return check_launch("k_quantize_q8k128");
+}
+
+int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row, float* out, void* stream) {
+  g_err[0] = 0;
+  const int be = block_elems(t);
+  if (be == 0) return fail(QR_EINVAL_TYPE, "unknown type %d", t);
+  if (n_rows < 0 || n_per_row <= 0 || n_per_row % be != 0)
+    return fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d", (long long)n_per_row, be);
+  if (n_rows == 0) return QR_OK;
+  if (n_per_row > INT32_MAX) return fail(QR_EOVERFLOW, "row too long");
+  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return fail(QR_EOVERFLOW, "size overflows");
+  if (!in || !out) return fail(QR_EINVAL_PTR, "in and out must be non-NULL");
+  if (!aligned16(in) || !aligned16(out)) return fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+  const int units_per_row = (int)(n_per_row / QK);
+  const int64_t n_units = n_rows * units_per_row;
+  const int64_t rb = (int64_t)qr_row_bytes(t, n_per_row);
+  const int grid = grid_for(n_units * 8, 256);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(in);
+  switch (t) {
+    case QR_Q4_0: hipLaunchKernelGGL(k_dequantize<QR_Q4_0>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
+    case QR_Q4_1: hipLaunchKernelGGL(k_dequantize<QR_Q4_1>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
+    case QR_Q5_0: hipLaunchKernelGGL(k_dequantize<QR_Q5_0>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
+    case QR_Q5_1: hipLaunchKernelGGL(k_dequantize<QR_Q5_1>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
+    case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
+    default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
+  }
+  return check_launch("k_dequantize");
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+"""Python binding of libqrow.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls (see
+include/qrow.h) and takes torch tensors that live on the GPU; all arithmetic
+runs in the library's HIP kernels. torch provides device memory and the
+stream. There is no CPU fallback: without the built library or a GPU the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqrow.so")
+
+QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q4_K, QR_Q8_K128 = range(6)
+QR_F32, QR_BF16 = 0, 1
+TYPES = {"q4_0": QR_Q4_0, "q4_1": QR_Q4_1, "q5_0": QR_Q5_0, "q5_1": QR_Q5_1,
+         "q4_k": QR_Q4_K, "q8_k128": QR_Q8_K128}
+ERRORS = {-1: "QR_EINVAL_TYPE", -2: "QR_EINVAL_SHAPE", -3: "QR_EINVAL_PTR",
+          -4: "QR_EOVERFLOW", -5: "QR_EDEVICE"}
+
+# Every symbol include/qrow.h declares.
+EXPORTS = ("qr_quantize_rows", "qr_quantize_rows_grouped",
+           "qr_quantize_activations_q8k128", "qr_dequantize_rows",
+           "qr_row_bytes", "qr_block_elems", "qr_solver_constants",
+           "qr_last_error")
+
+
+class QrowError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libqrow.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -c 'import "
+                "__graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+        L = C.CDLL(path)
+        vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+        L.qr_quantize_rows.argtypes = [i32, i32, vp, vp, i64, i64, vp, vp]
+        L.qr_quantize_rows_grouped.argtypes = [i32, i32, vp, vp, i64, i64, i64,
+                                               vp, vp]
+        L.qr_quantize_activations_q8k128.argtypes = [i32, vp, i64, i64, vp, vp]
+        L.qr_dequantize_rows.argtypes = [i32, vp, i64, i64, vp, vp]
+        L.qr_row_bytes.argtypes = [i32, i64]
+        L.qr_row_bytes.restype = C.c_size_t
+        L.qr_block_elems.argtypes = [i32]
+        L.qr_solver_constants.argtypes = [C.POINTER(C.c_int32)]
+        L.qr_last_error.restype = C.c_char_p
+        for name in (n for n in EXPORTS if n not in
+                     ("qr_row_bytes", "qr_block_elems", "qr_last_error",
+                      "qr_solver_constants")):
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _tid(t) -> int:
+    return TYPES[t.lower()] if isinstance(t, str) else int(t)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise QrowError(rc, qr_last_error())
+
+
+def _stream(x: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream")
+                      else int(stream))
+
+
+def _src_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return QR_F32
+    if x.dtype == torch.bfloat16:
+        return QR_BF16
+    raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+
+
+def _dev2d(x: torch.Tensor, name: str):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D tensor")
+
+
+def qr_last_error() -> str:
+    return load_library().qr_last_error().decode()
+
+
+def qr_row_bytes(t, n_per_row: int) -> int:
+    return int(load_library().qr_row_bytes(_tid(t), n_per_row))
+
+
+def qr_block_elems(t) -> int:
+    return int(load_library().qr_block_elems(_tid(t)))
+
+
+def qr_solver_constants() -> dict:
+    c = (C.c_int32 * 6)()
+    load_library().qr_solver_constants(c)
+    return {"cand_step_x4": c[0], "sym_cand": c[1], "sym_flip_passes": c[2],
+            "asym_cand": c[3], "asym_flip_passes": c[4], "group": c[5]}
+
+
+def _out(out, shape, dtype, device):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if out.shape != torch.Size(shape) or out.dtype != dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dtype} tensor of shape {shape}")
+    return out
+
+
+def qr_quantize_rows(t, x: torch.Tensor, imatrix=None, out=None, stream=None):
+    """Quantizes the rows of x ([n_rows, n_per_row], fp32/bf16, on the GPU)
+    with importances imatrix ([n_per_row] fp32 or None). Returns uint8
+    [n_rows, qr_row_bytes(t, n_per_row)]."""
+    _dev2d(x, "x")
+    tid = _tid(t)
+    n_rows, n = x.shape
+    rb = qr_row_bytes(tid, n)
+    out = _out(out, (n_rows, rb), torch.uint8, x.device)
+    q = None
+    if imatrix is not None:
+        if imatrix.dtype != torch.float32 or imatrix.numel() != n or not imatrix.is_cuda:
+            raise ValueError("imatrix must be a CUDA float32 tensor of n_per_row values")
+        q = imatrix.contiguous()
+    _check(load_library().qr_quantize_rows(
+        tid, _src_dtype(x), C.c_void_p(x.data_ptr()),
+        None if q is None else C.c_void_p(q.data_ptr()), n_rows, n,
+        C.c_void_p(out.data_ptr()), _stream(x, stream)))
+    return out
+
+
+def qr_quantize_rows_grouped(t, x: torch.Tensor, imatrix, rows_per_group: int,
+                             out=None, stream=None):
+    """x: [n_groups*rows_per_group, n]; imatrix: [n_groups, n] fp32 or None."""
+    _dev2d(x, "x")
+    tid = _tid(t)
+    n_rows, n = x.shape
+    if rows_per_group <= 0 or n_rows % rows_per_group:
+        raise ValueError("n_rows must be a multiple of rows_per_group")
+    n_groups = n_rows // rows_per_group
+    q = None
+    if imatrix is not None:
+        if imatrix.dtype != torch.float32 or tuple(imatrix.shape) != (n_groups, n):
+            raise ValueError("imatrix must be float32 [n_groups, n_per_row]")
+        q = imatrix.contiguous()
+    out = _out(out, (n_rows, qr_row_bytes(tid, n)), torch.uint8, x.device)
+    _check(load_library().qr_quantize_rows_grouped(
+        tid, _src_dtype(x), C.c_void_p(x.data_ptr()),
+        None if q is None else C.c_void_p(q.data_ptr()), n_groups,
+        rows_per_group, n, C.c_void_p(out.data_ptr()), _stream(x, stream)))
+    return out
+
+
+def qr_quantize_activations_q8k128(x: torch.Tensor, out=None, stream=None):
+    """x: [n_rows, n_per_row] fp32/bf16, n_per_row % 128 == 0."""
+    _dev2d(x, "x")
+    n_rows, n = x.shape
+    out = _out(out, (n_rows, qr_row_bytes(QR_Q8_K128, n)), torch.uint8, x.device)
+    _check(load_library().qr_quantize_activations_q8k128(
+        _src_dtype(x), C.c_void_p(x.data_ptr()), n_rows, n,
+        C.c_void_p(out.data_ptr()), _stream(x, stream)))
+    return out
+
+
+def qr_dequantize_rows(t, packed: torch.Tensor, n_rows: int, n_per_row: int,
+                       out=None, stream=None):
+    """packed: uint8 [n_rows, qr_row_bytes]; returns fp32 [n_rows, n_per_row]."""
+    tid = _tid(t)
+    if not packed.is_cuda or packed.dtype != torch.uint8 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous CUDA uint8 tensor")
+    if packed.numel() != n_rows * qr_row_bytes(tid, n_per_row):
+        raise ValueError("packed has the wrong size")
+    out = _out(out, (n_rows, n_per_row), torch.float32, packed.device)
+    _check(load_library().qr_dequantize_rows(
+        tid, C.c_void_p(packed.data_ptr()), n_rows, n_per_row,
+        C.c_void_p(out.data_ptr()), _stream(packed, stream)))
+    return out

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C-ABI.
+
+Bar: packed outputs are byte-identical to the oracle's. The one tolerated
+difference is a row whose sum of squares (accumulated in double in both, in
+different orders) lies so close to a float rounding midpoint that sigma2 may
+round to a neighbouring float; such a row must then equal the oracle's output
+for that neighbouring sigma2 exactly.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from post_weight_quantization_row_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k"]
+
+
+@pytest.fixture(scope="module")
+def qr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from post_weight_quantization_row_amd import qrow
+    qrow.load_library()
+    return qrow
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(x: np.ndarray, bf16: bool):
+    if bf16:
+        bits = synth.f32_to_bf16_bits(x)
+        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, F32)).cuda()
+
+
+def host_values(x: np.ndarray, bf16: bool) -> np.ndarray:
+    return synth.round_to_bf16(x) if bf16 else np.ascontiguousarray(x, F32)
+
+
+def sigma2_ambiguous(row: np.ndarray) -> bool:
+    s64 = oracle.row_sigma2_f64(row)
+    s32 = F32(s64)
+    for nb in (np.nextafter(s32, F32(np.inf)), np.nextafter(s32, F32(-np.inf))):
+        mid = (float(s32) + float(nb)) / 2
+        if abs(mid - s64) <= 1e-11 * abs(s64):
+            return True
+    return False
+
+
+def assert_rows_equal(t, gpu, ref, x, q_of_row):
+    """gpu, ref: uint8 [R, rb]; x: the fp32 rows both sides consumed."""
+    bad = np.nonzero((gpu != ref).any(axis=1))[0]
+    for r in bad:
+        ok = False
+        if sigma2_ambiguous(x[r]):
+            s32 = F32(oracle.row_sigma2_f64(x[r]))
+            for s in (np.nextafter(s32, F32(np.inf)), np.nextafter(s32, F32(-np.inf))):
+                if np.array_equal(gpu[r], oracle.quantize_row_sigma2(t, x[r], q_of_row(r), s)):
+                    ok = True
+        if not ok:
+            cols = np.nonzero(gpu[r] != ref[r])[0]
+            raise AssertionError(f"{t}: row {r} differs at bytes {cols[:16]} "
+                                 f"(gpu {gpu[r][cols[:8]]}, oracle {ref[r][cols[:8]]})")
+    return len(bad)
+
+
+# ---------------------------------------------------------------------------
+# small shapes: several waves of groups, ragged tails, every type and dtype
+
+SHAPES = [(1, 256), (5, 2304), (3, 4096), (33, 512), (2, 7168), (2, 11008 // 32 * 32)]
+
+
+@pytest.mark.parametrize("t", WEIGHT_TYPES)
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("qkind", ["lognormal", "none", "zero-columns", "tiny"])
+def test_weight_rows_small(qr, t, bf16, qkind):
+    rng = np.random.default_rng(zlib.crc32(f"{t}/{bf16}/{qkind}".encode()))
+    for n_rows, n in SHAPES:
+        if t == "q4_k" and n % 256:
+            n = n // 256 * 256
+        x = (0.02 * rng.standard_t(5, (n_rows, n))).astype(F32)
+        x[:, ::97] *= 30                              # sparse outliers
+        q = {"lognormal": np.exp(1.5 * rng.standard_normal(n)).astype(F32),
+             "none": None,
+             "zero-columns": np.where(rng.random(n) < 0.2, 0, np.exp(rng.standard_normal(n))).astype(F32),
+             "tiny": np.full(n, 1e-6, F32)}[qkind]
+        if qkind == "zero-columns":
+            q[:64] = 0.0                              # whole groups without data
+        say(f"case {t} bf16={bf16} q={qkind} shape=({n_rows},{n})")
+        xd = to_dev(x, bf16)
+        qd = None if q is None else torch.from_numpy(q).cuda()
+        got = qr.qr_quantize_rows(t, xd, qd).cpu().numpy()
+        xh = host_values(x, bf16)
+        ref = oracle.quantize_rows(t, xh, q, threads=8)
+        assert_rows_equal(t, got, ref, xh, lambda r: q)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_q8k128_small(qr, bf16):
+    rng = np.random.default_rng(7 + bf16)
+    for n_rows, n in [(1, 128), (3, 256), (37, 7168), (5, 128 * 33)]:
+        x = rng.standard_normal((n_rows, n)).astype(F32)
+        x[:, rng.integers(n)] = rng.uniform(1e4, 2e5, n_rows) * np.sign(rng.standard_normal(n_rows))
+        if n_rows > 2:
+            x[1, :128] = 0.0                          # an all-zero block
+            x[2, :128] = 1e-39                        # 127/amax overflows
+        say(f"case q8_k128 bf16={bf16} shape=({n_rows},{n})")
+        got = qr.qr_quantize_activations_q8k128(to_dev(x, bf16)).cpu().numpy()
+        ref = oracle.quantize_q8k128(host_values(x, bf16))
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("t", WEIGHT_TYPES + ["q8_k128"])
+def test_dequantize_matches_oracle_decoder(qr, t):
+    x, q = synth.q4_k_matrix(n_rows=24, n_per_row=1024)
+    xd = to_dev(x, False)
+    if t == "q8_k128":
+        packed = qr.qr_quantize_activations_q8k128(xd)
+    else:
+        packed = qr.qr_quantize_rows(t, xd, torch.from_numpy(q).cuda())
+    say(f"case dequantize {t}")
+    got = qr.qr_dequantize_rows(t, packed, 24, 1024).cpu().numpy()
+    ref = oracle.dequantize_rows(t, packed.cpu().numpy(), 24, 1024)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_degenerate_rows(qr):
+    n = 512
+    rows = np.zeros((6, n), F32)
+    rows[1] = 1e-30 * np.random.default_rng(1).standard_normal(n)   # sigma2 < 2^-96
+    rows[2] = 3e15 * np.random.default_rng(2).standard_normal(n)    # large values
+    rows[3, :] = 0.25                                                 # constant row
+    rows[4, ::2], rows[4, 1::2] = 0.5, -0.5                           # exact |x| ties
+    rows[5] = np.random.default_rng(3).standard_normal(n)
+    rows[5, 32:64] = 0.0                                              # zero group
+    for t in WEIGHT_TYPES:
+        for q in (None, np.exp(np.random.default_rng(4).standard_normal(n)).astype(F32)):
+            say(f"case degenerate {t} q={'none' if q is None else 'lognormal'}")
+            got = qr.qr_quantize_rows(t, to_dev(rows, False),
+                                      None if q is None else torch.from_numpy(q).cuda()).cpu().numpy()
+            ref = oracle.quantize_rows(t, rows, q)
+            assert_rows_equal(t, got, ref, rows, lambda r: q)
+
+
+def test_every_output_byte_written_and_guards_untouched(qr):
+    x, q = synth.q4_0_matrix(n_rows=7, n_per_row=2048)
+    for t in WEIGHT_TYPES:
+        rb = qr.qr_row_bytes(t, 2048)
+        outs = []
+        for poison in (0xA5, 0x5A):
+            buf = torch.full((7 * rb + 512,), poison, dtype=torch.uint8, device="cuda")
+            view = buf[256:256 + 7 * rb].view(7, rb)
+            say(f"case guard {t} poison={poison:#x}")
+            qr.qr_quantize_rows(t, to_dev(x, False), torch.from_numpy(q).cuda(), out=view)
+            b = buf.cpu().numpy()
+            assert np.all(b[:256] == poison) and np.all(b[256 + 7 * rb:] == poison)
+            outs.append(b[256:256 + 7 * rb])
+        assert np.array_equal(outs[0], outs[1])
+
+
+def test_runs_are_deterministic(qr):
+    x, q = synth.q4_k_matrix(n_rows=512, n_per_row=4096)
+    xd, qd = to_dev(x, False), torch.from_numpy(q).cuda()
+    a = qr.qr_quantize_rows("q4_k", xd, qd)
+    b = qr.qr_quantize_rows("q4_k", xd, qd)
+    assert torch.equal(a, b)
+
+
+def test_zero_rows_and_errors(qr):
+    x = torch.zeros((0, 256), device="cuda")
+    assert qr.qr_quantize_rows("q4_0", x).shape == (0, 20 * 8)
+    with pytest.raises(qr.QrowError):
+        qr.qr_quantize_rows("q4_k", torch.zeros((2, 128), device="cuda"))
+    with pytest.raises(qr.QrowError):
+        qr.qr_quantize_activations_q8k128(torch.zeros((2, 100), device="cuda"))
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times
+
+def test_full_q4_0_2048x2048(qr):
+    x, q = synth.q4_0_matrix()
+    say("case q4_0_2048x2048 full")
+    got = qr.qr_quantize_rows("q4_0", to_dev(x, False), torch.from_numpy(q).cuda()).cpu().numpy()
+    ref = oracle.quantize_rows("q4_0", x, q, threads=16)
+    assert_rows_equal("q4_0", got, ref, x, lambda r: q)
+
+
+def test_full_q4_k_11008x4096(qr):
+    x, q = synth.q4_k_matrix()
+    say("case q4_k_11008x4096 full")
+    got = qr.qr_quantize_rows("q4_k", to_dev(x, False), torch.from_numpy(q).cuda()).cpu().numpy()
+    ref = oracle.quantize_rows("q4_k", x, q, threads=16)
+    n_alt = assert_rows_equal("q4_k", got, ref, x, lambda r: q)
+    say(f"rows resolved by a neighbouring sigma2: {n_alt}")
+
+
+def test_full_q8_k128_8192x7168(qr):
+    x, ch = synth.q8_k128_activations()
+    say("case q8_k128_8192x7168 full")
+    got = qr.qr_quantize_activations_q8k128(to_dev(x, False)).cpu().numpy()
+    ref = oracle.quantize_q8k128(x, threads=16)
+    assert np.array_equal(got, ref)
+    y = qr.qr_dequantize_rows("q8_k128", torch.from_numpy(got).cuda(), 8192, 7168)
+    assert bool(torch.isfinite(y).all())          # no fp16-style overflow
+
+
+def test_stack_7b_sampled_rows(qr):
+    rng = np.random.default_rng(1003)
+    for layer in (0, 31):
+        for which in range(7):
+            typ, x, q = synth.torch_stack_matrix(layer, which, "cuda")
+            say(f"case stack layer={layer} matrix={synth.STACK_LAYER[which][0]} {typ} {tuple(x.shape)}")
+            got = qr.qr_quantize_rows(typ, x, q)
+            rows = np.sort(rng.choice(x.shape[0], 24, replace=False))
+            xs = x[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+            qh = q.cpu().numpy()
+            ref = oracle.quantize_rows(typ, xs, qh, threads=8)
+            assert_rows_equal(typ, got[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, xs, lambda r: qh)
+            del x, got
+
+
+def test_moe_256x2048x7168_grouped_sampled_rows(qr):
+    say("case moe_256x2048x7168 grouped")
+    x, q = synth.torch_moe_stack("cuda")
+    got = qr.qr_quantize_rows_grouped("q4_k", x, q, 2048)
+    zero = synth.moe_zero_experts()
+    rng = np.random.default_rng(1005)
+    experts = np.unique(np.concatenate([zero[:4], rng.choice(256, 12, replace=False), [255]]))
+    qh = q.cpu().numpy()
+    for e in experts:
+        rows = 2048 * e + np.sort(rng.choice(2048, 8, replace=False))
+        idx = torch.from_numpy(rows).cuda()
+        xs = x[idx].float().cpu().numpy()
+        ref = oracle.quantize_rows("q4_k", xs, qh[e])
+        assert_rows_equal("q4_k", got[idx].cpu().numpy(), ref, xs, lambda r: qh[e])
+    del x, got
