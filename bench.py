@@ -52,6 +52,74 @@ def timed_steps(fn, steps, warmup, flush):
     return sum(ms) / len(ms), min(ms), wall
 
 
+def _setup(name, dev):
+    """Returns (step function, algorithmic bytes per launch, elements)."""
+    import torch
+    from post_weight_quantization_row_amd import qrow, synth
+    if name == "q4_k_11008x4096":
+        x, q = synth.torch_q4_k_matrix(dev)
+        out = torch.empty((11008, qrow.qr_row_bytes("q4_k", 4096)), dtype=torch.uint8, device=dev)
+        return (lambda: qrow.qr_quantize_rows("q4_k", x, q, out=out),
+                x.numel() * 4 + q.numel() * 4 + out.numel(), x.numel())
+    if name == "q4_0_2048x2048":
+        x, q = synth.q4_0_matrix()
+        xd, qd = torch.from_numpy(x).to(dev), torch.from_numpy(q).to(dev)
+        out = torch.empty((2048, qrow.qr_row_bytes("q4_0", 2048)), dtype=torch.uint8, device=dev)
+        return (lambda: qrow.qr_quantize_rows("q4_0", xd, qd, out=out),
+                x.nbytes + q.nbytes + out.numel(), x.size)
+    if name == "q8_k128_8192x7168":
+        x, _ = synth.q8_k128_activations()
+        xd = torch.from_numpy(x).to(dev)
+        out = torch.empty((8192, qrow.qr_row_bytes("q8_k128", 7168)), dtype=torch.uint8, device=dev)
+        return (lambda: qrow.qr_quantize_activations_q8k128(xd, out=out),
+                x.nbytes + out.numel(), x.size)
+    if name == "dequantize_q4_k_11008x4096":
+        x, q = synth.torch_q4_k_matrix(dev)
+        packed = qrow.qr_quantize_rows("q4_k", x, q)
+        y = torch.empty_like(x)
+        return (lambda: qrow.qr_dequantize_rows("q4_k", packed, 11008, 4096, out=y),
+                packed.numel() + y.numel() * 4, y.numel())
+    if name == "stack_7b_layer0_bf16":
+        mats = [synth.torch_stack_matrix(0, w, dev) for w in range(7)]
+        outs = [torch.empty((x.shape[0], qrow.qr_row_bytes(t, x.shape[1])), dtype=torch.uint8, device=dev)
+                for t, x, q in mats]
+
+        def step():
+            for (t, x, q), o in zip(mats, outs):
+                qrow.qr_quantize_rows(t, x, q, out=o)
+        nb = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
+        return step, nb, sum(x.numel() for _, x, _ in mats)
+    if name == "moe_256x2048x7168":
+        x, q = synth.torch_moe_stack(dev)
+        out = torch.empty((x.shape[0], qrow.qr_row_bytes("q4_k", 7168)), dtype=torch.uint8, device=dev)
+        return (lambda: qrow.qr_quantize_rows_grouped("q4_k", x, q, 2048, out=out),
+                x.numel() * 2 + q.numel() * 4 + out.numel(), x.numel())
+    if name == "copy_1gib":
+        # plain device copy of a known size: calibrates the HBM byte counters
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        return (lambda: b.copy_(a)), 2 * a.numel() * 4, a.numel()
+    raise ValueError(name)
+
+
+ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
+                  "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
+                  "moe_256x2048x7168", "copy_1gib")
+
+
+def run_only(args, dev, flush):
+    step, nbytes, n_el = _setup(args.only, dev)
+    log(f"{args.only}: warmup {args.warmup}, steps {args.steps}")
+    ms, ms_min, wall = timed_steps(step, args.steps, args.warmup, flush)
+    print(json.dumps({"workload": args.only, "ms_per_step": round(ms, 5),
+                      "ms_min": round(ms_min, 5),
+                      "G_elements_per_s": round(n_el / ms / 1e6, 3),
+                      "algorithmic_bytes": nbytes,
+                      "GB/s": round(nbytes / ms / 1e6, 1),
+                      "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,6 +128,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads")
+    ap.add_argument("--only", default=None,
+                    choices=sorted(ONLY_WORKLOADS),
+                    help="time one workload alone (for profiler runs) and "
+                         "print its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
@@ -77,6 +149,9 @@ def main():
     qrow.load_library()
     dev = torch.device("cuda:0")
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    if args.only:
+        run_only(args, dev, flush)
+        return
 
     # ---- headline: Q4_K, 11008 x 4096 fp32
     n_rows, n = 11008, 4096

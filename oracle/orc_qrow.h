@@ -34,10 +34,18 @@ enum {
 
 /* Solver constants (the oracle's own copy). */
 #define ORC_CAND_STEP       0.25f /* spacing of the trial scales, in levels   */
+#ifndef ORC_SYM_CAND
 #define ORC_SYM_CAND        5     /* trial scales, symmetric blocks           */
-#define ORC_SYM_FLIP_PASSES 2     /* greedy flip passes, symmetric blocks     */
+#endif
+#ifndef ORC_SYM_FLIP_PASSES
+#define ORC_SYM_FLIP_PASSES 1     /* greedy flip passes, symmetric blocks     */
+#endif
+#ifndef ORC_ASYM_CAND
 #define ORC_ASYM_CAND       3     /* trial scales, asymmetric blocks          */
+#endif
+#ifndef ORC_ASYM_FLIP_PASSES
 #define ORC_ASYM_FLIP_PASSES 1    /* greedy flip passes, asymmetric blocks    */
+#endif
 
 /* Return codes. */
 #define ORC_OK       0

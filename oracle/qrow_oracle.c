@@ -352,14 +352,13 @@ int orc_solve_asym(int n, const float *x, const float *w, int nmax, int K,
     const float lo_level = 0.0f, hi_level = (float)nmax;
     int32_t inf_local[4] = {-1, 0, 0, 1};
 
-    /* Range of the block. Comparisons (not fminf/fmaxf) keep the first of two
-     * equal values, so the sign of a zero bound is fixed. */
+    /* Range of the block. Adding +0 turns a -0 bound into +0, so the result
+     * does not depend on which of two equal zeros fminf/fmaxf return. */
     float lo = x[0], hi = x[0];
-    for (int i = 1; i < n; ++i) {
-        lo = (x[i] < lo) ? x[i] : lo;
-        hi = (x[i] > hi) ? x[i] : hi;
-    }
-    if (k4) lo = (0.0f < lo) ? 0.0f : lo;  /* Q4_K stores the offset as -dmin*mn, mn >= 0 */
+    for (int i = 1; i < n; ++i) { lo = fminf(lo, x[i]); hi = fmaxf(hi, x[i]); }
+    lo = lo + 0.0f;
+    hi = hi + 0.0f;
+    if (k4) lo = fminf(lo, 0.0f);  /* Q4_K stores the offset as -dmin*mn, mn >= 0 */
 
     float Sw = 0.0f, Sx = 0.0f;
     for (int i = 0; i < n; ++i) {
@@ -383,7 +382,7 @@ int orc_solve_asym(int n, const float *x, const float *w, int nmax, int K,
      * trial is scored by its two-parameter least-squares fit. */
     const float range = hi - lo;
     int best = -1;
-    float bis = 0.0f;
+    float bis = 0.0f, bSl = 0.0f, bSll = 0.0f, bSlx = 0.0f;
     double bm = 0.0, bscore = 0.0;
     for (int k = 0; k < K; ++k) {
         float is = ((float)nmax + ORC_CAND_STEP * (float)cand_offset[k]) / range;
@@ -395,6 +394,7 @@ int orc_solve_asym(int n, const float *x, const float *w, int nmax, int K,
         fit_dm(Sw, Sx, Sl, Sll, Slx, k4, &d, &m, &score);
         if (best < 0 || score > bscore) {
             best = k; bis = is; bm = m; bscore = score;
+            bSl = Sl; bSll = Sll; bSlx = Slx;
         }
     }
     if (best < 0) {
@@ -408,21 +408,22 @@ int orc_solve_asym(int n, const float *x, const float *w, int nmax, int K,
     for (int i = 0; i < n; ++i) L[i] = clampf(rintf(xs[i] * bis), lo_level, hi_level);
 
     /* Flips (reading): the offset m of the winning trial is held fixed and
-     * the scale-only rule of flip_passes() is applied to y = x - m; then
-     * (d, m) are refitted jointly on the final levels. */
+     * the scale-only rule of flip_passes() is applied to y = x - m, starting
+     * from A = sum w y l = Slx - m*Sl and B = sum w l^2 = Sll of that trial;
+     * then (d, m) are refitted jointly on the final levels, with
+     * Sll = B and Slx = A + m*Sl. */
     const float mf = (float)bm;
-    float A = 0.0f, B = 0.0f;
     for (int i = 0; i < n; ++i) {
         y[i] = x[i] - mf;
         wy[i] = w[i] * y[i];
-        A = fmaf(wy[i], L[i], A);
-        B = fmaf(w[i] * L[i], L[i], B);
     }
+    float A = fmaf(-mf, bSl, bSlx), B = bSll;
     inf_local[0] = best;
     flip_passes(n, y, w, wy, lo_level, hi_level, F, L, &A, &B, inf_local);
 
-    float Sl, Sll, Slx;
-    asym_sums(n, w, wx, L, &Sl, &Sll, &Slx);
+    float Sl = 0.0f;
+    for (int i = 0; i < n; ++i) Sl = Sl + w[i] * L[i];
+    const float Sll = B, Slx = fmaf(mf, Sl, A);
     double d, m, score;
     fit_dm(Sw, Sx, Sl, Sll, Slx, k4, &d, &m, &score);
 

@@ -60,7 +60,7 @@ constexpr int LDS_BF16_STRIDE = 40;     // bf16 per staged group (32 + pad)
 // Solver constants: trial-scale spacing and counts, flip passes.
 constexpr float CAND_STEP = 0.25f;
 constexpr int SYM_CAND = 5;
-constexpr int SYM_FLIP_PASSES = 2;
+constexpr int SYM_FLIP_PASSES = 1;
 constexpr int ASYM_CAND = 3;
 constexpr int ASYM_FLIP_PASSES = 1;
 
@@ -95,15 +95,18 @@ __device__ __forceinline__ float sqrt_cr(float t, bool normal_range) {
 // -------------------------------------------------------------------------
 // row staging and the row statistic [WT 一]
 
+// The workgroup streams its row into LDS (16-byte coalesced loads; groups of
+// 32 padded to a 16-byte multiple) and returns this wave's sum of x^2 in
+// double, reduced across the wave.
 template <bool BF16>
-__device__ __forceinline__ double stage_row(const void* __restrict__ xrow, int n, void* lds, int lane) {
+__device__ __forceinline__ double stage_row(const void* __restrict__ xrow, int n, void* lds, int tid, int nthreads) {
   double acc = 0.0;
   if (!BF16) {
     const f32x4* src = reinterpret_cast<const f32x4*>(xrow);
     float* dst = reinterpret_cast<float*>(lds);
     const int n4 = n >> 2;
-#pragma unroll 4
-    for (int i = lane; i < n4; i += WAVE) {
+#pragma unroll 8
+    for (int i = tid; i < n4; i += nthreads) {
       f32x4 v = __builtin_nontemporal_load(src + i);
       const int e = i << 2;
       *reinterpret_cast<f32x4*>(dst + (e >> 5) * LDS_F32_STRIDE + (e & 31)) = v;
@@ -116,8 +119,8 @@ __device__ __forceinline__ double stage_row(const void* __restrict__ xrow, int n
     const u32x4* src = reinterpret_cast<const u32x4*>(xrow);
     uint16_t* dst = reinterpret_cast<uint16_t*>(lds);
     const int n8 = n >> 3;
-#pragma unroll 4
-    for (int i = lane; i < n8; i += WAVE) {
+#pragma unroll 8
+    for (int i = tid; i < n8; i += nthreads) {
       u32x4 v = __builtin_nontemporal_load(src + i);
       const int e = i << 3;
       *reinterpret_cast<u32x4*>(dst + (e >> 5) * LDS_BF16_STRIDE + (e & 31)) = v;
@@ -131,26 +134,29 @@ __device__ __forceinline__ double stage_row(const void* __restrict__ xrow, int n
       }
     }
   }
-  // wave reduction of the double partial sums
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, WAVE);
   return acc;
 }
 
+// Reads group g of the staged row. The empty asm is a compiler barrier: a
+// group is re-read from LDS when needed again instead of being kept live in
+// VGPRs.
 template <bool BF16>
 __device__ __forceinline__ void load_group(const void* lds, int g, float (&x)[QK]) {
+  asm volatile("" ::: "memory");
   if (!BF16) {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(lds) + g * LDS_F32_STRIDE);
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds) + g * LDS_F32_STRIDE);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      float4 v = p[k];
+      f32x4 v = p[k];
       x[4 * k] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
     }
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(lds) + g * LDS_BF16_STRIDE);
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(lds) + g * LDS_BF16_STRIDE);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint4 v = p[k];
+      u32x4 v = p[k];
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -162,38 +168,27 @@ __device__ __forceinline__ void load_group(const void* lds, int g, float (&x)[QK
 }
 
 // Importances of one 32-weight group [WT 一]: w = q * sqrt(fma(x, x, sigma2)),
-// q taken from the element's own column; a group whose importances are all
-// zero uses q = 1.
-__device__ __forceinline__ void group_weights(const float (&x)[QK], const float* __restrict__ q,
-                                              float sigma2, bool normal_range, float (&w)[QK]) {
-  float s[QK];
-#pragma unroll
-  for (int i = 0; i < QK; ++i) s[i] = sqrt_cr(fma_(x[i], x[i], sigma2), normal_range);
+// q taken from the element's own column (q == nullptr: q = 1).
+__device__ __forceinline__ void group_importances(const float (&x)[QK], const float* __restrict__ q,
+                                                  float sigma2, bool normal_range, float (&w)[QK]) {
   if (q) {
-    const float4* q4 = reinterpret_cast<const float4*>(q);
-    uint32_t any = 0;
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(q);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      float4 v = q4[k];
-      w[4 * k] = v.x * s[4 * k];
-      w[4 * k + 1] = v.y * s[4 * k + 1];
-      w[4 * k + 2] = v.z * s[4 * k + 2];
-      w[4 * k + 3] = v.w * s[4 * k + 3];
-    }
-#pragma unroll
-    for (int i = 0; i < QK; ++i) any |= fbits(w[i]) & 0x7fffffffu;
-    if (any == 0) {
-#pragma unroll
-      for (int i = 0; i < QK; ++i) w[i] = s[i];
+      const f32x4 v = q4[k];
+      w[4 * k] = v.x * sqrt_cr(fma_(x[4 * k], x[4 * k], sigma2), normal_range);
+      w[4 * k + 1] = v.y * sqrt_cr(fma_(x[4 * k + 1], x[4 * k + 1], sigma2), normal_range);
+      w[4 * k + 2] = v.z * sqrt_cr(fma_(x[4 * k + 2], x[4 * k + 2], sigma2), normal_range);
+      w[4 * k + 3] = v.w * sqrt_cr(fma_(x[4 * k + 3], x[4 * k + 3], sigma2), normal_range);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < QK; ++i) w[i] = s[i];
+    for (int i = 0; i < QK; ++i) w[i] = sqrt_cr(fma_(x[i], x[i], sigma2), normal_range);
   }
 }
 
 // -------------------------------------------------------------------------
-// greedy flip passes [WT 一]
+// greedy flip pass [WT 一]
 //
 // Fit y ~ d*l with d = A/B, A = sum w y l, B = sum w l^2. Element j moves one
 // level along s = sign(A) * sign(y_j*B - l_j*A) (the sign of the pages'
@@ -212,10 +207,12 @@ __device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&
     for (int j = 0; j < QK; ++j) {
       const float t = L[j] * A;
       const float e = fma_(y[j], B, -t);
-      const float s = ((fbits(A) ^ fbits(e)) & 0x80000000u) ? -1.0f : 1.0f;
+      const uint32_t sg = (fbits(A) ^ fbits(e)) & 0x80000000u;
+      const float s = __builtin_bit_cast(float, 0x3f800000u | sg);    // +-1
+      const float s2 = __builtin_bit_cast(float, 0x40000000u | sg);   // +-2
       const float lp = L[j] + s;
       const float A1 = fma_(s, wy[j], A);
-      const float B1 = fma_(w[j], fma_(2.0f * s, L[j], 1.0f), B);
+      const float B1 = fma_(w[j], fma_(s2, L[j], 1.0f), B);
       const bool keep = ((A1 * A1) * B > (A * A) * B1) && (B1 > 0.0f) && (lp >= lo) && (lp <= hi);
       A = keep ? A1 : A;
       B = keep ? B1 : B;
@@ -231,19 +228,31 @@ __device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&
 // -------------------------------------------------------------------------
 // symmetric group: levels -NMAX .. NMAX-1, one scale
 
-template <int NMAX>
-__device__ __forceinline__ float solve_sym(const float (&x)[QK], const float (&w)[QK], float (&L)[QK]) {
+template <int NMAX, bool BF16>
+__device__ __forceinline__ float solve_sym(const void* lds, int g, const float* __restrict__ q, float sigma2,
+                                           bool normal_range, float (&L)[QK]) {
   constexpr float LO = (float)-NMAX, HI = (float)(NMAX - 1);
-  // element of largest magnitude, first one on ties
-  float amax = fabsf(x[0]), xm = x[0];
+  float x[QK], w[QK], wx[QK];
+  load_group<BF16>(lds, g, x);
+  group_importances(x, q, sigma2, normal_range, w);
+  {  // a group with no importance at all falls back to q = 1
+    uint32_t any = 0;
 #pragma unroll
-  for (int i = 1; i < QK; ++i) {
-    const float a = fabsf(x[i]);
-    const bool g = a > amax;
-    amax = g ? a : amax;
-    xm = g ? x[i] : xm;
+    for (int i = 0; i < QK; ++i) any |= fbits(w[i]) & 0x7fffffffu;
+    if (any == 0) group_importances(x, nullptr, sigma2, normal_range, w);
   }
-  float wx[QK];
+  // element of largest magnitude, first one on ties: from max and min, with
+  // a scan only when +a and -a are both present
+  float xmax = x[0], xmin = x[0];
+#pragma unroll
+  for (int i = 1; i < QK; ++i) { xmax = fmaxf(xmax, x[i]); xmin = fminf(xmin, x[i]); }
+  const float amax = fmaxf(xmax, -xmin);
+  float xm = (xmax > -xmin) ? xmax : xmin;
+  if (xmax == -xmin) {
+    xm = x[QK - 1];
+#pragma unroll
+    for (int i = QK - 2; i >= 0; --i) xm = (fabsf(x[i]) == amax) ? x[i] : xm;
+  }
 #pragma unroll
   for (int i = 0; i < QK; ++i) wx[i] = w[i] * x[i];
 
@@ -310,62 +319,70 @@ __device__ __forceinline__ void fit_dm(float Sw_, float Sx_, float Sl_, float Sl
   score = dd * Slx + mm * Sx;
 }
 
-__device__ __forceinline__ void asym_sums(const float (&w)[QK], const float (&wx)[QK], const float (&L)[QK],
-                                          float& Sl, float& Sll, float& Slx) {
-  float a = 0.0f, b = 0.0f, c = 0.0f;
-#pragma unroll
-  for (int i = 0; i < QK; ++i) {
-    const float wl = w[i] * L[i];
-    a = a + wl;
-    b = fma_(wl, L[i], b);
-    c = fma_(wx[i], L[i], c);
-  }
-  Sl = a; Sll = b; Slx = c;
-}
-
-template <int NMAX, bool K4>
-__device__ __forceinline__ void solve_asym(const float (&x)[QK], const float (&w)[QK], float (&L)[QK],
-                                           float& d_out, float& m_out) {
+// Returns (d, m) and the levels; x, w are left in the arrays for the caller
+// (w: importances; x: overwritten).
+template <int NMAX, bool K4, bool BF16>
+__device__ __forceinline__ void solve_asym(const void* lds, int g, const float* __restrict__ q, float sigma2,
+                                           bool normal_range, float (&L)[QK], float& d_out, float& m_out) {
   constexpr float HI = (float)NMAX;
+  float x[QK], w[QK];
+  load_group<BF16>(lds, g, x);
+  group_importances(x, q, sigma2, normal_range, w);
+  float Sw = 0.0f;
+#pragma unroll
+  for (int i = 0; i < QK; ++i) Sw = Sw + w[i];
+  if (!(Sw > 0.0f)) {   // no importance at all: q = 1 for this group
+    group_importances(x, nullptr, sigma2, normal_range, w);
+    Sw = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QK; ++i) Sw = Sw + w[i];
+  }
   float lo = x[0], hi = x[0];
 #pragma unroll
-  for (int i = 1; i < QK; ++i) {
-    lo = (x[i] < lo) ? x[i] : lo;
-    hi = (x[i] > hi) ? x[i] : hi;
-  }
-  if (K4) lo = (0.0f < lo) ? 0.0f : lo;
+  for (int i = 1; i < QK; ++i) { lo = fminf(lo, x[i]); hi = fmaxf(hi, x[i]); }
+  lo = lo + 0.0f;   // a zero bound is +0 whichever zero min/max returned
+  hi = hi + 0.0f;
+  if (K4) lo = fminf(lo, 0.0f);
 
-  float wx[QK], xs[QK];
-  float Sw = 0.0f, Sx = 0.0f;
-#pragma unroll
-  for (int i = 0; i < QK; ++i) {
-    wx[i] = w[i] * x[i];
-    xs[i] = x[i] - lo;
-    Sw = Sw + w[i];
-    Sx = Sx + wx[i];
-  }
-  if (hi == lo || !(Sw > 0.0f)) {
+  if (hi == lo || !(Sw > 0.0f)) {   // constant group, or importances that underflow to 0
 #pragma unroll
     for (int i = 0; i < QK; ++i) L[i] = 0.0f;
     d_out = 0.0f;
     m_out = lo;
     return;
   }
+  float wx[QK], xs[QK];
+  float Sx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < QK; ++i) {
+    wx[i] = w[i] * x[i];
+    xs[i] = x[i] - lo;
+    Sx = Sx + wx[i];
+  }
   const float range = hi - lo;
   bool have = false;
-  float bis = 0.0f;
+  float bis = 0.0f, bSl = 0.0f, bSll = 0.0f, bSlx = 0.0f;
   double bm = 0.0, bscore = 0.0;
 #pragma unroll
   for (int k = 0; k < ASYM_CAND; ++k) {
     const float is = ((float)NMAX + CAND_STEP * (float)cand_offset(k)) / range;
+    // 0 <= xs <= range, so rint(xs * is) lies in [0, NMAX] for these
+    // trials and the clamp to the level range never acts.
+    float Sl = 0.0f, Sll = 0.0f, Slx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < QK; ++i) L[i] = med3(rne(xs[i] * is), 0.0f, HI);
-    float Sl, Sll, Slx;
-    asym_sums(w, wx, L, Sl, Sll, Slx);
+    for (int i = 0; i < QK; ++i) {
+      const float l = rne(xs[i] * is);
+      const float wl = w[i] * l;
+      Sl = Sl + wl;
+      Sll = fma_(wl, l, Sll);
+      Slx = fma_(wx[i], l, Slx);
+    }
     double d, m, score;
     fit_dm<K4>(Sw, Sx, Sl, Sll, Slx, d, m, score);
     const bool ok = __builtin_isfinite(is);
-    if (ok && (!have || score > bscore)) { have = true; bis = is; bm = m; bscore = score; }
+    if (ok && (!have || score > bscore)) {
+      have = true; bis = is; bm = m; bscore = score; bSl = Sl; bSll = Sll; bSlx = Slx;
+    }
   }
   if (!have) {
 #pragma unroll
@@ -375,25 +392,25 @@ __device__ __forceinline__ void solve_asym(const float (&x)[QK], const float (&w
     return;
   }
 #pragma unroll
-  for (int i = 0; i < QK; ++i) L[i] = med3(rne(xs[i] * bis), 0.0f, HI);
+  for (int i = 0; i < QK; ++i) L[i] = rne(xs[i] * bis);
 
   // flips with the offset of the winning trial held fixed, then a joint refit
   const float mf = (float)bm;
   float y[QK], wy[QK];
-  float A = 0.0f, B = 0.0f;
+  load_group<BF16>(lds, g, x);
 #pragma unroll
   for (int i = 0; i < QK; ++i) {
     y[i] = x[i] - mf;
     wy[i] = w[i] * y[i];
-    A = fma_(wy[i], L[i], A);
-    B = fma_(w[i] * L[i], L[i], B);
   }
+  float A = fma_(-mf, bSl, bSlx), B = bSll;
   flip_passes<ASYM_FLIP_PASSES>(y, w, wy, 0.0f, HI, L, A, B);
 
-  float Sl, Sll, Slx;
-  asym_sums(w, wx, L, Sl, Sll, Slx);
+  float Sl = 0.0f;
+#pragma unroll
+  for (int i = 0; i < QK; ++i) Sl = Sl + w[i] * L[i];
   double d, m, score;
-  fit_dm<K4>(Sw, Sx, Sl, Sll, Slx, d, m, score);
+  fit_dm<K4>(Sw, Sx, Sl, B, fma_(mf, Sl, A), d, m, score);
   d_out = (float)d;
   m_out = (float)m;
 }
@@ -427,37 +444,47 @@ __device__ __forceinline__ uint32_t pack_high_bits(const uint32_t (&u)[QK]) {
 __device__ __forceinline__ void store_u32(uint8_t* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
 
 // -------------------------------------------------------------------------
-// weight-row kernel
+// weight-row kernel: one workgroup of W waves per row (W = ceil(groups/64),
+// at most MAX_ROW_WAVES); every lane solves groups tid, tid + 64W, ...
+
+constexpr int MAX_ROW_WAVES = 8;
 
 template <int TYPE, bool BF16>
-__global__ __launch_bounds__(WAVE) void k_quantize_rows(const void* __restrict__ x, const float* __restrict__ imatrix,
-                                                        int n_per_row, int64_t rows_per_group,
-                                                        uint8_t* __restrict__ out, int64_t row_bytes) {
+__global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(3))) void k_quantize_rows(const void* __restrict__ x,
+                                                                        const float* __restrict__ imatrix,
+                                                                        int n_per_row, int64_t rows_per_group,
+                                                                        uint8_t* __restrict__ out,
+                                                                        int64_t row_bytes) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
   const int64_t row = blockIdx.x;
   const int n_groups = n_per_row / QK;
   const size_t elem = BF16 ? 2 : 4;
+  double* partial = reinterpret_cast<double*>(lds_raw + (size_t)n_groups * (BF16 ? 2 * LDS_BF16_STRIDE
+                                                                                  : 4 * LDS_F32_STRIDE));
 
   const void* xrow = reinterpret_cast<const unsigned char*>(x) + (size_t)row * n_per_row * elem;
-  const double ss = stage_row<BF16>(xrow, n_per_row, lds_raw, lane);
+  const double ss_wave = stage_row<BF16>(xrow, n_per_row, lds_raw, tid, nthreads);
+  if ((tid & (WAVE - 1)) == 0) partial[tid / WAVE] = ss_wave;
+  __syncthreads();
+  double ss = 0.0;
+  for (int k = 0; k < nthreads / WAVE; ++k) ss += partial[k];
   const float sigma2 = (float)(ss / (double)n_per_row);
   const bool normal_range = sigma2 >= 0x1p-96f && sigma2 <= 3.0e38f;
-  __syncthreads();
 
   const float* q = imatrix ? imatrix + (row / rows_per_group) * (int64_t)n_per_row : nullptr;
   uint8_t* orow = out + row * row_bytes;
 
-  for (int base = 0; base < n_groups; base += WAVE) {
-    const int g = base + lane;
+  for (int base = 0; base < n_groups; base += nthreads) {
+    const int g = base + tid;
     if (g >= n_groups) continue;
-    float xv[QK], w[QK], L[QK];
-    load_group<BF16>(lds_raw, g, xv);
-    group_weights(xv, q ? q + g * QK : nullptr, sigma2, normal_range, w);
+    const float* qg = q ? q + g * QK : nullptr;
+    float L[QK];
 
     if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
       constexpr int NMAX = TYPE == QR_Q4_0 ? 8 : 16;
-      const float d = solve_sym<NMAX>(xv, w, L);
+      const float d = solve_sym<NMAX, BF16>(lds_raw, g, qg, sigma2, normal_range, L);
       uint32_t u[QK];
 #pragma unroll
       for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + (float)NMAX);
@@ -475,7 +502,7 @@ __global__ __launch_bounds__(WAVE) void k_quantize_rows(const void* __restrict__
     } else if constexpr (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
       constexpr int NMAX = TYPE == QR_Q4_1 ? 15 : 31;
       float d, m;
-      solve_asym<NMAX, false>(xv, w, L, d, m);
+      solve_asym<NMAX, false, BF16>(lds_raw, g, qg, sigma2, normal_range, L, d, m);
       uint32_t u[QK];
 #pragma unroll
       for (int i = 0; i < QK; ++i) u[i] = (uint32_t)L[i];
@@ -492,7 +519,7 @@ __global__ __launch_bounds__(WAVE) void k_quantize_rows(const void* __restrict__
       }
     } else {  // QR_Q4_K: lanes 8s .. 8s+7 hold the sub-blocks of one super-block [KQ 一]
       float d, m;
-      solve_asym<15, true>(xv, w, L, d, m);
+      solve_asym<15, true, BF16>(lds_raw, g, qg, sigma2, normal_range, L, d, m);
       const float a = d > 0.0f ? d : 0.0f;
       const float b = -m > 0.0f ? -m : 0.0f;
       float A = a, Bm = b;
@@ -513,6 +540,8 @@ __global__ __launch_bounds__(WAVE) void k_quantize_rows(const void* __restrict__
         for (int i = 0; i < QK; ++i) u[i] = 0;
       } else {
         const float id = 1.0f / ds;
+        float xv[QK];
+        load_group<BF16>(lds_raw, g, xv);
 #pragma unroll
         for (int i = 0; i < QK; ++i) u[i] = (uint32_t)med3(rne((xv[i] + dm) * id), 0.0f, 15.0f);
       }
@@ -729,7 +758,10 @@ template <int TYPE, bool BF16>
 int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_row, int64_t rows_per_group,
                 void* out, size_t row_bytes, hipStream_t stream) {
   auto kern = k_quantize_rows<TYPE, BF16>;
-  const size_t lds = (size_t)(n_per_row / QK) * (BF16 ? LDS_BF16_STRIDE * 2 : LDS_F32_STRIDE * 4);
+  const int n_groups = n_per_row / QK;
+  int waves = (n_groups + WAVE - 1) / WAVE;
+  if (waves > MAX_ROW_WAVES) waves = MAX_ROW_WAVES;
+  const size_t lds = (size_t)n_groups * (BF16 ? LDS_BF16_STRIDE * 2 : LDS_F32_STRIDE * 4) + 8 * (size_t)waves;
   static bool attr_set = false;
   if (lds > 65536 && !attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -737,7 +769,7 @@ int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_r
     if (e != hipSuccess) return fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE), lds, stream, x, imatrix, n_per_row,
+  hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE * waves), lds, stream, x, imatrix, n_per_row,
                      rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes);
   return check_launch("k_quantize_rows");
 }
