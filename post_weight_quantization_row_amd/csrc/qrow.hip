@@ -168,23 +168,31 @@ __device__ __forceinline__ void load_group(const void* lds, int g, float (&x)[QK
 }
 
 // Importances of one 32-weight group [WT 一]: w = q * sqrt(fma(x, x, sigma2)),
-// q taken from the element's own column (q == nullptr: q = 1).
-__device__ __forceinline__ void group_importances(const float (&x)[QK], const float* __restrict__ q,
-                                                  float sigma2, bool normal_range, float (&w)[QK]) {
+// q taken from the element's own column (q == nullptr: q = 1). The range
+// test is uniform over the row, so each group takes one branch.
+template <bool NORMAL>
+__device__ __forceinline__ void group_importances_(const float (&x)[QK], const float* __restrict__ q,
+                                                   float sigma2, float (&w)[QK]) {
   if (q) {
     const f32x4* q4 = reinterpret_cast<const f32x4*>(q);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const f32x4 v = q4[k];
-      w[4 * k] = v.x * sqrt_cr(fma_(x[4 * k], x[4 * k], sigma2), normal_range);
-      w[4 * k + 1] = v.y * sqrt_cr(fma_(x[4 * k + 1], x[4 * k + 1], sigma2), normal_range);
-      w[4 * k + 2] = v.z * sqrt_cr(fma_(x[4 * k + 2], x[4 * k + 2], sigma2), normal_range);
-      w[4 * k + 3] = v.w * sqrt_cr(fma_(x[4 * k + 3], x[4 * k + 3], sigma2), normal_range);
+      w[4 * k] = v.x * sqrt_cr(fma_(x[4 * k], x[4 * k], sigma2), NORMAL);
+      w[4 * k + 1] = v.y * sqrt_cr(fma_(x[4 * k + 1], x[4 * k + 1], sigma2), NORMAL);
+      w[4 * k + 2] = v.z * sqrt_cr(fma_(x[4 * k + 2], x[4 * k + 2], sigma2), NORMAL);
+      w[4 * k + 3] = v.w * sqrt_cr(fma_(x[4 * k + 3], x[4 * k + 3], sigma2), NORMAL);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < QK; ++i) w[i] = sqrt_cr(fma_(x[i], x[i], sigma2), normal_range);
+    for (int i = 0; i < QK; ++i) w[i] = sqrt_cr(fma_(x[i], x[i], sigma2), NORMAL);
   }
+}
+
+__device__ __forceinline__ void group_importances(const float (&x)[QK], const float* __restrict__ q,
+                                                  float sigma2, bool normal_range, float (&w)[QK]) {
+  if (normal_range) group_importances_<true>(x, q, sigma2, w);
+  else group_importances_<false>(x, q, sigma2, w);
 }
 
 // -------------------------------------------------------------------------
@@ -196,7 +204,7 @@ __device__ __forceinline__ void group_importances(const float (&x)[QK], const fl
 // A' = A + s*w_j*y_j and B' = B + w_j*(2*s*l_j + 1). A pass that keeps no
 // move ends the loop for the wave; lanes that kept none repeat a pass whose
 // every decision is unchanged, so their result is the same.
-template <int F>
+template <int F, bool ZERO_LO>
 __device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&w)[QK], const float (&wy)[QK],
                                             float lo, float hi, float (&L)[QK], float& A_io, float& B_io) {
   float A = A_io, B = B_io;
@@ -213,7 +221,10 @@ __device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&
       const float lp = L[j] + s;
       const float A1 = fma_(s, wy[j], A);
       const float B1 = fma_(w[j], fma_(s2, L[j], 1.0f), B);
-      const bool keep = ((A1 * A1) * B > (A * A) * B1) && (B1 > 0.0f) && (lp >= lo) && (lp <= hi);
+      // levels [0, hi]: lp >= +0 and lp <= hi is one unsigned compare of
+      // the bit patterns (lp is never -0 here; negative values compare high)
+      const bool in_range = ZERO_LO ? (fbits(lp) <= fbits(hi)) : ((lp >= lo) && (lp <= hi));
+      const bool keep = ((A1 * A1) * B > (A * A) * B1) && (B1 > 0.0f) && in_range;
       A = keep ? A1 : A;
       B = keep ? B1 : B;
       L[j] = keep ? lp : L[j];
@@ -286,7 +297,7 @@ __device__ __forceinline__ float solve_sym(const void* lds, int g, const float* 
 #pragma unroll
   for (int i = 0; i < QK; ++i) L[i] = med3(rne(x[i] * bis), LO, HI);
   float A = bS1, B = bS2;
-  flip_passes<SYM_FLIP_PASSES>(x, w, wx, LO, HI, L, A, B);
+  flip_passes<SYM_FLIP_PASSES, false>(x, w, wx, LO, HI, L, A, B);
   return A / B;
 }
 
@@ -404,7 +415,7 @@ __device__ __forceinline__ void solve_asym(const void* lds, int g, const float* 
     wy[i] = w[i] * y[i];
   }
   float A = fma_(-mf, bSl, bSlx), B = bSll;
-  flip_passes<ASYM_FLIP_PASSES>(y, w, wy, 0.0f, HI, L, A, B);
+  flip_passes<ASYM_FLIP_PASSES, true>(y, w, wy, 0.0f, HI, L, A, B);
 
   float Sl = 0.0f;
 #pragma unroll
@@ -428,6 +439,23 @@ __device__ __forceinline__ uint4 pack_nibbles(const uint32_t (&u)[QK]) {
     for (int b = 0; b < 4; ++b) {
       const int i = 4 * k + b;
       v |= ((u[i] & 15u) | ((u[i + 16] & 15u) << 4)) << (8 * b);
+    }
+    o[k] = v;
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Same layout from codes held as floats (exact small integers): each byte
+// u_i + 16*u_{i+16} is formed in float and converted into place.
+__device__ __forceinline__ uint4 pack_nibbles_f(const float (&u)[QK]) {
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = 4 * k + b;
+      v = __builtin_amdgcn_cvt_pk_u8_f32(fma_(16.0f, u[i + 16], u[i]), b, v);
     }
     o[k] = v;
   }
@@ -485,15 +513,19 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
     if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
       constexpr int NMAX = TYPE == QR_Q4_0 ? 8 : 16;
       const float d = solve_sym<NMAX, BF16>(lds_raw, g, qg, sigma2, normal_range, L);
-      uint32_t u[QK];
-#pragma unroll
-      for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + (float)NMAX);
-      const uint4 qs = pack_nibbles(u);
       if constexpr (TYPE == QR_Q4_0) {
+        float uf[QK];
+#pragma unroll
+        for (int i = 0; i < QK; ++i) uf[i] = L[i] + (float)NMAX;
+        const uint4 qs = pack_nibbles_f(uf);
         uint8_t* p = orow + (size_t)g * 20;
         store_u32(p, fbits(d));
         store_u32(p + 4, qs.x); store_u32(p + 8, qs.y); store_u32(p + 12, qs.z); store_u32(p + 16, qs.w);
       } else {
+        uint32_t u[QK];
+#pragma unroll
+        for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + (float)NMAX);
+        const uint4 qs = pack_nibbles(u);
         uint8_t* p = orow + (size_t)g * 24;
         store_u32(p, fbits(d));
         store_u32(p + 4, pack_high_bits(u));
@@ -503,15 +535,16 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
       constexpr int NMAX = TYPE == QR_Q4_1 ? 15 : 31;
       float d, m;
       solve_asym<NMAX, false, BF16>(lds_raw, g, qg, sigma2, normal_range, L, d, m);
-      uint32_t u[QK];
-#pragma unroll
-      for (int i = 0; i < QK; ++i) u[i] = (uint32_t)L[i];
-      const uint4 qs = pack_nibbles(u);
       if constexpr (TYPE == QR_Q4_1) {
+        const uint4 qs = pack_nibbles_f(L);
         uint8_t* p = orow + (size_t)g * 24;
         store_u32(p, fbits(d)); store_u32(p + 4, fbits(m));
         store_u32(p + 8, qs.x); store_u32(p + 12, qs.y); store_u32(p + 16, qs.z); store_u32(p + 20, qs.w);
       } else {
+        uint32_t u[QK];
+#pragma unroll
+        for (int i = 0; i < QK; ++i) u[i] = (uint32_t)L[i];
+        const uint4 qs = pack_nibbles(u);
         uint8_t* p = orow + (size_t)g * 28;
         store_u32(p, fbits(d)); store_u32(p + 4, fbits(m));
         store_u32(p + 8, pack_high_bits(u));
@@ -534,18 +567,17 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
       const float sc = dA > 0.0f ? med3(rne(a / dA), 0.0f, 63.0f) : 0.0f;
       const float mn = dB > 0.0f ? med3(rne(b / dB), 0.0f, 63.0f) : 0.0f;
       const float ds = dA * sc, dm = dB * mn;
-      uint32_t u[QK];
+      float u[QK];
       if (ds == 0.0f) {
 #pragma unroll
-        for (int i = 0; i < QK; ++i) u[i] = 0;
+        for (int i = 0; i < QK; ++i) u[i] = 0.0f;
       } else {
         const float id = 1.0f / ds;
-        float xv[QK];
-        load_group<BF16>(lds_raw, g, xv);
+        load_group<BF16>(lds_raw, g, u);
 #pragma unroll
-        for (int i = 0; i < QK; ++i) u[i] = (uint32_t)med3(rne((xv[i] + dm) * id), 0.0f, 15.0f);
+        for (int i = 0; i < QK; ++i) u[i] = med3(rne((u[i] + dm) * id), 0.0f, 15.0f);
       }
-      const uint4 qs = pack_nibbles(u);
+      const uint4 qs = pack_nibbles_f(u);
       const int j = g & 7;
       uint64_t scb = (uint64_t)(uint32_t)sc << (6 * j);
       uint64_t mnb = (uint64_t)(uint32_t)mn << (6 * j);
