@@ -25,7 +25,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: VALU lane-operations per second
+# (packed fp32 instructions are not used, so one instruction = one op/lane)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Operations of the method per Q4_K weight (3 trial scales, 1 flip pass),
+# counted from the oracle's loops: see the operation table in the design
+# notes (row statistic 2, importance + zero test 4, range 2, w*x etc. 4,
+# trials 24, block solves 2.5, winner codes 4, flip setup 2, flip pass 19,
+# refit sums 2, Q4_K re-round and scales 5.5).
+ALG_OPS_PER_WEIGHT_Q4K = 71.0
 METRIC = "Gweights/s quantized (Q4_0, Q4_K) + achieved HBM GB/s fraction"
+COUNTERS = os.path.join(ROOT, "profiles", "q4_k_11008x4096_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "post_weight_quantization_row_amd", "csrc", "qrow.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the Q4_K kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    import hashlib
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+        with open(KERNEL_SRC, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != h:
+        return None
+    return int(c["hbm_bytes_per_launch"])
 
 
 def log(*a):
@@ -165,6 +192,7 @@ def main():
     alg_bytes = weights * 4 + n * 4 + n_rows * rb
     gws = weights / (ms * 1e-3) / 1e9
     gbs = alg_bytes / (ms * 1e-3) / 1e9
+    tops = ALG_OPS_PER_WEIGHT_Q4K * weights / (ms * 1e-3) / 1e12
     torch.cuda.synchronize()
     # back-to-back (input may stay in the Infinity Cache), for context only
     t = time.perf_counter()
@@ -190,13 +218,15 @@ def main():
                    "n_rows": n_rows, "n_per_row": n, "src": "f32",
                    "imatrix": "LogNormal(0,1.5) per column",
                    "cache_flush_between_steps": "1 GiB"},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+        "roofline": {"bound": "alu", "achieved": round(tops, 3),
+                     "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s",
+                     "frac": round(tops / VALU_PEAK_TOPS, 4),
+                     "traffic": measured_traffic(),
                      "kernel": "k_quantize_rows<Q4_K,f32>",
-                     "bytes_per_launch": alg_bytes},
+                     "alg_ops_per_weight": ALG_OPS_PER_WEIGHT_Q4K,
+                     "alg_bytes_per_launch": alg_bytes},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "hbm_GB/s": round(gbs, 1),
         "ms_per_step_min": round(ms_min, 5),
         "ms_per_step_back_to_back": round(ms_b2b, 5),
         "wall_s_timed_loop": round(wall, 4),

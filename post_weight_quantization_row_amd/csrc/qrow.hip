@@ -603,10 +603,46 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
 // -------------------------------------------------------------------------
 // Q8_K_128 activation kernel [Q8 修复方案]
 //
-// 32 lanes per 128-value block, one 4-value vector each; a wave covers two
-// blocks per step and keeps UNROLL steps of loads in flight.
+// A wave handles Q8_STEPS pairs of 128-value blocks (16 consecutive blocks, 8
+// KB of fp32 input) per iteration: lanes 0-31 hold one block and lanes 32-63
+// the next, one float4 per lane, all loads issued before any use. amax and
+// the per-32 sums are reduced with DPP row operations (one LDS-unit shuffle
+// for the last step). The 16 packed blocks (2240 bytes, 16-byte aligned) are
+// assembled in LDS and written with coalesced 16-byte stores.
 
-constexpr int Q8_UNROLL = 4;
+constexpr int Q8_STEPS = 8;                      // block pairs per wave iteration
+constexpr int Q8_CHUNK = Q8_STEPS * 2 * 140;     // output bytes per wave iteration
+
+// DPP helpers (gfx9 encodings): quad_perm, row_half_mirror, row_mirror, row_shl:8
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_SHL8 = 0x108;
+
+// max over each 32-lane half of the wave
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));   // max over 8
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));        // max over 16
+  return fmaxf(v, __shfl_xor(v, 16, 32));        // max over 32
+}
+
+// sum over each group of 8 lanes
+__device__ __forceinline__ int oct_sum(int v) {
+  v += dpp_i<DPP_QUAD_XOR1>(v);
+  v += dpp_i<DPP_QUAD_XOR2>(v);
+  return v + dpp_i<DPP_ROW_HALF_MIRROR>(v);
+}
 
 template <bool BF16>
 __device__ __forceinline__ float4 load4(const void* __restrict__ x, int64_t e) {
@@ -621,28 +657,30 @@ __device__ __forceinline__ float4 load4(const void* __restrict__ x, int64_t e) {
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_quantize_q8k128(const void* __restrict__ x, int64_t n_blocks,
-                                                         int blocks_per_row, uint8_t* __restrict__ out,
-                                                         int64_t row_bytes) {
+                                                         uint8_t* __restrict__ out) {
+  __shared__ __align__(16) uint32_t stage[4][Q8_CHUNK / 4];
   const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;            // which of the two blocks of a step
-  const int l32 = lane & 31;             // 4-value slot inside the block
+  const int wib = threadIdx.x >> 6;
+  const int half = lane >> 5;             // which block of a pair
+  const int l32 = lane & 31;              // 4-value slot inside the block
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-  const int64_t steps = (n_blocks + 1) >> 1;
+  uint32_t* st = stage[wib];
 
-  for (int64_t s0 = wave * Q8_UNROLL; s0 < steps; s0 += n_waves * Q8_UNROLL) {
-    float4 v[Q8_UNROLL];
+  // rows are contiguous and a multiple of 128 long, so block b of the whole
+  // tensor starts at value 128*b and its packed bytes at 140*b
+  for (int64_t b0 = wave * (2 * Q8_STEPS); b0 < n_blocks; b0 += n_waves * (2 * Q8_STEPS)) {
+    float4 v[Q8_STEPS];
 #pragma unroll
-    for (int u = 0; u < Q8_UNROLL; ++u) {
-      const int64_t blk = 2 * (s0 + u) + half;
+    for (int u = 0; u < Q8_STEPS; ++u) {
+      const int64_t blk = b0 + 2 * u + half;
       v[u] = blk < n_blocks ? load4<BF16>(x, blk * 128 + 4 * l32) : make_float4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < Q8_UNROLL; ++u) {
-      const int64_t blk = 2 * (s0 + u) + half;
+    for (int u = 0; u < Q8_STEPS; ++u) {
+      const int lb = 2 * u + half;        // block index within the chunk
       float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+      amax = half_wave_max(amax);
       const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
       const bool zero = !(amax > 0.0f) || !__builtin_isfinite(id);
       const float d = zero ? 0.0f : amax / 127.0f;
@@ -653,94 +691,105 @@ __global__ __launch_bounds__(256) void k_quantize_q8k128(const void* __restrict_
         q2 = (int32_t)med3(rne(v[u].z * id), -127.0f, 127.0f);
         q3 = (int32_t)med3(rne(v[u].w * id), -127.0f, 127.0f);
       }
-      int32_t sum = q0 + q1 + q2 + q3;
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) sum += __shfl_xor(sum, off, 8);
-      // sums of groups 0..3 sit on lanes 0, 8, 16, 24 of the block
-      const int32_t s1 = __shfl_down(sum, 8, 32);
-      if (blk < n_blocks) {
-        const int64_t r = blk / blocks_per_row, b = blk - r * blocks_per_row;
-        uint8_t* p = out + r * row_bytes + b * 140;
-        const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
-                                ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
-        store_u32(p + 4 + 4 * l32, packed);
-        if (l32 == 0) store_u32(p, fbits(d));
-        if (l32 == 0 || l32 == 16)
-          store_u32(p + 132 + (l32 >> 2), (uint32_t)(sum & 0xffff) | ((uint32_t)(s1 & 0xffff) << 16));
-      }
+      const int32_t sum = oct_sum(q0 + q1 + q2 + q3);     // sum of group l32/8
+      const int32_t s_next = dpp_i<DPP_ROW_SHL8>(sum);    // lanes 0, 16: groups 1, 3
+      uint32_t* bs = st + 35 * lb;                        // 140-byte block in the chunk
+      bs[1 + l32] = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
+                    ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+      if (l32 == 0) bs[0] = fbits(d);
+      if (l32 == 0 || l32 == 16)
+        bs[33 + (l32 >> 4)] = (uint32_t)(sum & 0xffff) | ((uint32_t)(s_next & 0xffff) << 16);
     }
+    // one wave's LDS accesses complete in order; the barrier only keeps the
+    // compiler from moving the reads above the writes
+    __builtin_amdgcn_wave_barrier();
+    // 16-byte stores of the chunk (its start 140*b0 is a multiple of 16)
+    const int64_t nb = (n_blocks - b0) < 2 * Q8_STEPS ? (n_blocks - b0) : 2 * Q8_STEPS;
+    const int nvec = (int)(nb * 140 / 16);
+    uint8_t* dst = out + b0 * 140;
+    for (int i = lane; i < nvec; i += WAVE)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(st + 4 * i), reinterpret_cast<u32x4*>(dst) + i);
+    if (lane == 0 && nb * 140 % 16) {                     // a partial last vector (ragged end)
+      for (int k = nvec * 4; k < (int)(nb * 140 / 4); ++k) reinterpret_cast<uint32_t*>(dst)[k] = st[k];
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
 // -------------------------------------------------------------------------
-// decoders: 8 lanes per 32-weight group, one float4 of output each
+// decoders: 8 lanes per 32-weight group, one float4 of output each; a wave
+// covers 8 groups per step and DQ_STEPS steps per iteration
+
+constexpr int DQ_STEPS = 2;
+
+// Rows are contiguous and hold whole blocks, so packed block B of the tensor
+// starts at byte B * block_bytes and 32-weight unit U's output at 32 * U.
+// Every word an item needs is loaded before any is used, so an item costs
+// one memory round trip.
+template <int TYPE>
+__device__ __forceinline__ void decode4(const uint8_t* __restrict__ in, int64_t U, int k, float (&o)[4]) {
+  if constexpr (TYPE == QR_Q8_K128) {
+    const uint8_t* p = in + (U >> 2) * 140;
+    const uint32_t dbits = *reinterpret_cast<const uint32_t*>(p);
+    const uint32_t qv = *reinterpret_cast<const uint32_t*>(p + 4 + 32 * (int)(U & 3) + 4 * k);
+    const float d = __builtin_bit_cast(float, dbits);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = d * (float)(int8_t)(qv >> (8 * i));
+  } else if constexpr (TYPE == QR_Q4_K) {
+    const uint8_t* p = in + (U >> 3) * 144;
+    const int j = (int)(U & 7);
+    const u32x4 h = *reinterpret_cast<const u32x4*>(p);       // 144*B is 16-byte aligned
+    const uint32_t bytes = *reinterpret_cast<const uint32_t*>(p + 16 + 16 * j + 4 * (k & 3));
+    const uint64_t scb = (uint64_t)h.y | ((uint64_t)(h.z & 0xffffu) << 32);
+    const uint64_t mnb = (uint64_t)(h.z >> 16) | ((uint64_t)h.w << 16);
+    const float dA = (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xffffu));
+    const float dB = (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x >> 16));
+    const float ds = dA * (float)(uint32_t)((scb >> (6 * j)) & 63u);
+    const float dm = dB * (float)(uint32_t)((mnb >> (6 * j)) & 63u);
+    const int sh = (k >> 2) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = fma_(ds, (float)((bytes >> (8 * i + sh)) & 15u), -dm);
+  } else {
+    constexpr int BB = TYPE == QR_Q4_0 ? 20 : (TYPE == QR_Q5_1 ? 28 : 24);
+    constexpr bool SYM = TYPE == QR_Q4_0 || TYPE == QR_Q5_0;
+    constexpr bool FIVE = TYPE == QR_Q5_0 || TYPE == QR_Q5_1;
+    constexpr int QS = (SYM ? 4 : 8) + (FIVE ? 4 : 0);          // offset of the nibbles
+    const uint8_t* p = in + U * BB;
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(p);
+    const uint32_t w1 = SYM ? 0u : *reinterpret_cast<const uint32_t*>(p + 4);
+    const uint32_t qh = FIVE ? *reinterpret_cast<const uint32_t*>(p + QS - 4) : 0u;
+    const uint32_t bytes = *reinterpret_cast<const uint32_t*>(p + QS + 4 * (k & 3));
+    const float d = __builtin_bit_cast(float, w0);
+    const int sh = (k >> 2) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t u = (bytes >> (8 * i + sh)) & 15u;
+      if (FIVE) u |= ((qh >> (4 * k + i)) & 1u) << 4;
+      if constexpr (SYM) o[i] = d * (float)((int32_t)u - (TYPE == QR_Q4_0 ? 8 : 16));
+      else o[i] = fma_(d, (float)u, __builtin_bit_cast(float, w1));
+    }
+  }
+}
 
 template <int TYPE>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ in, int64_t n_units,
-                                                    int units_per_row, int64_t row_bytes, float* __restrict__ out,
-                                                    int n_per_row) {
+                                                    float* __restrict__ out) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = tid; t < n_units * 8; t += nthreads) {
-    const int64_t unit = t >> 3;
-    const int k = (int)(t & 7);            // output elements 4k .. 4k+3 of the group
-    const int64_t r = unit / units_per_row;
-    const int gi = (int)(unit - r * units_per_row);
-    const uint8_t* row = in + r * row_bytes;
-    float o[4];
-    if constexpr (TYPE == QR_Q8_K128) {
-      const uint8_t* p = row + (size_t)(gi >> 2) * 140;
-      const float d = __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p));
-      const uint32_t qv = *reinterpret_cast<const uint32_t*>(p + 4 + 32 * (gi & 3) + 4 * k);
+  const int64_t n_items = n_units * 8;
+  for (int64_t t0 = tid; t0 < n_items; t0 += nthreads * DQ_STEPS) {
+    float o[DQ_STEPS][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = d * (float)(int8_t)(qv >> (8 * i));
-    } else {
-      const uint8_t* qs;
-      float scale, offset;   // x = scale * u + offset  (symmetric: d*(u - nmax))
-      uint32_t qh = 0;
-      int nmax = 0;
-      bool fused = true;
-      if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
-        const uint8_t* p = row + (size_t)gi * (TYPE == QR_Q4_0 ? 20 : 24);
-        scale = __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p));
-        offset = 0.0f;
-        nmax = TYPE == QR_Q4_0 ? 8 : 16;
-        fused = false;
-        if (TYPE == QR_Q5_0) qh = *reinterpret_cast<const uint32_t*>(p + 4);
-        qs = p + (TYPE == QR_Q4_0 ? 4 : 8);
-      } else if constexpr (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
-        const uint8_t* p = row + (size_t)gi * (TYPE == QR_Q4_1 ? 24 : 28);
-        scale = __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p));
-        offset = __builtin_bit_cast(float, *reinterpret_cast<const uint32_t*>(p + 4));
-        if (TYPE == QR_Q5_1) qh = *reinterpret_cast<const uint32_t*>(p + 8);
-        qs = p + (TYPE == QR_Q4_1 ? 8 : 12);
-      } else {  // Q4_K
-        const uint8_t* p = row + (size_t)(gi >> 3) * 144;
-        const int j = gi & 7;
-        const uint32_t h0 = *reinterpret_cast<const uint32_t*>(p);
-        const uint32_t h1 = *reinterpret_cast<const uint32_t*>(p + 4);
-        const uint32_t h2 = *reinterpret_cast<const uint32_t*>(p + 8);
-        const uint32_t h3 = *reinterpret_cast<const uint32_t*>(p + 12);
-        const uint64_t scb = (uint64_t)h1 | ((uint64_t)(h2 & 0xffffu) << 32);
-        const uint64_t mnb = (uint64_t)(h2 >> 16) | ((uint64_t)h3 << 16);
-        const float dA = (float)__builtin_bit_cast(_Float16, (uint16_t)(h0 & 0xffffu));
-        const float dB = (float)__builtin_bit_cast(_Float16, (uint16_t)(h0 >> 16));
-        scale = dA * (float)(uint32_t)((scb >> (6 * j)) & 63u);
-        offset = -(dB * (float)(uint32_t)((mnb >> (6 * j)) & 63u));
-        qs = p + 16 + 16 * j;
-      }
-      // elements 4k..4k+3: low nibbles of bytes 4k.. (k < 4) or high nibbles of bytes 4(k-4)..
-      const uint32_t bytes = *reinterpret_cast<const uint32_t*>(qs + 4 * (k & 3));
-      const int sh = (k >> 2) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t u = (bytes >> (8 * i + sh)) & 15u;
-        if (TYPE == QR_Q5_0 || TYPE == QR_Q5_1) u |= ((qh >> (4 * k + i)) & 1u) << 4;
-        o[i] = fused ? fma_(scale, (float)u, offset) : scale * (float)((int32_t)u - nmax);
-      }
+    for (int s = 0; s < DQ_STEPS; ++s) {
+      const int64_t t = t0 + s * nthreads;
+      if (t < n_items) decode4<TYPE>(in, t >> 3, (int)(t & 7), o[s]);
     }
-    float* dst = out + r * (int64_t)n_per_row + (int64_t)gi * QK + 4 * k;
-    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+    for (int s = 0; s < DQ_STEPS; ++s) {
+      const int64_t t = t0 + s * nthreads;
+      if (t < n_items)
+        __builtin_nontemporal_store(f32x4{o[s][0], o[s][1], o[s][2], o[s][3]}, reinterpret_cast<f32x4*>(out + 4 * t));
+    }
   }
 }
 
@@ -821,7 +870,7 @@ int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, in
 
 int grid_for(int64_t work_items, int per_block) {
   int64_t g = (work_items + per_block - 1) / per_block;
-  const int64_t cap = 256 * 32;   // enough workgroups to fill 256 CUs many times
+  const int64_t cap = 1 << 17;    // plenty of waves in flight for the streaming kernels
   if (g > cap) g = cap;
   return g < 1 ? 1 : (int)g;
 }
@@ -898,16 +947,15 @@ int qr_quantize_activations_q8k128(int src, const void* x, int64_t n_rows, int64
   if (!x || !out) return fail(QR_EINVAL_PTR, "x and out must be non-NULL");
   if (!aligned16(x) || !aligned16(out)) return fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
   const int64_t n_blocks = n_rows * (n_per_row / 128);
-  const int64_t steps = (n_blocks + 1) / 2;
-  const int grid = grid_for((steps + Q8_UNROLL - 1) / Q8_UNROLL, 4);
+  const int64_t chunks = (n_blocks + 2 * Q8_STEPS - 1) / (2 * Q8_STEPS);
+  const int grid = grid_for(chunks, 4);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t rb = (int64_t)qr_row_bytes(QR_Q8_K128, n_per_row);
   if (src == QR_F32)
-    hipLaunchKernelGGL(k_quantize_q8k128<false>, dim3(grid), dim3(256), 0, s, x, n_blocks, (int)(n_per_row / 128),
-                       reinterpret_cast<uint8_t*>(out), rb);
+    hipLaunchKernelGGL(k_quantize_q8k128<false>, dim3(grid), dim3(256), 0, s, x, n_blocks,
+                       reinterpret_cast<uint8_t*>(out));
   else
-    hipLaunchKernelGGL(k_quantize_q8k128<true>, dim3(grid), dim3(256), 0, s, x, n_blocks, (int)(n_per_row / 128),
-                       reinterpret_cast<uint8_t*>(out), rb);
+    hipLaunchKernelGGL(k_quantize_q8k128<true>, dim3(grid), dim3(256), 0, s, x, n_blocks,
+                       reinterpret_cast<uint8_t*>(out));
   return check_launch("k_quantize_q8k128");
 }
 
@@ -922,19 +970,17 @@ int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row,
   if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return fail(QR_EOVERFLOW, "size overflows");
   if (!in || !out) return fail(QR_EINVAL_PTR, "in and out must be non-NULL");
   if (!aligned16(in) || !aligned16(out)) return fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
-  const int units_per_row = (int)(n_per_row / QK);
-  const int64_t n_units = n_rows * units_per_row;
-  const int64_t rb = (int64_t)qr_row_bytes(t, n_per_row);
-  const int grid = grid_for(n_units * 8, 256);
+  const int64_t n_units = n_rows * (n_per_row / QK);
+  const int grid = grid_for((n_units * 8 + DQ_STEPS - 1) / DQ_STEPS, 256);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint8_t* p = reinterpret_cast<const uint8_t*>(in);
   switch (t) {
-    case QR_Q4_0: hipLaunchKernelGGL(k_dequantize<QR_Q4_0>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
-    case QR_Q4_1: hipLaunchKernelGGL(k_dequantize<QR_Q4_1>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
-    case QR_Q5_0: hipLaunchKernelGGL(k_dequantize<QR_Q5_0>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
-    case QR_Q5_1: hipLaunchKernelGGL(k_dequantize<QR_Q5_1>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
-    case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
-    default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_units, units_per_row, rb, out, (int)n_per_row); break;
+    case QR_Q4_0: hipLaunchKernelGGL(k_dequantize<QR_Q4_0>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
+    case QR_Q4_1: hipLaunchKernelGGL(k_dequantize<QR_Q4_1>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
+    case QR_Q5_0: hipLaunchKernelGGL(k_dequantize<QR_Q5_0>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
+    case QR_Q5_1: hipLaunchKernelGGL(k_dequantize<QR_Q5_1>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
+    case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
+    default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
   }
   return check_launch("k_dequantize");
 }

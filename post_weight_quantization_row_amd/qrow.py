@@ -14,7 +14,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqrow.so")
+# QROW_LIBRARY may name another build of the same library (A/B timing).
+LIB_PATH = os.environ.get("QROW_LIBRARY") or os.path.join(HERE, "libqrow.so")
 
 QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q4_K, QR_Q8_K128 = range(6)
 QR_F32, QR_BF16 = 0, 1
