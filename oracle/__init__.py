@@ -10,6 +10,7 @@ in the C file.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 import subprocess
@@ -43,48 +44,70 @@ def build(force: bool = True) -> str:
     return LIB
 
 
+_override = None
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Temporarily routes every call to another build of the oracle (the
+    mutation tests load deliberately broken copies this way)."""
+    global _override
+    prev = _override
+    _override = _load(path)
+    try:
+        yield
+    finally:
+        _override = prev
+
+
 def lib():
     global _lib
+    if _override is not None:
+        return _override
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB):
                 build(force=True)
-            L = C.CDLL(LIB)
-            f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
-            u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
-            i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
-            i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
-            vp = C.c_void_p
-            i64 = C.c_int64
-            L.orc_solver_constants.argtypes = [i32p]
-            L.orc_block_bytes.argtypes = [C.c_int]
-            L.orc_block_bytes.restype = C.c_size_t
-            L.orc_block_elems.argtypes = [C.c_int]
-            L.orc_row_bytes.argtypes = [C.c_int, i64]
-            L.orc_row_bytes.restype = C.c_size_t
-            L.orc_row_sigma2.argtypes = [f32p, i64]
-            L.orc_row_sigma2.restype = C.c_float
-            L.orc_row_sigma2_f64.argtypes = [f32p, i64]
-            L.orc_row_sigma2_f64.restype = C.c_double
-            L.orc_row_weights.argtypes = [f32p, vp, i64, C.c_float, f32p]
-            L.orc_solve_sym.argtypes = [C.c_int, f32p, f32p, C.c_int, C.c_int,
-                                        C.c_int, i8p, f32p, i32p]
-            L.orc_solve_asym.argtypes = [C.c_int, f32p, f32p, C.c_int, C.c_int,
-                                         C.c_int, C.c_int, u8p, f32p, f32p,
-                                         i32p]
-            L.orc_quantize_rows.argtypes = [C.c_int, vp, vp, i64, i64, vp]
-            L.orc_quantize_rows_grouped.argtypes = [C.c_int, vp, vp, i64, i64,
-                                                    i64, vp]
-            L.orc_quantize_row_sigma2.argtypes = [C.c_int, f32p, vp, i64,
-                                                  C.c_float, u8p]
-            L.orc_quantize_q8k128.argtypes = [vp, i64, i64, vp]
-            L.orc_dequantize_rows.argtypes = [C.c_int, vp, i64, i64, vp]
-            L.orc_f32_to_f16.argtypes = [C.c_float]
-            L.orc_f32_to_f16.restype = C.c_uint16
-            L.orc_f16_to_f32.argtypes = [C.c_uint16]
-            L.orc_f16_to_f32.restype = C.c_float
-            _lib = L
+            _lib = _load(LIB)
     return _lib
+
+
+def _load(path):
+    L = C.CDLL(path)
+    f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+    u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+    i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
+    i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+    vp = C.c_void_p
+    i64 = C.c_int64
+    L.orc_solver_constants.argtypes = [i32p]
+    L.orc_block_bytes.argtypes = [C.c_int]
+    L.orc_block_bytes.restype = C.c_size_t
+    L.orc_block_elems.argtypes = [C.c_int]
+    L.orc_row_bytes.argtypes = [C.c_int, i64]
+    L.orc_row_bytes.restype = C.c_size_t
+    L.orc_row_sigma2.argtypes = [f32p, i64]
+    L.orc_row_sigma2.restype = C.c_float
+    L.orc_row_sigma2_f64.argtypes = [f32p, i64]
+    L.orc_row_sigma2_f64.restype = C.c_double
+    L.orc_row_weights.argtypes = [f32p, vp, i64, C.c_float, f32p]
+    L.orc_solve_sym.argtypes = [C.c_int, f32p, f32p, C.c_int, C.c_int,
+                                C.c_int, i8p, f32p, i32p]
+    L.orc_solve_asym.argtypes = [C.c_int, f32p, f32p, C.c_int, C.c_int,
+                                 C.c_int, C.c_int, u8p, f32p, f32p,
+                                 i32p]
+    L.orc_quantize_rows.argtypes = [C.c_int, vp, vp, i64, i64, vp]
+    L.orc_quantize_rows_grouped.argtypes = [C.c_int, vp, vp, i64, i64,
+                                            i64, vp]
+    L.orc_quantize_row_sigma2.argtypes = [C.c_int, f32p, vp, i64,
+                                          C.c_float, u8p]
+    L.orc_quantize_q8k128.argtypes = [vp, i64, i64, vp]
+    L.orc_dequantize_rows.argtypes = [C.c_int, vp, i64, i64, vp]
+    L.orc_f32_to_f16.argtypes = [C.c_float]
+    L.orc_f32_to_f16.restype = C.c_uint16
+    L.orc_f16_to_f32.argtypes = [C.c_uint16]
+    L.orc_f16_to_f32.restype = C.c_float
+    return L
 
 
 def _tid(t) -> int:

@@ -1,0 +1,112 @@
+"""The pins bite: plausible mistakes planted in a copy of the oracle (a dropped
+term, a wrong sign, index or operand) must each fail at least one pin.
+
+Each mutant is one textual change to oracle/qrow_oracle.c, built with the
+oracle's own flags into a temporary library and loaded in place of the real
+one; then the pin tests of test_oracle_pins.py run against it. All of this
+is CPU work.
+"""
+import importlib.util
+import inspect
+import os
+import subprocess
+
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MUTANTS = [
+    # row statistic
+    ("sigma2: sum instead of mean", "return acc / (double)n;", "return acc;"),
+    ("sigma2: |x| instead of x^2", "acc += (double)x[j] * (double)x[j];", "acc += fabs((double)x[j]);"),
+    # importances
+    ("weight: sigma2 term dropped", "sqrtf(fmaf(x[j], x[j], sigma2))", "sqrtf(fmaf(x[j], x[j], 0.0f))"),
+    ("weight: imatrix only (no magnitude term)", "w[j] = q ? q[j] * s : s;", "w[j] = q ? q[j] : s;"),
+    ("weight: imatrix by in-block offset", "w[j] = q ? q[j] * s : s;", "w[j] = q ? q[j % 32] * s : s;"),
+    # symmetric solver
+    ("sym: largest element to the short end", "float is = -c / xm;", "float is = c / xm;"),
+    ("sym: suml2 without the level", "S2 = fmaf(w[i] * l, l, S2);", "S2 = fmaf(w[i], l, S2);"),
+    ("sym: first trial always wins", "better = lhs > rhs;", "better = 0;"),
+    ("sym: scale not refitted", "*d_out = A / B;", "*d_out = 1.0f / bis;"),
+    # flips
+    ("flip: direction reversed", "? -1.0f : 1.0f;", "? 1.0f : -1.0f;"),
+    ("flip: +1 dropped from suml2 update", "fmaf(2.0f * s, L[j], 1.0f)", "fmaf(2.0f * s, L[j], 0.0f)"),
+    ("flip: operands of the test transposed", "(A1 * A1) * B > (A * A) * B1", "(A1 * A1) * B1 > (A * A) * B"),
+    ("flip: every move kept", "if (better && B1 > 0.0f && lp >= lo_level && lp <= hi_level) {",
+     "if (B1 > 0.0f && lp >= lo_level && lp <= hi_level) {"),
+    # asymmetric solver
+    ("asym: offset formula uses Sx twice", "mm = (Sll * Sx - Sl * Slx) * r;", "mm = (Sll * Sx - Sl * Sx) * r;"),
+    ("asym: levels from x instead of x - lo", "xs[i] = x[i] - lo;", "xs[i] = x[i];"),
+    ("asym: flips start from Slx + m*Sl", "float A = fmaf(-mf, bSl, bSlx), B = bSll;", "float A = fmaf(mf, bSl, bSlx), B = bSll;"),
+    ("asym: Q4_K offset may be positive", "if (k4 && mm > 0.0) {", "if (0 && k4 && mm > 0.0) {"),
+    # Q4_K super-block
+    ("q4k: sub-scale multiplied by d16", "rintf(a[j] / dA)", "rintf(a[j] * dA)"),
+    ("q4k: re-round with +dm sign flipped", "rintf((x[32 * j + i] + dm) * id)", "rintf((x[32 * j + i] - dm) * id)"),
+    ("q4k: super-scale over 64", "orc_f32_to_f16(amx / 63.0f)", "orc_f32_to_f16(amx / 64.0f)"),
+    ("f16: subnormals flushed", "if (e < -14) e = -14;", "if (e < -14) return sign;"),
+    # Q8_K_128
+    ("q8: 128 levels", "127.0f / amax", "128.0f / amax"),
+    ("q8: sums over the wrong codes", "for (int i = 0; i < 32; ++i) s += q[32 * g + i];",
+     "for (int i = 0; i < 32; ++i) s += q[i];"),
+    # packing and decoding
+    ("pack: high nibble from element i+8", "((u[i + 16] & 15) << 4)", "((u[i + 8] & 15) << 4)"),
+    ("decode: symmetric offset dropped", "o[i] = d * (float)((int)u[i] - nmax);", "o[i] = d * (float)((int)u[i]);"),
+]
+
+
+def _pins_module():
+    spec = importlib.util.spec_from_file_location("pins_for_mutants",
+                                                  os.path.join(HERE, "test_oracle_pins.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _pin_calls(mod):
+    """(name, callable) for every pin; parametrized pins get one small case."""
+    params = {
+        "test_sym_brute_force_tiny_blocks": dict(n=3, nmax=4, unit_w=False),
+        "test_asym_brute_force_tiny_blocks": dict(n=3, nmax=3),
+        "test_exact_lattice_rows_round_trip": dict(t="q4_0", nmax=8, sym=True),
+        "test_power_of_two_constant_imatrix_equals_none": dict(t="q4_k"),
+    }
+    calls = []
+    for name, fn in inspect.getmembers(mod, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        kw = params.get(name, {})
+        calls.append((name, lambda fn=fn, kw=kw: fn(**kw)))
+    # extra parametrizations that exercise the other formats
+    calls.append(("round trip q5_1", lambda: mod.test_exact_lattice_rows_round_trip("q5_1", 31, False)))
+    calls.append(("round trip q5_0", lambda: mod.test_exact_lattice_rows_round_trip("q5_0", 16, True)))
+    calls.append(("brute force sym 4/8", lambda: mod.test_sym_brute_force_tiny_blocks(4, 8, True)))
+    return calls
+
+
+def test_every_mutant_is_distinct_and_applies():
+    src = open(oracle.SRC).read()
+    for name, old, new in MUTANTS:
+        assert src.count(old) == 1, f"{name}: pattern not found exactly once"
+        assert old != new
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(oracle.SRC).read()
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new, 1))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, "-I", oracle.HERE, "-o", str(so), str(path), "-lm"],
+                   check=True, capture_output=True)
+    mod = _pins_module()
+    caught = []
+    with oracle.using_library(str(so)):
+        for pin, call in _pin_calls(mod):
+            try:
+                call()
+            except Exception as e:          # an assertion or a rejected result
+                caught.append((pin, type(e).__name__))
+                break
+    assert caught, f"no pin caught the mutant: {name}"

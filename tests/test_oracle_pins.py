@@ -324,6 +324,34 @@ def test_sym_brute_force_tiny_blocks(n, nmax, unit_w):
     assert hits >= 30          # reported: the heuristic usually finds the optimum
 
 
+def test_trial_choice_is_the_best_trial_computed_independently():
+    # The trials are recomputed here in numpy float32 from their definition
+    # (largest element to -(nmax + 0.25k); range scaled to nmax + 0.25k) and
+    # scored by their exact least-squares error: the oracle's pick (no flips)
+    # must be as good as the best of them, to float resolution.
+    rng = np.random.default_rng(22)
+    for _ in range(200):
+        x, w = random_block(rng, wspread=1.5)
+        xd, wd = np.float64(x), np.float64(w)
+        tol = 1e-6 * np.sum(wd * xd * xd)
+        i = int(np.argmax(np.abs(x)))
+        errs = []
+        for k in (0, -1, 1, -2, 2):
+            is_ = F32(-(8 + 0.25 * k)) / x[i]
+            l = np.clip(np.rint(x * is_), -8, 7)
+            errs.append(ls_sym_error(x, w, l))
+        l0, d0, _ = oracle.solve_sym(x, w, 8, F=0)
+        assert ls_sym_error(x, w, l0) <= min(errs) + tol
+        lo, hi = x.min(), x.max()
+        aerrs = []
+        for k in (0, -1, 1):
+            is_ = F32(15 + 0.25 * k) / F32(hi - lo)
+            l = np.clip(np.rint((x - lo) * is_), 0, 15)
+            aerrs.append(ls_asym_error_all(x, w, l[None, :])[0])
+        la, da, ma, _ = oracle.solve_asym(x, w, 15, F=0)
+        assert err_asym(x, w, la, da, ma) <= min(aerrs) + tol
+
+
 def test_sym_degenerate_blocks_give_zero_blocks():
     z = np.zeros(32, F32)
     l, d, info = oracle.solve_sym(z, np.ones(32, F32), 8)
@@ -477,6 +505,28 @@ def test_q4k_superblock_properties_and_layout():
             assert np.array_equal(got, ref)
     rel = np.sqrt(np.mean((y - x) ** 2) / np.mean(x ** 2))
     assert rel < 0.12                          # a 4.5-bit code is a useful code
+
+
+def test_q4k_exact_lattice_round_trip():
+    # x = D*sc_j*u - M*mn_j with D, M powers of two, sc, mn 6-bit (largest
+    # 63) and u spanning 0..15 in every sub-block: the fitted sub-scales are
+    # D*sc_j and -M*mn_j to float rounding, so the fp16 super-scales are
+    # D and M, the 6-bit values are recovered and the decode is exact.
+    rng = np.random.default_rng(23)
+    D, M = 2.0 ** -6, 2.0 ** -7
+    for _ in range(5):
+        sc = rng.integers(1, 64, 8)
+        mn = rng.integers(0, 64, 8)
+        sc[rng.integers(8)] = 63
+        mn[rng.integers(8)] = 63
+        u = rng.integers(0, 16, (8, 32))
+        u[:, 0], u[:, 1] = 0, 15
+        x = (D * sc[:, None] * u - M * mn[:, None]).astype(F32).reshape(1, 256)
+        out = oracle.quantize_rows("q4_k", x, None)[0]
+        d, dmin, sc2, mn2, u2 = parse_q4k(out)
+        assert d == F32(D) and dmin == F32(M)
+        assert list(sc2) == list(sc) and list(mn2) == list(mn)
+        assert np.array_equal(oracle.dequantize_rows("q4_k", out, 1, 256)[0], x[0])
 
 
 # --------------------------------------------------------------------------
