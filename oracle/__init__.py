@@ -21,6 +21,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qrow_oracle.c")
+SOURCES = [SRC, os.path.join(HERE, "imatrix_oracle.c")]
 LIB = os.path.join(HERE, "liborc_qrow.so")
 
 Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128 = range(6)
@@ -38,8 +39,8 @@ def build(force: bool = True) -> str:
     """Compile liborc_qrow.so with gcc (float contraction off)."""
     if force or not os.path.exists(LIB):
         tmp = LIB + ".tmp"
-        subprocess.run(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"], check=True,
-                       cwd=HERE)
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, *SOURCES, "-lm"],
+                       check=True, cwd=HERE)
         os.replace(tmp, LIB)
     return LIB
 
@@ -103,6 +104,12 @@ def _load(path):
                                           C.c_float, u8p]
     L.orc_quantize_q8k128.argtypes = [vp, i64, i64, vp]
     L.orc_dequantize_rows.argtypes = [C.c_int, vp, i64, i64, vp]
+    f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+    i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+    L.orc_imatrix_accumulate.argtypes = [f32p, i64, i64, i64, vp, i64, i64,
+                                         f64p, i64p]
+    L.orc_imatrix_merge.argtypes = [f64p, i64p, f64p, i64p, i64, i64]
+    L.orc_imatrix_finalize.argtypes = [f64p, i64p, i64, i64, f32p]
     L.orc_f32_to_f16.argtypes = [C.c_float]
     L.orc_f32_to_f16.restype = C.c_uint16
     L.orc_f16_to_f32.argtypes = [C.c_uint16]
@@ -291,6 +298,57 @@ def dequantize_rows(t, packed, n_rows: int, n_per_row: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("orc_dequantize_rows failed")
     return out
+
+
+def imatrix_new(n_experts: int, n_cols: int):
+    """A fresh accumulator state: (sums float64 [E, C], counts int64 [E])."""
+    return np.zeros((n_experts, n_cols), np.float64), np.zeros(n_experts, np.int64)
+
+
+def imatrix_accumulate(state, act, ids=None):
+    """Adds one batch to state in place. act: [T, C] (one row per token) or
+    [T, S, C] with S == top_k (one row per routed slot); ids: [T, top_k]
+    int32 expert ids, or None for a dense tensor."""
+    sums, counts = state
+    a = _f32(act)
+    if a.ndim == 2:
+        a = a[:, None, :]
+    T, S, Cc = a.shape
+    E = sums.shape[0]
+    if sums.shape != (E, Cc) or counts.shape != (E,):
+        raise ValueError("state does not match the activations")
+    if ids is None:
+        k = 0
+        pid = None
+    else:
+        idv = np.ascontiguousarray(ids, dtype=np.int32)
+        if idv.ndim != 2 or idv.shape[0] != T:
+            raise ValueError("ids must be [n_tokens, top_k]")
+        k = idv.shape[1]
+        pid = idv.ctypes.data_as(C.c_void_p)
+    rc = lib().orc_imatrix_accumulate(a, T, S, Cc, pid, k, E, sums, counts)
+    if rc != 0:
+        raise ValueError("orc_imatrix_accumulate: invalid arguments")
+    return state
+
+
+def imatrix_merge(state, other):
+    """Adds other's sums and counts into state (in place)."""
+    sums, counts = state
+    s2 = np.ascontiguousarray(other[0], np.float64)
+    c2 = np.ascontiguousarray(other[1], np.int64)
+    if s2.shape != sums.shape or c2.shape != counts.shape:
+        raise ValueError("states differ in shape")
+    lib().orc_imatrix_merge(sums, counts, s2, c2, sums.shape[0], sums.shape[1])
+    return state
+
+
+def imatrix_finalize(state) -> np.ndarray:
+    """Importances q [E, C] float32 (0 for experts with no tokens)."""
+    sums, counts = state
+    q = np.zeros(sums.shape, np.float32)
+    lib().orc_imatrix_finalize(sums, counts, sums.shape[0], sums.shape[1], q)
+    return q
 
 
 def f32_to_f16_bits(v: float) -> int:

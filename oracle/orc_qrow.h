@@ -102,6 +102,20 @@ int orc_quantize_q8k128(const float *x, int64_t n_rows, int64_t n_per_row,
 int orc_dequantize_rows(int type, const uint8_t *in, int64_t n_rows,
                         int64_t n_per_row, float *out);
 
+/* Importance-matrix accumulator (imatrix_oracle.c). State: sums
+ * [n_experts, n_cols] double and counts [n_experts], added to in place.
+ * act is [n_tokens, n_slots, n_cols]; ids is [n_tokens, top_k] or NULL for
+ * a dense tensor (then n_experts == 1 and n_slots == 1). */
+int orc_imatrix_accumulate(const float *act, int64_t n_tokens, int64_t n_slots,
+                           int64_t n_cols, const int32_t *ids, int64_t top_k,
+                           int64_t n_experts, double *sums, int64_t *counts);
+int orc_imatrix_merge(double *sums, int64_t *counts, const double *src_sums,
+                      const int64_t *src_counts, int64_t n_experts,
+                      int64_t n_cols);
+/* q = sums / count in double, rounded once to float; 0 where count == 0. */
+int orc_imatrix_finalize(const double *sums, const int64_t *counts,
+                         int64_t n_experts, int64_t n_cols, float *q);
+
 /* IEEE-754 binary16 conversions (round to nearest-even, subnormals kept). */
 uint16_t orc_f32_to_f16(float f);
 float    orc_f16_to_f32(uint16_t h);

@@ -20,6 +20,15 @@ available here). Their shapes and value distributions are:
 * ``moe_256x2048x7168``: 256 experts of bf16 [2048, 7168], x = 0.01*N(0,1) *
   s_{e,r} with s ~ LogNormal(0, 0.5) per expert row; per-expert importance
   LogNormal(0, 2), with 26 experts (10%) set to 1e-6.
+* ``imatrix_moe_256x8_4096x7168``: importance accumulation for a stacked
+  expert tensor: 4096 tokens of bf16 hidden states [4096, 7168] (one row per
+  token, seen by each of its experts), a[t, c] = s_c * N(0,1) with channel
+  scales s_c ~ LogNormal(0, 1) and 0.1% of the channels (at least one)
+  multiplied by 20; each token routed to 8 distinct experts out of 256 by
+  Gumbel top-k over log-popularities N(0, 0.5), with 3 experts that are never
+  routed (partial coverage).
+* ``imatrix_dense_4096x4096``: importance accumulation for a dense tensor:
+  4096 tokens of bf16 activations [4096, 4096] drawn as above.
 
 Two back-ends draw the same recipes: numpy (CPU, used by the CPU tests and by
 small GPU tests) and torch on the GPU (used for the multi-GB stacks). The two
@@ -43,6 +52,13 @@ WORKLOADS = {
     "moe_256x2048x7168": dict(type="q4_k", dtype="bf16", n_experts=256,
                               n_rows=2048, n_per_row=7168, seed=1005,
                               n_zero_experts=26),
+    "imatrix_moe_256x8_4096x7168": dict(type="imatrix", dtype="bf16",
+                                        n_tokens=4096, n_cols=7168,
+                                        n_experts=256, top_k=8, n_slots=1,
+                                        n_dead=3, seed=1006),
+    "imatrix_dense_4096x4096": dict(type="imatrix", dtype="bf16",
+                                    n_tokens=4096, n_cols=4096, n_experts=1,
+                                    top_k=0, n_slots=1, n_dead=0, seed=1007),
 }
 
 # The seven matrices of one 7B-shaped layer: (name, type, n_rows, n_per_row).
@@ -148,6 +164,47 @@ def moe_expert(e: int, n_rows=2048, n_per_row=7168, seed=1005, rows=None):
     z = 0.01 * rng(seed, "x", e).standard_normal((n_rows, n_per_row))[:r]
     s = np.exp(0.5 * rng(seed, "rowscale", e).standard_normal((n_rows, 1)))[:r]
     return round_to_bf16((z * s).astype(np.float32))
+
+
+def calib_activations(n_tokens, n_cols, seed, n_slots=1, outlier_frac=1e-3,
+                      outlier_gain=20.0, bf16=True):
+    """Calibration-like activations [n_tokens, n_slots, n_cols] (n_slots == 1
+    gives [n_tokens, n_cols]): per-channel scales LogNormal(0, 1), a few
+    outlier channels; float32 holding bf16 values when ``bf16``."""
+    g = rng(seed, "act")
+    s = np.exp(rng(seed, "channel-scale").standard_normal(n_cols))
+    k = max(1, int(round(outlier_frac * n_cols)))
+    s[rng(seed, "outlier-channels").choice(n_cols, size=k, replace=False)] *= outlier_gain
+    shape = (n_tokens, n_cols) if n_slots == 1 else (n_tokens, n_slots, n_cols)
+    a = (g.standard_normal(shape) * s).astype(np.float32)
+    return round_to_bf16(a) if bf16 else a
+
+
+def routing_ids(n_tokens, n_experts, top_k, seed, n_dead=0, spread=0.5):
+    """[n_tokens, top_k] int32: top_k distinct experts per token, drawn by
+    Gumbel top-k over log-popularities N(0, spread); ``n_dead`` experts are
+    never chosen. Each row lists its experts in decreasing score order."""
+    if n_experts - n_dead < top_k:
+        raise ValueError("not enough live experts for top_k")
+    logp = spread * rng(seed, "popularity").standard_normal(n_experts)
+    if n_dead:
+        logp[rng(seed, "dead").choice(n_experts, size=n_dead, replace=False)] = -np.inf
+    score = logp + rng(seed, "gumbel").gumbel(size=(n_tokens, n_experts))
+    top = np.argpartition(-score, top_k - 1, axis=1)[:, :top_k]
+    order = np.argsort(-np.take_along_axis(score, top, axis=1), axis=1, kind="stable")
+    return np.take_along_axis(top, order, axis=1).astype(np.int32)
+
+
+def imatrix_inputs(name):
+    """(activations, ids or None, n_experts) of an imatrix workload."""
+    w = WORKLOADS[name]
+    a = calib_activations(w["n_tokens"], w["n_cols"], w["seed"], w["n_slots"],
+                          bf16=w["dtype"] == "bf16")
+    if w["top_k"] == 0:
+        return a, None, 1
+    ids = routing_ids(w["n_tokens"], w["n_experts"], w["top_k"], w["seed"],
+                      n_dead=w["n_dead"])
+    return a, ids, w["n_experts"]
 
 
 # --------------------------------------------------------------------------

@@ -1,10 +1,10 @@
 """The pins bite: plausible mistakes planted in a copy of the oracle (a dropped
 term, a wrong sign, index or operand) must each fail at least one pin.
 
-Each mutant is one textual change to oracle/qrow_oracle.c, built with the
-oracle's own flags into a temporary library and loaded in place of the real
-one; then the pin tests of test_oracle_pins.py run against it. All of this
-is CPU work.
+Each mutant is one textual change to one of the oracle's C sources, built
+with the oracle's own flags into a temporary library and loaded in place of
+the real one; then the pin tests (test_oracle_pins.py and
+test_imatrix_oracle_pins.py) run against it. All of this is CPU work.
 """
 import importlib.util
 import inspect
@@ -53,18 +53,38 @@ MUTANTS = [
     # packing and decoding
     ("pack: high nibble from element i+8", "((u[i + 16] & 15) << 4)", "((u[i + 8] & 15) << 4)"),
     ("decode: symmetric offset dropped", "o[i] = d * (float)((int)u[i] - nmax);", "o[i] = d * (float)((int)u[i]);"),
+    # importance-matrix accumulator
+    ("imatrix: |a| instead of a^2", "acc[c] += (double)a[c] * (double)a[c];", "acc[c] += fabs((double)a[c]);"),
+    ("imatrix: repeated expert counted twice", "                    continue;                       /* already counted */",
+     "                    ;"),
+    ("imatrix: slot row ignored", "const int64_t row = t * n_slots + (n_slots == 1 ? 0 : s);",
+     "const int64_t row = t * n_slots;"),
+    ("imatrix: count per slot", "counts[e] += 1;", "counts[e] += n_route;"),
+    ("imatrix: mean over count + 1", "/ (double)counts[e])", "/ (double)(counts[e] + 1))"),
+    ("imatrix: merge drops the counts", "counts[e] += src_counts[e];", "(void)src_counts;"),
+    ("imatrix: merge overwrites the sums", "sums[e * n_cols + c] += src_sums[e * n_cols + c];",
+     "sums[e * n_cols + c] = src_sums[e * n_cols + c];"),
 ]
 
 
-def _pins_module():
-    spec = importlib.util.spec_from_file_location("pins_for_mutants",
-                                                  os.path.join(HERE, "test_oracle_pins.py"))
-    mod = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(mod)
-    return mod
+PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py")
 
 
-def _pin_calls(mod):
+def _pins_modules():
+    mods = []
+    for i, f in enumerate(PIN_FILES):
+        spec = importlib.util.spec_from_file_location(f"pins_for_mutants_{i}", os.path.join(HERE, f))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mods.append(mod)
+    return mods
+
+
+def _sources():
+    return {p: open(p).read() for p in oracle.SOURCES}
+
+
+def _pin_calls(mods):
     """(name, callable) for every pin; parametrized pins get one small case."""
     params = {
         "test_sym_brute_force_tiny_blocks": dict(n=3, nmax=4, unit_w=False),
@@ -73,11 +93,13 @@ def _pin_calls(mod):
         "test_power_of_two_constant_imatrix_equals_none": dict(t="q4_k"),
     }
     calls = []
-    for name, fn in inspect.getmembers(mod, inspect.isfunction):
-        if not name.startswith("test_"):
-            continue
-        kw = params.get(name, {})
-        calls.append((name, lambda fn=fn, kw=kw: fn(**kw)))
+    for mod in mods:
+        for name, fn in inspect.getmembers(mod, inspect.isfunction):
+            if not name.startswith("test_") or fn.__module__ != mod.__name__:
+                continue
+            kw = params.get(name, {})
+            calls.append((name, lambda fn=fn, kw=kw: fn(**kw)))
+    mod = mods[0]
     # extra parametrizations that exercise the other formats
     calls.append(("round trip q5_1", lambda: mod.test_exact_lattice_rows_round_trip("q5_1", 31, False)))
     calls.append(("round trip q5_0", lambda: mod.test_exact_lattice_rows_round_trip("q5_0", 16, True)))
@@ -86,24 +108,26 @@ def _pin_calls(mod):
 
 
 def test_every_mutant_is_distinct_and_applies():
-    src = open(oracle.SRC).read()
+    srcs = _sources()
     for name, old, new in MUTANTS:
-        assert src.count(old) == 1, f"{name}: pattern not found exactly once"
+        assert sum(t.count(old) for t in srcs.values()) == 1, f"{name}: pattern not found exactly once"
         assert old != new
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(tmp_path, name, old, new):
-    src = open(oracle.SRC).read()
-    path = tmp_path / "mutant.c"
-    path.write_text(src.replace(old, new, 1))
+    paths = []
+    for p, text in _sources().items():
+        path = tmp_path / os.path.basename(p)
+        path.write_text(text.replace(old, new, 1))
+        paths.append(str(path))
     so = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", *oracle.CFLAGS, "-I", oracle.HERE, "-o", str(so), str(path), "-lm"],
+    subprocess.run(["gcc", *oracle.CFLAGS, "-I", oracle.HERE, "-o", str(so), *paths, "-lm"],
                    check=True, capture_output=True)
-    mod = _pins_module()
+    mods = _pins_modules()
     caught = []
     with oracle.using_library(str(so)):
-        for pin, call in _pin_calls(mod):
+        for pin, call in _pin_calls(mods):
             try:
                 call()
             except Exception as e:          # an assertion or a rejected result
