@@ -13,11 +13,12 @@
 //       Q8_K_128 activation blocks.
 //
 // Execution model (gfx950, wave64):
-//  * Weight rows: one workgroup of one wave per row. The wave streams the
-//    row from HBM once with coalesced 16-byte loads into LDS (32-element
-//    groups padded to a 16-byte multiple so that per-lane group reads are
-//    bank-conflict free) while accumulating sum x^2 in double; a wave
-//    reduction gives sigma2. Each lane then owns one 32-element group at a
+//  * Weight rows: one workgroup per row, of one wave per 64 groups of 32
+//    weights (at most eight waves). The workgroup streams the row from HBM
+//    once with coalesced 16-byte loads into LDS (32-element groups padded to
+//    a 16-byte multiple so that per-lane group reads are bank-conflict free)
+//    while accumulating sum x^2 in double; a workgroup reduction gives
+//    sigma2. Each lane then owns one 32-element group at a
 //    time and solves it entirely in VGPRs: importances, trial scales,
 //    least-squares sums, the sequential flip passes (sequential within a
 //    lane, parallel across the 64 lanes), packing. For Q4_K, eight
@@ -44,6 +45,7 @@
 #include <stdio.h>
 
 #include "qrow.h"
+#include "qr_internal.h"
 
 namespace {
 
@@ -796,15 +798,6 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 // -------------------------------------------------------------------------
 // host side
 
-thread_local char g_err[512];
-
-int fail(int code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof g_err, fmt, ap);
-  va_end(ap);
-  return code;
-}
 
 int block_elems(int t) {
   switch (t) {
@@ -827,13 +820,8 @@ size_t block_bytes(int t) {
   }
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned16(const void* p) { return qr_aligned(p, 16); }
 
-int check_launch(const char* what) {
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(QR_EDEVICE, "%s: %s", what, hipGetErrorString(e));
-  return QR_OK;
-}
 
 template <int TYPE, bool BF16>
 int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_row, int64_t rows_per_group,
@@ -847,12 +835,12 @@ int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_r
   if (lds > 65536 && !attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-    if (e != hipSuccess) return fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return qr_fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE * waves), lds, stream, x, imatrix, n_per_row,
                      rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes);
-  return check_launch("k_quantize_rows");
+  return qr_check_launch("k_quantize_rows");
 }
 
 template <bool BF16>
@@ -864,7 +852,7 @@ int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, in
     case QR_Q5_0: return launch_rows<QR_Q5_0, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
     case QR_Q5_1: return launch_rows<QR_Q5_1, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
     case QR_Q4_K: return launch_rows<QR_Q4_K, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
-    default: return fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
+    default: return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   }
 }
 
@@ -876,6 +864,24 @@ int grid_for(int64_t work_items, int per_block) {
 }
 
 }  // namespace
+
+static thread_local char g_err[512];
+
+void qr_clear_error() { g_err[0] = 0; }
+
+int qr_fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int qr_check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return qr_fail(QR_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return QR_OK;
+}
 
 extern "C" {
 
@@ -900,26 +906,26 @@ void qr_solver_constants(int32_t* c) {
 
 int qr_quantize_rows_grouped(int t, int src, const void* x, const float* imatrix, int64_t n_groups,
                              int64_t rows_per_group, int64_t n_per_row, void* out, void* stream) {
-  g_err[0] = 0;
-  if (t < QR_Q4_0 || t > QR_Q4_K) return fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
-  if (src != QR_F32 && src != QR_BF16) return fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
-  if (n_groups < 0 || rows_per_group < 0) return fail(QR_EINVAL_SHAPE, "negative row count");
+  qr_clear_error();
+  if (t < QR_Q4_0 || t > QR_Q4_K) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
+  if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
+  if (n_groups < 0 || rows_per_group < 0) return qr_fail(QR_EINVAL_SHAPE, "negative row count");
   const int be = block_elems(t);
   const int64_t max_row = src == QR_F32 ? QR_MAX_ROW_F32 : QR_MAX_ROW_BF16;
   if (n_per_row <= 0 || n_per_row % be != 0 || n_per_row > max_row)
-    return fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d and at most %lld",
+    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d and at most %lld",
                 (long long)n_per_row, be, (long long)max_row);
   if (rows_per_group != 0 && n_groups > INT64_MAX / rows_per_group)
-    return fail(QR_EOVERFLOW, "n_groups * rows_per_group overflows");
+    return qr_fail(QR_EOVERFLOW, "n_groups * rows_per_group overflows");
   const int64_t n_rows = n_groups * rows_per_group;
   if (n_rows == 0) return QR_OK;
-  if (n_rows > (int64_t)UINT32_MAX) return fail(QR_EOVERFLOW, "n_rows=%lld exceeds 2^32-1", (long long)n_rows);
+  if (n_rows > (int64_t)UINT32_MAX) return qr_fail(QR_EOVERFLOW, "n_rows=%lld exceeds 2^32-1", (long long)n_rows);
   const size_t rb = qr_row_bytes(t, n_per_row);
   if ((uint64_t)n_rows > SIZE_MAX / rb || (uint64_t)n_rows > SIZE_MAX / ((uint64_t)n_per_row * 4))
-    return fail(QR_EOVERFLOW, "buffer size overflows");
-  if (!x || !out) return fail(QR_EINVAL_PTR, "x and out must be non-NULL");
+    return qr_fail(QR_EOVERFLOW, "buffer size overflows");
+  if (!x || !out) return qr_fail(QR_EINVAL_PTR, "x and out must be non-NULL");
   if (!aligned16(x) || !aligned16(out) || (imatrix && !aligned16(imatrix)))
-    return fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+    return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return src == QR_F32
              ? dispatch_rows<false>(t, x, imatrix, n_rows, (int)n_per_row, rows_per_group, out, rb, s)
@@ -929,23 +935,23 @@ int qr_quantize_rows_grouped(int t, int src, const void* x, const float* imatrix
 int qr_quantize_rows(int t, int src, const void* x, const float* imatrix, int64_t n_rows, int64_t n_per_row,
                      void* out, void* stream) {
   if (n_rows < 0) {
-    g_err[0] = 0;
-    return fail(QR_EINVAL_SHAPE, "negative row count");
+    qr_clear_error();
+    return qr_fail(QR_EINVAL_SHAPE, "negative row count");
   }
   return qr_quantize_rows_grouped(t, src, x, imatrix, 1, n_rows, n_per_row, out, stream);
 }
 
 int qr_quantize_activations_q8k128(int src, const void* x, int64_t n_rows, int64_t n_per_row, void* out,
                                    void* stream) {
-  g_err[0] = 0;
-  if (src != QR_F32 && src != QR_BF16) return fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
+  qr_clear_error();
+  if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
   if (n_rows < 0 || n_per_row <= 0 || n_per_row % 128 != 0)
-    return fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of 128", (long long)n_per_row);
+    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of 128", (long long)n_per_row);
   if (n_rows == 0) return QR_OK;
-  if (n_per_row / 128 > INT32_MAX) return fail(QR_EOVERFLOW, "row too long");
-  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return fail(QR_EOVERFLOW, "size overflows");
-  if (!x || !out) return fail(QR_EINVAL_PTR, "x and out must be non-NULL");
-  if (!aligned16(x) || !aligned16(out)) return fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+  if (n_per_row / 128 > INT32_MAX) return qr_fail(QR_EOVERFLOW, "row too long");
+  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return qr_fail(QR_EOVERFLOW, "size overflows");
+  if (!x || !out) return qr_fail(QR_EINVAL_PTR, "x and out must be non-NULL");
+  if (!aligned16(x) || !aligned16(out)) return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
   const int64_t n_blocks = n_rows * (n_per_row / 128);
   const int64_t chunks = (n_blocks + 2 * Q8_STEPS - 1) / (2 * Q8_STEPS);
   const int grid = grid_for(chunks, 4);
@@ -956,20 +962,20 @@ int qr_quantize_activations_q8k128(int src, const void* x, int64_t n_rows, int64
   else
     hipLaunchKernelGGL(k_quantize_q8k128<true>, dim3(grid), dim3(256), 0, s, x, n_blocks,
                        reinterpret_cast<uint8_t*>(out));
-  return check_launch("k_quantize_q8k128");
+  return qr_check_launch("k_quantize_q8k128");
 }
 
 int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row, float* out, void* stream) {
-  g_err[0] = 0;
+  qr_clear_error();
   const int be = block_elems(t);
-  if (be == 0) return fail(QR_EINVAL_TYPE, "unknown type %d", t);
+  if (be == 0) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
   if (n_rows < 0 || n_per_row <= 0 || n_per_row % be != 0)
-    return fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d", (long long)n_per_row, be);
+    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d", (long long)n_per_row, be);
   if (n_rows == 0) return QR_OK;
-  if (n_per_row > INT32_MAX) return fail(QR_EOVERFLOW, "row too long");
-  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return fail(QR_EOVERFLOW, "size overflows");
-  if (!in || !out) return fail(QR_EINVAL_PTR, "in and out must be non-NULL");
-  if (!aligned16(in) || !aligned16(out)) return fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+  if (n_per_row > INT32_MAX) return qr_fail(QR_EOVERFLOW, "row too long");
+  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return qr_fail(QR_EOVERFLOW, "size overflows");
+  if (!in || !out) return qr_fail(QR_EINVAL_PTR, "in and out must be non-NULL");
+  if (!aligned16(in) || !aligned16(out)) return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
   const int64_t n_units = n_rows * (n_per_row / QK);
   const int grid = grid_for((n_units * 8 + DQ_STEPS - 1) / DQ_STEPS, 256);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -982,7 +988,7 @@ int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row,
     case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
     default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
   }
-  return check_launch("k_dequantize");
+  return qr_check_launch("k_dequantize");
 }
 
 }  // extern "C"

@@ -1,7 +1,7 @@
 """Python binding of libqrow.so (argument marshalling only).
 
 Every function has the name of the C entry point it calls (see
-include/qrow.h) and takes torch tensors that live on the GPU; all arithmetic
+include/qrow.h and include/qrow_imatrix.h) and takes torch tensors that live on the GPU; all arithmetic
 runs in the library's HIP kernels. torch provides device memory and the
 stream. There is no CPU fallback: without the built library or a GPU the
 calls raise.
@@ -24,11 +24,14 @@ TYPES = {"q4_0": QR_Q4_0, "q4_1": QR_Q4_1, "q5_0": QR_Q5_0, "q5_1": QR_Q5_1,
 ERRORS = {-1: "QR_EINVAL_TYPE", -2: "QR_EINVAL_SHAPE", -3: "QR_EINVAL_PTR",
           -4: "QR_EOVERFLOW", -5: "QR_EDEVICE"}
 
-# Every symbol include/qrow.h declares.
+# Every symbol include/qrow.h and include/qrow_imatrix.h declare.
 EXPORTS = ("qr_quantize_rows", "qr_quantize_rows_grouped",
            "qr_quantize_activations_q8k128", "qr_dequantize_rows",
            "qr_row_bytes", "qr_block_elems", "qr_solver_constants",
-           "qr_last_error")
+           "qr_last_error", "qr_imatrix_workspace_bytes",
+           "qr_imatrix_accumulate", "qr_imatrix_merge",
+           "qr_imatrix_finalize")
+IMX_MAX_EXPERTS, IMX_MAX_TOP_K = 1024, 64
 
 
 class QrowError(RuntimeError):
@@ -60,9 +63,15 @@ def load_library(path: str = LIB_PATH):
         L.qr_block_elems.argtypes = [i32]
         L.qr_solver_constants.argtypes = [C.POINTER(C.c_int32)]
         L.qr_last_error.restype = C.c_char_p
+        L.qr_imatrix_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.qr_imatrix_workspace_bytes.restype = C.c_size_t
+        L.qr_imatrix_accumulate.argtypes = [i32, vp, i64, i64, i64, vp, i64,
+                                            i64, vp, vp, vp, C.c_size_t, vp]
+        L.qr_imatrix_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+        L.qr_imatrix_finalize.argtypes = [vp, vp, i64, i64, vp, vp]
         for name in (n for n in EXPORTS if n not in
                      ("qr_row_bytes", "qr_block_elems", "qr_last_error",
-                      "qr_solver_constants")):
+                      "qr_solver_constants", "qr_imatrix_workspace_bytes")):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -192,4 +201,94 @@ def qr_dequantize_rows(t, packed: torch.Tensor, n_rows: int, n_per_row: int,
     _check(load_library().qr_dequantize_rows(
         tid, C.c_void_p(packed.data_ptr()), n_rows, n_per_row,
         C.c_void_p(out.data_ptr()), _stream(packed, stream)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# importance-matrix accumulator (include/qrow_imatrix.h)
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def qr_imatrix_workspace_bytes(n_tokens: int, top_k: int, n_experts: int,
+                               n_cols: int) -> int:
+    return int(load_library().qr_imatrix_workspace_bytes(n_tokens, top_k,
+                                                         n_experts, n_cols))
+
+
+def imatrix_state(n_experts: int, n_cols: int, device):
+    """A fresh accumulator: (sums float64 [E, C], counts int64 [E]), zeros."""
+    return (torch.zeros((n_experts, n_cols), dtype=torch.float64, device=device),
+            torch.zeros(n_experts, dtype=torch.int64, device=device))
+
+
+def _check_state(sums, counts, n_experts=None, n_cols=None):
+    if (not isinstance(sums, torch.Tensor) or not sums.is_cuda or sums.dtype != torch.float64
+            or sums.dim() != 2 or not sums.is_contiguous()):
+        raise ValueError("sums must be a contiguous CUDA float64 [n_experts, n_cols] tensor")
+    if (not isinstance(counts, torch.Tensor) or not counts.is_cuda or counts.dtype != torch.int64
+            or tuple(counts.shape) != (sums.shape[0],) or not counts.is_contiguous()):
+        raise ValueError("counts must be a contiguous CUDA int64 [n_experts] tensor")
+    if n_experts is not None and sums.shape[0] != n_experts:
+        raise ValueError("sums has the wrong number of experts")
+    if n_cols is not None and sums.shape[1] != n_cols:
+        raise ValueError("sums has the wrong number of columns")
+
+
+def qr_imatrix_accumulate(act: torch.Tensor, sums: torch.Tensor, counts: torch.Tensor,
+                          ids=None, workspace=None, stream=None):
+    """Adds act to the state (sums, counts) in place.
+
+    act: [n_tokens, n_cols] (one row per token) or [n_tokens, top_k, n_cols]
+    (one row per routed slot), fp32 or bf16, on the GPU. ids: int32
+    [n_tokens, top_k] expert ids on the GPU, or None for a dense tensor.
+    workspace: a CUDA uint8 tensor of at least qr_imatrix_workspace_bytes
+    bytes, or None to have one allocated here."""
+    if not isinstance(act, torch.Tensor) or not act.is_cuda or not act.is_contiguous():
+        raise TypeError("act must be a contiguous CUDA tensor")
+    if act.dim() == 2:
+        n_tokens, n_cols = act.shape
+        n_slots = 1
+    elif act.dim() == 3:
+        n_tokens, n_slots, n_cols = act.shape
+    else:
+        raise ValueError("act must be [n_tokens, n_cols] or [n_tokens, n_slots, n_cols]")
+    _check_state(sums, counts, n_cols=n_cols)
+    n_experts = sums.shape[0]
+    top_k = 0
+    if ids is not None:
+        if (not ids.is_cuda or ids.dtype != torch.int32 or ids.dim() != 2
+                or ids.shape[0] != n_tokens or not ids.is_contiguous()):
+            raise ValueError("ids must be a contiguous CUDA int32 [n_tokens, top_k] tensor")
+        top_k = ids.shape[1]
+    need = qr_imatrix_workspace_bytes(n_tokens, top_k, n_experts, n_cols)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=act.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().qr_imatrix_accumulate(
+        _src_dtype(act), _ptr(act), n_tokens, n_slots, n_cols, _ptr(ids), top_k,
+        n_experts, _ptr(sums), _ptr(counts), _ptr(workspace), ws_bytes,
+        _stream(act, stream)))
+    return sums, counts
+
+
+def qr_imatrix_merge(sums, counts, src_sums, src_counts, stream=None):
+    """(sums, counts) += (src_sums, src_counts), in place."""
+    _check_state(sums, counts)
+    _check_state(src_sums, src_counts, sums.shape[0], sums.shape[1])
+    _check(load_library().qr_imatrix_merge(
+        _ptr(sums), _ptr(counts), _ptr(src_sums), _ptr(src_counts),
+        sums.shape[0], sums.shape[1], _stream(sums, stream)))
+    return sums, counts
+
+
+def qr_imatrix_finalize(sums, counts, out=None, stream=None):
+    """Importances q = sums / counts as fp32 [n_experts, n_cols] (0 where a
+    count is 0)."""
+    _check_state(sums, counts)
+    out = _out(out, tuple(sums.shape), torch.float32, sums.device)
+    _check(load_library().qr_imatrix_finalize(
+        _ptr(sums), _ptr(counts), sums.shape[0], sums.shape[1], _ptr(out),
+        _stream(sums, stream)))
     return out

@@ -2,6 +2,7 @@
 declares, agrees with the oracle on formats and solver constants, and
 rejects bad arguments before touching the GPU (no compute calls here)."""
 import ctypes as C
+import glob
 import os
 import re
 
@@ -12,13 +13,16 @@ import oracle
 from post_weight_quantization_row_amd import qrow
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "qrow.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qr_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(qr_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 8
+    assert len(HEADERS) == 2 and len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(qrow.EXPORTS) == names
@@ -86,3 +90,55 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         qrow.qr_quantize_rows("q4_0", torch.zeros(4, 256), None)
+
+
+def test_imatrix_workspace_sizes():
+    ws = qrow.qr_imatrix_workspace_bytes
+    # dense, few tokens: one slab, nothing needed
+    assert ws(100, 0, 1, 4096) == 0
+    # dense, 4096 tokens x 8 chunks of 512 columns: 64 slabs of 64 tokens,
+    # double partials [64, 1, 4096] + int32 counts [64, 1] (256-byte aligned)
+    assert ws(4096, 0, 1, 4096) == 64 * 4096 * 8 + 256
+    # 256 experts x 14 chunks already fill the chip: only the routing bitmap
+    assert ws(4096, 8, 256, 7168) == 256 * 128 * 4
+    # invalid shapes give 0
+    assert ws(4096, 0, 2, 4096) == 0 and ws(4096, 8, 256, 7) == 0
+    assert ws(-1, 0, 1, 64) == 0 and ws(16, 65, 4, 64) == 0
+
+
+def test_imatrix_argument_validation_without_a_gpu(lib):
+    fake = C.c_void_p(0x10000)       # never dereferenced: calls fail first
+    acc = lib.qr_imatrix_accumulate
+    # src dtype
+    assert acc(2, fake, 16, 1, 64, None, 0, 1, fake, fake, None, 0, None) == -1
+    # n_cols not a multiple of 8, too many experts, dense with experts
+    assert acc(0, fake, 16, 1, 60, None, 0, 1, fake, fake, None, 0, None) == -2
+    assert acc(0, fake, 16, 1, 64, fake, 2, 1025, fake, fake, None, 0, None) == -2
+    assert acc(0, fake, 16, 1, 64, None, 0, 2, fake, fake, None, 0, None) == -2
+    assert "dense tensor" in qrow.qr_last_error()
+    # routed (top_k > 0) without ids
+    assert acc(0, fake, 16, 1, 64, None, 2, 4, fake, fake, fake, 1 << 20, None) == -3
+    # top_k and slots
+    assert acc(0, fake, 16, 1, 64, fake, 65, 8, fake, fake, None, 0, None) == -2
+    assert acc(0, fake, 16, 3, 64, fake, 2, 8, fake, fake, None, 0, None) == -2
+    # too many rows for int32 row indices
+    assert acc(0, fake, 2 ** 31, 1, 64, fake, 2, 8, fake, fake, None, 0, None) == -4
+    # no tokens: a no-op, even with NULL pointers
+    assert acc(0, None, 0, 1, 64, None, 0, 1, None, None, None, 0, None) == 0
+    # pointers and alignment
+    assert acc(0, None, 16, 1, 64, None, 0, 1, fake, fake, None, 0, None) == -3
+    assert acc(0, C.c_void_p(0x10008), 16, 1, 64, None, 0, 1, fake, fake, None, 0, None) == -3
+    assert acc(0, fake, 16, 1, 64, C.c_void_p(0x10002), 2, 4, fake, fake, None, 0, None) == -3
+    # a routed call needs the bitmap workspace: missing, too small, misaligned
+    need = lib.qr_imatrix_workspace_bytes(16, 2, 4, 64)
+    assert need > 0
+    assert acc(0, fake, 16, 1, 64, fake, 2, 4, fake, fake, None, 0, None) == -3
+    assert acc(0, fake, 16, 1, 64, fake, 2, 4, fake, fake, fake, need - 1, None) == -2
+    assert acc(0, fake, 16, 1, 64, fake, 2, 4, fake, fake, C.c_void_p(0x10010), need, None) == -3
+    # merge and finalize
+    assert lib.qr_imatrix_merge(fake, fake, fake, fake, -1, 8, None) == -2
+    assert lib.qr_imatrix_merge(None, None, None, None, 0, 8, None) == 0
+    assert lib.qr_imatrix_merge(fake, None, fake, fake, 2, 8, None) == -3
+    assert lib.qr_imatrix_finalize(fake, fake, 2, -8, fake, None) == -2
+    assert lib.qr_imatrix_finalize(fake, fake, 2, 8, None, None) == -3
+    assert lib.qr_imatrix_finalize(None, None, 0, 8, None, None) == 0
