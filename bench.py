@@ -8,8 +8,11 @@ qr_quantize_rows over the whole matrix: load, row statistic, importances,
 trial scales, least squares, flips, super-block scales, packing.
 
 Protocol: W untimed warm-up steps, then K timed steps. Before every step a
-1 GiB buffer is overwritten (outside the timed interval) so that neither L2
-nor the 256 MB Infinity Cache holds the input. Each step is bracketed by HIP
+1 GiB buffer is read (outside the timed interval) so that neither L2 nor the
+256 MB Infinity Cache holds the input. It is read rather than written so
+that no dirty lines of the flush buffer are left to be written back to HBM
+inside the timed interval (a written flush slows streaming kernels by up to
+a third that way). Each step is bracketed by HIP
 events recorded on the stream the kernel is launched on; ms_per_step is
 their mean. The whole loop is bracketed by torch.cuda.synchronize().
 
@@ -59,17 +62,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def evict(flush):
+    """Reads the whole flush buffer (1 GiB), evicting L2 and Infinity Cache."""
+    import torch
+    torch.sum(flush[0], dim=0, out=flush[1])
+
+
 def timed_steps(fn, steps, warmup, flush):
     import torch
     for _ in range(warmup):
-        flush.fill_(1.0)
+        evict(flush)
         fn()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        flush.fill_(float(i))
+        evict(flush)
         starts[i].record()
         fn()
         ends[i].record()
@@ -81,6 +90,7 @@ def timed_steps(fn, steps, warmup, flush):
 
 def _setup(name, dev):
     """Returns (step function, algorithmic bytes per launch, elements)."""
+    import numpy as np
     import torch
     from post_weight_quantization_row_amd import qrow, synth
     if name == "q4_k_11008x4096":
@@ -121,6 +131,19 @@ def _setup(name, dev):
         out = torch.empty((x.shape[0], qrow.qr_row_bytes("q4_k", 7168)), dtype=torch.uint8, device=dev)
         return (lambda: qrow.qr_quantize_rows_grouped("q4_k", x, q, 2048, out=out),
                 x.numel() * 2 + q.numel() * 4 + out.numel(), x.numel())
+    if name.startswith("imatrix_"):
+        a, ids, E = synth.imatrix_inputs(name)
+        w = synth.WORKLOADS[name]
+        bits = synth.f32_to_bf16_bits(a)
+        ad = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        idd = None if ids is None else torch.from_numpy(ids).to(dev)
+        sums, counts = qrow.imatrix_state(E, w["n_cols"], dev)
+        need = qrow.qr_imatrix_workspace_bytes(w["n_tokens"], w["top_k"], E, w["n_cols"])
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        # unique activation bytes, routing ids, state read and written
+        nb = ad.numel() * 2 + (0 if ids is None else ids.nbytes) + 2 * (sums.numel() * 8 + counts.numel() * 8)
+        return (lambda: qrow.qr_imatrix_accumulate(ad, sums, counts, idd, workspace=ws),
+                nb, ad.numel())
     if name == "copy_1gib":
         # plain device copy of a known size: calibrates the HBM byte counters
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -129,9 +152,11 @@ def _setup(name, dev):
     raise ValueError(name)
 
 
+IMATRIX_WORKLOADS = ("imatrix_moe_256x8_4096x7168", "imatrix_moe_slots_256x8_4096x2048",
+                     "imatrix_dense_4096x4096")
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "copy_1gib")
+                  "moe_256x2048x7168", "copy_1gib") + IMATRIX_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -175,7 +200,8 @@ def main():
         sys.exit(1)
     qrow.load_library()
     dev = torch.device("cuda:0")
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    flush = (torch.ones(1 << 28, dtype=torch.float32, device=dev),   # 1 GiB
+             torch.zeros((), dtype=torch.float32, device=dev))
     if args.only:
         run_only(args, dev, flush)
         return
@@ -217,7 +243,7 @@ def main():
         "config": {"workload": "q4_k_11008x4096", "type": "q4_k",
                    "n_rows": n_rows, "n_per_row": n, "src": "f32",
                    "imatrix": "LogNormal(0,1.5) per column",
-                   "cache_flush_between_steps": "1 GiB"},
+                   "cache_flush_between_steps": "1 GiB read"},
         "roofline": {"bound": "alu", "achieved": round(tops, 3),
                      "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s",
                      "frac": round(tops / VALU_PEAK_TOPS, 4),
@@ -272,6 +298,13 @@ def main():
         bd = out.numel() + y.numel() * 4
         extra["dequantize_q4_k_11008x4096"] = {"ms": round(md, 5),
                                                "hbm_frac": round(bd / (md * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # importance-matrix accumulation (the step that produces the imatrix)
+        for name in IMATRIX_WORKLOADS:
+            fn, nb, n_el = _setup(name, dev)
+            mi, _, _ = timed_steps(fn, 10, 2, flush)
+            extra[name] = {"ms": round(mi, 5), "alg_bytes": nb,
+                           "GB/s": round(nb / (mi * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(nb / (mi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         result["extra"] = extra
 
     print(json.dumps(result), flush=True)

@@ -13,14 +13,15 @@
 // float atomics (the result must not depend on timing):
 //  * k_imx_route (routed tensors only): turns the routing ids into a bitmap
 //    [n_experts][n_tokens / 32]: bit t of expert e is set iff some slot of
-//    token t names e. One workgroup per 512 tokens builds its words for all
-//    experts in LDS (LDS atomic OR: order-free) and writes them out, so a
-//    repeated expert within a token collapses to one bit.
+//    token t names e. One workgroup per 64 tokens loads their ids at once,
+//    builds its words for all experts in LDS (LDS atomic OR: order-free) and
+//    writes them out, so a repeated expert within a token collapses to one
+//    bit.
 //  * k_imx_gather: one workgroup per (512-column chunk, expert, token slab).
 //    Wave 0 expands the expert's bitmap words of a 4096-token window into an
-//    ascending token list in LDS; the four waves then take list entries
+//    ascending token list in LDS; the eight waves then take list entries
 //    round-robin, each lane streaming 8 columns of a row per 16-byte load
-//    (bf16) with four rows in flight, and accumulate a^2 in double. The
+//    (bf16), eight rows in flight, and accumulate a^2 in double. The
 //    waves are combined in a fixed order. With one slab the workgroup owns
 //    its (expert, chunk) cells and adds into the state directly; otherwise
 //    it writes a partial that k_imx_reduce adds up in slab order.
@@ -41,17 +42,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
-constexpr int IMX_WAVES = 4;                     // waves per gather workgroup
+constexpr int IMX_WAVES = 8;                     // waves per gather workgroup
 constexpr int IMX_THREADS = WAVE * IMX_WAVES;
 constexpr int IMX_LANE_COLS = 8;                 // columns per lane
 constexpr int IMX_CHUNK = WAVE * IMX_LANE_COLS;  // columns per workgroup
 constexpr int IMX_WIN_WORDS = 128;               // bitmap words per window
 constexpr int IMX_WIN = IMX_WIN_WORDS * 32;      // tokens per window
-constexpr int IMX_UNROLL = 4;                    // rows in flight per wave
-constexpr int IMX_ROUTE_WORDS = 16;              // words per expert per route workgroup
+constexpr int IMX_UNROLL = 8;                    // rows in flight per wave
+constexpr int IMX_ROUTE_WORDS = 2;               // words per expert per route workgroup
 constexpr int IMX_ROUTE_THREADS = 256;
-constexpr int IMX_TARGET_WGS = 1024;             // workgroups wanted per gather launch
-constexpr int IMX_MIN_SLAB_ROWS = 64;            // mean rows per (expert, slab), at least
+constexpr int IMX_ROUTE_PER_THREAD = IMX_ROUTE_WORDS * 32 * QR_IMX_MAX_TOP_K / IMX_ROUTE_THREADS;
+constexpr int IMX_TARGET_WGS = 256;              // gather workgroups wanted (8 waves each)
+constexpr int IMX_MIN_SLAB_ROWS = 128;           // mean rows per (expert, slab), at least
+constexpr int IMX_REDUCE_BATCH = 32;              // slab partials loaded at once
+constexpr int IMX_RED_BYTES = (IMX_WAVES - 1) * IMX_CHUNK * 8;  // wave partials
+constexpr int IMX_LDS_BYTES = IMX_RED_BYTES > IMX_WIN * 4 ? IMX_RED_BYTES : IMX_WIN * 4;
 
 __host__ __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -70,11 +75,19 @@ __global__ __launch_bounds__(IMX_ROUTE_THREADS) void k_imx_route(const int32_t* 
   const int64_t pairs_left = (n_tokens - t0) * top_k;
   const int n_pairs = (int)min64((int64_t)IMX_ROUTE_WORDS * 32 * top_k, pairs_left);
   const int32_t* ids_blk = ids + t0 * top_k;
-  for (int p = tid; p < n_pairs; p += IMX_ROUTE_THREADS) {
-    const int e = ids_blk[p];
-    if ((unsigned)e < (unsigned)n_experts) {
-      const int lt = p / top_k;  // token within this workgroup's 512
-      atomicOr(&words[e * IMX_ROUTE_WORDS + (lt >> 5)], 1u << (lt & 31));
+  // all loads first (independent), then the LDS updates
+  int v[IMX_ROUTE_PER_THREAD];
+#pragma unroll
+  for (int j = 0; j < IMX_ROUTE_PER_THREAD; ++j) {
+    const int p = tid + j * IMX_ROUTE_THREADS;
+    v[j] = p < n_pairs ? ids_blk[p] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < IMX_ROUTE_PER_THREAD; ++j) {
+    const int p = tid + j * IMX_ROUTE_THREADS;
+    if ((unsigned)v[j] < (unsigned)n_experts) {
+      const int lt = p / top_k;  // token within this workgroup's span
+      atomicOr(&words[v[j] * IMX_ROUTE_WORDS + (lt >> 5)], 1u << (lt & 31));
     }
   }
   __syncthreads();
@@ -97,30 +110,46 @@ __device__ __forceinline__ void add_sq(double (&acc)[IMX_LANE_COLS], const float
   }
 }
 
+// One lane's 8 columns of one row as loaded: 16 bytes of bf16 or 32 bytes
+// of fp32 (the bf16 form uses the first vector only).
+struct RawCols {
+  u32x4 a, b;
+};
+
 template <bool BF16>
-__device__ __forceinline__ void load_cols(const void* __restrict__ act, int64_t elem, bool on,
-                                          float (&v)[IMX_LANE_COLS]) {
-  if (BF16) {
-    u32x4 r = {0u, 0u, 0u, 0u};
-    if (on) r = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(act) + elem);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[2 * k] = __builtin_bit_cast(float, r[k] << 16);
-      v[2 * k + 1] = __builtin_bit_cast(float, r[k] & 0xFFFF0000u);
-    }
-  } else {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-    if (on) {
-      const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(act) + elem);
-      a = p[0];
-      b = p[1];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[k] = a[k];
-      v[4 + k] = b[k];
+__device__ __forceinline__ RawCols load_cols(const void* __restrict__ act, int64_t elem, bool on) {
+  RawCols r;
+  r.a = u32x4{0u, 0u, 0u, 0u};
+  r.b = u32x4{0u, 0u, 0u, 0u};
+  if (on) {
+    if (BF16) {
+      r.a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(act) + elem);
+    } else {
+      const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(act) + elem);
+      r.a = p[0];
+      r.b = p[1];
     }
   }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void add_raw(double (&acc)[IMX_LANE_COLS], const RawCols& r) {
+  float v[IMX_LANE_COLS];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (BF16) {
+      v[2 * k] = __builtin_bit_cast(float, r.a[k] << 16);
+      v[2 * k + 1] = __builtin_bit_cast(float, r.a[k] & 0xFFFF0000u);
+    } else {
+      // copy the element out first: a bit cast of a vector-element lvalue
+      // reads element 0 whatever the index
+      const uint32_t lo = r.a[k], hi = r.b[k];
+      v[k] = __builtin_bit_cast(float, lo);
+      v[4 + k] = __builtin_bit_cast(float, hi);
+    }
+  }
+  add_sq(acc, v);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -139,9 +168,12 @@ __global__ __launch_bounds__(IMX_THREADS) void k_imx_gather(
     int top_k, const uint32_t* __restrict__ bitmap, int64_t n_words, int64_t slab_tokens, int n_experts,
     double* __restrict__ sums, int64_t* __restrict__ counts, double* __restrict__ part,
     int32_t* __restrict__ part_counts) {
-  __shared__ int32_t list[ROUTED ? IMX_WIN : 1];  // act row index of each routed token
+  // The token list (act row of each routed token, during the windows) and
+  // the wave partials (after them) share one buffer.
+  __shared__ double lds_buf[IMX_LDS_BYTES / 8];
   __shared__ int32_t list_len;
-  __shared__ double red[IMX_WAVES - 1][IMX_CHUNK];
+  int32_t* list = reinterpret_cast<int32_t*>(lds_buf);
+  double(*red)[IMX_CHUNK] = reinterpret_cast<double(*)[IMX_CHUNK]>(lds_buf);
 
   const int chunk = blockIdx.x;
   const int e = blockIdx.y;
@@ -200,13 +232,22 @@ __global__ __launch_bounds__(IMX_THREADS) void k_imx_gather(
       __syncthreads();
       n = list_len;
       if (n_slots > 1) {
-        // per-slot rows: the row of token t is that of its first slot naming e
+        // per-slot rows: the row of token t is that of its first slot naming
+        // e (one exists: the bitmap bit came from one of its slots); eight
+        // ids are loaded at a time
         for (int i = threadIdx.x; i < n; i += IMX_THREADS) {
           const int64_t t = list[i] / n_slots;
           const int32_t* r = ids + t * top_k;
-          int s = 0;
-          while (s < top_k && r[s] != e) ++s;
-          list[i] += s;  // s < top_k: the bitmap bit came from one of these slots
+          int found = -1;
+          for (int s0 = 0; s0 < top_k && found < 0; s0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = s0 + j < top_k ? r[s0 + j] : -1;
+#pragma unroll
+            for (int j = 7; j >= 0; --j)
+              if (v[j] == e) found = s0 + j;
+          }
+          list[i] += found;
         }
         __syncthreads();
       }
@@ -215,24 +256,28 @@ __global__ __launch_bounds__(IMX_THREADS) void k_imx_gather(
     }
     matched += n;
 
-    // Entries wave, wave + 4, wave + 8, ... in ascending order per lane.
-    for (int base = wave; base < n; base += IMX_WAVES * IMX_UNROLL) {
-      float v[IMX_UNROLL][IMX_LANE_COLS];
+    // Entries wave, wave + W, wave + 2W, ... (W waves) in ascending order
+    // per lane, U rows in flight (128 bytes per lane).
+    constexpr int U = BF16 ? IMX_UNROLL : IMX_UNROLL / 2;
+    for (int base = wave; base < n; base += IMX_WAVES * U) {
+      RawCols r[U];
 #pragma unroll
-      for (int u = 0; u < IMX_UNROLL; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int i = base + u * IMX_WAVES;
         const bool ok = i < n;  // uniform across the wave
         const int64_t row = ROUTED ? (int64_t)list[ok ? i : 0] : w0 + (ok ? i : 0);
-        load_cols<BF16>(act, row * n_cols + col, ok && active, v[u]);
+        r[u] = load_cols<BF16>(act, row * n_cols + col, ok && active);
       }
 #pragma unroll
-      for (int u = 0; u < IMX_UNROLL; ++u)
-        if (base + u * IMX_WAVES < n) add_sq(acc, v[u]);
+      for (int u = 0; u < U; ++u)
+        if (base + u * IMX_WAVES < n) add_raw<BF16>(acc, r[u]);
     }
     if (ROUTED) __syncthreads();  // the list is rebuilt for the next window
   }
 
-  // Combine the waves in the fixed order ((w0 + w1) + w2) + w3.
+  // Combine the waves in the fixed order (((w0 + w1) + w2) + ...) + w7. The
+  // partials overwrite the token list: the barrier that ends every routed
+  // window orders its last reads before these writes.
   if (wave > 0) {
 #pragma unroll
     for (int k = 0; k < IMX_LANE_COLS; ++k) red[wave - 1][lane * IMX_LANE_COLS + k] = acc[k];
@@ -263,14 +308,21 @@ __global__ __launch_bounds__(IMX_THREADS) void k_imx_gather(
 }
 
 // Adds the slab partials into the state, in slab order.
-__global__ __launch_bounds__(256) void k_imx_reduce(const double* __restrict__ part,
+__global__ __launch_bounds__(64) void k_imx_reduce(const double* __restrict__ part,
                                                     const int32_t* __restrict__ part_counts, int n_slabs,
                                                     int64_t n_cells, int n_experts, double* __restrict__ sums,
                                                     int64_t* __restrict__ counts) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_cells; i += stride) {
-    double s = part[i];
-    for (int k = 1; k < n_slabs; ++k) s += part[(int64_t)k * n_cells + i];
+    double s = 0.0;  // (0 + p0) + p1 ...: the sums are non-negative
+    for (int k0 = 0; k0 < n_slabs; k0 += IMX_REDUCE_BATCH) {
+      double v[IMX_REDUCE_BATCH];  // one batch of loads in flight
+#pragma unroll
+      for (int j = 0; j < IMX_REDUCE_BATCH; ++j)
+        v[j] = k0 + j < n_slabs ? part[(int64_t)(k0 + j) * n_cells + i] : 0.0;
+#pragma unroll
+      for (int j = 0; j < IMX_REDUCE_BATCH; ++j) s += v[j];
+    }
     sums[i] += s;
   }
   if (blockIdx.x == 0) {
@@ -378,21 +430,17 @@ void dispatch_gather(bool routed, bool direct, dim3 grid, hipStream_t s, const v
                      int n_slots, int64_t n_cols, const int32_t* ids, int top_k, const uint32_t* bitmap,
                      int64_t n_words, int64_t slab_tokens, int n_experts, double* sums, int64_t* counts,
                      double* part, int32_t* part_counts) {
+#define QR_IMX_LAUNCH(R, D)                                                                                     \
+  launch_gather<BF16, R, D>(grid, s, act, n_tokens, n_slots, n_cols, ids, top_k, bitmap, n_words, slab_tokens, \
+                            n_experts, sums, counts, part, part_counts)
   if (routed) {
-    if (direct)
-      launch_gather<BF16, true, true>(grid, s, act, n_tokens, n_slots, n_cols, ids, top_k, bitmap, n_words,
-                                      slab_tokens, n_experts, sums, counts, part, part_counts);
-    else
-      launch_gather<BF16, true, false>(grid, s, act, n_tokens, n_slots, n_cols, ids, top_k, bitmap, n_words,
-                                       slab_tokens, n_experts, sums, counts, part, part_counts);
+    if (direct) QR_IMX_LAUNCH(true, true);
+    else QR_IMX_LAUNCH(true, false);
   } else {
-    if (direct)
-      launch_gather<BF16, false, true>(grid, s, act, n_tokens, n_slots, n_cols, ids, top_k, bitmap, n_words,
-                                       slab_tokens, n_experts, sums, counts, part, part_counts);
-    else
-      launch_gather<BF16, false, false>(grid, s, act, n_tokens, n_slots, n_cols, ids, top_k, bitmap, n_words,
-                                        slab_tokens, n_experts, sums, counts, part, part_counts);
+    if (direct) QR_IMX_LAUNCH(false, true);
+    else QR_IMX_LAUNCH(false, false);
   }
+#undef QR_IMX_LAUNCH
 }
 
 int elementwise_grid(int64_t n) {
@@ -458,8 +506,10 @@ int qr_imatrix_accumulate(int src, const void* act, int64_t n_tokens, int64_t n_
   rc = qr_check_launch("k_imx_gather");
   if (rc != QR_OK || direct) return rc;
   const int64_t n_cells = n_experts * n_cols;
-  hipLaunchKernelGGL(k_imx_reduce, dim3(elementwise_grid(n_cells)), dim3(256), 0, s, part, part_counts,
-                     (int)p.slabs, n_cells, (int)n_experts, sums, counts);
+  int64_t rgrid = (n_cells + 63) / 64;
+  if (rgrid > 8192) rgrid = 8192;
+  hipLaunchKernelGGL(k_imx_reduce, dim3((uint32_t)rgrid), dim3(64), 0, s, part, part_counts, (int)p.slabs,
+                     n_cells, (int)n_experts, sums, counts);
   return qr_check_launch("k_imx_reduce");
 }
 

@@ -27,6 +27,9 @@ available here). Their shapes and value distributions are:
   multiplied by 20; each token routed to 8 distinct experts out of 256 by
   Gumbel top-k over log-popularities N(0, 0.5), with 3 experts that are never
   routed (partial coverage).
+* ``imatrix_moe_slots_256x8_4096x2048``: as the expert case above for the
+  down projection: one bf16 row of 2048 values per routed slot,
+  [4096, 8, 2048], each seen only by the expert of its slot.
 * ``imatrix_dense_4096x4096``: importance accumulation for a dense tensor:
   4096 tokens of bf16 activations [4096, 4096] drawn as above.
 
@@ -56,6 +59,10 @@ WORKLOADS = {
                                         n_tokens=4096, n_cols=7168,
                                         n_experts=256, top_k=8, n_slots=1,
                                         n_dead=3, seed=1006),
+    "imatrix_moe_slots_256x8_4096x2048": dict(type="imatrix", dtype="bf16",
+                                              n_tokens=4096, n_cols=2048,
+                                              n_experts=256, top_k=8,
+                                              n_slots=8, n_dead=3, seed=1008),
     "imatrix_dense_4096x4096": dict(type="imatrix", dtype="bf16",
                                     n_tokens=4096, n_cols=4096, n_experts=1,
                                     top_k=0, n_slots=1, n_dead=0, seed=1007),

@@ -96,9 +96,9 @@ def test_imatrix_workspace_sizes():
     ws = qrow.qr_imatrix_workspace_bytes
     # dense, few tokens: one slab, nothing needed
     assert ws(100, 0, 1, 4096) == 0
-    # dense, 4096 tokens x 8 chunks of 512 columns: 64 slabs of 64 tokens,
-    # double partials [64, 1, 4096] + int32 counts [64, 1] (256-byte aligned)
-    assert ws(4096, 0, 1, 4096) == 64 * 4096 * 8 + 256
+    # dense, 4096 tokens x 8 chunks of 512 columns: 32 slabs of 128 tokens,
+    # double partials [32, 1, 4096] + int32 counts [32, 1] (256-byte aligned)
+    assert ws(4096, 0, 1, 4096) == 32 * 4096 * 8 + 256
     # 256 experts x 14 chunks already fill the chip: only the routing bitmap
     assert ws(4096, 8, 256, 7168) == 256 * 128 * 4
     # invalid shapes give 0

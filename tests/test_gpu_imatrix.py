@@ -205,7 +205,8 @@ def test_no_tokens_is_a_no_op(qr):
     assert bool((sums == 1.5).all()) and not counts.any()
 
 
-@pytest.mark.parametrize("name", ["imatrix_moe_256x8_4096x7168", "imatrix_dense_4096x4096"])
+@pytest.mark.parametrize("name", ["imatrix_moe_256x8_4096x7168", "imatrix_moe_slots_256x8_4096x2048",
+                                  "imatrix_dense_4096x4096"])
 def test_full_size_workloads(qr, name):
     a, ids, E = synth.imatrix_inputs(name)
     say(f"full size {name}")
