@@ -21,7 +21,8 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qrow_oracle.c")
-SOURCES = [SRC, os.path.join(HERE, "imatrix_oracle.c")]
+SOURCES = [SRC, os.path.join(HERE, "imatrix_oracle.c"),
+           os.path.join(HERE, "matmul_oracle.c")]
 LIB = os.path.join(HERE, "liborc_qrow.so")
 
 Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128 = range(6)
@@ -110,6 +111,9 @@ def _load(path):
                                          f64p, i64p]
     L.orc_imatrix_merge.argtypes = [f64p, i64p, f64p, i64p, i64, i64]
     L.orc_imatrix_finalize.argtypes = [f64p, i64p, i64, i64, f32p]
+    f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+    L.orc_matmul_q8k128.argtypes = [C.c_int, u8p, u8p, i64, i64, i64, f64p, vp]
+    L.orc_matmul_q8_1.argtypes = [C.c_int, u8p, f32p, i64, i64, i64, f32p]
     L.orc_f32_to_f16.argtypes = [C.c_float]
     L.orc_f32_to_f16.restype = C.c_uint16
     L.orc_f16_to_f32.argtypes = [C.c_uint16]
@@ -349,6 +353,37 @@ def imatrix_finalize(state) -> np.ndarray:
     q = np.zeros(sums.shape, np.float32)
     lib().orc_imatrix_finalize(sums, counts, sums.shape[0], sums.shape[1], q)
     return q
+
+
+def matmul_q8k128(t, w_packed, x_packed, n_out: int, n_tok: int, n_in: int,
+                  with_magnitude: bool = False):
+    """y [n_tok, n_out] float64 = dequant(w) @ dequant(x).T over the exact
+    decoded values; with_magnitude also returns the bound magnitude S."""
+    t = _tid(t)
+    w = np.ascontiguousarray(w_packed, dtype=np.uint8).reshape(-1)
+    x = np.ascontiguousarray(x_packed, dtype=np.uint8).reshape(-1)
+    if w.size != n_out * row_bytes(t, n_in) or x.size != n_tok * row_bytes(Q8_K128, n_in):
+        raise ValueError("packed buffers have the wrong size")
+    y = np.zeros((n_tok, n_out), np.float64)
+    s = np.zeros((n_tok, n_out), np.float64) if with_magnitude else None
+    rc = lib().orc_matmul_q8k128(t, w, x, n_out, n_tok, n_in, y, _ptr(s))
+    if rc != 0:
+        raise ValueError("orc_matmul_q8k128: invalid arguments")
+    return (y, s) if with_magnitude else y
+
+
+def matmul_q8_1(t, w_packed, x, n_out: int):
+    """The Q8_1 formulation (fp16 d, fp16 s) for Q4_1/Q5_1 weights and fp32
+    activations x [n_tok, n_in]: y [n_tok, n_out] float32."""
+    t = _tid(t)
+    xv = _f32(x)
+    n_tok, n_in = xv.shape
+    w = np.ascontiguousarray(w_packed, dtype=np.uint8).reshape(-1)
+    y = np.zeros((n_tok, n_out), np.float32)
+    rc = lib().orc_matmul_q8_1(t, w, xv, n_out, n_tok, n_in, y)
+    if rc != 0:
+        raise ValueError("orc_matmul_q8_1: invalid arguments")
+    return y
 
 
 def f32_to_f16_bits(v: float) -> int:

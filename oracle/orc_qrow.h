@@ -116,6 +116,19 @@ int orc_imatrix_merge(double *sums, int64_t *counts, const double *src_sums,
 int orc_imatrix_finalize(const double *sums, const int64_t *counts,
                          int64_t n_experts, int64_t n_cols, float *q);
 
+/* Product of quantized weight rows w [n_out, row_bytes(type, n_in)] with
+ * Q8_K_128 activation rows x [n_tok, row_bytes(Q8_K128, n_in)] (matmul_oracle.c):
+ * y[t * n_out + r] = sum_i w[r][i] * a[t][i] in double over the exact decoded
+ * values; s_abs (or NULL) receives sum_i (|scale part| + |offset part|)*|a_i|. */
+int orc_matmul_q8k128(int type, const uint8_t *w, const uint8_t *x,
+                      int64_t n_out, int64_t n_tok, int64_t n_in, double *y,
+                      double *s_abs);
+/* The same product for Q4_1/Q5_1 weights with fp32 activations quantized to
+ * Q8_1 (32 values, fp16 d and fp16 s = d * sum(q)), the offset part taken
+ * from s, in float: the formulation whose s overflows. */
+int orc_matmul_q8_1(int type, const uint8_t *w, const float *x, int64_t n_out,
+                    int64_t n_tok, int64_t n_in, float *y);
+
 /* IEEE-754 binary16 conversions (round to nearest-even, subnormals kept). */
 uint16_t orc_f32_to_f16(float f);
 float    orc_f16_to_f32(uint16_t h);

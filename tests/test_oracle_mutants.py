@@ -64,10 +64,19 @@ MUTANTS = [
     ("imatrix: merge drops the counts", "counts[e] += src_counts[e];", "(void)src_counts;"),
     ("imatrix: merge overwrites the sums", "sums[e * n_cols + c] += src_sums[e * n_cols + c];",
      "sums[e * n_cols + c] = src_sums[e * n_cols + c];"),
+    # product with Q8_K_128 activations (and the Q8_1 comparison)
+    ("matmul: Q4_0 offset 7", "bv = sym ? d * (five ? 16 : 8) : -m;", "bv = sym ? d * (five ? 16 : 7) : -m;"),
+    ("matmul: Q4_K scale from the offset field", "av = rd_f16(p) * field6(p + 4, j) * u;",
+     "av = rd_f16(p) * field6(p + 10, j) * u;"),
+    ("matmul: Q4_K high nibble", "const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);",
+     "const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] & 15);"),
+    ("matmul: activation block stride", "const uint8_t *p = row + blk * 140;", "const uint8_t *p = row + blk * 136;"),
+    ("matmul: offset sign", "acc += (a[i] - b[i]) * xt[i];", "acc += (a[i] + b[i]) * xt[i];"),
+    ("q8_1: s without d", "orc_f32_to_f16(d * (float)sum)", "orc_f32_to_f16((float)sum)"),
 ]
 
 
-PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py")
+PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py", "test_matmul_oracle_pins.py")
 
 
 def _pins_modules():
@@ -91,6 +100,7 @@ def _pin_calls(mods):
         "test_asym_brute_force_tiny_blocks": dict(n=3, nmax=3),
         "test_exact_lattice_rows_round_trip": dict(t="q4_0", nmax=8, sym=True),
         "test_power_of_two_constant_imatrix_equals_none": dict(t="q4_k"),
+        "test_product_equals_library_matmul_of_decoded_values": dict(t="q4_k"),
     }
     calls = []
     for mod in mods:
@@ -104,6 +114,9 @@ def _pin_calls(mods):
     calls.append(("round trip q5_1", lambda: mod.test_exact_lattice_rows_round_trip("q5_1", 31, False)))
     calls.append(("round trip q5_0", lambda: mod.test_exact_lattice_rows_round_trip("q5_0", 16, True)))
     calls.append(("brute force sym 4/8", lambda: mod.test_sym_brute_force_tiny_blocks(4, 8, True)))
+    mm = mods[2]
+    for t in ("q4_0", "q5_1"):
+        calls.append((f"matmul {t}", lambda t=t: mm.test_product_equals_library_matmul_of_decoded_values(t)))
     return calls
 
 
