@@ -144,6 +144,17 @@ def _setup(name, dev):
         nb = ad.numel() * 2 + (0 if ids is None else ids.nbytes) + 2 * (sums.numel() * 8 + counts.numel() * 8)
         return (lambda: qrow.qr_imatrix_accumulate(ad, sums, counts, idd, workspace=ws),
                 nb, ad.numel())
+    if name.startswith("mmq_"):
+        # weights and activations quantized by the library, then the product
+        t, x, q, a = synth.matmul_sources(name)
+        xd, qd, ad = (torch.from_numpy(v).to(dev) for v in (x, q, a))
+        w = qrow.qr_quantize_rows(t, xd, qd)
+        xa = qrow.qr_quantize_activations_q8k128(ad)
+        n_in = x.shape[1]
+        y = torch.empty((a.shape[0], x.shape[0]), dtype=torch.float32, device=dev)
+        del xd
+        return (lambda: qrow.qr_matmul_q8k128(t, w, xa, n_in, out=y),
+                w.numel() + xa.numel() + y.numel() * 4, x.size)
     if name == "copy_1gib":
         # plain device copy of a known size: calibrates the HBM byte counters
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -154,9 +165,10 @@ def _setup(name, dev):
 
 IMATRIX_WORKLOADS = ("imatrix_moe_256x8_4096x7168", "imatrix_moe_slots_256x8_4096x2048",
                      "imatrix_dense_4096x4096")
+MATMUL_WORKLOADS = ("mmq_q4_k_11008x4096_t1", "mmq_q4_0_4096x4096_t8")
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "copy_1gib") + IMATRIX_WORKLOADS
+                  "moe_256x2048x7168", "copy_1gib") + IMATRIX_WORKLOADS + MATMUL_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -299,7 +311,8 @@ def main():
         extra["dequantize_q4_k_11008x4096"] = {"ms": round(md, 5),
                                                "hbm_frac": round(bd / (md * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # importance-matrix accumulation (the step that produces the imatrix)
-        for name in IMATRIX_WORKLOADS:
+        # and the product with Q8_K_128 activations (the step that consumes both)
+        for name in IMATRIX_WORKLOADS + MATMUL_WORKLOADS:
             fn, nb, n_el = _setup(name, dev)
             mi, _, _ = timed_steps(fn, 10, 2, flush)
             extra[name] = {"ms": round(mi, 5), "alg_bytes": nb,

@@ -1,0 +1,56 @@
+/*
+ * qrow_matmul.h -- C-ABI of libqrow.so, part 3: the product of quantized
+ * weight rows with Q8_K_128 activations, the consumer of both formats.
+ *
+ * The operation follows this page (cited by title and section):
+ *  [Q8] "ik_llama.cpp 量化精度修复实录：用 Q8_K_128 替代 Q8_1 …". Section
+ *       修复前的数值隐患: the weight codes are multiplied with the 8-bit
+ *       activation codes in integer arithmetic and the weight offset is
+ *       removed with a per-block sum of the activation codes; stored as
+ *       s = d * sum(q) in fp16 (Q8_1), that sum overflows on large
+ *       activations. Section 修复方案: Q8_K_128 stores the sum per 32 codes
+ *       as an int16 that is not multiplied by d, so the correction is exact
+ *       integer arithmetic.
+ *
+ * Conventions are those of qrow.h (device pointers, 16-byte aligned;
+ * asynchronous calls on `stream`; 0 or a negative QR_E* code with nothing
+ * launched on failure; nothing allocated).
+ */
+#ifndef QROW_MATMUL_H
+#define QROW_MATMUL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QR_MATMUL_MAX_IN 32768   /* longest row (n_in) */
+
+/*
+ * qr_matmul_q8k128 -- y[t][r] = sum_i W[r][i] * A[t][i] [Q8 修复方案].
+ *  t      weight type: QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1 or QR_Q4_K.
+ *  w      packed weight rows [n_out, qr_row_bytes(t, n_in)] (the output of
+ *         qr_quantize_rows).
+ *  x      packed Q8_K_128 activation rows [n_tok, qr_row_bytes(QR_Q8_K128,
+ *         n_in)] (the output of qr_quantize_activations_q8k128).
+ *  y      fp32 [n_tok, n_out], written completely.
+ * W and A are the values the blocks encode. Per 32 weights the codes are
+ * multiplied with the activation codes in int32 (four products per
+ * instruction), the weight offset is folded in with the block's int16 code
+ * sum (Q4_0, Q5_0: sum(u*q) - 8 or 16 * bsum; Q4_1, Q5_1: m * bsum; Q4_K:
+ * dmin*mn_j * bsum_j), and the scales are applied in fp32. The fp32 sums are
+ * taken in a fixed order (reproducible bit for bit); against the exact
+ * product each output is within (n_in/1024 + 9) * 2^-24 of
+ * sum_i (|scale part_i| + |offset part_i|) * |A[t][i]|.
+ * Limits: n_in a positive multiple of 128 (256 for Q4_K), at most
+ * QR_MATMUL_MAX_IN. n_out == 0 or n_tok == 0 is a no-op.
+ */
+int qr_matmul_q8k128(int t, const void *w, const void *x, int64_t n_out,
+                     int64_t n_tok, int64_t n_in, float *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -5,7 +5,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "qrow.hip"),
-           os.path.join(HERE, "csrc", "imatrix.hip")]
+           os.path.join(HERE, "csrc", "imatrix.hip"),
+           os.path.join(HERE, "csrc", "matmul.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqrow.so")
 

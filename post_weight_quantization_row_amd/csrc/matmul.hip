@@ -1,0 +1,379 @@
+// matmul.hip -- gfx950 kernel and C-ABI of the product of quantized weight
+// rows with Q8_K_128 activation rows (declared in qrow_matmul.h).
+//
+// Following this page (cited by title and section):
+//  [Q8] "ik_llama.cpp 量化精度修复实录：用 Q8_K_128 替代 Q8_1 …", sections
+//       修复前的数值隐患 and 修复方案: integer products of weight and activation
+//       codes, the weight offset removed with the activation code sums, which
+//       Q8_K_128 keeps as unscaled int16 per 32 codes.
+//
+// Execution model (gfx950, wave64). A workgroup of four waves owns a few
+// weight rows and a tile of TT tokens. With TT > 1 the tile's activation
+// rows (one contiguous range) are unpacked once into LDS (codes, fp32
+// scales, code sums), 16 bytes per load where aligned; with one token each
+// lane reads its groups' activation words from the packed row (L2-resident)
+// together with the weights. L lanes own a row (64 for one token, 32 for a
+// tile); lane s takes the row's 32-weight groups s, s + L, ..., loads their
+// packed bytes unconditionally so that a batch is in flight at once
+// (consecutive lanes read consecutive blocks), expands the 4-bit codes (and
+// the fifth bit) into bytes, and for every token forms sum(u*q) with eight
+// v_dot4 instructions, folds the offset with the int16 code sum, and adds
+// the scaled term in fp32. A butterfly over the row's lanes gives its
+// outputs. One token is bound by reading the weights from HBM; tiles of
+// tokens by instruction issue (eight v_dot4 plus about thirty addressing,
+// LDS and scaling instructions per 32 weights and token).
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "qr_internal.h"
+#include "qrow.h"
+#include "qrow_matmul.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr int MMQ_WAVES = 4;
+constexpr int MMQ_THREADS = WAVE * MMQ_WAVES;
+// Lanes per weight row and groups per lane per batch: one token (a decode
+// step) gives each row a whole wave, one group at a time; a tile of tokens
+// gives each row half a wave, two groups at a time (measured best of 16/32/64
+// lanes x 1/2/4 groups).
+__host__ __device__ constexpr int mmq_lanes(int tt) { return tt == 1 ? 64 : 32; }
+__host__ __device__ constexpr int mmq_batch(int tt) { return tt == 1 ? 1 : 2; }
+__host__ __device__ constexpr int mmq_rows(int tt) { return MMQ_THREADS / mmq_lanes(tt); }
+constexpr int MMQ_LDS_BUDGET = 64 * 1024;         // bytes of staged activations
+constexpr int Q8_BLOCK_WORDS = 35;                // 140-byte Q8_K_128 block
+
+// LDS bytes for a tile of tt tokens of n_in values: codes, scales, sums.
+__host__ __device__ constexpr int64_t mmq_lds_bytes(int tt, int64_t n_in) {
+  return (int64_t)tt * (n_in + n_in / 128 * 4 + n_in / 32 * 4);
+}
+
+// 4 bits t (0..15) spread into bit 0 of each byte: bit k -> bit 8k.
+__device__ __forceinline__ uint32_t spread4(uint32_t t) { return (t * 0x00204081u) & 0x01010101u; }
+
+__device__ __forceinline__ uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+__device__ __forceinline__ float half_bits(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
+}
+
+// One 32-weight group of a row, ready for the token loop: the codes as
+// bytes (lo: elements 0..15, hi: 16..31) and the float parts of the decode.
+struct Group {
+  uint32_t lo[4], hi[4];
+  float sa;  // scale part:  d (legacy) or d*sc (Q4_K)
+  float sb;  // offset part: the level offset 8/16 (symmetric), m (Q4_1/Q5_1) or dmin*mn (Q4_K)
+};
+
+// The packed bytes of one group as loaded (up to eight words), kept apart
+// from the decoding so that a batch of loads can be in flight at once.
+struct RawGroup {
+  uint32_t v[8];
+};
+
+template <int TYPE>
+__device__ __forceinline__ RawGroup load_raw(const uint8_t* __restrict__ row, int g) {
+  RawGroup R;
+  if (TYPE == QR_Q4_K) {
+    const uint8_t* sb = row + (int64_t)(g >> 3) * 144;
+    const u32x4 h = *reinterpret_cast<const u32x4*>(sb);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(sb + 16 + 16 * (g & 7));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      R.v[k] = h[k];
+      R.v[4 + k] = c[k];
+    }
+  } else {
+    constexpr int WORDS = TYPE == QR_Q4_0 ? 5 : TYPE == QR_Q5_1 ? 7 : 6;
+    const uint8_t* p = row + (int64_t)g * (WORDS * 4);
+#pragma unroll
+    for (int k = 0; k < WORDS; ++k) R.v[k] = ld32(p + 4 * k);
+  }
+  return R;
+}
+
+// One token's activation words for one 32-value group of a packed Q8_K_128
+// row: the 8 code words, the word holding its int16 code sum, the scale.
+struct RawAct {
+  uint32_t q[8];
+  uint32_t sums;
+  uint32_t d;
+};
+
+__device__ __forceinline__ RawAct load_act(const uint8_t* __restrict__ xrow, int g) {
+  RawAct A;
+  const uint8_t* blk = xrow + (int64_t)(g >> 2) * (Q8_BLOCK_WORDS * 4);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) A.q[c] = ld32(blk + 4 + 32 * (g & 3) + 4 * c);
+  A.sums = ld32(blk + 132 + 4 * ((g & 3) >> 1));
+  A.d = ld32(blk);
+  return A;
+}
+
+template <int TYPE>
+__device__ __forceinline__ Group unpack(const RawGroup& R, int g) {
+  Group G;
+  uint32_t qh = 0;
+  int qs0;  // first word of the 16 code bytes
+  if (TYPE == QR_Q4_K) {
+    const int j = g & 7;
+    const uint32_t h1 = R.v[1], h2 = R.v[2], h3 = R.v[3];
+    const uint64_t sc6 = (uint64_t)h1 | ((uint64_t)(h2 & 0xffffu) << 32);
+    const uint64_t mn6 = (uint64_t)(h2 >> 16) | ((uint64_t)h3 << 16);
+    const float d = half_bits(R.v[0]), dmin = half_bits(R.v[0] >> 16);
+    G.sa = d * (float)((sc6 >> (6 * j)) & 63);     // exact: 11-bit times 6-bit
+    G.sb = dmin * (float)((mn6 >> (6 * j)) & 63);
+    qs0 = 4;
+  } else {
+    G.sa = __builtin_bit_cast(float, R.v[0]);
+    if (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) G.sb = __builtin_bit_cast(float, R.v[1]);
+    else G.sb = TYPE == QR_Q4_0 ? 8.0f : 16.0f;
+    if (TYPE == QR_Q5_0) qh = R.v[1];
+    if (TYPE == QR_Q5_1) qh = R.v[2];
+    qs0 = TYPE == QR_Q4_0 ? 1 : TYPE == QR_Q5_1 ? 3 : 2;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t wk = R.v[qs0 + k];
+    G.lo[k] = wk & 0x0f0f0f0fu;
+    G.hi[k] = (wk >> 4) & 0x0f0f0f0fu;
+    if (TYPE == QR_Q5_0 || TYPE == QR_Q5_1) {
+      G.lo[k] |= spread4((qh >> (4 * k)) & 15u) << 4;
+      G.hi[k] |= spread4((qh >> (16 + 4 * k)) & 15u) << 4;
+    }
+  }
+  return G;
+}
+
+template <int TYPE, int TT>
+__global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k128(const uint8_t* __restrict__ w,
+                                                               const uint8_t* __restrict__ x, int64_t n_out,
+                                                               int64_t n_tok, int n_in, int64_t w_row_bytes,
+                                                               float* __restrict__ y) {
+  extern __shared__ uint32_t lds[];
+  const int nb = n_in / 128;  // activation blocks per row
+  const int ng = n_in / 32;   // 32-value groups per row
+  // Block-major over the tile (block tb = t * nb + b): code words
+  // [TT * nb][32], scales [TT * nb], code sums [TT * nb][4].
+  uint32_t* lq = lds;
+  float* ld = reinterpret_cast<float*>(lds + TT * nb * 32);
+  int32_t* lsum = reinterpret_cast<int32_t*>(ld + TT * nb);
+
+  // L lanes own one row; lane s takes the row's groups s, s + L, ..., NF at
+  // a time, the next batch requested before the current one is used.
+  constexpr int L = mmq_lanes(TT);
+  constexpr int NF = mmq_batch(TT);
+  constexpr int STEP = L * NF;
+  const int sub = threadIdx.x & (L - 1);
+  const int64_t r = (int64_t)blockIdx.x * mmq_rows(TT) + threadIdx.x / L;
+  const bool row_ok = r < n_out;
+  const uint8_t* row = w + (row_ok ? r : 0) * w_row_bytes;
+  const int64_t t0 = (int64_t)blockIdx.y * TT;
+  const uint8_t* xt = x + t0 * (int64_t)nb * Q8_BLOCK_WORDS * 4;
+  RawGroup cur[NF], nxt[NF];
+  RawAct acur[TT == 1 ? NF : 1], anxt[TT == 1 ? NF : 1];
+  auto load_batch = [&](RawGroup (&b)[NF], RawAct (&ab)[TT == 1 ? NF : 1], int g0) {
+    // unconditional loads (past the end: the row's last group, unused), so
+    // that the whole batch is issued back to back; with one token the
+    // group's activation words come with it
+#pragma unroll
+    for (int u = 0; u < NF; ++u) {
+      const int g = g0 + u * L;
+      const int gc = g < ng ? g : ng - 1;
+      b[u] = load_raw<TYPE>(row, gc);
+      if (TT == 1) ab[TT == 1 ? u : 0] = load_act(xt, gc);
+    }
+  };
+  if (TT > 1) {
+    // The tile's activation rows are contiguous: stage them with eight
+    // independent loads in flight per thread (absent tokens read as 0),
+    // 16 bytes at a time when the tile is 16-byte aligned.
+    const int total = TT * nb * Q8_BLOCK_WORDS;
+    const int64_t tok_left = n_tok - t0;
+    const int valid = tok_left >= TT ? total : (int)tok_left * nb * Q8_BLOCK_WORDS;
+    auto put = [&](int idx, uint32_t v) {
+      const int tb = idx / Q8_BLOCK_WORDS;
+      const int k = idx - tb * Q8_BLOCK_WORDS;
+      if (k == 0) {
+        ld[tb] = __builtin_bit_cast(float, v);
+      } else if (k <= 32) {
+        lq[tb * 32 + (k - 1)] = v;
+      } else {
+        const int g = tb * 4 + (k - 33) * 2;
+        lsum[g] = (int32_t)(int16_t)(v & 0xffffu);
+        lsum[g + 1] = (int32_t)(int16_t)(v >> 16);
+      }
+    };
+    if ((nb & 3) == 0) {
+      const int chunks = total / 4, valid4 = valid / 4;
+      for (int base = threadIdx.x; base < chunks; base += MMQ_THREADS * 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = base + j * MMQ_THREADS;
+          v[j] = *reinterpret_cast<const u32x4*>(xt + (int64_t)(c < valid4 ? c : valid4 - 1) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = base + j * MMQ_THREADS;
+          if (c < chunks) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t ve = v[j][e];
+              put(4 * c + e, c < valid4 ? ve : 0u);
+            }
+          }
+        }
+      }
+    } else {
+      for (int base = threadIdx.x; base < total; base += MMQ_THREADS * 8) {
+        uint32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int idx = base + j * MMQ_THREADS;
+          v[j] = ld32(xt + (int64_t)(idx < valid ? idx : valid - 1) * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int idx = base + j * MMQ_THREADS;
+          if (idx < total) put(idx, idx < valid ? v[j] : 0u);
+        }
+      }
+    }
+  }
+  load_batch(cur, acur, sub);
+  if (TT > 1) __syncthreads();
+
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+  for (int g0 = sub; g0 < ng && row_ok; g0 += STEP) {
+    if (g0 + STEP < ng) load_batch(nxt, anxt, g0 + STEP);
+#pragma unroll
+    for (int u = 0; u < NF; ++u) {
+      const int g = g0 + u * L;
+      if (g >= ng) break;
+      const Group G = unpack<TYPE>(cur[u], g);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const int tg = t * ng + g;  // group index within the tile
+        uint32_t a[8];
+        int bs;
+        float da;
+        if (TT > 1) {
+          const u32x4* qa = reinterpret_cast<const u32x4*>(lq + tg * 8);
+          const u32x4 a0 = qa[0], a1 = qa[1];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            a[c] = a0[c];
+            a[4 + c] = a1[c];
+          }
+          bs = lsum[tg];
+          da = ld[tg >> 2];
+        } else {
+          // one token: the words loaded with the group
+          const RawAct& A = acur[TT == 1 ? u : 0];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) a[c] = A.q[c];
+          bs = (int)(int16_t)((g & 1) ? (A.sums >> 16) : (A.sums & 0xffffu));
+          da = __builtin_bit_cast(float, A.d);
+        }
+        int isum = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) isum = __builtin_amdgcn_sdot4((int)G.lo[c], (int)a[c], isum, false);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) isum = __builtin_amdgcn_sdot4((int)G.hi[c], (int)a[4 + c], isum, false);
+        if (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
+          // d * (sum(u*q) - offset * bsum), exact in int32
+          const int I = isum - (TYPE == QR_Q4_0 ? 8 : 16) * bs;
+          acc[t] = __builtin_fmaf(G.sa * da, (float)I, acc[t]);
+        } else if (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
+          // d * sum(u*q) + m * bsum
+          const float part = __builtin_fmaf(G.sa, (float)isum, G.sb * (float)bs);
+          acc[t] = __builtin_fmaf(da, part, acc[t]);
+        } else {
+          // d*sc * sum(u*q) - dmin*mn * bsum
+          const float part = __builtin_fmaf(G.sa, (float)isum, -(G.sb * (float)bs));
+          acc[t] = __builtin_fmaf(da, part, acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NF; ++u) cur[u] = nxt[u];
+    if (TT == 1) {
+#pragma unroll
+      for (int u = 0; u < NF; ++u) acur[TT == 1 ? u : 0] = anxt[TT == 1 ? u : 0];
+    }
+  }
+  // butterfly over the row's lanes: all of them end with the sums
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+#pragma unroll
+    for (int m = L / 2; m >= 1; m >>= 1) acc[t] += __shfl_xor(acc[t], m, L);
+  }
+  if (row_ok && sub < TT && t0 + sub < n_tok) {
+    float v = acc[0];
+#pragma unroll
+    for (int t = 1; t < TT; ++t)
+      if (sub == t) v = acc[t];
+    y[(t0 + sub) * n_out + r] = v;
+  }
+}
+
+template <int TYPE>
+int launch_type(int tt, const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in,
+                int64_t w_row_bytes, float* y, hipStream_t s) {
+  const int rows = mmq_rows(tt);
+  const dim3 grid((uint32_t)((n_out + rows - 1) / rows), (uint32_t)((n_tok + tt - 1) / tt));
+  const size_t lds = tt > 1 ? (size_t)mmq_lds_bytes(tt, n_in) : 0;
+  switch (tt) {
+    case 8: hipLaunchKernelGGL((k_matmul_q8k128<TYPE, 8>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
+    case 4: hipLaunchKernelGGL((k_matmul_q8k128<TYPE, 4>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
+    case 2: hipLaunchKernelGGL((k_matmul_q8k128<TYPE, 2>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
+    default: hipLaunchKernelGGL((k_matmul_q8k128<TYPE, 1>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
+  }
+  return qr_check_launch("k_matmul_q8k128");
+}
+
+}  // namespace
+
+extern "C" {
+
+int qr_matmul_q8k128(int t, const void* w, const void* x, int64_t n_out, int64_t n_tok, int64_t n_in, float* y,
+                     void* stream) {
+  qr_clear_error();
+  if (t < QR_Q4_0 || t > QR_Q4_K) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
+  const int64_t mult = t == QR_Q4_K ? 256 : 128;
+  if (n_in <= 0 || n_in % mult != 0 || n_in > QR_MATMUL_MAX_IN)
+    return qr_fail(QR_EINVAL_SHAPE, "n_in=%lld must be a positive multiple of %lld and at most %d", (long long)n_in,
+                   (long long)mult, QR_MATMUL_MAX_IN);
+  if (n_out < 0 || n_tok < 0) return qr_fail(QR_EINVAL_SHAPE, "negative n_out or n_tok");
+  if (n_out == 0 || n_tok == 0) return QR_OK;
+  if (n_out > (int64_t)UINT32_MAX * mmq_rows(1) || n_out > INT64_MAX / n_tok)
+    return qr_fail(QR_EOVERFLOW, "n_out or n_tok too large");
+  if (!w || !x || !y) return qr_fail(QR_EINVAL_PTR, "w, x and y must be non-NULL");
+  if (!qr_aligned(w, 16) || !qr_aligned(x, 16) || !qr_aligned(y, 16))
+    return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+  // tokens per tile: as many as fit (up to 8) in the activation budget
+  int tt = n_tok >= 8 ? 8 : n_tok >= 4 ? 4 : n_tok >= 2 ? 2 : 1;
+  while (tt > 1 && mmq_lds_bytes(tt, n_in) > MMQ_LDS_BUDGET) tt >>= 1;
+  if ((n_tok + tt - 1) / tt > 65535) return qr_fail(QR_EOVERFLOW, "n_tok=%lld needs too many token tiles", (long long)n_tok);
+  const int64_t wrb = (int64_t)qr_row_bytes(t, n_in);
+  const uint8_t* pw = reinterpret_cast<const uint8_t*>(w);
+  const uint8_t* px = reinterpret_cast<const uint8_t*>(x);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (t) {
+    case QR_Q4_0: return launch_type<QR_Q4_0>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+    case QR_Q4_1: return launch_type<QR_Q4_1>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+    case QR_Q5_0: return launch_type<QR_Q5_0>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+    case QR_Q5_1: return launch_type<QR_Q5_1>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+    default: return launch_type<QR_Q4_K>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+  }
+}
+
+}  // extern "C"

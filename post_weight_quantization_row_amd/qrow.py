@@ -1,7 +1,7 @@
 """Python binding of libqrow.so (argument marshalling only).
 
 Every function has the name of the C entry point it calls (see
-include/qrow.h and include/qrow_imatrix.h) and takes torch tensors that live on the GPU; all arithmetic
+include/qrow.h, include/qrow_imatrix.h and include/qrow_matmul.h) and takes torch tensors that live on the GPU; all arithmetic
 runs in the library's HIP kernels. torch provides device memory and the
 stream. There is no CPU fallback: without the built library or a GPU the
 calls raise.
@@ -24,13 +24,13 @@ TYPES = {"q4_0": QR_Q4_0, "q4_1": QR_Q4_1, "q5_0": QR_Q5_0, "q5_1": QR_Q5_1,
 ERRORS = {-1: "QR_EINVAL_TYPE", -2: "QR_EINVAL_SHAPE", -3: "QR_EINVAL_PTR",
           -4: "QR_EOVERFLOW", -5: "QR_EDEVICE"}
 
-# Every symbol include/qrow.h and include/qrow_imatrix.h declare.
+# Every symbol the headers under include/ declare.
 EXPORTS = ("qr_quantize_rows", "qr_quantize_rows_grouped",
            "qr_quantize_activations_q8k128", "qr_dequantize_rows",
            "qr_row_bytes", "qr_block_elems", "qr_solver_constants",
            "qr_last_error", "qr_imatrix_workspace_bytes",
            "qr_imatrix_accumulate", "qr_imatrix_merge",
-           "qr_imatrix_finalize")
+           "qr_imatrix_finalize", "qr_matmul_q8k128")
 IMX_MAX_EXPERTS, IMX_MAX_TOP_K = 1024, 64
 
 
@@ -69,6 +69,7 @@ def load_library(path: str = LIB_PATH):
                                             i64, vp, vp, vp, C.c_size_t, vp]
         L.qr_imatrix_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.qr_imatrix_finalize.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.qr_matmul_q8k128.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp]
         for name in (n for n in EXPORTS if n not in
                      ("qr_row_bytes", "qr_block_elems", "qr_last_error",
                       "qr_solver_constants", "qr_imatrix_workspace_bytes")):
@@ -291,4 +292,25 @@ def qr_imatrix_finalize(sums, counts, out=None, stream=None):
     _check(load_library().qr_imatrix_finalize(
         _ptr(sums), _ptr(counts), sums.shape[0], sums.shape[1], _ptr(out),
         _stream(sums, stream)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# product with Q8_K_128 activations (include/qrow_matmul.h)
+
+def qr_matmul_q8k128(t, w: torch.Tensor, x: torch.Tensor, n_in: int, out=None, stream=None):
+    """y [n_tok, n_out] fp32 = W @ A.T for packed weight rows w (uint8
+    [n_out, qr_row_bytes(t, n_in)]) and packed Q8_K_128 activation rows x
+    (uint8 [n_tok, qr_row_bytes("q8_k128", n_in)]), both on the GPU."""
+    tid = _tid(t)
+    for name, a in (("w", w), ("x", x)):
+        if (not isinstance(a, torch.Tensor) or not a.is_cuda or a.dtype != torch.uint8
+                or a.dim() != 2 or not a.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous 2-D CUDA uint8 tensor")
+    if w.shape[1] != qr_row_bytes(tid, n_in) or x.shape[1] != qr_row_bytes(QR_Q8_K128, n_in):
+        raise ValueError("packed row lengths do not match n_in")
+    n_out, n_tok = w.shape[0], x.shape[0]
+    out = _out(out, (n_tok, n_out), torch.float32, w.device)
+    _check(load_library().qr_matmul_q8k128(
+        tid, _ptr(w), _ptr(x), n_out, n_tok, n_in, _ptr(out), _stream(w, stream)))
     return out

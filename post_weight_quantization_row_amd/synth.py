@@ -32,6 +32,12 @@ available here). Their shapes and value distributions are:
   [4096, 8, 2048], each seen only by the expert of its slot.
 * ``imatrix_dense_4096x4096``: importance accumulation for a dense tensor:
   4096 tokens of bf16 activations [4096, 4096] drawn as above.
+* ``mmq_q4_k_11008x4096_t1``: product of the Q4_K-quantized
+  ``q4_k_11008x4096`` matrix (with its importances) with one token of fp32
+  activations drawn as the calibration activations above, quantized to
+  Q8_K_128 (a decode step).
+* ``mmq_q4_0_4096x4096_t8``: product of the Q4_0-quantized first attention
+  matrix of ``stack_7b_32x7`` with 8 such tokens.
 
 Two back-ends draw the same recipes: numpy (CPU, used by the CPU tests and by
 small GPU tests) and torch on the GPU (used for the multi-GB stacks). The two
@@ -63,6 +69,12 @@ WORKLOADS = {
                                               n_tokens=4096, n_cols=2048,
                                               n_experts=256, top_k=8,
                                               n_slots=8, n_dead=3, seed=1008),
+    "mmq_q4_k_11008x4096_t1": dict(type="matmul", wtype="q4_k", n_out=11008,
+                                   n_in=4096, n_tok=1, weights="q4_k_11008x4096",
+                                   seed=1009),
+    "mmq_q4_0_4096x4096_t8": dict(type="matmul", wtype="q4_0", n_out=4096,
+                                  n_in=4096, n_tok=8, weights="stack_7b_32x7",
+                                  seed=1010),
     "imatrix_dense_4096x4096": dict(type="imatrix", dtype="bf16",
                                     n_tokens=4096, n_cols=4096, n_experts=1,
                                     top_k=0, n_slots=1, n_dead=0, seed=1007),
@@ -200,6 +212,18 @@ def routing_ids(n_tokens, n_experts, top_k, seed, n_dead=0, spread=0.5):
     top = np.argpartition(-score, top_k - 1, axis=1)[:, :top_k]
     order = np.argsort(-np.take_along_axis(score, top, axis=1), axis=1, kind="stable")
     return np.take_along_axis(top, order, axis=1).astype(np.int32)
+
+
+def matmul_sources(name):
+    """(weight type, fp32 weights, importances, fp32 activations) of a
+    matmul workload; the caller quantizes both."""
+    w = WORKLOADS[name]
+    if w["weights"] == "q4_k_11008x4096":
+        x, q = q4_k_matrix()
+    else:
+        _, x, q = stack_matrix(0, 0)
+    a = calib_activations(w["n_tok"], w["n_in"], w["seed"], bf16=False)
+    return w["wtype"], x, q, a
 
 
 def imatrix_inputs(name):

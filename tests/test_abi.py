@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(HEADERS) == 2 and len(names) == 12
+    assert len(HEADERS) == 3 and len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(qrow.EXPORTS) == names
@@ -142,3 +142,18 @@ def test_imatrix_argument_validation_without_a_gpu(lib):
     assert lib.qr_imatrix_finalize(fake, fake, 2, -8, fake, None) == -2
     assert lib.qr_imatrix_finalize(fake, fake, 2, 8, None, None) == -3
     assert lib.qr_imatrix_finalize(None, None, 0, 8, None, None) == 0
+
+
+def test_matmul_argument_validation_without_a_gpu(lib):
+    fake = C.c_void_p(0x10000)       # never dereferenced: calls fail first
+    mm = lib.qr_matmul_q8k128
+    assert mm(5, fake, fake, 4, 2, 256, fake, None) == -1      # not a weight type
+    assert mm(4, fake, fake, 4, 2, 128, fake, None) == -2      # Q4_K needs 256
+    assert mm(0, fake, fake, 4, 2, 96, fake, None) == -2       # not a multiple of 128
+    assert mm(0, fake, fake, 4, 2, 65536, fake, None) == -2    # too long
+    assert mm(0, fake, fake, -1, 2, 256, fake, None) == -2
+    assert mm(0, None, None, 0, 2, 256, None, None) == 0       # empty: no-op
+    assert mm(0, None, None, 4, 0, 256, None, None) == 0
+    assert mm(0, None, fake, 4, 2, 256, fake, None) == -3
+    assert mm(0, fake, C.c_void_p(0x10004), 4, 2, 256, fake, None) == -3
+    assert mm(0, fake, fake, 4, 2 ** 30, 32768, fake, None) == -4   # too many token tiles
