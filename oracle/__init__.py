@@ -26,6 +26,8 @@ SOURCES = [SRC, os.path.join(HERE, "imatrix_oracle.c"),
 LIB = os.path.join(HERE, "liborc_qrow.so")
 
 Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128 = range(6)
+WEIGHTINGS = {"sqrt_sigma2_x2": 0, "x2": 1, "abs_x": 2, "sigma2_plus_x2": 3,
+              "sigma_plus_abs_x": 4, "imatrix_only": 5}
 TYPE_NAMES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1,
               "q4_k": Q4_K, "q8_k128": Q8_K128}
 
@@ -104,6 +106,10 @@ def _load(path):
     L.orc_quantize_row_sigma2.argtypes = [C.c_int, f32p, vp, i64,
                                           C.c_float, u8p]
     L.orc_quantize_q8k128.argtypes = [vp, i64, i64, vp]
+    L.orc_row_weights_mode.argtypes = [f32p, vp, i64, C.c_float, C.c_int, f32p]
+    L.orc_quantize_rows_weighted.argtypes = [C.c_int, vp, vp, i64, i64, C.c_int, vp]
+    L.orc_quantize_row_sigma2_mode.argtypes = [C.c_int, f32p, vp, i64, C.c_float,
+                                               C.c_int, u8p]
     L.orc_dequantize_rows.argtypes = [C.c_int, vp, i64, i64, vp]
     f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
     i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
@@ -200,6 +206,51 @@ def solve_asym(x, w, nmax, K=None, F=None, k4=False):
     if rc != 0:
         raise ValueError("orc_solve_asym: invalid arguments")
     return l, d[0], m[0], info
+
+
+def _wid(mode) -> int:
+    return WEIGHTINGS[mode] if isinstance(mode, str) else int(mode)
+
+
+def row_weights_mode(x, q, sigma2, mode) -> np.ndarray:
+    x = _f32(x)
+    qq = None if q is None else _f32(q)
+    w = np.empty_like(x)
+    lib().orc_row_weights_mode(x, _ptr(qq), x.size, np.float32(sigma2), _wid(mode), w)
+    return w
+
+
+def quantize_rows_weighted(t, x, imatrix, mode, threads: int = 1) -> np.ndarray:
+    """quantize_rows with a weighting (name or number, see WEIGHTINGS)."""
+    t = _tid(t)
+    x = _f32(x)
+    n_rows, n = x.shape
+    rb = row_bytes(t, n)
+    q = None if imatrix is None else _f32(imatrix)
+    out = np.zeros((n_rows, rb), np.uint8)
+    m = _wid(mode)
+
+    def run(r0, r1):
+        if r1 > r0:
+            rc = lib().orc_quantize_rows_weighted(t, _ptr(x[r0:r1]), _ptr(q), r1 - r0,
+                                                  n, m, _ptr(out[r0:r1]))
+            if rc != 0:
+                raise ValueError("orc_quantize_rows_weighted failed")
+
+    _rows_parallel(n_rows, run, threads)
+    return out
+
+
+def quantize_row_sigma2_mode(t, x, q, sigma2, mode) -> np.ndarray:
+    t = _tid(t)
+    x = _f32(x).ravel()
+    qq = None if q is None else _f32(q)
+    out = np.zeros(row_bytes(t, x.size), np.uint8)
+    rc = lib().orc_quantize_row_sigma2_mode(t, x, _ptr(qq), x.size,
+                                            np.float32(sigma2), _wid(mode), out)
+    if rc != 0:
+        raise ValueError("orc_quantize_row_sigma2_mode failed")
+    return out
 
 
 def _rows_parallel(n_rows, fn, threads):

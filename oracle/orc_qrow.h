@@ -69,6 +69,27 @@ double orc_row_sigma2_f64(const float *x, int64_t n);
 void orc_row_weights(const float *x, const float *q, int64_t n, float sigma2,
                      float *w);
 
+/* Weightings: w_j = q_j * m(x_j) with m one of the magnitude forms below
+ * (values fixed; the GPU library's enum must match). */
+enum {
+    ORC_W_SQRT_SIGMA2_X2 = 0,   /* sqrtf(fmaf(x, x, sigma2)) -- the default */
+    ORC_W_X2 = 1,               /* x * x                                     */
+    ORC_W_ABS_X = 2,            /* |x|                                       */
+    ORC_W_SIGMA2_PLUS_X2 = 3,   /* fmaf(x, x, sigma2)                        */
+    ORC_W_SIGMA_PLUS_ABS_X = 4, /* sqrtf(sigma2) + |x|                       */
+    ORC_W_IMATRIX_ONLY = 5      /* 1                                          */
+};
+void orc_row_weights_mode(const float *x, const float *q, int64_t n,
+                          float sigma2, int mode, float *w);
+/* orc_quantize_rows with a weighting; with a group of all-zero importances
+ * the same weighting is taken with q = 1. */
+int orc_quantize_rows_weighted(int type, const float *x, const float *imatrix,
+                               int64_t n_rows, int64_t n_per_row, int mode,
+                               uint8_t *out);
+int orc_quantize_row_sigma2_mode(int type, const float *x, const float *q,
+                                 int64_t n_per_row, float sigma2, int mode,
+                                 uint8_t *out);
+
 /* Block solvers on n <= 256 elements with explicit weights w.
  * info[0] = index of the winning trial scale (-1: zero block),
  * info[1] = flips accepted, info[2] = passes run,

@@ -157,6 +157,37 @@ float orc_row_sigma2(const float *x, int64_t n)
     return (float)orc_row_sigma2_f64(x, n);
 }
 
+/* The magnitude factor of element importance under each weighting
+ * [WT 一, 二]: the pages' sqrt(sigma2 + x^2), and the forms that section
+ * lists as tried before it (x^2, |x|, sigma2 + x^2, sigma + |x|) and the
+ * imatrix alone (factor 1). Reading: sigma2 + x^2 is one fused operation in
+ * both forms that use it, sigma = sqrtf(sigma2) correctly rounded. */
+static float magnitude(float x, float sigma2, float sigma, int mode)
+{
+    switch (mode) {
+    case ORC_W_X2:              return x * x;
+    case ORC_W_ABS_X:           return fabsf(x);
+    case ORC_W_SIGMA2_PLUS_X2:  return fmaf(x, x, sigma2);
+    case ORC_W_SIGMA_PLUS_ABS_X: return sigma + fabsf(x);
+    case ORC_W_IMATRIX_ONLY:    return 1.0f;
+    default:                    return sqrtf(fmaf(x, x, sigma2));
+    }
+}
+
+void orc_row_weights_mode(const float *x, const float *q, int64_t n,
+                          float sigma2, int mode, float *w)
+{
+    if (mode == ORC_W_SQRT_SIGMA2_X2) {
+        orc_row_weights(x, q, n, sigma2, w);
+        return;
+    }
+    const float sigma = sqrtf(sigma2);
+    for (int64_t j = 0; j < n; ++j) {
+        const float m = magnitude(x[j], sigma2, sigma, mode);
+        w[j] = q ? q[j] * m : m;
+    }
+}
+
 void orc_row_weights(const float *x, const float *q, int64_t n, float sigma2,
                      float *w)
 {
@@ -549,18 +580,19 @@ static void quantize_q4k(const float *x, const float *w, uint8_t *out)
 /* row drivers                                                                */
 
 static int quantize_row_impl(int type, const float *x, const float *q,
-                             int64_t n, float sigma2, float *w, uint8_t *out)
+                             int64_t n, float sigma2, int mode, float *w,
+                             uint8_t *out)
 {
     const int be = orc_block_elems(type);
     const size_t bb = orc_block_bytes(type);
-    orc_row_weights(x, q, n, sigma2, w);
+    orc_row_weights_mode(x, q, n, sigma2, mode, w);
     /* A 32-weight group (the unit every fit works on: a legacy block or a
      * Q4_K sub-block) whose importances are all zero -- an imatrix with no
      * data on those columns -- falls back to unit importances (reading). */
     for (int64_t g = 0; g < n / 32; ++g) {
         int all_zero = 1;
         for (int i = 0; i < 32; ++i) if (w[32 * g + i] != 0.0f) { all_zero = 0; break; }
-        if (all_zero) orc_row_weights(x + 32 * g, NULL, 32, sigma2, w + 32 * g);
+        if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, mode, w + 32 * g);
     }
     for (int64_t ib = 0; ib < n / be; ++ib) {
         const float *xb = x + ib * be;
@@ -577,22 +609,32 @@ static int weight_type_ok(int type)
            type == ORC_Q5_1 || type == ORC_Q4_K;
 }
 
-int orc_quantize_row_sigma2(int type, const float *x, const float *q,
-                            int64_t n_per_row, float sigma2, uint8_t *out)
+int orc_quantize_row_sigma2_mode(int type, const float *x, const float *q,
+                                 int64_t n_per_row, float sigma2, int mode,
+                                 uint8_t *out)
 {
-    if (!weight_type_ok(type) || orc_row_bytes(type, n_per_row) == 0) return ORC_EINVAL;
+    if (!weight_type_ok(type) || orc_row_bytes(type, n_per_row) == 0 ||
+        mode < 0 || mode > ORC_W_IMATRIX_ONLY) return ORC_EINVAL;
     float *w = (float *)malloc(sizeof(float) * (size_t)n_per_row);
     if (!w) return ORC_EINVAL;
-    int rc = quantize_row_impl(type, x, q, n_per_row, sigma2, w, out);
+    int rc = quantize_row_impl(type, x, q, n_per_row, sigma2, mode, w, out);
     free(w);
     return rc;
 }
 
-int orc_quantize_rows_grouped(int type, const float *x, const float *imatrix,
-                              int64_t n_groups, int64_t rows_per_group,
-                              int64_t n_per_row, uint8_t *out)
+int orc_quantize_row_sigma2(int type, const float *x, const float *q,
+                            int64_t n_per_row, float sigma2, uint8_t *out)
 {
-    if (!weight_type_ok(type) || n_groups < 0 || rows_per_group < 0) return ORC_EINVAL;
+    return orc_quantize_row_sigma2_mode(type, x, q, n_per_row, sigma2,
+                                        ORC_W_SQRT_SIGMA2_X2, out);
+}
+
+static int quantize_rows_mode(int type, const float *x, const float *imatrix,
+                              int64_t n_groups, int64_t rows_per_group,
+                              int64_t n_per_row, int mode, uint8_t *out)
+{
+    if (!weight_type_ok(type) || n_groups < 0 || rows_per_group < 0 ||
+        mode < 0 || mode > ORC_W_IMATRIX_ONLY) return ORC_EINVAL;
     size_t rb = orc_row_bytes(type, n_per_row);
     if (rb == 0) return ORC_EINVAL;
     float *w = (float *)malloc(sizeof(float) * (size_t)n_per_row);
@@ -601,10 +643,26 @@ int orc_quantize_rows_grouped(int type, const float *x, const float *imatrix,
         const float *xr = x + r * n_per_row;
         const float *q = imatrix ? imatrix + (r / rows_per_group) * n_per_row : NULL;
         quantize_row_impl(type, xr, q, n_per_row, orc_row_sigma2(xr, n_per_row),
-                          w, out + (size_t)r * rb);
+                          mode, w, out + (size_t)r * rb);
     }
     free(w);
     return ORC_OK;
+}
+
+int orc_quantize_rows_grouped(int type, const float *x, const float *imatrix,
+                              int64_t n_groups, int64_t rows_per_group,
+                              int64_t n_per_row, uint8_t *out)
+{
+    return quantize_rows_mode(type, x, imatrix, n_groups, rows_per_group,
+                              n_per_row, ORC_W_SQRT_SIGMA2_X2, out);
+}
+
+int orc_quantize_rows_weighted(int type, const float *x, const float *imatrix,
+                               int64_t n_rows, int64_t n_per_row, int mode,
+                               uint8_t *out)
+{
+    if (n_rows == 0) return weight_type_ok(type) && orc_row_bytes(type, n_per_row) ? ORC_OK : ORC_EINVAL;
+    return quantize_rows_mode(type, x, imatrix, 1, n_rows, n_per_row, mode, out);
 }
 
 int orc_quantize_rows(int type, const float *x, const float *imatrix,

@@ -73,10 +73,19 @@ MUTANTS = [
     ("matmul: activation block stride", "const uint8_t *p = row + blk * 140;", "const uint8_t *p = row + blk * 136;"),
     ("matmul: offset sign", "acc += (a[i] - b[i]) * xt[i];", "acc += (a[i] + b[i]) * xt[i];"),
     ("q8_1: s without d", "orc_f32_to_f16(d * (float)sum)", "orc_f32_to_f16((float)sum)"),
+    # weightings
+    ("weighting: |x| without abs", "case ORC_W_ABS_X:           return fabsf(x);",
+     "case ORC_W_ABS_X:           return x;"),
+    ("weighting: sigma not rooted", "const float sigma = sqrtf(sigma2);", "const float sigma = sigma2;"),
+    ("weighting: fallback ignores the mode",
+     "if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, mode, w + 32 * g);",
+     "if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, 0, w + 32 * g);"),
+    ("weighting: imatrix dropped", "w[j] = q ? q[j] * m : m;", "w[j] = m;"),
 ]
 
 
-PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py", "test_matmul_oracle_pins.py")
+PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py", "test_matmul_oracle_pins.py",
+             "test_weighting_oracle_pins.py")
 
 
 def _pins_modules():
@@ -101,6 +110,9 @@ def _pin_calls(mods):
         "test_exact_lattice_rows_round_trip": dict(t="q4_0", nmax=8, sym=True),
         "test_power_of_two_constant_imatrix_equals_none": dict(t="q4_k"),
         "test_product_equals_library_matmul_of_decoded_values": dict(t="q4_k"),
+        "test_each_mode_passes_its_weights_to_the_solver": dict(mode="x2"),
+        "test_zero_importance_groups_fall_back_per_mode": dict(mode="x2"),
+        "test_power_of_two_scaling_scales_the_scales": dict(mode="abs_x"),
     }
     calls = []
     for mod in mods:
@@ -114,6 +126,9 @@ def _pin_calls(mods):
     calls.append(("round trip q5_1", lambda: mod.test_exact_lattice_rows_round_trip("q5_1", 31, False)))
     calls.append(("round trip q5_0", lambda: mod.test_exact_lattice_rows_round_trip("q5_0", 16, True)))
     calls.append(("brute force sym 4/8", lambda: mod.test_sym_brute_force_tiny_blocks(4, 8, True)))
+    wm = mods[3]
+    for mode in ("abs_x", "sigma_plus_abs_x"):
+        calls.append((f"fallback {mode}", lambda mode=mode: wm.test_zero_importance_groups_fall_back_per_mode(mode)))
     mm = mods[2]
     for t in ("q4_0", "q5_1"):
         calls.append((f"matmul {t}", lambda t=t: mm.test_product_equals_library_matmul_of_decoded_values(t)))
