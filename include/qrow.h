@@ -68,6 +68,17 @@ typedef enum {
 
 typedef enum { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
 
+/* Element importance w = q * m(x) [WT 一, 二]: the pages' form and the
+ * magnitude forms the pages list as tried before it, for ablation. */
+typedef enum {
+    QR_W_SQRT_SIGMA2_X2 = 0,    /* m = sqrtf(fmaf(x, x, sigma2))  (the pages') */
+    QR_W_X2 = 1,                /* m = x * x                                   */
+    QR_W_ABS_X = 2,             /* m = |x|                                     */
+    QR_W_SIGMA2_PLUS_X2 = 3,    /* m = fmaf(x, x, sigma2)                      */
+    QR_W_SIGMA_PLUS_ABS_X = 4,  /* m = sqrtf(sigma2) + |x|                     */
+    QR_W_IMATRIX_ONLY = 5       /* m = 1: the imatrix alone                    */
+} qr_weighting;
+
 #define QR_OK            0
 #define QR_EINVAL_TYPE  -1  /* unknown type, or a type the call does not take */
 #define QR_EINVAL_SHAPE -2  /* n_per_row not a positive multiple of the block
@@ -113,6 +124,19 @@ int qr_quantize_rows_grouped(int t, int src, const void *x,
                              const float *imatrix, int64_t n_groups,
                              int64_t rows_per_group, int64_t n_per_row,
                              void *out, void *stream);
+
+/*
+ * qr_quantize_rows_weighted -- qr_quantize_rows with another element
+ * importance: w_j = imatrix[j] * m(x_j) with m given by `weighting`
+ * (qr_weighting; QR_EINVAL_TYPE otherwise). A 32-weight group whose w are
+ * all zero uses imatrix = 1 with the same m. QR_W_SQRT_SIGMA2_X2 gives
+ * exactly the output of qr_quantize_rows. The results are bit-identical to
+ * the CPU oracle of this project for every weighting.
+ */
+int qr_quantize_rows_weighted(int t, int src, const void *x,
+                              const float *imatrix, int64_t n_rows,
+                              int64_t n_per_row, int weighting, void *out,
+                              void *stream);
 
 /*
  * qr_quantize_activations_q8k128 -- the Q8_K_128 activation quantizer

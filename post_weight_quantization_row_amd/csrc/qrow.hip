@@ -191,10 +191,62 @@ __device__ __forceinline__ void group_importances_(const float (&x)[QK], const f
   }
 }
 
+// What a row's importances depend on besides x and q.
+struct RowImp {
+  float sigma2;  // row statistic
+  float sigma;   // its correctly rounded square root (the sigma + |x| form)
+  bool normal;   // sigma2 in the range of the fast correctly rounded root
+  int mode;      // weighting (qr_weighting); always 0 in the default kernels
+};
+
+// The other weightings [WT 一, 二]: w = q * m(x) with m one of the magnitude
+// forms the pages list as tried before sqrt(sigma2 + x^2), or m = 1 (the
+// imatrix alone).
+template <int MODE>
+__device__ __forceinline__ float magnitude(float x, const RowImp& r) {
+  if (MODE == QR_W_X2) return x * x;
+  if (MODE == QR_W_ABS_X) return fabsf(x);
+  if (MODE == QR_W_SIGMA2_PLUS_X2) return fma_(x, x, r.sigma2);
+  if (MODE == QR_W_SIGMA_PLUS_ABS_X) return r.sigma + fabsf(x);
+  return 1.0f;
+}
+
+template <int MODE>
+__device__ __forceinline__ void group_importances_mode(const float (&x)[QK], const float* __restrict__ q,
+                                                       const RowImp& r, float (&w)[QK]) {
+  if (q) {
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(q);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f32x4 v = q4[k];
+      w[4 * k] = v.x * magnitude<MODE>(x[4 * k], r);
+      w[4 * k + 1] = v.y * magnitude<MODE>(x[4 * k + 1], r);
+      w[4 * k + 2] = v.z * magnitude<MODE>(x[4 * k + 2], r);
+      w[4 * k + 3] = v.w * magnitude<MODE>(x[4 * k + 3], r);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < QK; ++i) w[i] = magnitude<MODE>(x[i], r);
+  }
+}
+
+// VAR: the kernel takes a weighting at run time (uniform over the launch);
+// otherwise it is compiled for the pages' form only.
+template <bool VAR>
 __device__ __forceinline__ void group_importances(const float (&x)[QK], const float* __restrict__ q,
-                                                  float sigma2, bool normal_range, float (&w)[QK]) {
-  if (normal_range) group_importances_<true>(x, q, sigma2, w);
-  else group_importances_<false>(x, q, sigma2, w);
+                                                  const RowImp& r, float (&w)[QK]) {
+  if (VAR && r.mode != QR_W_SQRT_SIGMA2_X2) {
+    switch (r.mode) {
+      case QR_W_X2: group_importances_mode<QR_W_X2>(x, q, r, w); break;
+      case QR_W_ABS_X: group_importances_mode<QR_W_ABS_X>(x, q, r, w); break;
+      case QR_W_SIGMA2_PLUS_X2: group_importances_mode<QR_W_SIGMA2_PLUS_X2>(x, q, r, w); break;
+      case QR_W_SIGMA_PLUS_ABS_X: group_importances_mode<QR_W_SIGMA_PLUS_ABS_X>(x, q, r, w); break;
+      default: group_importances_mode<QR_W_IMATRIX_ONLY>(x, q, r, w); break;
+    }
+    return;
+  }
+  if (r.normal) group_importances_<true>(x, q, r.sigma2, w);
+  else group_importances_<false>(x, q, r.sigma2, w);
 }
 
 // -------------------------------------------------------------------------
@@ -241,18 +293,18 @@ __device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&
 // -------------------------------------------------------------------------
 // symmetric group: levels -NMAX .. NMAX-1, one scale
 
-template <int NMAX, bool BF16>
-__device__ __forceinline__ float solve_sym(const void* lds, int g, const float* __restrict__ q, float sigma2,
-                                           bool normal_range, float (&L)[QK]) {
+template <int NMAX, bool BF16, bool VAR>
+__device__ __forceinline__ float solve_sym(const void* lds, int g, const float* __restrict__ q, const RowImp& imp,
+                                           float (&L)[QK]) {
   constexpr float LO = (float)-NMAX, HI = (float)(NMAX - 1);
   float x[QK], w[QK], wx[QK];
   load_group<BF16>(lds, g, x);
-  group_importances(x, q, sigma2, normal_range, w);
+  group_importances<VAR>(x, q, imp, w);
   {  // a group with no importance at all falls back to q = 1
     uint32_t any = 0;
 #pragma unroll
     for (int i = 0; i < QK; ++i) any |= fbits(w[i]) & 0x7fffffffu;
-    if (any == 0) group_importances(x, nullptr, sigma2, normal_range, w);
+    if (any == 0) group_importances<VAR>(x, nullptr, imp, w);
   }
   // element of largest magnitude, first one on ties: from max and min, with
   // a scan only when +a and -a are both present
@@ -334,18 +386,18 @@ __device__ __forceinline__ void fit_dm(float Sw_, float Sx_, float Sl_, float Sl
 
 // Returns (d, m) and the levels; x, w are left in the arrays for the caller
 // (w: importances; x: overwritten).
-template <int NMAX, bool K4, bool BF16>
-__device__ __forceinline__ void solve_asym(const void* lds, int g, const float* __restrict__ q, float sigma2,
-                                           bool normal_range, float (&L)[QK], float& d_out, float& m_out) {
+template <int NMAX, bool K4, bool BF16, bool VAR>
+__device__ __forceinline__ void solve_asym(const void* lds, int g, const float* __restrict__ q, const RowImp& imp,
+                                           float (&L)[QK], float& d_out, float& m_out) {
   constexpr float HI = (float)NMAX;
   float x[QK], w[QK];
   load_group<BF16>(lds, g, x);
-  group_importances(x, q, sigma2, normal_range, w);
+  group_importances<VAR>(x, q, imp, w);
   float Sw = 0.0f;
 #pragma unroll
   for (int i = 0; i < QK; ++i) Sw = Sw + w[i];
   if (!(Sw > 0.0f)) {   // no importance at all: q = 1 for this group
-    group_importances(x, nullptr, sigma2, normal_range, w);
+    group_importances<VAR>(x, nullptr, imp, w);
     Sw = 0.0f;
 #pragma unroll
     for (int i = 0; i < QK; ++i) Sw = Sw + w[i];
@@ -479,12 +531,12 @@ __device__ __forceinline__ void store_u32(uint8_t* p, uint32_t v) { *reinterpret
 
 constexpr int MAX_ROW_WAVES = 8;
 
-template <int TYPE, bool BF16>
+template <int TYPE, bool BF16, bool VAR>
 __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(3))) void k_quantize_rows(const void* __restrict__ x,
                                                                         const float* __restrict__ imatrix,
                                                                         int n_per_row, int64_t rows_per_group,
                                                                         uint8_t* __restrict__ out,
-                                                                        int64_t row_bytes) {
+                                                                        int64_t row_bytes, int weighting) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -502,6 +554,11 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
   for (int k = 0; k < nthreads / WAVE; ++k) ss += partial[k];
   const float sigma2 = (float)(ss / (double)n_per_row);
   const bool normal_range = sigma2 >= 0x1p-96f && sigma2 <= 3.0e38f;
+  RowImp imp;
+  imp.sigma2 = sigma2;
+  imp.normal = normal_range;
+  imp.mode = VAR ? weighting : QR_W_SQRT_SIGMA2_X2;
+  imp.sigma = VAR && weighting == QR_W_SIGMA_PLUS_ABS_X ? sqrt_cr(sigma2, normal_range) : 0.0f;
 
   const float* q = imatrix ? imatrix + (row / rows_per_group) * (int64_t)n_per_row : nullptr;
   uint8_t* orow = out + row * row_bytes;
@@ -514,7 +571,7 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
 
     if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
       constexpr int NMAX = TYPE == QR_Q4_0 ? 8 : 16;
-      const float d = solve_sym<NMAX, BF16>(lds_raw, g, qg, sigma2, normal_range, L);
+      const float d = solve_sym<NMAX, BF16, VAR>(lds_raw, g, qg, imp, L);
       if constexpr (TYPE == QR_Q4_0) {
         float uf[QK];
 #pragma unroll
@@ -536,7 +593,7 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
     } else if constexpr (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
       constexpr int NMAX = TYPE == QR_Q4_1 ? 15 : 31;
       float d, m;
-      solve_asym<NMAX, false, BF16>(lds_raw, g, qg, sigma2, normal_range, L, d, m);
+      solve_asym<NMAX, false, BF16, VAR>(lds_raw, g, qg, imp, L, d, m);
       if constexpr (TYPE == QR_Q4_1) {
         const uint4 qs = pack_nibbles_f(L);
         uint8_t* p = orow + (size_t)g * 24;
@@ -554,7 +611,7 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
       }
     } else {  // QR_Q4_K: lanes 8s .. 8s+7 hold the sub-blocks of one super-block [KQ 一]
       float d, m;
-      solve_asym<15, true, BF16>(lds_raw, g, qg, sigma2, normal_range, L, d, m);
+      solve_asym<15, true, BF16, VAR>(lds_raw, g, qg, imp, L, d, m);
       const float a = d > 0.0f ? d : 0.0f;
       const float b = -m > 0.0f ? -m : 0.0f;
       float A = a, Bm = b;
@@ -823,10 +880,10 @@ size_t block_bytes(int t) {
 bool aligned16(const void* p) { return qr_aligned(p, 16); }
 
 
-template <int TYPE, bool BF16>
+template <int TYPE, bool BF16, bool VAR>
 int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_row, int64_t rows_per_group,
-                void* out, size_t row_bytes, hipStream_t stream) {
-  auto kern = k_quantize_rows<TYPE, BF16>;
+                void* out, size_t row_bytes, int weighting, hipStream_t stream) {
+  auto kern = k_quantize_rows<TYPE, BF16, VAR>;
   const int n_groups = n_per_row / QK;
   int waves = (n_groups + WAVE - 1) / WAVE;
   if (waves > MAX_ROW_WAVES) waves = MAX_ROW_WAVES;
@@ -839,21 +896,58 @@ int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_r
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE * waves), lds, stream, x, imatrix, n_per_row,
-                     rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes);
+                     rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes, weighting);
   return qr_check_launch("k_quantize_rows");
 }
 
-template <bool BF16>
+template <bool BF16, bool VAR>
 int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, int n_per_row,
-                  int64_t rows_per_group, void* out, size_t row_bytes, hipStream_t s) {
+                  int64_t rows_per_group, void* out, size_t row_bytes, int weighting, hipStream_t s) {
+#define QR_ROWS_LAUNCH(T) \
+  launch_rows<T, BF16, VAR>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, weighting, s)
   switch (t) {
-    case QR_Q4_0: return launch_rows<QR_Q4_0, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
-    case QR_Q4_1: return launch_rows<QR_Q4_1, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
-    case QR_Q5_0: return launch_rows<QR_Q5_0, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
-    case QR_Q5_1: return launch_rows<QR_Q5_1, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
-    case QR_Q4_K: return launch_rows<QR_Q4_K, BF16>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, s);
+    case QR_Q4_0: return QR_ROWS_LAUNCH(QR_Q4_0);
+    case QR_Q4_1: return QR_ROWS_LAUNCH(QR_Q4_1);
+    case QR_Q5_0: return QR_ROWS_LAUNCH(QR_Q5_0);
+    case QR_Q5_1: return QR_ROWS_LAUNCH(QR_Q5_1);
+    case QR_Q4_K: return QR_ROWS_LAUNCH(QR_Q4_K);
     default: return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   }
+#undef QR_ROWS_LAUNCH
+}
+
+// Validation and launch shared by the row quantizers. The pages' weighting
+// runs in the kernels compiled for it alone; the others in the variants.
+int quantize_rows_common(int t, int src, const void* x, const float* imatrix, int64_t n_groups,
+                         int64_t rows_per_group, int64_t n_per_row, int weighting, void* out, void* stream) {
+  if (t < QR_Q4_0 || t > QR_Q4_K) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
+  if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
+  if (weighting < QR_W_SQRT_SIGMA2_X2 || weighting > QR_W_IMATRIX_ONLY)
+    return qr_fail(QR_EINVAL_TYPE, "weighting %d is not a qr_weighting", weighting);
+  if (n_groups < 0 || rows_per_group < 0) return qr_fail(QR_EINVAL_SHAPE, "negative row count");
+  const int be = block_elems(t);
+  const int64_t max_row = src == QR_F32 ? QR_MAX_ROW_F32 : QR_MAX_ROW_BF16;
+  if (n_per_row <= 0 || n_per_row % be != 0 || n_per_row > max_row)
+    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d and at most %lld",
+                (long long)n_per_row, be, (long long)max_row);
+  if (rows_per_group != 0 && n_groups > INT64_MAX / rows_per_group)
+    return qr_fail(QR_EOVERFLOW, "n_groups * rows_per_group overflows");
+  const int64_t n_rows = n_groups * rows_per_group;
+  if (n_rows == 0) return QR_OK;
+  if (n_rows > (int64_t)UINT32_MAX) return qr_fail(QR_EOVERFLOW, "n_rows=%lld exceeds 2^32-1", (long long)n_rows);
+  const size_t rb = qr_row_bytes(t, n_per_row);
+  if ((uint64_t)n_rows > SIZE_MAX / rb || (uint64_t)n_rows > SIZE_MAX / ((uint64_t)n_per_row * 4))
+    return qr_fail(QR_EOVERFLOW, "buffer size overflows");
+  if (!x || !out) return qr_fail(QR_EINVAL_PTR, "x and out must be non-NULL");
+  if (!aligned16(x) || !aligned16(out) || (imatrix && !aligned16(imatrix)))
+    return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int n = (int)n_per_row;
+  if (weighting == QR_W_SQRT_SIGMA2_X2)
+    return src == QR_F32 ? dispatch_rows<false, false>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, 0, s)
+                         : dispatch_rows<true, false>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, 0, s);
+  return src == QR_F32 ? dispatch_rows<false, true>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, weighting, s)
+                       : dispatch_rows<true, true>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, weighting, s);
 }
 
 int grid_for(int64_t work_items, int per_block) {
@@ -907,29 +1001,15 @@ void qr_solver_constants(int32_t* c) {
 int qr_quantize_rows_grouped(int t, int src, const void* x, const float* imatrix, int64_t n_groups,
                              int64_t rows_per_group, int64_t n_per_row, void* out, void* stream) {
   qr_clear_error();
-  if (t < QR_Q4_0 || t > QR_Q4_K) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
-  if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
-  if (n_groups < 0 || rows_per_group < 0) return qr_fail(QR_EINVAL_SHAPE, "negative row count");
-  const int be = block_elems(t);
-  const int64_t max_row = src == QR_F32 ? QR_MAX_ROW_F32 : QR_MAX_ROW_BF16;
-  if (n_per_row <= 0 || n_per_row % be != 0 || n_per_row > max_row)
-    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d and at most %lld",
-                (long long)n_per_row, be, (long long)max_row);
-  if (rows_per_group != 0 && n_groups > INT64_MAX / rows_per_group)
-    return qr_fail(QR_EOVERFLOW, "n_groups * rows_per_group overflows");
-  const int64_t n_rows = n_groups * rows_per_group;
-  if (n_rows == 0) return QR_OK;
-  if (n_rows > (int64_t)UINT32_MAX) return qr_fail(QR_EOVERFLOW, "n_rows=%lld exceeds 2^32-1", (long long)n_rows);
-  const size_t rb = qr_row_bytes(t, n_per_row);
-  if ((uint64_t)n_rows > SIZE_MAX / rb || (uint64_t)n_rows > SIZE_MAX / ((uint64_t)n_per_row * 4))
-    return qr_fail(QR_EOVERFLOW, "buffer size overflows");
-  if (!x || !out) return qr_fail(QR_EINVAL_PTR, "x and out must be non-NULL");
-  if (!aligned16(x) || !aligned16(out) || (imatrix && !aligned16(imatrix)))
-    return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return src == QR_F32
-             ? dispatch_rows<false>(t, x, imatrix, n_rows, (int)n_per_row, rows_per_group, out, rb, s)
-             : dispatch_rows<true>(t, x, imatrix, n_rows, (int)n_per_row, rows_per_group, out, rb, s);
+  return quantize_rows_common(t, src, x, imatrix, n_groups, rows_per_group, n_per_row, QR_W_SQRT_SIGMA2_X2, out,
+                              stream);
+}
+
+int qr_quantize_rows_weighted(int t, int src, const void* x, const float* imatrix, int64_t n_rows,
+                              int64_t n_per_row, int weighting, void* out, void* stream) {
+  qr_clear_error();
+  if (n_rows < 0) return qr_fail(QR_EINVAL_SHAPE, "negative row count");
+  return quantize_rows_common(t, src, x, imatrix, 1, n_rows, n_per_row, weighting, out, stream);
 }
 
 int qr_quantize_rows(int t, int src, const void* x, const float* imatrix, int64_t n_rows, int64_t n_per_row,

@@ -19,6 +19,9 @@ LIB_PATH = os.environ.get("QROW_LIBRARY") or os.path.join(HERE, "libqrow.so")
 
 QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q4_K, QR_Q8_K128 = range(6)
 QR_F32, QR_BF16 = 0, 1
+# element-importance weightings (qr_weighting)
+WEIGHTINGS = {"sqrt_sigma2_x2": 0, "x2": 1, "abs_x": 2, "sigma2_plus_x2": 3,
+              "sigma_plus_abs_x": 4, "imatrix_only": 5}
 TYPES = {"q4_0": QR_Q4_0, "q4_1": QR_Q4_1, "q5_0": QR_Q5_0, "q5_1": QR_Q5_1,
          "q4_k": QR_Q4_K, "q8_k128": QR_Q8_K128}
 ERRORS = {-1: "QR_EINVAL_TYPE", -2: "QR_EINVAL_SHAPE", -3: "QR_EINVAL_PTR",
@@ -30,7 +33,8 @@ EXPORTS = ("qr_quantize_rows", "qr_quantize_rows_grouped",
            "qr_row_bytes", "qr_block_elems", "qr_solver_constants",
            "qr_last_error", "qr_imatrix_workspace_bytes",
            "qr_imatrix_accumulate", "qr_imatrix_merge",
-           "qr_imatrix_finalize", "qr_matmul_q8k128")
+           "qr_imatrix_finalize", "qr_matmul_q8k128",
+           "qr_quantize_rows_weighted")
 IMX_MAX_EXPERTS, IMX_MAX_TOP_K = 1024, 64
 
 
@@ -70,6 +74,7 @@ def load_library(path: str = LIB_PATH):
         L.qr_imatrix_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.qr_imatrix_finalize.argtypes = [vp, vp, i64, i64, vp, vp]
         L.qr_matmul_q8k128.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp]
+        L.qr_quantize_rows_weighted.argtypes = [i32, i32, vp, vp, i64, i64, i32, vp, vp]
         for name in (n for n in EXPORTS if n not in
                      ("qr_row_bytes", "qr_block_elems", "qr_last_error",
                       "qr_solver_constants", "qr_imatrix_workspace_bytes")):
@@ -153,6 +158,26 @@ def qr_quantize_rows(t, x: torch.Tensor, imatrix=None, out=None, stream=None):
     _check(load_library().qr_quantize_rows(
         tid, _src_dtype(x), C.c_void_p(x.data_ptr()),
         None if q is None else C.c_void_p(q.data_ptr()), n_rows, n,
+        C.c_void_p(out.data_ptr()), _stream(x, stream)))
+    return out
+
+
+def qr_quantize_rows_weighted(t, x: torch.Tensor, imatrix, weighting, out=None, stream=None):
+    """qr_quantize_rows with another element importance: weighting is a
+    name of WEIGHTINGS or its number."""
+    _dev2d(x, "x")
+    tid = _tid(t)
+    wid = WEIGHTINGS[weighting] if isinstance(weighting, str) else int(weighting)
+    n_rows, n = x.shape
+    out = _out(out, (n_rows, qr_row_bytes(tid, n)), torch.uint8, x.device)
+    q = None
+    if imatrix is not None:
+        if imatrix.dtype != torch.float32 or imatrix.numel() != n or not imatrix.is_cuda:
+            raise ValueError("imatrix must be a CUDA float32 tensor of n_per_row values")
+        q = imatrix.contiguous()
+    _check(load_library().qr_quantize_rows_weighted(
+        tid, _src_dtype(x), C.c_void_p(x.data_ptr()),
+        None if q is None else C.c_void_p(q.data_ptr()), n_rows, n, wid,
         C.c_void_p(out.data_ptr()), _stream(x, stream)))
     return out
 

@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(HEADERS) == 3 and len(names) == 13
+    assert len(HEADERS) == 3 and len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(qrow.EXPORTS) == names
@@ -157,3 +157,13 @@ def test_matmul_argument_validation_without_a_gpu(lib):
     assert mm(0, None, fake, 4, 2, 256, fake, None) == -3
     assert mm(0, fake, C.c_void_p(0x10004), 4, 2, 256, fake, None) == -3
     assert mm(0, fake, fake, 4, 2 ** 30, 32768, fake, None) == -4   # too many token tiles
+
+
+def test_weighting_enum_agrees_with_the_oracle_and_is_validated(lib):
+    assert qrow.WEIGHTINGS == oracle.WEIGHTINGS
+    fake = C.c_void_p(0x10000)
+    assert lib.qr_quantize_rows_weighted(0, 0, fake, None, 4, 256, 6, fake, None) == -1
+    assert lib.qr_quantize_rows_weighted(0, 0, fake, None, 4, 256, -1, fake, None) == -1
+    assert "weighting" in qrow.qr_last_error()
+    assert lib.qr_quantize_rows_weighted(0, 0, fake, None, -1, 256, 1, fake, None) == -2
+    assert lib.qr_quantize_rows_weighted(0, 0, None, None, 0, 256, 1, None, None) == 0
