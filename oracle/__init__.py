@@ -22,7 +22,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qrow_oracle.c")
 SOURCES = [SRC, os.path.join(HERE, "imatrix_oracle.c"),
-           os.path.join(HERE, "matmul_oracle.c")]
+           os.path.join(HERE, "matmul_oracle.c"),
+           os.path.join(HERE, "stats_oracle.c")]
 LIB = os.path.join(HERE, "liborc_qrow.so")
 
 Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128 = range(6)
@@ -120,6 +121,7 @@ def _load(path):
     f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
     L.orc_matmul_q8k128.argtypes = [C.c_int, u8p, u8p, i64, i64, i64, f64p, vp]
     L.orc_matmul_q8_1.argtypes = [C.c_int, u8p, f32p, i64, i64, i64, f32p]
+    L.orc_quantize_stats.argtypes = [C.c_int, f32p, u8p, vp, i64, i64, f64p, f32p, f32p]
     L.orc_f32_to_f16.argtypes = [C.c_float]
     L.orc_f32_to_f16.restype = C.c_uint16
     L.orc_f16_to_f32.argtypes = [C.c_uint16]
@@ -435,6 +437,28 @@ def matmul_q8_1(t, w_packed, x, n_out: int):
     if rc != 0:
         raise ValueError("orc_matmul_q8_1: invalid arguments")
     return y
+
+
+def quantize_stats(t, x, packed, imatrix=None) -> dict:
+    """Error statistics of packed rows against x (float32 [n_rows, n]):
+    sums of e^2, x^2, q e^2, q x^2 (double), max |e| and the nearest-rank
+    95th percentile of |e|, e = x - decoded in float."""
+    t = _tid(t)
+    xv = _f32(x)
+    n_rows, n = xv.shape
+    p = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
+    if p.size != n_rows * row_bytes(t, n):
+        raise ValueError("packed buffer has the wrong size")
+    q = None if imatrix is None else _f32(imatrix)
+    sums = np.zeros(4, np.float64)
+    mx = np.zeros(1, np.float32)
+    p95 = np.zeros(1, np.float32)
+    rc = lib().orc_quantize_stats(t, xv, p, _ptr(q), n_rows, n, sums, mx, p95)
+    if rc != 0:
+        raise ValueError("orc_quantize_stats: invalid arguments")
+    return {"sum_err2": sums[0], "sum_x2": sums[1], "sum_werr2": sums[2],
+            "sum_wx2": sums[3], "max_abs_err": mx[0], "p95_abs_err": p95[0],
+            "n": n_rows * n}
 
 
 def f32_to_f16_bits(v: float) -> int:

@@ -150,6 +150,14 @@ int orc_matmul_q8k128(int type, const uint8_t *w, const uint8_t *x,
 int orc_matmul_q8_1(int type, const uint8_t *w, const float *x, int64_t n_out,
                     int64_t n_tok, int64_t n_in, float *y);
 
+/* Error statistics of packed rows against the rows they came from
+ * (stats_oracle.c): sums[4] = {sum e^2, sum x^2, sum q e^2, sum q x^2} in
+ * double, e = x - xhat in float; *max_abs = max |e|; *p95_abs = the
+ * ceil(0.95 N)-th smallest |e|. q (or NULL) is per column. */
+int orc_quantize_stats(int type, const float *x, const uint8_t *packed,
+                       const float *q, int64_t n_rows, int64_t n_per_row,
+                       double *sums, float *max_abs, float *p95_abs);
+
 /* IEEE-754 binary16 conversions (round to nearest-even, subnormals kept). */
 uint16_t orc_f32_to_f16(float f);
 float    orc_f16_to_f32(uint16_t h);

@@ -81,11 +81,18 @@ MUTANTS = [
      "if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, mode, w + 32 * g);",
      "if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, 0, w + 32 * g);"),
     ("weighting: imatrix dropped", "w[j] = q ? q[j] * m : m;", "w[j] = m;"),
+    # error statistics
+    ("stats: percentile rank rounded down", "const int64_t k = (95 * n + 99) / 100;",
+     "const int64_t k = (95 * n) / 100;"),
+    ("stats: weighted error without q", "qe2 += qi * (ed * ed);", "qe2 += ed * ed;"),
+    ("stats: maximum of the signed error", "mx = fmaxf(mx, ae[i]);", "mx = fmaxf(mx, e);"),
+    ("stats: imatrix by row", "const double qi = q ? (double)q[i % n_per_row] : 1.0;",
+     "const double qi = q ? (double)q[i / n_per_row] : 1.0;"),
 ]
 
 
 PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py", "test_matmul_oracle_pins.py",
-             "test_weighting_oracle_pins.py")
+             "test_weighting_oracle_pins.py", "test_stats_oracle_pins.py")
 
 
 def _pins_modules():
@@ -113,6 +120,8 @@ def _pin_calls(mods):
         "test_each_mode_passes_its_weights_to_the_solver": dict(mode="x2"),
         "test_zero_importance_groups_fall_back_per_mode": dict(mode="x2"),
         "test_power_of_two_scaling_scales_the_scales": dict(mode="abs_x"),
+        "test_against_numpy_on_the_decoded_rows": dict(t="q4_k"),
+        "test_nearest_rank": dict(n=64, k=61),
     }
     calls = []
     for mod in mods:

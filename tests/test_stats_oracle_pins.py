@@ -1,0 +1,75 @@
+"""Pins for the quantization error statistics of the oracle.
+
+Source: "量化方法论实证：为什么 LQER/L²QER 难以改进 ik_llama.cpp 的 k-quants 与
+i-quants", section 3.2 (RMSE = sqrt(total error / samples), maximum error,
+95th percentile). Checked against numpy (sums, maximum, and numpy's
+nearest-rank percentile, method "inverted_cdf") on the oracle decoder's
+output, against blocks built by hand with known errors, and against a
+lattice that quantizes exactly.
+"""
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+from post_weight_quantization_row_amd import synth
+
+F32 = np.float32
+
+
+@pytest.mark.parametrize("t", ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q8_k128"])
+def test_against_numpy_on_the_decoded_rows(t):
+    x, q = synth.q4_k_matrix(24, 1024, seed=111)
+    packed = oracle.quantize_q8k128(x) if t == "q8_k128" else oracle.quantize_rows(t, x, q)
+    st = oracle.quantize_stats(t, x, packed, q)
+    xh = oracle.dequantize_rows(t, packed, 24, 1024)
+    e = x - xh                                          # float32 subtraction
+    ae = np.abs(e)
+    e64, x64, q64 = e.astype(np.float64), x.astype(np.float64), q.astype(np.float64)
+    assert st["max_abs_err"] == ae.max()
+    assert st["p95_abs_err"] == np.percentile(ae, 95, method="inverted_cdf")
+    assert np.isclose(st["sum_err2"], np.sum(e64 * e64), rtol=1e-12, atol=0)
+    assert np.isclose(st["sum_x2"], np.sum(x64 * x64), rtol=1e-12, atol=0)
+    assert np.isclose(st["sum_werr2"], np.sum(q64 * e64 * e64), rtol=1e-12, atol=0)
+    assert np.isclose(st["sum_wx2"], np.sum(q64 * x64 * x64), rtol=1e-12, atol=0)
+    assert st["n"] == x.size
+
+
+def test_hand_built_block_with_known_errors():
+    # one Q4_0 block, d = 1, codes u = 8 + k: decodes to k exactly; x = k + e
+    # with chosen errors e, so |e| is known element by element
+    k = np.arange(32) % 16 - 8
+    u = k + 8
+    blk = struct.pack("<f", 1.0) + bytes(int(u[i] | (u[i + 16] << 4)) for i in range(16))
+    e = (np.arange(32) - 12) * 2.0 ** -6                # -0.1875 .. 0.3007
+    x = (k + e).astype(F32).reshape(1, 32)
+    st = oracle.quantize_stats("q4_0", x, np.frombuffer(blk, np.uint8), None)
+    ae = np.sort(np.abs(e))
+    assert st["max_abs_err"] == F32(ae[-1])
+    # ceil(0.95 * 32) = 31: the 31st smallest of 32
+    assert st["p95_abs_err"] == F32(ae[30])
+    assert st["sum_err2"] == np.sum(e * e)
+    assert st["sum_werr2"] == st["sum_err2"]            # no imatrix: q = 1
+
+
+@pytest.mark.parametrize("n,k", [(32, 31), (64, 61), (128, 122), (256, 244)])
+def test_nearest_rank(n, k):
+    # distinct errors 1..n (times 2^-8) in random order: the p95 is the k-th
+    rng = np.random.default_rng(n)
+    e = rng.permutation(np.arange(1, n + 1)) * 2.0 ** -8
+    u = np.full(32, 8)
+    blk = struct.pack("<f", 1.0) + bytes(int(u[i] | (u[i + 16] << 4)) for i in range(16))
+    x = e.astype(F32).reshape(-1, 32)                   # decoded values are all 0
+    st = oracle.quantize_stats("q4_0", x, np.frombuffer(blk * (n // 32), np.uint8), None)
+    assert st["p95_abs_err"] == F32(k * 2.0 ** -8)
+    assert st["max_abs_err"] == F32(n * 2.0 ** -8)
+
+
+def test_exact_lattice_has_no_error():
+    k = np.arange(256) % 16 - 8
+    x = (k * 2.0 ** -4).astype(F32).reshape(1, 256)
+    x[0, 0] = -0.5                                       # the largest magnitude maps to -8
+    packed = oracle.quantize_rows("q4_0", x, None)
+    st = oracle.quantize_stats("q4_0", x, packed, None)
+    assert st["sum_err2"] == 0.0 and st["max_abs_err"] == 0.0 and st["p95_abs_err"] == 0.0
