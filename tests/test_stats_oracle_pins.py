@@ -51,6 +51,10 @@ def test_hand_built_block_with_known_errors():
     assert st["p95_abs_err"] == F32(ae[30])
     assert st["sum_err2"] == np.sum(e * e)
     assert st["sum_werr2"] == st["sum_err2"]            # no imatrix: q = 1
+    # the mirrored errors: now the largest |e| belongs to a negative e
+    xm = (k - e).astype(F32).reshape(1, 32)
+    sm = oracle.quantize_stats("q4_0", xm, np.frombuffer(blk, np.uint8), None)
+    assert sm["max_abs_err"] == F32(ae[-1]) and sm["p95_abs_err"] == F32(ae[30])
 
 
 @pytest.mark.parametrize("n,k", [(32, 31), (64, 61), (128, 122), (256, 244)])
