@@ -6,7 +6,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "qrow.hip"),
            os.path.join(HERE, "csrc", "imatrix.hip"),
-           os.path.join(HERE, "csrc", "matmul.hip")]
+           os.path.join(HERE, "csrc", "matmul.hip"),
+           os.path.join(HERE, "csrc", "stats.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqrow.so")
 

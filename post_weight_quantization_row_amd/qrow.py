@@ -34,7 +34,8 @@ EXPORTS = ("qr_quantize_rows", "qr_quantize_rows_grouped",
            "qr_last_error", "qr_imatrix_workspace_bytes",
            "qr_imatrix_accumulate", "qr_imatrix_merge",
            "qr_imatrix_finalize", "qr_matmul_q8k128",
-           "qr_quantize_rows_weighted")
+           "qr_quantize_rows_weighted", "qr_stats_workspace_bytes",
+           "qr_quantize_stats")
 IMX_MAX_EXPERTS, IMX_MAX_TOP_K = 1024, 64
 
 
@@ -75,9 +76,13 @@ def load_library(path: str = LIB_PATH):
         L.qr_imatrix_finalize.argtypes = [vp, vp, i64, i64, vp, vp]
         L.qr_matmul_q8k128.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp]
         L.qr_quantize_rows_weighted.argtypes = [i32, i32, vp, vp, i64, i64, i32, vp, vp]
+        L.qr_stats_workspace_bytes.argtypes = [i64, i64]
+        L.qr_stats_workspace_bytes.restype = C.c_size_t
+        L.qr_quantize_stats.argtypes = [i32, i32, vp, vp, vp, i64, i64, vp, vp, C.c_size_t, vp]
         for name in (n for n in EXPORTS if n not in
                      ("qr_row_bytes", "qr_block_elems", "qr_last_error",
-                      "qr_solver_constants", "qr_imatrix_workspace_bytes")):
+                      "qr_solver_constants", "qr_imatrix_workspace_bytes",
+                      "qr_stats_workspace_bytes")):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -339,3 +344,48 @@ def qr_matmul_q8k128(t, w: torch.Tensor, x: torch.Tensor, n_in: int, out=None, s
     _check(load_library().qr_matmul_q8k128(
         tid, _ptr(w), _ptr(x), n_out, n_tok, n_in, _ptr(out), _stream(w, stream)))
     return out
+
+
+# --------------------------------------------------------------------------
+# error statistics (include/qrow_stats.h)
+
+QR_STATS_BYTES = 48   # sizeof(qr_stats)
+
+
+def qr_stats_workspace_bytes(n_rows: int, n_per_row: int) -> int:
+    return int(load_library().qr_stats_workspace_bytes(n_rows, n_per_row))
+
+
+def qr_quantize_stats(t, x: torch.Tensor, packed: torch.Tensor, imatrix=None, workspace=None,
+                      stream=None) -> dict:
+    """Error statistics of packed rows against x (see qr_stats); returns the
+    struct's fields plus rmse, rel_rmse and weighted_rel_rmse (this copies
+    the 48-byte result to the host, which waits for the stream)."""
+    import numpy as np
+    _dev2d(x, "x")
+    tid = _tid(t)
+    n_rows, n = x.shape
+    if (not packed.is_cuda or packed.dtype != torch.uint8 or not packed.is_contiguous()
+            or packed.numel() != n_rows * qr_row_bytes(tid, n)):
+        raise ValueError("packed must be a contiguous CUDA uint8 tensor of the rows' packed bytes")
+    q = None
+    if imatrix is not None:
+        if imatrix.dtype != torch.float32 or imatrix.numel() != n or not imatrix.is_cuda:
+            raise ValueError("imatrix must be a CUDA float32 tensor of n_per_row values")
+        q = imatrix.contiguous()
+    if workspace is None:
+        workspace = torch.empty(qr_stats_workspace_bytes(n_rows, n), dtype=torch.uint8, device=x.device)
+    out = torch.zeros(QR_STATS_BYTES, dtype=torch.uint8, device=x.device)
+    _check(load_library().qr_quantize_stats(
+        tid, _src_dtype(x), _ptr(x), _ptr(packed), _ptr(q), n_rows, n, _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(x, stream)))
+    raw = out.cpu().numpy()
+    sums = raw[:32].view(np.float64)
+    mx, p95 = raw[32:40].view(np.float32)
+    res = {"sum_err2": float(sums[0]), "sum_x2": float(sums[1]), "sum_werr2": float(sums[2]),
+           "sum_wx2": float(sums[3]), "max_abs_err": float(mx), "p95_abs_err": float(p95),
+           "n": int(raw[40:48].view(np.int64)[0])}
+    res["rmse"] = (res["sum_err2"] / res["n"]) ** 0.5 if res["n"] else 0.0
+    res["rel_rmse"] = (res["sum_err2"] / res["sum_x2"]) ** 0.5 if res["sum_x2"] > 0 else 0.0
+    res["weighted_rel_rmse"] = (res["sum_werr2"] / res["sum_wx2"]) ** 0.5 if res["sum_wx2"] > 0 else 0.0
+    return res

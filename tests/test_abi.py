@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(HEADERS) == 3 and len(names) == 14
+    assert len(HEADERS) == 4 and len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(qrow.EXPORTS) == names
@@ -167,3 +167,18 @@ def test_weighting_enum_agrees_with_the_oracle_and_is_validated(lib):
     assert "weighting" in qrow.qr_last_error()
     assert lib.qr_quantize_rows_weighted(0, 0, fake, None, -1, 256, 1, fake, None) == -2
     assert lib.qr_quantize_rows_weighted(0, 0, None, None, 0, 256, 1, None, None) == 0
+
+
+def test_stats_argument_validation_without_a_gpu(lib):
+    fake = C.c_void_p(0x10000)
+    ws = lib.qr_stats_workspace_bytes(4, 256)
+    assert ws > 0 and lib.qr_stats_workspace_bytes(4, 0) == 0
+    st = lib.qr_quantize_stats
+    assert st(6, 0, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
+    assert st(0, 2, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
+    assert st(4, 0, fake, fake, None, 4, 128, fake, fake, ws, None) == -2    # Q4_K: 256
+    assert st(0, 0, None, None, None, 0, 256, None, None, 0, None) == 0       # no rows
+    assert st(0, 0, fake, fake, None, 2 ** 31, 4096, fake, fake, ws, None) == -4
+    assert st(0, 0, fake, fake, None, 4, 256, None, fake, ws, None) == -3
+    assert st(0, 0, fake, fake, None, 4, 256, fake, C.c_void_p(0x10010), ws, None) == -3
+    assert st(0, 0, fake, fake, None, 4, 256, fake, fake, ws - 1, None) == -2
