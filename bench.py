@@ -155,6 +155,14 @@ def _setup(name, dev):
         del xd
         return (lambda: qrow.qr_matmul_q8k128(t, w, xa, n_in, out=y),
                 w.numel() + xa.numel() + y.numel() * 4, x.size)
+    if name == "stats_q4_k_11008x4096":
+        # error statistics of the Q4_K matrix against its source
+        x, q = synth.torch_q4_k_matrix(dev)
+        packed = qrow.qr_quantize_rows("q4_k", x, q)
+        ws = torch.empty(qrow.qr_stats_workspace_bytes(*x.shape), dtype=torch.uint8, device=dev)
+        # one read of the source and the packed rows (the kernels make three)
+        return (lambda: qrow.qr_quantize_stats("q4_k", x, packed, q, workspace=ws),
+                x.numel() * 4 + packed.numel() + q.numel() * 4, x.numel())
     if name == "copy_1gib":
         # plain device copy of a known size: calibrates the HBM byte counters
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -166,9 +174,10 @@ def _setup(name, dev):
 IMATRIX_WORKLOADS = ("imatrix_moe_256x8_4096x7168", "imatrix_moe_slots_256x8_4096x2048",
                      "imatrix_dense_4096x4096")
 MATMUL_WORKLOADS = ("mmq_q4_k_11008x4096_t1", "mmq_q4_0_4096x4096_t8")
+STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "copy_1gib") + IMATRIX_WORKLOADS + MATMUL_WORKLOADS
+                  "moe_256x2048x7168", "copy_1gib") + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -182,6 +191,22 @@ def run_only(args, dev, flush):
                       "GB/s": round(nbytes / ms / 1e6, 1),
                       "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}),
           flush=True)
+
+
+def weighting_ablation(x, q, flush):
+    """Each element-importance weighting on the Q4_K matrix: quantization
+    time and the error statistics of its output (relative RMSE, imatrix-
+    weighted relative RMSE, max and p95 of |e|)."""
+    from post_weight_quantization_row_amd import qrow
+    rows = {}
+    for mode in qrow.WEIGHTINGS:
+        out = qrow.qr_quantize_rows_weighted("q4_k", x, q, mode)
+        ms, _, _ = timed_steps(lambda: qrow.qr_quantize_rows_weighted("q4_k", x, q, mode, out=out), 5, 1, flush)
+        st = qrow.qr_quantize_stats("q4_k", x, out, q)
+        rows[mode] = {"ms": round(ms, 5), "rel_rmse": round(st["rel_rmse"], 6),
+                      "weighted_rel_rmse": round(st["weighted_rel_rmse"], 6),
+                      "max_abs_err": st["max_abs_err"], "p95_abs_err": st["p95_abs_err"]}
+    return rows
 
 
 def main():
@@ -312,12 +337,13 @@ def main():
                                                "hbm_frac": round(bd / (md * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # importance-matrix accumulation (the step that produces the imatrix)
         # and the product with Q8_K_128 activations (the step that consumes both)
-        for name in IMATRIX_WORKLOADS + MATMUL_WORKLOADS:
+        for name in IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS:
             fn, nb, n_el = _setup(name, dev)
             mi, _, _ = timed_steps(fn, 10, 2, flush)
             extra[name] = {"ms": round(mi, 5), "alg_bytes": nb,
                            "GB/s": round(nb / (mi * 1e-3) / 1e9, 1),
                            "hbm_frac": round(nb / (mi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        extra["weighting_ablation_q4_k_11008x4096"] = weighting_ablation(x, q, flush)
         result["extra"] = extra
 
     print(json.dumps(result), flush=True)
