@@ -55,6 +55,11 @@ static int field6(const uint8_t *p, int j)
 /* Level code u of element i (0..31) of a legacy 32-weight block at p. */
 static int legacy_code(int type, const uint8_t *p, int i)
 {
+    if (type == ORC_Q6_0) {
+        const uint8_t *qs = p + 12;
+        const int lo = i < 16 ? (qs[i] & 15) : (qs[i - 16] >> 4);
+        return lo | (((p[4 + i / 4] >> (2 * (i % 4))) & 3) << 4);
+    }
     const int sym = type == ORC_Q4_0 || type == ORC_Q5_0;
     const int five = type == ORC_Q5_0 || type == ORC_Q5_1;
     const uint8_t *qh = p + (sym ? 4 : 8);
@@ -82,12 +87,12 @@ static void weight_parts(int type, const uint8_t *row, int64_t n, double *a,
                 av = rd_f16(p) * field6(p + 4, j) * u;
                 bv = rd_f16(p + 2) * field6(p + 10, j);
             } else {
-                const int sym = type == ORC_Q4_0 || type == ORC_Q5_0;
+                const int sym = type == ORC_Q4_0 || type == ORC_Q5_0 || type == ORC_Q6_0;
                 const int five = type == ORC_Q5_0 || type == ORC_Q5_1;
                 const double d = rd_f32(p);
                 const double m = sym ? 0.0 : rd_f32(p + 4);
                 av = d * legacy_code(type, p, i);
-                bv = sym ? d * (five ? 16 : 8) : -m;
+                bv = sym ? d * (type == ORC_Q6_0 ? 32 : five ? 16 : 8) : -m;
             }
             a[blk * be + i] = av;
             b[blk * be + i] = bv;
@@ -110,7 +115,7 @@ int orc_matmul_q8k128(int type, const uint8_t *w, const uint8_t *x,
                       int64_t n_out, int64_t n_tok, int64_t n_in, double *y,
                       double *s_abs)
 {
-    if (type < ORC_Q4_0 || type > ORC_Q4_K || n_out < 0 || n_tok < 0 ||
+    if (type < ORC_Q4_0 || type > ORC_Q6_0 || type == ORC_Q8_K128 || n_out < 0 || n_tok < 0 ||
         n_in <= 0 || n_in % 128 || n_in % orc_block_elems(type))
         return ORC_EINVAL;
     const size_t wrb = orc_row_bytes(type, n_in);

@@ -29,7 +29,8 @@ enum {
     ORC_Q5_0 = 2,    /* 32 weights, levels -16..15, fp32 scale            24 B */
     ORC_Q5_1 = 3,    /* 32 weights, levels 0..31, fp32 scale + fp32 min   28 B */
     ORC_Q4_K = 4,    /* 256 weights, 8x32 sub-blocks, 6-bit sc/mn, fp16 d 144 B */
-    ORC_Q8_K128 = 5  /* 128 activations, fp32 d, int8, int16 sums/32     140 B */
+    ORC_Q8_K128 = 5, /* 128 activations, fp32 d, int8, int16 sums/32     140 B */
+    ORC_Q6_0 = 6     /* 32 weights, levels -32..31, fp32 scale, 2-bit plane 28 B */
 };
 
 /* Solver constants (the oracle's own copy). */

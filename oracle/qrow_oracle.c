@@ -58,7 +58,7 @@ void orc_solver_constants(int32_t *c)
 int orc_block_elems(int type)
 {
     switch (type) {
-    case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0: case ORC_Q5_1: return 32;
+    case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0: case ORC_Q5_1: case ORC_Q6_0: return 32;
     case ORC_Q4_K: return 256;
     case ORC_Q8_K128: return 128;
     default: return 0;
@@ -74,6 +74,7 @@ size_t orc_block_bytes(int type)
     case ORC_Q5_1: return 4 + 4 + 4 + 16;    /* d, m, 5th bits, nibbles  */
     case ORC_Q4_K: return 2 + 2 + 6 + 6 + 128; /* d16, dmin16, sc6, mn6, qs */
     case ORC_Q8_K128: return 4 + 128 + 8;    /* d, int8 x128, int16 x4   */
+    case ORC_Q6_0: return 4 + 8 + 16;        /* d, 2-bit plane, nibbles  */
     default: return 0;
     }
 }
@@ -483,10 +484,28 @@ static uint32_t pack_high_bits32(const uint8_t *u)
     return qh;
 }
 
+/* The two high bits of the 6-bit codes: bits 2i, 2i+1 of a 64-bit
+ * little-endian plane hold bits 4 and 5 of u_i. */
+static void pack_plane2(const uint8_t *u, uint8_t *qh)
+{
+    uint64_t v = 0;
+    for (int i = 0; i < 32; ++i) v |= (uint64_t)((u[i] >> 4) & 3) << (2 * i);
+    for (int k = 0; k < 8; ++k) qh[k] = (uint8_t)(v >> (8 * k));
+}
+
 static void quantize_block32(int type, const float *x, const float *w, uint8_t *out)
 {
     uint8_t u[32];
-    if (type == ORC_Q4_0 || type == ORC_Q5_0) {
+    if (type == ORC_Q6_0) {
+        /* [WT 一]: the same symmetric routine on 6-bit levels -32..31 */
+        int8_t l[32];
+        float d;
+        orc_solve_sym(32, x, w, 32, ORC_SYM_CAND, ORC_SYM_FLIP_PASSES, l, &d, NULL);
+        for (int i = 0; i < 32; ++i) u[i] = (uint8_t)(l[i] + 32);
+        put_f32(out, d);
+        pack_plane2(u, out + 4);
+        pack_nibbles32(u, out + 12);
+    } else if (type == ORC_Q4_0 || type == ORC_Q5_0) {
         int nmax = type == ORC_Q4_0 ? 8 : 16;
         int8_t l[32];
         float d;
@@ -606,7 +625,7 @@ static int quantize_row_impl(int type, const float *x, const float *q,
 static int weight_type_ok(int type)
 {
     return type == ORC_Q4_0 || type == ORC_Q4_1 || type == ORC_Q5_0 ||
-           type == ORC_Q5_1 || type == ORC_Q4_K;
+           type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0;
 }
 
 int orc_quantize_row_sigma2_mode(int type, const float *x, const float *q,
@@ -771,6 +790,17 @@ int orc_dequantize_rows(int type, const uint8_t *in, int64_t n_rows,
             case ORC_Q8_K128: {
                 float d = get_f32(p);
                 for (int i = 0; i < 128; ++i) o[i] = d * (float)(int8_t)p[4 + i];
+                break;
+            }
+            case ORC_Q6_0: {
+                float d = get_f32(p);
+                uint64_t plane = 0;
+                for (int k = 0; k < 8; ++k) plane |= (uint64_t)p[4 + k] << (8 * k);
+                unpack_nibbles32(p + 12, u);
+                for (int i = 0; i < 32; ++i) {
+                    u[i] |= (uint8_t)(((plane >> (2 * i)) & 3) << 4);
+                    o[i] = d * (float)((int)u[i] - 32);
+                }
                 break;
             }
             default:

@@ -15,7 +15,7 @@ import oracle
 from post_weight_quantization_row_amd import synth
 
 F32 = np.float32
-TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k"]
+TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0"]
 
 
 def q8_block(d: float, q) -> bytes:

@@ -65,7 +65,8 @@ MUTANTS = [
     ("imatrix: merge overwrites the sums", "sums[e * n_cols + c] += src_sums[e * n_cols + c];",
      "sums[e * n_cols + c] = src_sums[e * n_cols + c];"),
     # product with Q8_K_128 activations (and the Q8_1 comparison)
-    ("matmul: Q4_0 offset 7", "bv = sym ? d * (five ? 16 : 8) : -m;", "bv = sym ? d * (five ? 16 : 7) : -m;"),
+    ("matmul: Q4_0 offset 7", "bv = sym ? d * (type == ORC_Q6_0 ? 32 : five ? 16 : 8) : -m;",
+     "bv = sym ? d * (type == ORC_Q6_0 ? 32 : five ? 16 : 7) : -m;"),
     ("matmul: Q4_K scale from the offset field", "av = rd_f16(p) * field6(p + 4, j) * u;",
      "av = rd_f16(p) * field6(p + 10, j) * u;"),
     ("matmul: Q4_K high nibble", "const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);",
@@ -81,6 +82,12 @@ MUTANTS = [
      "if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, mode, w + 32 * g);",
      "if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, 0, w + 32 * g);"),
     ("weighting: imatrix dropped", "w[j] = q ? q[j] * m : m;", "w[j] = m;"),
+    # Q6_0
+    ("q6_0: plane bits shifted by one", "v |= (uint64_t)((u[i] >> 4) & 3) << (2 * i);",
+     "v |= (uint64_t)((u[i] >> 4) & 3) << (2 * i + 1);"),
+    ("q6_0: decode offset 31", "o[i] = d * (float)((int)u[i] - 32);", "o[i] = d * (float)((int)u[i] - 31);"),
+    ("matmul: Q6_0 offset 16", "bv = sym ? d * (type == ORC_Q6_0 ? 32 : five ? 16 : 8) : -m;",
+     "bv = sym ? d * (type == ORC_Q6_0 ? 16 : five ? 16 : 8) : -m;"),
     # error statistics
     ("stats: percentile rank rounded down", "const int64_t k = (95 * n + 99) / 100;",
      "const int64_t k = (95 * n) / 100;"),
@@ -134,12 +141,13 @@ def _pin_calls(mods):
     # extra parametrizations that exercise the other formats
     calls.append(("round trip q5_1", lambda: mod.test_exact_lattice_rows_round_trip("q5_1", 31, False)))
     calls.append(("round trip q5_0", lambda: mod.test_exact_lattice_rows_round_trip("q5_0", 16, True)))
+    calls.append(("round trip q6_0", lambda: mod.test_exact_lattice_rows_round_trip("q6_0", 32, True)))
     calls.append(("brute force sym 4/8", lambda: mod.test_sym_brute_force_tiny_blocks(4, 8, True)))
     wm = mods[3]
     for mode in ("abs_x", "sigma_plus_abs_x"):
         calls.append((f"fallback {mode}", lambda mode=mode: wm.test_zero_importance_groups_fall_back_per_mode(mode)))
     mm = mods[2]
-    for t in ("q4_0", "q5_1"):
+    for t in ("q4_0", "q5_1", "q6_0"):
         calls.append((f"matmul {t}", lambda t=t: mm.test_product_equals_library_matmul_of_decoded_values(t)))
     return calls
 

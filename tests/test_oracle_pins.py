@@ -619,7 +619,23 @@ def test_q5_layouts_put_the_fifth_bit_in_a_plane():
     assert list(out[8:24]) == [int((u[i] & 15) | ((u[i + 16] & 15) << 4)) for i in range(16)]
 
 
-@pytest.mark.parametrize("t,nmax,sym", [("q4_0", 8, True), ("q5_0", 16, True),
+def test_q6_0_layout_puts_two_high_bits_in_a_plane():
+    # [WT 一] names q6_0 among the types that share the weighting; its
+    # layout here: fp32 d | 2-bit plane (bits 2i, 2i+1 = bits 4, 5 of u_i) |
+    # low nibbles as in the 4-bit types; 28 bytes per 32 weights
+    k = np.arange(32) * 2 - 32                      # -32, -30, ..., 30
+    k[1] = 31
+    x = (k * 2.0 ** -3).astype(F32).reshape(1, 32)
+    out = oracle.quantize_rows("q6_0", x, None)[0]
+    assert out.size == 28
+    assert np.frombuffer(bytes(out[:4]), F32)[0] == F32(2.0 ** -3)
+    u = k + 32
+    assert int.from_bytes(bytes(out[4:12]), "little") == sum(((int(u[i]) >> 4) & 3) << (2 * i) for i in range(32))
+    assert list(out[12:28]) == [int((u[i] & 15) | ((u[i + 16] & 15) << 4)) for i in range(16)]
+    assert np.array_equal(oracle.dequantize_rows("q6_0", out, 1, 32), x)
+
+
+@pytest.mark.parametrize("t,nmax,sym", [("q4_0", 8, True), ("q5_0", 16, True), ("q6_0", 32, True),
                                         ("q4_1", 15, False), ("q5_1", 31, False)])
 def test_exact_lattice_rows_round_trip(t, nmax, sym):
     rng = np.random.default_rng(20)
@@ -642,7 +658,7 @@ def test_exact_lattice_rows_round_trip(t, nmax, sym):
         assert np.max(np.abs(x - y)) <= 1e-5 * np.max(np.abs(x))
 
 
-@pytest.mark.parametrize("t", ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k"])
+@pytest.mark.parametrize("t", ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0"])
 def test_power_of_two_constant_imatrix_equals_none(t):
     x, _ = synth.q4_k_matrix(n_rows=8, n_per_row=512)
     a = oracle.quantize_rows(t, x, np.full(512, 4.0, F32))

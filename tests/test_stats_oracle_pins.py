@@ -18,7 +18,7 @@ from post_weight_quantization_row_amd import synth
 F32 = np.float32
 
 
-@pytest.mark.parametrize("t", ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q8_k128"])
+@pytest.mark.parametrize("t", ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q8_k128", "q6_0"])
 def test_against_numpy_on_the_decoded_rows(t):
     x, q = synth.q4_k_matrix(24, 1024, seed=111)
     packed = oracle.quantize_q8k128(x) if t == "q8_k128" else oracle.quantize_rows(t, x, q)
