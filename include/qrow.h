@@ -40,6 +40,9 @@
  *  Q5_1  28 B: f32 d | f32 m | u32 qh | u8 qs[16]   levels 0..31
  *     qs[i] holds u_i (low nibble) and u_{i+16} (high nibble); bit i of qh
  *     is bit 4 of u_i.
+ *  Q6_0  28 B: f32 d | u8 qh[8] | u8 qs[16]  levels -32..31,     u = l+32
+ *     qs as above holds the low 4 bits; bits 2i and 2i+1 of the 64-bit
+ *     little-endian qh are bits 4 and 5 of u_i.
  *  Q4_K 144 B per 256: f16 d | f16 dmin | sc[8] as 6-bit fields in 6 B |
  *     mn[8] as 6-bit fields in 6 B | u8 qs[128]; field j sits at bit 6j;
  *     sub-block j (32 weights) uses qs[16j .. 16j+15] as above and decodes
@@ -63,7 +66,8 @@ typedef enum {
     QR_Q5_0 = 2,
     QR_Q5_1 = 3,
     QR_Q4_K = 4,
-    QR_Q8_K128 = 5
+    QR_Q8_K128 = 5,
+    QR_Q6_0 = 6
 } qr_type;
 
 typedef enum { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
@@ -96,7 +100,8 @@ typedef enum {
 /*
  * qr_quantize_rows -- importance-weighted quantization of weight rows [WT 一],
  * [KQ 一], [LQ 2.1].
- *  t        QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1 or QR_Q4_K (else EINVAL_TYPE).
+ *  t        QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q6_0 or QR_Q4_K (else
+ *           EINVAL_TYPE).
  *  src      QR_F32 or QR_BF16: element type of x.
  *  x        [n_rows, n_per_row] weights, row-major.
  *  imatrix  [n_per_row] fp32 importances shared by all rows, or NULL for

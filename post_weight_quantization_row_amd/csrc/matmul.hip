@@ -53,6 +53,11 @@ __host__ __device__ constexpr int64_t mmq_lds_bytes(int tt, int64_t n_in) {
   return (int64_t)tt * (n_in + n_in / 128 * 4 + n_in / 32 * 4);
 }
 
+// Four 2-bit fields of b (bits 2e, 2e+1) spread to bits 8e, 8e+1.
+__device__ __forceinline__ uint32_t spread2(uint32_t b) {
+  return (b & 3u) | ((b & 0x0cu) << 6) | ((b & 0x30u) << 12) | ((b & 0xc0u) << 18);
+}
+
 // 4 bits t (0..15) spread into bit 0 of each byte: bit k -> bit 8k.
 __device__ __forceinline__ uint32_t spread4(uint32_t t) { return (t * 0x00204081u) & 0x01010101u; }
 
@@ -89,7 +94,7 @@ __device__ __forceinline__ RawGroup load_raw(const uint8_t* __restrict__ row, in
       R.v[4 + k] = c[k];
     }
   } else {
-    constexpr int WORDS = TYPE == QR_Q4_0 ? 5 : TYPE == QR_Q5_1 ? 7 : 6;
+    constexpr int WORDS = TYPE == QR_Q4_0 ? 5 : (TYPE == QR_Q5_1 || TYPE == QR_Q6_0) ? 7 : 6;
     const uint8_t* p = row + (int64_t)g * (WORDS * 4);
 #pragma unroll
     for (int k = 0; k < WORDS; ++k) R.v[k] = ld32(p + 4 * k);
@@ -129,6 +134,10 @@ __device__ __forceinline__ Group unpack(const RawGroup& R, int g) {
     G.sa = d * (float)((sc6 >> (6 * j)) & 63);     // exact: 11-bit times 6-bit
     G.sb = dmin * (float)((mn6 >> (6 * j)) & 63);
     qs0 = 4;
+  } else if (TYPE == QR_Q6_0) {
+    G.sa = __builtin_bit_cast(float, R.v[0]);
+    G.sb = 32.0f;
+    qs0 = 3;
   } else {
     G.sa = __builtin_bit_cast(float, R.v[0]);
     if (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) G.sb = __builtin_bit_cast(float, R.v[1]);
@@ -145,6 +154,10 @@ __device__ __forceinline__ Group unpack(const RawGroup& R, int g) {
     if (TYPE == QR_Q5_0 || TYPE == QR_Q5_1) {
       G.lo[k] |= spread4((qh >> (4 * k)) & 15u) << 4;
       G.hi[k] |= spread4((qh >> (16 + 4 * k)) & 15u) << 4;
+    }
+    if (TYPE == QR_Q6_0) {  // bits 4, 5 from the 2-bit plane (byte k of each half)
+      G.lo[k] |= spread2((R.v[1] >> (8 * k)) & 255u) << 4;
+      G.hi[k] |= spread2((R.v[2] >> (8 * k)) & 255u) << 4;
     }
   }
   return G;
@@ -288,9 +301,9 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k128(const uint8_t* __
         for (int c = 0; c < 4; ++c) isum = __builtin_amdgcn_sdot4((int)G.lo[c], (int)a[c], isum, false);
 #pragma unroll
         for (int c = 0; c < 4; ++c) isum = __builtin_amdgcn_sdot4((int)G.hi[c], (int)a[4 + c], isum, false);
-        if (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
+        if (TYPE == QR_Q4_0 || TYPE == QR_Q5_0 || TYPE == QR_Q6_0) {
           // d * (sum(u*q) - offset * bsum), exact in int32
-          const int I = isum - (TYPE == QR_Q4_0 ? 8 : 16) * bs;
+          const int I = isum - (TYPE == QR_Q4_0 ? 8 : TYPE == QR_Q5_0 ? 16 : 32) * bs;
           acc[t] = __builtin_fmaf(G.sa * da, (float)I, acc[t]);
         } else if (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
           // d * sum(u*q) + m * bsum
@@ -347,7 +360,7 @@ extern "C" {
 int qr_matmul_q8k128(int t, const void* w, const void* x, int64_t n_out, int64_t n_tok, int64_t n_in, float* y,
                      void* stream) {
   qr_clear_error();
-  if (t < QR_Q4_0 || t > QR_Q4_K) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
+  if (!qr_is_weight_type(t)) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   const int64_t mult = t == QR_Q4_K ? 256 : 128;
   if (n_in <= 0 || n_in % mult != 0 || n_in > QR_MATMUL_MAX_IN)
     return qr_fail(QR_EINVAL_SHAPE, "n_in=%lld must be a positive multiple of %lld and at most %d", (long long)n_in,
@@ -372,6 +385,7 @@ int qr_matmul_q8k128(int t, const void* w, const void* x, int64_t n_out, int64_t
     case QR_Q4_1: return launch_type<QR_Q4_1>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
     case QR_Q5_0: return launch_type<QR_Q5_0>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
     case QR_Q5_1: return launch_type<QR_Q5_1>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+    case QR_Q6_0: return launch_type<QR_Q6_0>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
     default: return launch_type<QR_Q4_K>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
   }
 }

@@ -569,7 +569,23 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
     const float* qg = q ? q + g * QK : nullptr;
     float L[QK];
 
-    if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
+    if constexpr (TYPE == QR_Q6_0) {
+      const float d = solve_sym<32, BF16, VAR>(lds_raw, g, qg, imp, L);
+      uint32_t u[QK];
+#pragma unroll
+      for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + 32.0f);
+      uint32_t h0 = 0, h1 = 0;  // bits 4 and 5 of each code, two bits apiece
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        h0 |= ((u[i] >> 4) & 3u) << (2 * i);
+        h1 |= ((u[16 + i] >> 4) & 3u) << (2 * i);
+      }
+      const uint4 qs = pack_nibbles(u);
+      uint8_t* p = orow + (size_t)g * 28;
+      store_u32(p, fbits(d));
+      store_u32(p + 4, h0); store_u32(p + 8, h1);
+      store_u32(p + 12, qs.x); store_u32(p + 16, qs.y); store_u32(p + 20, qs.z); store_u32(p + 24, qs.w);
+    } else if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
       constexpr int NMAX = TYPE == QR_Q4_0 ? 8 : 16;
       const float d = solve_sym<NMAX, BF16, VAR>(lds_raw, g, qg, imp, L);
       if constexpr (TYPE == QR_Q4_0) {
@@ -808,6 +824,18 @@ __device__ __forceinline__ void decode4(const uint8_t* __restrict__ in, int64_t 
     const int sh = (k >> 2) * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = fma_(ds, (float)((bytes >> (8 * i + sh)) & 15u), -dm);
+  } else if constexpr (TYPE == QR_Q6_0) {
+    const uint8_t* p = in + U * 28;
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(p);
+    const uint32_t qh = *reinterpret_cast<const uint32_t*>(p + 4 + 4 * (k >> 2));  // plane of elements 16*(k/4)..
+    const uint32_t bytes = *reinterpret_cast<const uint32_t*>(p + 12 + 4 * (k & 3));
+    const float d = __builtin_bit_cast(float, w0);
+    const int sh = (k >> 2) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = ((bytes >> (8 * i + sh)) & 15u) | (((qh >> (2 * (4 * (k & 3) + i))) & 3u) << 4);
+      o[i] = d * (float)((int32_t)u - 32);
+    }
   } else {
     constexpr int BB = TYPE == QR_Q4_0 ? 20 : (TYPE == QR_Q5_1 ? 28 : 24);
     constexpr bool SYM = TYPE == QR_Q4_0 || TYPE == QR_Q5_0;
@@ -858,7 +886,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 
 int block_elems(int t) {
   switch (t) {
-    case QR_Q4_0: case QR_Q4_1: case QR_Q5_0: case QR_Q5_1: return 32;
+    case QR_Q4_0: case QR_Q4_1: case QR_Q5_0: case QR_Q5_1: case QR_Q6_0: return 32;
     case QR_Q4_K: return 256;
     case QR_Q8_K128: return 128;
     default: return 0;
@@ -873,6 +901,7 @@ size_t block_bytes(int t) {
     case QR_Q5_1: return 28;
     case QR_Q4_K: return 144;
     case QR_Q8_K128: return 140;
+    case QR_Q6_0: return 28;
     default: return 0;
   }
 }
@@ -911,6 +940,7 @@ int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, in
     case QR_Q5_0: return QR_ROWS_LAUNCH(QR_Q5_0);
     case QR_Q5_1: return QR_ROWS_LAUNCH(QR_Q5_1);
     case QR_Q4_K: return QR_ROWS_LAUNCH(QR_Q4_K);
+    case QR_Q6_0: return QR_ROWS_LAUNCH(QR_Q6_0);
     default: return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   }
 #undef QR_ROWS_LAUNCH
@@ -920,7 +950,7 @@ int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, in
 // runs in the kernels compiled for it alone; the others in the variants.
 int quantize_rows_common(int t, int src, const void* x, const float* imatrix, int64_t n_groups,
                          int64_t rows_per_group, int64_t n_per_row, int weighting, void* out, void* stream) {
-  if (t < QR_Q4_0 || t > QR_Q4_K) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
+  if (!qr_is_weight_type(t)) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
   if (weighting < QR_W_SQRT_SIGMA2_X2 || weighting > QR_W_IMATRIX_ONLY)
     return qr_fail(QR_EINVAL_TYPE, "weighting %d is not a qr_weighting", weighting);
@@ -1066,6 +1096,7 @@ int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row,
     case QR_Q5_0: hipLaunchKernelGGL(k_dequantize<QR_Q5_0>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
     case QR_Q5_1: hipLaunchKernelGGL(k_dequantize<QR_Q5_1>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
     case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
+    case QR_Q6_0: hipLaunchKernelGGL(k_dequantize<QR_Q6_0>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
     default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
   }
   return qr_check_launch("k_dequantize");

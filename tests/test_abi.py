@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_formats_agree_with_the_oracle(lib):
-    for t in range(6):
+    for t in range(7):
         assert lib.qr_block_elems(t) == oracle.block_elems(t)
         for n in (0, 32, 128, 256, 4096, 7168, 11008, 100):
             assert lib.qr_row_bytes(t, n) == oracle.row_bytes(t, n)
@@ -174,7 +174,7 @@ def test_stats_argument_validation_without_a_gpu(lib):
     ws = lib.qr_stats_workspace_bytes(4, 256)
     assert ws > 0 and lib.qr_stats_workspace_bytes(4, 0) == 0
     st = lib.qr_quantize_stats
-    assert st(6, 0, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
+    assert st(7, 0, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
     assert st(0, 2, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
     assert st(4, 0, fake, fake, None, 4, 128, fake, fake, ws, None) == -2    # Q4_K: 256
     assert st(0, 0, None, None, None, 0, 256, None, None, 0, None) == 0       # no rows

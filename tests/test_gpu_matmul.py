@@ -21,7 +21,7 @@ from post_weight_quantization_row_amd import synth
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k"]
+TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0"]
 
 
 @pytest.fixture(scope="module")

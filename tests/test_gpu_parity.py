@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
-WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k"]
+WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0"]
 
 
 @pytest.fixture(scope="module")

@@ -19,7 +19,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
-TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k"]
+TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0"]
 MODES = list(oracle.WEIGHTINGS)
 
 
