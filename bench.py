@@ -163,6 +163,14 @@ def _setup(name, dev):
         # one read of the source and the packed rows (the kernels make three)
         return (lambda: qrow.qr_quantize_stats("q4_k", x, packed, q, workspace=ws),
                 x.numel() * 4 + packed.numel() + q.numel() * 4, x.numel())
+    if name == "mix_q4_k_m_stack_7b":
+        plan, mats, outs = _mix_stack(dev)
+
+        def step():
+            for t, (x, q), o in zip(plan.tensors, mats, outs):
+                qrow.qr_quantize_rows(t.type, x, q, out=o)
+        nb = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (x, q), o in zip(mats, outs))
+        return step, nb, plan.weights
     if name == "copy_1gib":
         # plain device copy of a known size: calibrates the HBM byte counters
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -171,13 +179,49 @@ def _setup(name, dev):
     raise ValueError(name)
 
 
+def _mix_stack(dev):
+    """The 32-layer 7B-shaped stack (bf16, resident) with its Q4_K_M-style
+    plan: Q4_K everywhere, Q6_0 for attn_v and ffn_down in the layers that
+    fit a +10% size budget."""
+    import torch
+    from post_weight_quantization_row_amd import mix, qrow, synth
+    plan = mix.plan_stack()
+    mats = [synth.torch_stack_matrix(t.layer, t.which, dev)[1:] for t in plan.tensors]
+    outs = [torch.empty((t.n_rows, qrow.qr_row_bytes(t.type, t.n_per_row)), dtype=torch.uint8, device=dev)
+            for t in plan.tensors]
+    return plan, mats, outs
+
+
+def mix_stack_entry(dev, flush):
+    """Time to quantize the whole stack with the plan, and the stack's error
+    against the same stack at plain Q4_K."""
+    from post_weight_quantization_row_amd import mix, qrow
+    plan, mats, outs = _mix_stack(dev)
+
+    def step():
+        for t, (x, q), o in zip(plan.tensors, mats, outs):
+            qrow.qr_quantize_rows(t.type, x, q, out=o)
+    nb = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (x, q), o in zip(mats, outs))
+    ms, _, _ = timed_steps(step, 3, 1, flush)
+    by_name = {t.name: m for t, m in zip(plan.tensors, mats)}
+    ev = mix.evaluate(plan, lambda t: by_name[t.name])
+    return {"ms": round(ms, 4), "tensors": len(plan.tensors), "launches": len(plan.tensors),
+            "Gweights/s": round(plan.weights / ms / 1e6, 3), "alg_bytes": nb,
+            "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "promoted_layers": len(plan.promoted_layers),
+            "bytes": ev["bytes"], "base_bytes": ev["base_bytes"], "bpw": round(ev["bpw"], 4),
+            "rel_rmse": round(ev["rel_rmse"], 6), "base_rel_rmse": round(ev["base_rel_rmse"], 6),
+            "weighted_rel_rmse": round(ev["weighted_rel_rmse"], 6),
+            "base_weighted_rel_rmse": round(ev["base_weighted_rel_rmse"], 6)}
+
+
 IMATRIX_WORKLOADS = ("imatrix_moe_256x8_4096x7168", "imatrix_moe_slots_256x8_4096x2048",
                      "imatrix_dense_4096x4096")
 MATMUL_WORKLOADS = ("mmq_q4_k_11008x4096_t1", "mmq_q4_0_4096x4096_t8")
 STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "copy_1gib") + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
+                  "moe_256x2048x7168", "copy_1gib", "mix_q4_k_m_stack_7b") + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -344,6 +388,7 @@ def main():
                            "GB/s": round(nb / (mi * 1e-3) / 1e9, 1),
                            "hbm_frac": round(nb / (mi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         extra["weighting_ablation_q4_k_11008x4096"] = weighting_ablation(x, q, flush)
+        extra["mix_q4_k_m_stack_7b"] = mix_stack_entry(dev, flush)
         result["extra"] = extra
 
     print(json.dumps(result), flush=True)

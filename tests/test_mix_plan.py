@@ -1,0 +1,95 @@
+"""The per-tensor type plan ("3.2 K-quants 与重要性矩阵：量化兵器谱", section 一:
+Q4_K_M raises the attention and FFN down projections to 6 bits in proportion,
+for about a tenth more size than plain 4 bits). Host arithmetic only: the
+sizes are recounted here from the oracle's row sizes, not the library's."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from post_weight_quantization_row_amd import mix, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def recount(plan):
+    return sum(t.n_rows * oracle.row_bytes(t.type, t.n_per_row) for t in plan.tensors)
+
+
+def test_default_plan_is_q4_k_m_shaped():
+    p = mix.plan_stack()
+    assert len(p.tensors) == 32 * len(synth.STACK_LAYER)
+    assert p.bytes == recount(p)
+    base = sum(r * n for _, _, r, n in synth.STACK_LAYER) * 32 * 144 // 256
+    assert p.base_bytes() == base
+    growth = p.bytes / base - 1
+    assert 0.05 < growth <= 0.10          # about a tenth over plain 4 bits
+    assert 4.5 < 8 * p.bytes / p.weights < 5.0
+    for t in p.tensors:
+        role = t.name.split(".", 2)[2]
+        want = "q6_0" if (t.layer in p.promoted_layers and role in ("attn_v", "ffn_down")) else "q4_k"
+        assert t.type == want, t.name
+
+
+@pytest.mark.parametrize("budget", [0.0, 0.02, 0.05, 0.1, 0.15, 0.3])
+@pytest.mark.parametrize("layers", [1, 2, 7, 32])
+def test_budget_is_kept_and_filled(budget, layers):
+    p = mix.plan_stack(layers, budget=budget)
+    base = p.base_bytes()
+    assert p.bytes <= base * (1 + budget) + 1e-6
+    k = len(p.promoted_layers)
+    assert len(set(p.promoted_layers)) == k and all(0 <= i < layers for i in p.promoted_layers)
+    if k < layers:
+        # one more promoted layer would break the budget
+        one = mix.plan_stack(1, budget=10.0)
+        extra = one.bytes - one.base_bytes()
+        assert p.bytes + extra > base * (1 + budget)
+
+
+@pytest.mark.parametrize("k,n", [(1, 32), (2, 32), (18, 32), (31, 32), (5, 7), (3, 3)])
+def test_promoted_layers_are_spread(k, n):
+    s = mix._spread(k, n)
+    assert len(s) == k == len(set(s))
+    if k >= 2:
+        assert s[0] == 0 and s[-1] == n - 1
+        gaps = [b - a for a, b in zip(s, s[1:])]
+        assert max(gaps) - min(gaps) <= 1
+
+
+def test_zero_and_large_budgets():
+    assert mix.plan_stack(4, budget=0.0).promoted_layers == []
+    assert all(t.type == "q4_k" for t in mix.plan_stack(4, budget=0.0).tensors)
+    p = mix.plan_stack(4, budget=5.0)
+    assert p.promoted_layers == [0, 1, 2, 3]
+    assert sum(t.type == "q6_0" for t in p.tensors) == 8
+
+
+def test_other_roles_and_types():
+    p = mix.plan_stack(8, base="q4_0", high="q5_1", roles=("attn_q", "attn_k", "attn_v", "attn_o"),
+                       budget=0.1)
+    assert p.bytes == recount(p)
+    assert {t.type for t in p.tensors} == {"q4_0", "q5_1"}
+    assert all(t.type == "q4_0" for t in p.tensors if "ffn" in t.name)
+    with pytest.raises(ValueError):
+        mix.plan_stack(2, roles=("attn_x",))
+    with pytest.raises(ValueError):
+        mix.plan_stack(2, high="q8_k128")
+
+
+def test_summary_totals():
+    p = mix.plan_stack(2)
+    s = mix.summary(p, {"sum_err2": 1.0, "sum_x2": 4.0, "sum_werr2": 9.0, "sum_wx2": 16.0},
+                    {"sum_err2": 4.0, "sum_x2": 4.0, "sum_werr2": 0.0, "sum_wx2": 0.0})
+    assert s["rel_rmse"] == 0.5 and s["weighted_rel_rmse"] == 0.75
+    assert s["base_rel_rmse"] == 1.0 and s["base_weighted_rel_rmse"] == 0.0
+    assert s["bytes"] == recount(p)
+
+
+def test_dry_run_command_line():
+    out = subprocess.run([sys.executable, "-m", "post_weight_quantization_row_amd.mix", "--dry-run",
+                          "--layers", "4"], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert "promoted layers" in out.stdout and "total:" in out.stdout
+    assert "q6_0" in out.stdout
