@@ -26,11 +26,13 @@ SOURCES = [SRC, os.path.join(HERE, "imatrix_oracle.c"),
            os.path.join(HERE, "stats_oracle.c")]
 LIB = os.path.join(HERE, "liborc_qrow.so")
 
-Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128, Q6_0 = range(7)
+Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128, Q6_0, Q8_K64, Q8_K16 = range(9)
 WEIGHTINGS = {"sqrt_sigma2_x2": 0, "x2": 1, "abs_x": 2, "sigma2_plus_x2": 3,
               "sigma_plus_abs_x": 4, "imatrix_only": 5}
 TYPE_NAMES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1,
-              "q4_k": Q4_K, "q8_k128": Q8_K128, "q6_0": Q6_0}
+              "q4_k": Q4_K, "q8_k128": Q8_K128, "q6_0": Q6_0,
+              "q8_k64": Q8_K64, "q8_k16": Q8_K16}
+ACT_TYPES = ("q8_k128", "q8_k64", "q8_k16")
 
 _lib = None
 _lock = threading.Lock()
@@ -107,6 +109,7 @@ def _load(path):
     L.orc_quantize_row_sigma2.argtypes = [C.c_int, f32p, vp, i64,
                                           C.c_float, u8p]
     L.orc_quantize_q8k128.argtypes = [vp, i64, i64, vp]
+    L.orc_quantize_q8k.argtypes = [C.c_int, vp, i64, i64, vp]
     L.orc_row_weights_mode.argtypes = [f32p, vp, i64, C.c_float, C.c_int, f32p]
     L.orc_quantize_rows_weighted.argtypes = [C.c_int, vp, vp, i64, i64, C.c_int, vp]
     L.orc_quantize_row_sigma2_mode.argtypes = [C.c_int, f32p, vp, i64, C.c_float,
@@ -120,6 +123,7 @@ def _load(path):
     L.orc_imatrix_finalize.argtypes = [f64p, i64p, i64, i64, f32p]
     f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
     L.orc_matmul_q8k128.argtypes = [C.c_int, u8p, u8p, i64, i64, i64, f64p, vp]
+    L.orc_matmul_q8k.argtypes = [C.c_int, C.c_int, u8p, u8p, i64, i64, i64, f64p, vp]
     L.orc_matmul_q8_1.argtypes = [C.c_int, u8p, f32p, i64, i64, i64, f32p]
     L.orc_quantize_stats.argtypes = [C.c_int, f32p, u8p, vp, i64, i64, f64p, f32p, f32p]
     L.orc_f32_to_f16.argtypes = [C.c_float]
@@ -328,6 +332,25 @@ def quantize_row_sigma2(t, x, q, sigma2) -> np.ndarray:
     return out
 
 
+def quantize_q8k(t, x, threads: int = 1) -> np.ndarray:
+    """Activation rows x [n_rows, n] to the Q8_K format t (q8_k128, q8_k64
+    or q8_k16)."""
+    t = _tid(t)
+    x = _f32(x)
+    n_rows, n = x.shape
+    rb = row_bytes(t, n)
+    if rb == 0 or t not in (Q8_K128, Q8_K64, Q8_K16):
+        raise ValueError("not a Q8_K type, or n_per_row is not a multiple of its block")
+    out = np.zeros((n_rows, rb), np.uint8)
+
+    def run(r0, r1):
+        if r1 > r0:
+            lib().orc_quantize_q8k(t, _ptr(x[r0:r1]), r1 - r0, n, _ptr(out[r0:r1]))
+
+    _rows_parallel(n_rows, run, threads)
+    return out
+
+
 def quantize_q8k128(x, threads: int = 1) -> np.ndarray:
     x = _f32(x)
     n_rows, n = x.shape
@@ -409,19 +432,21 @@ def imatrix_finalize(state) -> np.ndarray:
 
 
 def matmul_q8k128(t, w_packed, x_packed, n_out: int, n_tok: int, n_in: int,
-                  with_magnitude: bool = False):
+                  with_magnitude: bool = False, act="q8_k128"):
     """y [n_tok, n_out] float64 = dequant(w) @ dequant(x).T over the exact
-    decoded values; with_magnitude also returns the bound magnitude S."""
+    decoded values; with_magnitude also returns the bound magnitude S. act
+    names the activations' Q8_K block size (q8_k128, q8_k64, q8_k16)."""
     t = _tid(t)
+    a = _tid(act)
     w = np.ascontiguousarray(w_packed, dtype=np.uint8).reshape(-1)
     x = np.ascontiguousarray(x_packed, dtype=np.uint8).reshape(-1)
-    if w.size != n_out * row_bytes(t, n_in) or x.size != n_tok * row_bytes(Q8_K128, n_in):
+    if w.size != n_out * row_bytes(t, n_in) or x.size != n_tok * row_bytes(a, n_in):
         raise ValueError("packed buffers have the wrong size")
     y = np.zeros((n_tok, n_out), np.float64)
     s = np.zeros((n_tok, n_out), np.float64) if with_magnitude else None
-    rc = lib().orc_matmul_q8k128(t, w, x, n_out, n_tok, n_in, y, _ptr(s))
+    rc = lib().orc_matmul_q8k(t, a, w, x, n_out, n_tok, n_in, y, _ptr(s))
     if rc != 0:
-        raise ValueError("orc_matmul_q8k128: invalid arguments")
+        raise ValueError("orc_matmul_q8k: invalid arguments")
     return (y, s) if with_magnitude else y
 
 

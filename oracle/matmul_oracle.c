@@ -15,8 +15,8 @@
  *
  * The product is defined plainly: y[t][r] = sum_i w[r][i] * a[t][i], with w
  * and a the exact values the packed blocks encode (Q4_0: d*(u-8); Q5_0:
- * d*(u-16); Q4_1, Q5_1: d*u + m; Q4_K: (d*sc_j)*u - dmin*mn_j; Q8_K_128:
- * d*q), taken in double in ascending i. Each part is exact in double; only
+ * d*(u-16); Q4_1, Q5_1: d*u + m; Q4_K: (d*sc_j)*u - dmin*mn_j; Q8_K_128 and
+ * its 64- and 16-value siblings: d*q), taken in double in ascending i. Each part is exact in double; only
  * the products and the sum round. The oracle also returns
  * S = sum_i (|scale part| + |offset part|) * |a_i|, the magnitude that bounds
  * the rounding error of any float evaluation of the same sum.
@@ -100,26 +100,43 @@ static void weight_parts(int type, const uint8_t *row, int64_t n, double *a,
     }
 }
 
-/* Exact activation values of a packed Q8_K_128 row. */
-static void act_values(const uint8_t *row, int64_t n, double *x)
+/* Exact activation values of a packed row of any Q8_K block size. */
+static void act_values(int act_type, const uint8_t *row, int64_t n, double *x)
 {
-    for (int64_t blk = 0; blk < n / 128; ++blk) {
-        const uint8_t *p = row + blk * 140;
+    const int B = orc_block_elems(act_type);
+    const size_t ab = orc_block_bytes(act_type);
+    for (int64_t blk = 0; blk < n / B; ++blk) {
+        const uint8_t *p = row + blk * ab;
         const double d = rd_f32(p);
-        for (int i = 0; i < 128; ++i)
-            x[blk * 128 + i] = d * (double)(int8_t)p[4 + i];
+        for (int i = 0; i < B; ++i)
+            x[blk * B + i] = d * (double)(int8_t)p[4 + i];
     }
+}
+
+static int is_weight_type(int type)
+{
+    return type == ORC_Q4_0 || type == ORC_Q4_1 || type == ORC_Q5_0 ||
+           type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0;
 }
 
 int orc_matmul_q8k128(int type, const uint8_t *w, const uint8_t *x,
                       int64_t n_out, int64_t n_tok, int64_t n_in, double *y,
                       double *s_abs)
 {
-    if (type < ORC_Q4_0 || type > ORC_Q6_0 || type == ORC_Q8_K128 || n_out < 0 || n_tok < 0 ||
-        n_in <= 0 || n_in % 128 || n_in % orc_block_elems(type))
+    return orc_matmul_q8k(type, ORC_Q8_K128, w, x, n_out, n_tok, n_in, y, s_abs);
+}
+
+int orc_matmul_q8k(int type, int act_type, const uint8_t *w, const uint8_t *x,
+                   int64_t n_out, int64_t n_tok, int64_t n_in, double *y,
+                   double *s_abs)
+{
+    if (!is_weight_type(type) ||
+        (act_type != ORC_Q8_K128 && act_type != ORC_Q8_K64 && act_type != ORC_Q8_K16) ||
+        n_out < 0 || n_tok < 0 || n_in <= 0 || n_in % orc_block_elems(act_type) ||
+        n_in % orc_block_elems(type))
         return ORC_EINVAL;
     const size_t wrb = orc_row_bytes(type, n_in);
-    const size_t xrb = orc_row_bytes(ORC_Q8_K128, n_in);
+    const size_t xrb = orc_row_bytes(act_type, n_in);
     double *a = malloc(sizeof(double) * n_in);
     double *b = malloc(sizeof(double) * n_in);
     double *xv = malloc(sizeof(double) * n_in * (n_tok > 0 ? n_tok : 1));
@@ -128,7 +145,7 @@ int orc_matmul_q8k128(int type, const uint8_t *w, const uint8_t *x,
         return ORC_EINVAL;
     }
     for (int64_t t = 0; t < n_tok; ++t)
-        act_values(x + t * xrb, n_in, xv + t * n_in);
+        act_values(act_type, x + t * xrb, n_in, xv + t * n_in);
     for (int64_t r = 0; r < n_out; ++r) {
         weight_parts(type, w + r * wrb, n_in, a, b);
         for (int64_t t = 0; t < n_tok; ++t) {

@@ -30,7 +30,9 @@ enum {
     ORC_Q5_1 = 3,    /* 32 weights, levels 0..31, fp32 scale + fp32 min   28 B */
     ORC_Q4_K = 4,    /* 256 weights, 8x32 sub-blocks, 6-bit sc/mn, fp16 d 144 B */
     ORC_Q8_K128 = 5, /* 128 activations, fp32 d, int8, int16 sums/32     140 B */
-    ORC_Q6_0 = 6     /* 32 weights, levels -32..31, fp32 scale, 2-bit plane 28 B */
+    ORC_Q6_0 = 6,    /* 32 weights, levels -32..31, fp32 scale, 2-bit plane 28 B */
+    ORC_Q8_K64 = 7,  /* 64 activations, fp32 d, int8, int16 sums/32       72 B */
+    ORC_Q8_K16 = 8   /* 16 activations, fp32 d, int8, int16 sum, 2 B pad   24 B */
 };
 
 /* Solver constants (the oracle's own copy). */
@@ -119,6 +121,10 @@ int orc_quantize_row_sigma2(int type, const float *x, const float *q,
 /* Q8_K_128 activation quantizer. */
 int orc_quantize_q8k128(const float *x, int64_t n_rows, int64_t n_per_row,
                         uint8_t *out);
+/* The Q8_K family by block size: type is ORC_Q8_K128, ORC_Q8_K64 or
+ * ORC_Q8_K16. */
+int orc_quantize_q8k(int type, const float *x, int64_t n_rows,
+                     int64_t n_per_row, uint8_t *out);
 
 /* Decoder for every format above. */
 int orc_dequantize_rows(int type, const uint8_t *in, int64_t n_rows,
@@ -145,6 +151,11 @@ int orc_imatrix_finalize(const double *sums, const int64_t *counts,
 int orc_matmul_q8k128(int type, const uint8_t *w, const uint8_t *x,
                       int64_t n_out, int64_t n_tok, int64_t n_in, double *y,
                       double *s_abs);
+/* The same product with activations of any Q8_K block size (act_type
+ * ORC_Q8_K128, ORC_Q8_K64 or ORC_Q8_K16). */
+int orc_matmul_q8k(int type, int act_type, const uint8_t *w, const uint8_t *x,
+                   int64_t n_out, int64_t n_tok, int64_t n_in, double *y,
+                   double *s_abs);
 /* The same product for Q4_1/Q5_1 weights with fp32 activations quantized to
  * Q8_1 (32 values, fp16 d and fp16 s = d * sum(q)), the offset part taken
  * from s, in float: the formulation whose s overflows. */

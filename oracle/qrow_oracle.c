@@ -61,6 +61,8 @@ int orc_block_elems(int type)
     case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0: case ORC_Q5_1: case ORC_Q6_0: return 32;
     case ORC_Q4_K: return 256;
     case ORC_Q8_K128: return 128;
+    case ORC_Q8_K64: return 64;
+    case ORC_Q8_K16: return 16;
     default: return 0;
     }
 }
@@ -75,6 +77,8 @@ size_t orc_block_bytes(int type)
     case ORC_Q4_K: return 2 + 2 + 6 + 6 + 128; /* d16, dmin16, sc6, mn6, qs */
     case ORC_Q8_K128: return 4 + 128 + 8;    /* d, int8 x128, int16 x4   */
     case ORC_Q6_0: return 4 + 8 + 16;        /* d, 2-bit plane, nibbles  */
+    case ORC_Q8_K64: return 4 + 64 + 4;      /* d, int8 x64, int16 x2    */
+    case ORC_Q8_K16: return 4 + 16 + 2 + 2;  /* d, int8 x16, int16, pad  */
     default: return 0;
     }
 }
@@ -694,38 +698,56 @@ int orc_quantize_rows(int type, const float *x, const float *imatrix,
 /* ------------------------------------------------------------------------ */
 /* Q8_K_128 [Q8 §修复方案]                                                    */
 
+/* One Q8_K block of B values (B = 128, 64 or 16): the scale, the codes,
+ * then one int16 code sum per 32 codes (one per block when B = 16), then
+ * zero bytes up to the block size. */
+static void quantize_q8k_block(const float *xb, int B, size_t bb, uint8_t *o)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < B; ++i) amax = fmaxf(amax, fabsf(xb[i]));
+    /* Readings: codes q = rint(x * 127/amax) in -127..127, scale
+     * d = amax/127 stored as float, an all-zero block (or one whose
+     * 127/amax is not finite) stores zeros. */
+    float id = amax > 0.0f ? 127.0f / amax : 0.0f;
+    int zero = !(amax > 0.0f) || !isfinite(id);
+    float d = zero ? 0.0f : amax / 127.0f;
+    int8_t q[128];
+    for (int i = 0; i < B; ++i)
+        q[i] = zero ? 0 : (int8_t)clampf(rintf(xb[i] * id), -127.0f, 127.0f);
+    put_f32(o, d);
+    memcpy(o + 4, q, (size_t)B);
+    const int gs = B < 32 ? B : 32;
+    for (int g = 0; g < B / gs; ++g) {
+        int s = 0;
+        for (int i = 0; i < gs; ++i) s += q[gs * g + i];
+        int16_t s16 = (int16_t)s;   /* |s| <= 32*127 = 4064 */
+        o[4 + B + 2 * g] = (uint8_t)(uint16_t)s16;
+        o[5 + B + 2 * g] = (uint8_t)((uint16_t)s16 >> 8);
+    }
+    for (size_t k = 4 + (size_t)B + 2 * (size_t)(B / gs); k < bb; ++k)
+        o[k] = 0;
+}
+
+int orc_quantize_q8k(int type, const float *x, int64_t n_rows,
+                     int64_t n_per_row, uint8_t *out)
+{
+    if (type != ORC_Q8_K128 && type != ORC_Q8_K64 && type != ORC_Q8_K16)
+        return ORC_EINVAL;
+    size_t rb = orc_row_bytes(type, n_per_row);
+    if (rb == 0 || n_rows < 0) return ORC_EINVAL;
+    const int B = orc_block_elems(type);
+    const size_t bb = orc_block_bytes(type);
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int64_t ib = 0; ib < n_per_row / B; ++ib)
+            quantize_q8k_block(x + r * n_per_row + ib * B, B, bb,
+                               out + (size_t)r * rb + (size_t)ib * bb);
+    return ORC_OK;
+}
+
 int orc_quantize_q8k128(const float *x, int64_t n_rows, int64_t n_per_row,
                         uint8_t *out)
 {
-    size_t rb = orc_row_bytes(ORC_Q8_K128, n_per_row);
-    if (rb == 0 || n_rows < 0) return ORC_EINVAL;
-    for (int64_t r = 0; r < n_rows; ++r) {
-        for (int64_t ib = 0; ib < n_per_row / 128; ++ib) {
-            const float *xb = x + r * n_per_row + ib * 128;
-            uint8_t *o = out + (size_t)r * rb + (size_t)ib * 140;
-            float amax = 0.0f;
-            for (int i = 0; i < 128; ++i) amax = fmaxf(amax, fabsf(xb[i]));
-            /* Readings: codes q = rint(x * 127/amax) in -127..127, scale
-             * d = amax/127 stored as float, an all-zero block (or one
-             * whose 127/amax is not finite) stores zeros. */
-            float id = amax > 0.0f ? 127.0f / amax : 0.0f;
-            int zero = !(amax > 0.0f) || !isfinite(id);
-            float d = zero ? 0.0f : amax / 127.0f;
-            int8_t q[128];
-            for (int i = 0; i < 128; ++i)
-                q[i] = zero ? 0 : (int8_t)clampf(rintf(xb[i] * id), -127.0f, 127.0f);
-            put_f32(o, d);
-            memcpy(o + 4, q, 128);
-            for (int g = 0; g < 4; ++g) {
-                int s = 0;
-                for (int i = 0; i < 32; ++i) s += q[32 * g + i];
-                int16_t s16 = (int16_t)s;   /* |s| <= 32*127 = 4064 */
-                o[132 + 2 * g] = (uint8_t)(uint16_t)s16;
-                o[133 + 2 * g] = (uint8_t)((uint16_t)s16 >> 8);
-            }
-        }
-    }
-    return ORC_OK;
+    return orc_quantize_q8k(ORC_Q8_K128, x, n_rows, n_per_row, out);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -787,9 +809,9 @@ int orc_dequantize_rows(int type, const uint8_t *in, int64_t n_rows,
                 }
                 break;
             }
-            case ORC_Q8_K128: {
+            case ORC_Q8_K128: case ORC_Q8_K64: case ORC_Q8_K16: {
                 float d = get_f32(p);
-                for (int i = 0; i < 128; ++i) o[i] = d * (float)(int8_t)p[4 + i];
+                for (int i = 0; i < be; ++i) o[i] = d * (float)(int8_t)p[4 + i];
                 break;
             }
             case ORC_Q6_0: {

@@ -48,8 +48,12 @@ MUTANTS = [
     ("f16: subnormals flushed", "if (e < -14) e = -14;", "if (e < -14) return sign;"),
     # Q8_K_128
     ("q8: 128 levels", "127.0f / amax", "128.0f / amax"),
-    ("q8: sums over the wrong codes", "for (int i = 0; i < 32; ++i) s += q[32 * g + i];",
-     "for (int i = 0; i < 32; ++i) s += q[i];"),
+    ("q8: sums over the wrong codes", "for (int i = 0; i < gs; ++i) s += q[gs * g + i];",
+     "for (int i = 0; i < gs; ++i) s += q[i];"),
+    ("q8k16: sums over 32 codes", "const int gs = B < 32 ? B : 32;", "const int gs = 32;"),
+    ("q8k: padding not zero", "        o[k] = 0;", "        o[k] = 0x55;"),
+    ("q8k: amax over the first 16 values", "for (int i = 0; i < B; ++i) amax = fmaxf(amax, fabsf(xb[i]));",
+     "for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xb[i]));"),
     # packing and decoding
     ("pack: high nibble from element i+8", "((u[i + 16] & 15) << 4)", "((u[i + 8] & 15) << 4)"),
     ("decode: symmetric offset dropped", "o[i] = d * (float)((int)u[i] - nmax);", "o[i] = d * (float)((int)u[i]);"),
@@ -71,7 +75,7 @@ MUTANTS = [
      "av = rd_f16(p) * field6(p + 10, j) * u;"),
     ("matmul: Q4_K high nibble", "const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);",
      "const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] & 15);"),
-    ("matmul: activation block stride", "const uint8_t *p = row + blk * 140;", "const uint8_t *p = row + blk * 136;"),
+    ("matmul: activation block stride", "const uint8_t *p = row + blk * ab;", "const uint8_t *p = row + blk * (ab - 4);"),
     ("matmul: offset sign", "acc += (a[i] - b[i]) * xt[i];", "acc += (a[i] + b[i]) * xt[i];"),
     ("q8_1: s without d", "orc_f32_to_f16(d * (float)sum)", "orc_f32_to_f16((float)sum)"),
     # weightings
@@ -99,7 +103,7 @@ MUTANTS = [
 
 
 PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py", "test_matmul_oracle_pins.py",
-             "test_weighting_oracle_pins.py", "test_stats_oracle_pins.py")
+             "test_weighting_oracle_pins.py", "test_stats_oracle_pins.py", "test_q8k_family_oracle_pins.py")
 
 
 def _pins_modules():
@@ -129,6 +133,9 @@ def _pin_calls(mods):
         "test_power_of_two_scaling_scales_the_scales": dict(mode="abs_x"),
         "test_against_numpy_on_the_decoded_rows": dict(t="q4_k"),
         "test_nearest_rank": dict(n=64, k=61),
+        "test_block_bytes_by_hand": dict(t="q8_k16"),
+        "test_error_within_half_a_step_of_the_block_maximum": dict(t="q8_k16"),
+        "test_family_product_equals_library_matmul": dict(t="q4_1", act="q8_k16"),
     }
     calls = []
     for mod in mods:
@@ -149,7 +156,18 @@ def _pin_calls(mods):
     mm = mods[2]
     for t in ("q4_0", "q5_1", "q6_0"):
         calls.append((f"matmul {t}", lambda t=t: mm.test_product_equals_library_matmul_of_decoded_values(t)))
+    qm = mods[5]
+    for t in ("q8_k64", "q8_k128"):
+        calls.append((f"q8k bytes {t}", lambda t=t: qm.test_block_bytes_by_hand(t)))
+    calls.append(("q8k64 product", lambda: qm.test_family_product_equals_library_matmul("q4_0", "q8_k64")))
     return calls
+
+
+def test_every_pin_call_passes_on_the_oracle():
+    # a pin that fails (or cannot be called) without a mutant would count
+    # as catching every mutant
+    for name, call in _pin_calls(_pins_modules()):
+        call()
 
 
 def test_every_mutant_is_distinct_and_applies():
