@@ -110,6 +110,13 @@ def _setup(name, dev):
         out = torch.empty((8192, qrow.qr_row_bytes("q8_k128", 7168)), dtype=torch.uint8, device=dev)
         return (lambda: qrow.qr_quantize_activations_q8k128(xd, out=out),
                 x.nbytes + out.numel(), x.size)
+    if name in ("q8_k64_8192x7168", "q8_k16_8192x7168"):
+        act = name.split("_8192")[0]
+        x, _ = synth.q8_k128_activations()
+        xd = torch.from_numpy(x).to(dev)
+        out = torch.empty((8192, qrow.qr_row_bytes(act, 7168)), dtype=torch.uint8, device=dev)
+        return (lambda: qrow.qr_quantize_activations_q8k(act, xd, out=out),
+                x.nbytes + out.numel(), x.size)
     if name == "dequantize_q4_k_11008x4096":
         x, q = synth.torch_q4_k_matrix(dev)
         packed = qrow.qr_quantize_rows("q4_k", x, q)
@@ -146,14 +153,19 @@ def _setup(name, dev):
                 nb, ad.numel())
     if name.startswith("mmq_"):
         # weights and activations quantized by the library, then the product
+        # (activations Q8_K_128 unless the name ends in another Q8_K format)
+        act = "q8_k128"
+        for a_t in ("q8_k64", "q8_k16"):
+            if name.endswith("_" + a_t):
+                act, name = a_t, name[:-len(a_t) - 1]
         t, x, q, a = synth.matmul_sources(name)
         xd, qd, ad = (torch.from_numpy(v).to(dev) for v in (x, q, a))
         w = qrow.qr_quantize_rows(t, xd, qd)
-        xa = qrow.qr_quantize_activations_q8k128(ad)
+        xa = qrow.qr_quantize_activations_q8k(act, ad)
         n_in = x.shape[1]
         y = torch.empty((a.shape[0], x.shape[0]), dtype=torch.float32, device=dev)
         del xd
-        return (lambda: qrow.qr_matmul_q8k128(t, w, xa, n_in, out=y),
+        return (lambda: qrow.qr_matmul_q8k(t, act, w, xa, n_in, out=y),
                 w.numel() + xa.numel() + y.numel() * 4, x.size)
     if name == "stats_q4_k_11008x4096":
         # error statistics of the Q4_K matrix against its source
@@ -217,11 +229,13 @@ def mix_stack_entry(dev, flush):
 
 IMATRIX_WORKLOADS = ("imatrix_moe_256x8_4096x7168", "imatrix_moe_slots_256x8_4096x2048",
                      "imatrix_dense_4096x4096")
-MATMUL_WORKLOADS = ("mmq_q4_k_11008x4096_t1", "mmq_q4_0_4096x4096_t8")
+MATMUL_WORKLOADS = ("mmq_q4_k_11008x4096_t1", "mmq_q4_0_4096x4096_t8",
+                    "mmq_q4_k_11008x4096_t1_q8_k16", "mmq_q4_0_4096x4096_t8_q8_k16")
+ACT_WORKLOADS = ("q8_k64_8192x7168", "q8_k16_8192x7168")
 STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "copy_1gib", "mix_q4_k_m_stack_7b") + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
+                  "moe_256x2048x7168", "copy_1gib", "mix_q4_k_m_stack_7b") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -235,6 +249,34 @@ def run_only(args, dev, flush):
                       "GB/s": round(nbytes / ms / 1e6, 1),
                       "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}),
           flush=True)
+
+
+def activation_block_ablation(dev, flush):
+    """Each Q8_K block size on calibration-like activations (8192 x 7168,
+    per-channel LogNormal scales, 0.1% outlier channels at 20x): the
+    quantization time of the 8192x7168 matrix, bytes per value, relative
+    RMSE of the activations, and the relative error of the product of 8 such
+    tokens with the Q4_0 4096x4096 weights against the product of the
+    decoded weights with the unquantized activations (float64)."""
+    import torch
+    from post_weight_quantization_row_amd import qrow, synth
+    x = synth.calib_activations(8192, 7168, seed=1012, bf16=False)
+    xd = torch.from_numpy(x).to(dev)
+    t, wx, wq, a = synth.matmul_sources("mmq_q4_0_4096x4096_t8")
+    w = qrow.qr_quantize_rows(t, torch.from_numpy(wx).to(dev), torch.from_numpy(wq).to(dev))
+    W = qrow.qr_dequantize_rows(t, w, wx.shape[0], wx.shape[1]).double()
+    ad = torch.from_numpy(a).to(dev)
+    exact = ad.double() @ W.T
+    rows = {}
+    for act in qrow.ACT_TYPES:
+        out = qrow.qr_quantize_activations_q8k(act, xd)
+        ms, _, _ = timed_steps(lambda: qrow.qr_quantize_activations_q8k(act, xd, out=out), 5, 1, flush)
+        st = qrow.qr_quantize_stats(act, xd, out)
+        y = qrow.qr_matmul_q8k(t, act, w, qrow.qr_quantize_activations_q8k(act, ad), wx.shape[1]).double()
+        rows[act] = {"ms": round(ms, 5), "bytes_per_value": round(out.numel() / x.size, 4),
+                     "rel_rmse": round(st["rel_rmse"], 6),
+                     "product_rel_err": round(float(torch.linalg.norm(y - exact) / torch.linalg.norm(exact)), 6)}
+    return rows
 
 
 def weighting_ablation(x, q, flush):
@@ -381,7 +423,7 @@ def main():
                                                "hbm_frac": round(bd / (md * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # importance-matrix accumulation (the step that produces the imatrix)
         # and the product with Q8_K_128 activations (the step that consumes both)
-        for name in IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS:
+        for name in ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS:
             fn, nb, n_el = _setup(name, dev)
             mi, _, _ = timed_steps(fn, 10, 2, flush)
             extra[name] = {"ms": round(mi, 5), "alg_bytes": nb,
@@ -389,6 +431,7 @@ def main():
                            "hbm_frac": round(nb / (mi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         extra["weighting_ablation_q4_k_11008x4096"] = weighting_ablation(x, q, flush)
         extra["mix_q4_k_m_stack_7b"] = mix_stack_entry(dev, flush)
+        extra["activation_block_ablation_calib_8192x7168"] = activation_block_ablation(dev, flush)
         result["extra"] = extra
 
     print(json.dumps(result), flush=True)

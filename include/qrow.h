@@ -49,6 +49,8 @@
  *     to (d*sc_j)*u - dmin*mn_j.
  *  Q8_K128 140 B per 128: f32 d | i8 q[128] | i16 bsum[4]; bsum[g] is the
  *     plain sum of q[32g .. 32g+31], not multiplied by d.
+ *  Q8_K64   72 B per 64:  f32 d | i8 q[64] | i16 bsum[2] (sums of 32 codes).
+ *  Q8_K16   24 B per 16:  f32 d | i8 q[16] | i16 bsum | 2 zero bytes.
  */
 #ifndef QROW_H
 #define QROW_H
@@ -67,7 +69,9 @@ typedef enum {
     QR_Q5_1 = 3,
     QR_Q4_K = 4,
     QR_Q8_K128 = 5,
-    QR_Q6_0 = 6
+    QR_Q6_0 = 6,
+    QR_Q8_K64 = 7,
+    QR_Q8_K16 = 8
 } qr_type;
 
 typedef enum { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
@@ -156,11 +160,28 @@ int qr_quantize_activations_q8k128(int src, const void *x, int64_t n_rows,
                                    int64_t n_per_row, void *out, void *stream);
 
 /*
+ * qr_quantize_activations_q8k -- the Q8_K activation family by block size
+ * [Q8 修复方案 for the 128-value block; 技术启示与后续演进 names Q8_K64 and
+ * Q8_K16 as later members built on the same idea: an f32 scale and integer
+ * code sums that are not multiplied by it]. t is QR_Q8_K128, QR_Q8_K64 or
+ * QR_Q8_K16; each block of B = 128, 64 or 16 values is quantized exactly as
+ * above (amax, rint(x * 127/amax), d = amax/127) and stored as
+ *   Q8_K64: [f32 d][i8 q[64]][i16 bsum[2]]              72 bytes
+ *   Q8_K16: [f32 d][i8 q[16]][i16 bsum][2 zero bytes]   24 bytes
+ * with bsum the sum of each 32 codes (of the block's 16 codes for Q8_K16),
+ * little-endian. n_per_row must be a positive multiple of B; out holds
+ * n_rows * qr_row_bytes(t, n_per_row) bytes. Errors as above, and
+ * QR_EINVAL_TYPE for any other t.
+ */
+int qr_quantize_activations_q8k(int t, int src, const void *x, int64_t n_rows,
+                                int64_t n_per_row, void *out, void *stream);
+
+/*
  * qr_dequantize_rows -- decoder for every type above. in is the packed
  * [n_rows, qr_row_bytes(t, n_per_row)] buffer; out is fp32
  * [n_rows, n_per_row]. Symmetric blocks decode to d*(u - nmax), asymmetric
- * ones to fmaf(d, u, m), Q4_K to fmaf(f32(d)*sc, u, -(f32(dmin)*mn)), Q8_K128
- * to d*q.
+ * ones to fmaf(d, u, m), Q4_K to fmaf(f32(d)*sc, u, -(f32(dmin)*mn)), the
+ * Q8_K family to d*q.
  */
 int qr_dequantize_rows(int t, const void *in, int64_t n_rows,
                        int64_t n_per_row, float *out, void *stream);
@@ -169,7 +190,7 @@ int qr_dequantize_rows(int t, const void *in, int64_t n_rows,
  * non-negative multiple of the block length. */
 size_t qr_row_bytes(int t, int64_t n_per_row);
 
-/* Elements per block: 32, 256 or 128; 0 for an unknown type. */
+/* Elements per block: 32, 256, 128, 64 or 16; 0 for an unknown type. */
 int qr_block_elems(int t);
 
 /* Fills c[0..5] = {4 * trial-scale step, symmetric trials, symmetric flip

@@ -1,6 +1,7 @@
 /*
  * qrow_matmul.h -- C-ABI of libqrow.so, part 3: the product of quantized
- * weight rows with Q8_K_128 activations, the consumer of both formats.
+ * weight rows with Q8_K activations (128, 64 or 16 values per block), the
+ * consumer of both formats.
  *
  * The operation follows this page (cited by title and section):
  *  [Q8] "ik_llama.cpp 量化精度修复实录：用 Q8_K_128 替代 Q8_1 …". Section
@@ -49,6 +50,22 @@ extern "C" {
  */
 int qr_matmul_q8k128(int t, const void *w, const void *x, int64_t n_out,
                      int64_t n_tok, int64_t n_in, float *y, void *stream);
+
+/*
+ * qr_matmul_q8k -- the same product with activations of any Q8_K block size
+ * [Q8 技术启示与后续演进: Q8_K64 and Q8_K16 keep Q8_K_128's f32 scale and
+ * unscaled int16 code sums]. act is QR_Q8_K128, QR_Q8_K64 or QR_Q8_K16 and x
+ * holds [n_tok, qr_row_bytes(act, n_in)] (the output of
+ * qr_quantize_activations_q8k). With Q8_K16 each 32-weight group meets two
+ * activation blocks: the integer dot product and the offset fold are taken
+ * per 16 values and the two scaled terms added in that order, which doubles
+ * the fp32 additions per lane: the bound becomes (n_in/512 + 9) * 2^-24 of
+ * the same magnitude. Limits: n_in a positive multiple of the larger of the
+ * two block lengths (32 or 256 for the weights), at most QR_MATMUL_MAX_IN;
+ * QR_EINVAL_TYPE for an act outside the family.
+ */
+int qr_matmul_q8k(int t, int act, const void *w, const void *x, int64_t n_out,
+                  int64_t n_tok, int64_t n_in, float *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -51,8 +51,9 @@ size_t qr_stats_workspace_bytes(int64_t n_rows, int64_t n_per_row);
  * p95 are exact (the percentile by a radix selection over the bits of |e|,
  * in three counting passes); the sums are double, added in a fixed order
  * (reproducible bit for bit), each within n * 2^-52 of its exact value,
- * relative. Limits: n_rows * n_per_row < 2^32. Calls that share `out` or
- * the workspace must be ordered on one stream.
+ * relative. Limits: n_rows * n_per_row < 2^32; n_per_row a multiple of 32
+ * (for Q8_K16: an even number of blocks). Calls that share `out` or the
+ * workspace must be ordered on one stream.
  */
 int qr_quantize_stats(int t, int src, const void *x, const void *packed,
                       const float *imatrix, int64_t n_rows, int64_t n_per_row,

@@ -1,11 +1,13 @@
 // matmul.hip -- gfx950 kernel and C-ABI of the product of quantized weight
-// rows with Q8_K_128 activation rows (declared in qrow_matmul.h).
+// rows with Q8_K activation rows of 128, 64 or 16 values per block
+// (declared in qrow_matmul.h).
 //
 // Following this page (cited by title and section):
 //  [Q8] "ik_llama.cpp 量化精度修复实录：用 Q8_K_128 替代 Q8_1 …", sections
 //       修复前的数值隐患 and 修复方案: integer products of weight and activation
 //       codes, the weight offset removed with the activation code sums, which
-//       Q8_K_128 keeps as unscaled int16 per 32 codes.
+//       Q8_K_128 keeps as unscaled int16 per 32 codes; section 技术启示与后续演进
+//       for the 64- and 16-value members of the family.
 //
 // Execution model (gfx950, wave64). A workgroup of four waves owns a few
 // weight rows and a tile of TT tokens. With TT > 1 the tile's activation
@@ -21,7 +23,9 @@
 // the scaled term in fp32. A butterfly over the row's lanes gives its
 // outputs. One token is bound by reading the weights from HBM; tiles of
 // tokens by instruction issue (eight v_dot4 plus about thirty addressing,
-// LDS and scaling instructions per 32 weights and token).
+// LDS and scaling instructions per 32 weights and token). With 16-value
+// activation blocks a weight group spans two activation scales: the two
+// halves of the dot product are scaled and added separately.
 
 #include <hip/hip_runtime.h>
 
@@ -46,11 +50,16 @@ __host__ __device__ constexpr int mmq_lanes(int tt) { return tt == 1 ? 64 : 32; 
 __host__ __device__ constexpr int mmq_batch(int tt) { return tt == 1 ? 1 : 2; }
 __host__ __device__ constexpr int mmq_rows(int tt) { return MMQ_THREADS / mmq_lanes(tt); }
 constexpr int MMQ_LDS_BUDGET = 64 * 1024;         // bytes of staged activations
-constexpr int Q8_BLOCK_WORDS = 35;                // 140-byte Q8_K_128 block
+
+// Activation formats: values per block, words per packed block, values per
+// code sum (Q8_K128: 140 B, Q8_K64: 72 B, Q8_K16: 24 B with a zero pad).
+__host__ __device__ constexpr int act_block(int act) { return act == QR_Q8_K128 ? 128 : act == QR_Q8_K64 ? 64 : 16; }
+__host__ __device__ constexpr int act_words(int act) { return act == QR_Q8_K128 ? 35 : act == QR_Q8_K64 ? 18 : 6; }
+__host__ __device__ constexpr int act_sum_unit(int act) { return act == QR_Q8_K16 ? 16 : 32; }
 
 // LDS bytes for a tile of tt tokens of n_in values: codes, scales, sums.
-__host__ __device__ constexpr int64_t mmq_lds_bytes(int tt, int64_t n_in) {
-  return (int64_t)tt * (n_in + n_in / 128 * 4 + n_in / 32 * 4);
+__host__ __device__ constexpr int64_t mmq_lds_bytes(int tt, int64_t n_in, int act) {
+  return (int64_t)tt * (n_in + n_in / act_block(act) * 4 + n_in / act_sum_unit(act) * 4);
 }
 
 // Four 2-bit fields of b (bits 2e, 2e+1) spread to bits 8e, 8e+1.
@@ -102,21 +111,42 @@ __device__ __forceinline__ RawGroup load_raw(const uint8_t* __restrict__ row, in
   return R;
 }
 
-// One token's activation words for one 32-value group of a packed Q8_K_128
-// row: the 8 code words, the word holding its int16 code sum, the scale.
+// One token's activation words for one 32-value group of a packed
+// activation row: the 8 code words, the word(s) holding its int16 code
+// sum(s), the scale(s) (the second sum and scale only for 16-value blocks,
+// whose two blocks cover the group's halves).
 struct RawAct {
   uint32_t q[8];
-  uint32_t sums;
-  uint32_t d;
+  uint32_t sums, sums1;
+  uint32_t d, d1;
 };
 
+template <int ACT>
 __device__ __forceinline__ RawAct load_act(const uint8_t* __restrict__ xrow, int g) {
   RawAct A;
-  const uint8_t* blk = xrow + (int64_t)(g >> 2) * (Q8_BLOCK_WORDS * 4);
+  if constexpr (ACT == QR_Q8_K16) {
+    const uint8_t* b0 = xrow + (int64_t)g * 48;
+    const uint8_t* b1 = b0 + 24;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) A.q[c] = ld32(blk + 4 + 32 * (g & 3) + 4 * c);
-  A.sums = ld32(blk + 132 + 4 * ((g & 3) >> 1));
-  A.d = ld32(blk);
+    for (int c = 0; c < 4; ++c) {
+      A.q[c] = ld32(b0 + 4 + 4 * c);
+      A.q[4 + c] = ld32(b1 + 4 + 4 * c);
+    }
+    A.sums = ld32(b0 + 20);
+    A.sums1 = ld32(b1 + 20);
+    A.d = ld32(b0);
+    A.d1 = ld32(b1);
+  } else {
+    constexpr int PER = act_block(ACT) / 32;           // groups per block
+    const uint8_t* blk = xrow + (int64_t)(g / PER) * (act_words(ACT) * 4);
+    const int gi = g & (PER - 1);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) A.q[c] = ld32(blk + 4 + 32 * gi + 4 * c);
+    A.sums = ld32(blk + 4 + act_block(ACT) + 4 * (gi >> 1));
+    A.d = ld32(blk);
+    A.sums1 = 0;
+    A.d1 = 0;
+  }
   return A;
 }
 
@@ -163,18 +193,40 @@ __device__ __forceinline__ Group unpack(const RawGroup& R, int g) {
   return G;
 }
 
-template <int TYPE, int TT>
-__global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k128(const uint8_t* __restrict__ w,
-                                                               const uint8_t* __restrict__ x, int64_t n_out,
-                                                               int64_t n_tok, int n_in, int64_t w_row_bytes,
-                                                               float* __restrict__ y) {
+// The scaled term of one activation block's share of a group: I = sum(u*q)
+// over that share, bs its code sum, da its scale.
+template <int TYPE>
+__device__ __forceinline__ float add_term(const Group& G, int I, int bs, float da, float acc) {
+  if (TYPE == QR_Q4_0 || TYPE == QR_Q5_0 || TYPE == QR_Q6_0) {
+    // d * (sum(u*q) - offset * bsum), exact in int32
+    const int J = I - (TYPE == QR_Q4_0 ? 8 : TYPE == QR_Q5_0 ? 16 : 32) * bs;
+    return __builtin_fmaf(G.sa * da, (float)J, acc);
+  } else if (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
+    // d * sum(u*q) + m * bsum
+    return __builtin_fmaf(da, __builtin_fmaf(G.sa, (float)I, G.sb * (float)bs), acc);
+  } else {
+    // d*sc * sum(u*q) - dmin*mn * bsum
+    return __builtin_fmaf(da, __builtin_fmaf(G.sa, (float)I, -(G.sb * (float)bs)), acc);
+  }
+}
+
+template <int TYPE, int ACT, int TT>
+__global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k(const uint8_t* __restrict__ w,
+                                                            const uint8_t* __restrict__ x, int64_t n_out,
+                                                            int64_t n_tok, int n_in, int64_t w_row_bytes,
+                                                            float* __restrict__ y) {
+  constexpr int AB = act_block(ACT);          // values per activation block
+  constexpr int AW = act_words(ACT);          // words per packed activation block
+  constexpr int CW = AB / 4;                  // code words per activation block
+  constexpr bool SPLIT = ACT == QR_Q8_K16;    // two activation blocks per group
   extern __shared__ uint32_t lds[];
-  const int nb = n_in / 128;  // activation blocks per row
+  const int nb = n_in / AB;   // activation blocks per row
   const int ng = n_in / 32;   // 32-value groups per row
   // Block-major over the tile (block tb = t * nb + b): code words
-  // [TT * nb][32], scales [TT * nb], code sums [TT * nb][4].
+  // [TT * nb][CW] (that is, [TT * ng][8]), scales [TT * nb], code sums
+  // [TT * n_in / sum unit].
   uint32_t* lq = lds;
-  float* ld = reinterpret_cast<float*>(lds + TT * nb * 32);
+  float* ld = reinterpret_cast<float*>(lds + TT * nb * CW);
   int32_t* lsum = reinterpret_cast<int32_t*>(ld + TT * nb);
 
   // L lanes own one row; lane s takes the row's groups s, s + L, ..., NF at
@@ -187,7 +239,7 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k128(const uint8_t* __
   const bool row_ok = r < n_out;
   const uint8_t* row = w + (row_ok ? r : 0) * w_row_bytes;
   const int64_t t0 = (int64_t)blockIdx.y * TT;
-  const uint8_t* xt = x + t0 * (int64_t)nb * Q8_BLOCK_WORDS * 4;
+  const uint8_t* xt = x + t0 * (int64_t)nb * AW * 4;
   RawGroup cur[NF], nxt[NF];
   RawAct acur[TT == 1 ? NF : 1], anxt[TT == 1 ? NF : 1];
   auto load_batch = [&](RawGroup (&b)[NF], RawAct (&ab)[TT == 1 ? NF : 1], int g0) {
@@ -199,30 +251,32 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k128(const uint8_t* __
       const int g = g0 + u * L;
       const int gc = g < ng ? g : ng - 1;
       b[u] = load_raw<TYPE>(row, gc);
-      if (TT == 1) ab[TT == 1 ? u : 0] = load_act(xt, gc);
+      if (TT == 1) ab[TT == 1 ? u : 0] = load_act<ACT>(xt, gc);
     }
   };
   if (TT > 1) {
     // The tile's activation rows are contiguous: stage them with eight
     // independent loads in flight per thread (absent tokens read as 0),
-    // 16 bytes at a time when the tile is 16-byte aligned.
-    const int total = TT * nb * Q8_BLOCK_WORDS;
+    // 16 bytes at a time when the rows are whole 16-byte vectors.
+    const int total = TT * nb * AW;
     const int64_t tok_left = n_tok - t0;
-    const int valid = tok_left >= TT ? total : (int)tok_left * nb * Q8_BLOCK_WORDS;
+    const int valid = tok_left >= TT ? total : (int)tok_left * nb * AW;
     auto put = [&](int idx, uint32_t v) {
-      const int tb = idx / Q8_BLOCK_WORDS;
-      const int k = idx - tb * Q8_BLOCK_WORDS;
+      const int tb = idx / AW;
+      const int k = idx - tb * AW;
       if (k == 0) {
         ld[tb] = __builtin_bit_cast(float, v);
-      } else if (k <= 32) {
-        lq[tb * 32 + (k - 1)] = v;
+      } else if (k <= CW) {
+        lq[tb * CW + (k - 1)] = v;
+      } else if (SPLIT) {
+        lsum[tb] = (int32_t)(int16_t)(v & 0xffffu);  // the upper half is the pad
       } else {
-        const int g = tb * 4 + (k - 33) * 2;
+        const int g = tb * (AB / 32) + (k - 1 - CW) * 2;
         lsum[g] = (int32_t)(int16_t)(v & 0xffffu);
         lsum[g + 1] = (int32_t)(int16_t)(v >> 16);
       }
     };
-    if ((nb & 3) == 0) {
+    if ((nb * AW) % 4 == 0) {
       const int chunks = total / 4, valid4 = valid / 4;
       for (int base = threadIdx.x; base < chunks; base += MMQ_THREADS * 8) {
         u32x4 v[8];
@@ -276,8 +330,8 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k128(const uint8_t* __
       for (int t = 0; t < TT; ++t) {
         const int tg = t * ng + g;  // group index within the tile
         uint32_t a[8];
-        int bs;
-        float da;
+        int bs, bs1 = 0;
+        float da, da1 = 0.0f;
         if (TT > 1) {
           const u32x4* qa = reinterpret_cast<const u32x4*>(lq + tg * 8);
           const u32x4 a0 = qa[0], a1 = qa[1];
@@ -286,33 +340,42 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k128(const uint8_t* __
             a[c] = a0[c];
             a[4 + c] = a1[c];
           }
-          bs = lsum[tg];
-          da = ld[tg >> 2];
+          if (SPLIT) {
+            bs = lsum[2 * tg];
+            bs1 = lsum[2 * tg + 1];
+            da = ld[2 * tg];
+            da1 = ld[2 * tg + 1];
+          } else {
+            bs = lsum[tg];
+            da = ld[tg / (AB / 32)];
+          }
         } else {
           // one token: the words loaded with the group
           const RawAct& A = acur[TT == 1 ? u : 0];
 #pragma unroll
           for (int c = 0; c < 8; ++c) a[c] = A.q[c];
-          bs = (int)(int16_t)((g & 1) ? (A.sums >> 16) : (A.sums & 0xffffu));
-          da = __builtin_bit_cast(float, A.d);
+          if (SPLIT) {
+            bs = (int)(int16_t)(A.sums & 0xffffu);
+            bs1 = (int)(int16_t)(A.sums1 & 0xffffu);
+            da = __builtin_bit_cast(float, A.d);
+            da1 = __builtin_bit_cast(float, A.d1);
+          } else {
+            bs = (int)(int16_t)((g & 1) ? (A.sums >> 16) : (A.sums & 0xffffu));
+            da = __builtin_bit_cast(float, A.d);
+          }
         }
-        int isum = 0;
+        int ilo = 0, ihi = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) isum = __builtin_amdgcn_sdot4((int)G.lo[c], (int)a[c], isum, false);
+        for (int c = 0; c < 4; ++c) ilo = __builtin_amdgcn_sdot4((int)G.lo[c], (int)a[c], ilo, false);
+        if (SPLIT) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) isum = __builtin_amdgcn_sdot4((int)G.hi[c], (int)a[4 + c], isum, false);
-        if (TYPE == QR_Q4_0 || TYPE == QR_Q5_0 || TYPE == QR_Q6_0) {
-          // d * (sum(u*q) - offset * bsum), exact in int32
-          const int I = isum - (TYPE == QR_Q4_0 ? 8 : TYPE == QR_Q5_0 ? 16 : 32) * bs;
-          acc[t] = __builtin_fmaf(G.sa * da, (float)I, acc[t]);
-        } else if (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
-          // d * sum(u*q) + m * bsum
-          const float part = __builtin_fmaf(G.sa, (float)isum, G.sb * (float)bs);
-          acc[t] = __builtin_fmaf(da, part, acc[t]);
+          for (int c = 0; c < 4; ++c) ihi = __builtin_amdgcn_sdot4((int)G.hi[c], (int)a[4 + c], ihi, false);
+          acc[t] = add_term<TYPE>(G, ilo, bs, da, acc[t]);
+          acc[t] = add_term<TYPE>(G, ihi, bs1, da1, acc[t]);
         } else {
-          // d*sc * sum(u*q) - dmin*mn * bsum
-          const float part = __builtin_fmaf(G.sa, (float)isum, -(G.sb * (float)bs));
-          acc[t] = __builtin_fmaf(da, part, acc[t]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ilo = __builtin_amdgcn_sdot4((int)G.hi[c], (int)a[4 + c], ilo, false);
+          acc[t] = add_term<TYPE>(G, ilo, bs, da, acc[t]);
         }
       }
     }
@@ -338,30 +401,46 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k128(const uint8_t* __
   }
 }
 
-template <int TYPE>
+template <int TYPE, int ACT>
 int launch_type(int tt, const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in,
                 int64_t w_row_bytes, float* y, hipStream_t s) {
   const int rows = mmq_rows(tt);
   const dim3 grid((uint32_t)((n_out + rows - 1) / rows), (uint32_t)((n_tok + tt - 1) / tt));
-  const size_t lds = tt > 1 ? (size_t)mmq_lds_bytes(tt, n_in) : 0;
+  const size_t lds = tt > 1 ? (size_t)mmq_lds_bytes(tt, n_in, ACT) : 0;
   switch (tt) {
-    case 8: hipLaunchKernelGGL((k_matmul_q8k128<TYPE, 8>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
-    case 4: hipLaunchKernelGGL((k_matmul_q8k128<TYPE, 4>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
-    case 2: hipLaunchKernelGGL((k_matmul_q8k128<TYPE, 2>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
-    default: hipLaunchKernelGGL((k_matmul_q8k128<TYPE, 1>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
+    case 8: hipLaunchKernelGGL((k_matmul_q8k<TYPE, ACT, 8>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
+    case 4: hipLaunchKernelGGL((k_matmul_q8k<TYPE, ACT, 4>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
+    case 2: hipLaunchKernelGGL((k_matmul_q8k<TYPE, ACT, 2>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
+    default: hipLaunchKernelGGL((k_matmul_q8k<TYPE, ACT, 1>), grid, dim3(MMQ_THREADS), lds, s, w, x, n_out, n_tok, n_in, w_row_bytes, y); break;
   }
-  return qr_check_launch("k_matmul_q8k128");
+  return qr_check_launch("k_matmul_q8k");
+}
+
+template <int ACT>
+int launch_act(int t, int tt, const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in,
+               int64_t wrb, float* y, hipStream_t s) {
+  switch (t) {
+    case QR_Q4_0: return launch_type<QR_Q4_0, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q4_1: return launch_type<QR_Q4_1, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q5_0: return launch_type<QR_Q5_0, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q5_1: return launch_type<QR_Q5_1, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q6_0: return launch_type<QR_Q6_0, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
+    default: return launch_type<QR_Q4_K, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
+  }
 }
 
 }  // namespace
 
 extern "C" {
 
-int qr_matmul_q8k128(int t, const void* w, const void* x, int64_t n_out, int64_t n_tok, int64_t n_in, float* y,
-                     void* stream) {
+int qr_matmul_q8k(int t, int act, const void* w, const void* x, int64_t n_out, int64_t n_tok, int64_t n_in,
+                  float* y, void* stream) {
   qr_clear_error();
   if (!qr_is_weight_type(t)) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
-  const int64_t mult = t == QR_Q4_K ? 256 : 128;
+  if (act != QR_Q8_K128 && act != QR_Q8_K64 && act != QR_Q8_K16)
+    return qr_fail(QR_EINVAL_TYPE, "activation type %d is not a Q8_K type", act);
+  const int64_t wb = t == QR_Q4_K ? 256 : 32;
+  const int64_t mult = wb > act_block(act) ? wb : act_block(act);
   if (n_in <= 0 || n_in % mult != 0 || n_in > QR_MATMUL_MAX_IN)
     return qr_fail(QR_EINVAL_SHAPE, "n_in=%lld must be a positive multiple of %lld and at most %d", (long long)n_in,
                    (long long)mult, QR_MATMUL_MAX_IN);
@@ -374,20 +453,22 @@ int qr_matmul_q8k128(int t, const void* w, const void* x, int64_t n_out, int64_t
     return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
   // tokens per tile: as many as fit (up to 8) in the activation budget
   int tt = n_tok >= 8 ? 8 : n_tok >= 4 ? 4 : n_tok >= 2 ? 2 : 1;
-  while (tt > 1 && mmq_lds_bytes(tt, n_in) > MMQ_LDS_BUDGET) tt >>= 1;
+  while (tt > 1 && mmq_lds_bytes(tt, n_in, act) > MMQ_LDS_BUDGET) tt >>= 1;
   if ((n_tok + tt - 1) / tt > 65535) return qr_fail(QR_EOVERFLOW, "n_tok=%lld needs too many token tiles", (long long)n_tok);
   const int64_t wrb = (int64_t)qr_row_bytes(t, n_in);
   const uint8_t* pw = reinterpret_cast<const uint8_t*>(w);
   const uint8_t* px = reinterpret_cast<const uint8_t*>(x);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  switch (t) {
-    case QR_Q4_0: return launch_type<QR_Q4_0>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
-    case QR_Q4_1: return launch_type<QR_Q4_1>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
-    case QR_Q5_0: return launch_type<QR_Q5_0>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
-    case QR_Q5_1: return launch_type<QR_Q5_1>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
-    case QR_Q6_0: return launch_type<QR_Q6_0>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
-    default: return launch_type<QR_Q4_K>(tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+  switch (act) {
+    case QR_Q8_K64: return launch_act<QR_Q8_K64>(t, tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+    case QR_Q8_K16: return launch_act<QR_Q8_K16>(t, tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
+    default: return launch_act<QR_Q8_K128>(t, tt, pw, px, n_out, n_tok, (int)n_in, wrb, y, s);
   }
+}
+
+int qr_matmul_q8k128(int t, const void* w, const void* x, int64_t n_out, int64_t n_tok, int64_t n_in, float* y,
+                     void* stream) {
+  return qr_matmul_q8k(t, QR_Q8_K128, w, x, n_out, n_tok, n_in, y, stream);
 }
 
 }  // extern "C"

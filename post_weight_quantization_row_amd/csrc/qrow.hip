@@ -676,17 +676,21 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
 }
 
 // -------------------------------------------------------------------------
-// Q8_K_128 activation kernel [Q8 修复方案]
+// Q8_K activation kernels [Q8 修复方案; 技术启示与后续演进 for the 64- and
+// 16-value blocks]
 //
-// A wave handles Q8_STEPS pairs of 128-value blocks (16 consecutive blocks, 8
-// KB of fp32 input) per iteration: lanes 0-31 hold one block and lanes 32-63
-// the next, one float4 per lane, all loads issued before any use. amax and
-// the per-32 sums are reduced with DPP row operations (one LDS-unit shuffle
-// for the last step). The 16 packed blocks (2240 bytes, 16-byte aligned) are
-// assembled in LDS and written with coalesced 16-byte stores.
+// B/4 lanes own a block of B values (one float4 each): a wave holds 2, 4 or
+// 16 consecutive blocks per step and Q8_STEPS steps per iteration (8 KB of
+// fp32 input), all loads issued before any use. amax and the code sums are
+// reduced over the block's lanes with DPP row operations (one LDS-unit
+// shuffle for the last step of a 128-value block). The packed blocks of an
+// iteration (a 16-byte aligned run) are assembled in LDS and written with
+// coalesced 16-byte stores.
 
-constexpr int Q8_STEPS = 8;                      // block pairs per wave iteration
-constexpr int Q8_CHUNK = Q8_STEPS * 2 * 140;     // output bytes per wave iteration
+constexpr int Q8_STEPS = 8;                      // wave steps per iteration
+
+__host__ __device__ constexpr int q8_block_bytes(int b) { return b == 128 ? 140 : b == 64 ? 72 : 24; }
+__host__ __device__ constexpr int q8_chunk_blocks(int b) { return (256 / b) * Q8_STEPS; }
 
 // DPP helpers (gfx9 encodings): quad_perm, row_half_mirror, row_mirror, row_shl:8
 template <int CTRL>
@@ -730,32 +734,61 @@ __device__ __forceinline__ float4 load4(const void* __restrict__ x, int64_t e) {
                      __builtin_bit_cast(float, v.y << 16), __builtin_bit_cast(float, v.y & 0xffff0000u));
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_quantize_q8k128(const void* __restrict__ x, int64_t n_blocks,
-                                                         uint8_t* __restrict__ out) {
-  __shared__ __align__(16) uint32_t stage[4][Q8_CHUNK / 4];
+// max over each group of 4 lanes
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  return fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+}
+
+// max over each row of 16 lanes
+__device__ __forceinline__ float row_max(float v) {
+  v = quad_max(v);
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+}
+
+// sum over each group of 4 lanes
+__device__ __forceinline__ int quad_sum(int v) {
+  v += dpp_i<DPP_QUAD_XOR1>(v);
+  return v + dpp_i<DPP_QUAD_XOR2>(v);
+}
+
+template <int B>
+__device__ __forceinline__ float block_max(float v) {
+  if constexpr (B == 128) return half_wave_max(v);
+  else if constexpr (B == 64) return row_max(v);
+  else return quad_max(v);
+}
+
+template <int B, bool BF16>
+__global__ __launch_bounds__(256) void k_quantize_q8k(const void* __restrict__ x, int64_t n_blocks,
+                                                      uint8_t* __restrict__ out) {
+  constexpr int LPB = B / 4;                       // lanes per block
+  constexpr int BPS = WAVE / LPB;                  // blocks per wave step
+  constexpr int BW = q8_block_bytes(B) / 4;        // words per packed block
+  constexpr int CB = q8_chunk_blocks(B);           // blocks per iteration
+  __shared__ __align__(16) uint32_t stage[4][CB * BW];
   const int lane = threadIdx.x & 63;
   const int wib = threadIdx.x >> 6;
-  const int half = lane >> 5;             // which block of a pair
-  const int l32 = lane & 31;              // 4-value slot inside the block
+  const int sub = lane / LPB;             // which block of a step
+  const int lb = lane % LPB;              // 4-value slot inside the block
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   uint32_t* st = stage[wib];
 
-  // rows are contiguous and a multiple of 128 long, so block b of the whole
-  // tensor starts at value 128*b and its packed bytes at 140*b
-  for (int64_t b0 = wave * (2 * Q8_STEPS); b0 < n_blocks; b0 += n_waves * (2 * Q8_STEPS)) {
+  // rows are contiguous and hold whole blocks, so block b of the whole
+  // tensor starts at value B*b and its packed bytes at block_bytes*b
+  for (int64_t b0 = wave * CB; b0 < n_blocks; b0 += n_waves * CB) {
     float4 v[Q8_STEPS];
 #pragma unroll
     for (int u = 0; u < Q8_STEPS; ++u) {
-      const int64_t blk = b0 + 2 * u + half;
-      v[u] = blk < n_blocks ? load4<BF16>(x, blk * 128 + 4 * l32) : make_float4(0, 0, 0, 0);
+      const int64_t blk = b0 + BPS * u + sub;
+      v[u] = blk < n_blocks ? load4<BF16>(x, blk * B + 4 * lb) : make_float4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < Q8_STEPS; ++u) {
-      const int lb = 2 * u + half;        // block index within the chunk
       float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
-      amax = half_wave_max(amax);
+      amax = block_max<B>(amax);
       const float id = amax > 0.0f ? 127.0f / amax : 0.0f;
       const bool zero = !(amax > 0.0f) || !__builtin_isfinite(id);
       const float d = zero ? 0.0f : amax / 127.0f;
@@ -766,30 +799,38 @@ __global__ __launch_bounds__(256) void k_quantize_q8k128(const void* __restrict_
         q2 = (int32_t)med3(rne(v[u].z * id), -127.0f, 127.0f);
         q3 = (int32_t)med3(rne(v[u].w * id), -127.0f, 127.0f);
       }
-      const int32_t sum = oct_sum(q0 + q1 + q2 + q3);     // sum of group l32/8
-      const int32_t s_next = dpp_i<DPP_ROW_SHL8>(sum);    // lanes 0, 16: groups 1, 3
-      uint32_t* bs = st + 35 * lb;                        // 140-byte block in the chunk
-      bs[1 + l32] = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
-                    ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
-      if (l32 == 0) bs[0] = fbits(d);
-      if (l32 == 0 || l32 == 16)
-        bs[33 + (l32 >> 4)] = (uint32_t)(sum & 0xffff) | ((uint32_t)(s_next & 0xffff) << 16);
+      uint32_t* bs = st + BW * (BPS * u + sub);   // this block in the chunk
+      bs[1 + lb] = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
+                   ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+      if (lb == 0) bs[0] = fbits(d);
+      if constexpr (B == 16) {
+        const int32_t sum = quad_sum(q0 + q1 + q2 + q3);   // the block's 16 codes
+        if (lb == 0) bs[5] = (uint32_t)(sum & 0xffff);     // upper half: the zero pad
+      } else {
+        const int32_t sum = oct_sum(q0 + q1 + q2 + q3);    // sum of group lb/8
+        const int32_t s_next = dpp_i<DPP_ROW_SHL8>(sum);   // lanes 0, 16 of a row: the next group
+        if (lb == 0 || (B == 128 && lb == 16))
+          bs[(B == 128 ? 33 : 17) + (lb >> 4)] = (uint32_t)(sum & 0xffff) | ((uint32_t)(s_next & 0xffff) << 16);
+      }
     }
     // one wave's LDS accesses complete in order; the barrier only keeps the
     // compiler from moving the reads above the writes
     __builtin_amdgcn_wave_barrier();
-    // 16-byte stores of the chunk (its start 140*b0 is a multiple of 16)
-    const int64_t nb = (n_blocks - b0) < 2 * Q8_STEPS ? (n_blocks - b0) : 2 * Q8_STEPS;
-    const int nvec = (int)(nb * 140 / 16);
-    uint8_t* dst = out + b0 * 140;
+    // 16-byte stores of the chunk (its start block_bytes*b0 is a multiple of 16)
+    const int64_t nb = (n_blocks - b0) < CB ? (n_blocks - b0) : CB;
+    const int nvec = (int)(nb * BW / 4);
+    uint8_t* dst = out + b0 * (4 * BW);
     for (int i = lane; i < nvec; i += WAVE)
       __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(st + 4 * i), reinterpret_cast<u32x4*>(dst) + i);
-    if (lane == 0 && nb * 140 % 16) {                     // a partial last vector (ragged end)
-      for (int k = nvec * 4; k < (int)(nb * 140 / 4); ++k) reinterpret_cast<uint32_t*>(dst)[k] = st[k];
+    if (lane == 0 && (nb * BW) % 4) {                      // a partial last vector (ragged end)
+      for (int k = nvec * 4; k < (int)(nb * BW); ++k) reinterpret_cast<uint32_t*>(dst)[k] = st[k];
     }
     __builtin_amdgcn_wave_barrier();
   }
 }
+static_assert(q8_chunk_blocks(128) * 140 % 16 == 0 && q8_chunk_blocks(64) * 72 % 16 == 0 &&
+                  q8_chunk_blocks(16) * 24 % 16 == 0,
+              "every iteration's output starts 16-byte aligned");
 
 // -------------------------------------------------------------------------
 // decoders: 8 lanes per 32-weight group, one float4 of output each; a wave
@@ -803,10 +844,22 @@ constexpr int DQ_STEPS = 2;
 // one memory round trip.
 template <int TYPE>
 __device__ __forceinline__ void decode4(const uint8_t* __restrict__ in, int64_t U, int k, float (&o)[4]) {
-  if constexpr (TYPE == QR_Q8_K128) {
-    const uint8_t* p = in + (U >> 2) * 140;
-    const uint32_t dbits = *reinterpret_cast<const uint32_t*>(p);
-    const uint32_t qv = *reinterpret_cast<const uint32_t*>(p + 4 + 32 * (int)(U & 3) + 4 * k);
+  if constexpr (TYPE == QR_Q8_K128 || TYPE == QR_Q8_K64 || TYPE == QR_Q8_K16) {
+    // values 32U + 4k .. +3: block (32U + 4k) / B, code word ((32U + 4k) % B) / 4
+    const uint8_t* blk;
+    int off;
+    if constexpr (TYPE == QR_Q8_K128) {
+      blk = in + (U >> 2) * 140;
+      off = 4 + 32 * (int)(U & 3) + 4 * k;
+    } else if constexpr (TYPE == QR_Q8_K64) {
+      blk = in + (U >> 1) * 72;
+      off = 4 + 32 * (int)(U & 1) + 4 * k;
+    } else {
+      blk = in + (2 * U + (k >> 2)) * 24;
+      off = 4 + 4 * (k & 3);
+    }
+    const uint32_t dbits = *reinterpret_cast<const uint32_t*>(blk);
+    const uint32_t qv = *reinterpret_cast<const uint32_t*>(blk + off);
     const float d = __builtin_bit_cast(float, dbits);
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = d * (float)(int8_t)(qv >> (8 * i));
@@ -858,12 +911,12 @@ __device__ __forceinline__ void decode4(const uint8_t* __restrict__ in, int64_t 
   }
 }
 
+// n_items = values / 4 (a Q8_K16 tensor may end halfway through a unit)
 template <int TYPE>
-__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ in, int64_t n_units,
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ in, int64_t n_items,
                                                     float* __restrict__ out) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-  const int64_t n_items = n_units * 8;
   for (int64_t t0 = tid; t0 < n_items; t0 += nthreads * DQ_STEPS) {
     float o[DQ_STEPS][4];
 #pragma unroll
@@ -889,6 +942,8 @@ int block_elems(int t) {
     case QR_Q4_0: case QR_Q4_1: case QR_Q5_0: case QR_Q5_1: case QR_Q6_0: return 32;
     case QR_Q4_K: return 256;
     case QR_Q8_K128: return 128;
+    case QR_Q8_K64: return 64;
+    case QR_Q8_K16: return 16;
     default: return 0;
   }
 }
@@ -902,6 +957,8 @@ size_t block_bytes(int t) {
     case QR_Q4_K: return 144;
     case QR_Q8_K128: return 140;
     case QR_Q6_0: return 28;
+    case QR_Q8_K64: return 72;
+    case QR_Q8_K16: return 24;
     default: return 0;
   }
 }
@@ -1051,28 +1108,46 @@ int qr_quantize_rows(int t, int src, const void* x, const float* imatrix, int64_
   return qr_quantize_rows_grouped(t, src, x, imatrix, 1, n_rows, n_per_row, out, stream);
 }
 
-int qr_quantize_activations_q8k128(int src, const void* x, int64_t n_rows, int64_t n_per_row, void* out,
-                                   void* stream) {
+int qr_quantize_activations_q8k(int t, int src, const void* x, int64_t n_rows, int64_t n_per_row, void* out,
+                                void* stream) {
   qr_clear_error();
+  if (t != QR_Q8_K128 && t != QR_Q8_K64 && t != QR_Q8_K16)
+    return qr_fail(QR_EINVAL_TYPE, "type %d is not a Q8_K activation type", t);
   if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
-  if (n_rows < 0 || n_per_row <= 0 || n_per_row % 128 != 0)
-    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of 128", (long long)n_per_row);
+  const int B = block_elems(t);
+  if (n_rows < 0 || n_per_row <= 0 || n_per_row % B != 0)
+    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld must be a positive multiple of %d", (long long)n_per_row, B);
   if (n_rows == 0) return QR_OK;
-  if (n_per_row / 128 > INT32_MAX) return qr_fail(QR_EOVERFLOW, "row too long");
+  if (n_per_row / B > INT32_MAX) return qr_fail(QR_EOVERFLOW, "row too long");
   if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return qr_fail(QR_EOVERFLOW, "size overflows");
   if (!x || !out) return qr_fail(QR_EINVAL_PTR, "x and out must be non-NULL");
   if (!aligned16(x) || !aligned16(out)) return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
-  const int64_t n_blocks = n_rows * (n_per_row / 128);
-  const int64_t chunks = (n_blocks + 2 * Q8_STEPS - 1) / (2 * Q8_STEPS);
+  const int64_t n_blocks = n_rows * (n_per_row / B);
+  const int64_t chunks = (n_blocks + q8_chunk_blocks(B) - 1) / q8_chunk_blocks(B);
   const int grid = grid_for(chunks, 4);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (src == QR_F32)
-    hipLaunchKernelGGL(k_quantize_q8k128<false>, dim3(grid), dim3(256), 0, s, x, n_blocks,
-                       reinterpret_cast<uint8_t*>(out));
-  else
-    hipLaunchKernelGGL(k_quantize_q8k128<true>, dim3(grid), dim3(256), 0, s, x, n_blocks,
-                       reinterpret_cast<uint8_t*>(out));
-  return qr_check_launch("k_quantize_q8k128");
+  uint8_t* o = reinterpret_cast<uint8_t*>(out);
+  const bool bf = src == QR_BF16;
+  switch (B) {
+    case 128:
+      if (bf) hipLaunchKernelGGL((k_quantize_q8k<128, true>), dim3(grid), dim3(256), 0, s, x, n_blocks, o);
+      else hipLaunchKernelGGL((k_quantize_q8k<128, false>), dim3(grid), dim3(256), 0, s, x, n_blocks, o);
+      break;
+    case 64:
+      if (bf) hipLaunchKernelGGL((k_quantize_q8k<64, true>), dim3(grid), dim3(256), 0, s, x, n_blocks, o);
+      else hipLaunchKernelGGL((k_quantize_q8k<64, false>), dim3(grid), dim3(256), 0, s, x, n_blocks, o);
+      break;
+    default:
+      if (bf) hipLaunchKernelGGL((k_quantize_q8k<16, true>), dim3(grid), dim3(256), 0, s, x, n_blocks, o);
+      else hipLaunchKernelGGL((k_quantize_q8k<16, false>), dim3(grid), dim3(256), 0, s, x, n_blocks, o);
+      break;
+  }
+  return qr_check_launch("k_quantize_q8k");
+}
+
+int qr_quantize_activations_q8k128(int src, const void* x, int64_t n_rows, int64_t n_per_row, void* out,
+                                   void* stream) {
+  return qr_quantize_activations_q8k(QR_Q8_K128, src, x, n_rows, n_per_row, out, stream);
 }
 
 int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row, float* out, void* stream) {
@@ -1086,18 +1161,20 @@ int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row,
   if ((uint64_t)n_rows > (uint64_t)INT64_MAX / ((uint64_t)n_per_row * 4)) return qr_fail(QR_EOVERFLOW, "size overflows");
   if (!in || !out) return qr_fail(QR_EINVAL_PTR, "in and out must be non-NULL");
   if (!aligned16(in) || !aligned16(out)) return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
-  const int64_t n_units = n_rows * (n_per_row / QK);
-  const int grid = grid_for((n_units * 8 + DQ_STEPS - 1) / DQ_STEPS, 256);
+  const int64_t n_items = n_rows * n_per_row / 4;
+  const int grid = grid_for((n_items + DQ_STEPS - 1) / DQ_STEPS, 256);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint8_t* p = reinterpret_cast<const uint8_t*>(in);
   switch (t) {
-    case QR_Q4_0: hipLaunchKernelGGL(k_dequantize<QR_Q4_0>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
-    case QR_Q4_1: hipLaunchKernelGGL(k_dequantize<QR_Q4_1>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
-    case QR_Q5_0: hipLaunchKernelGGL(k_dequantize<QR_Q5_0>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
-    case QR_Q5_1: hipLaunchKernelGGL(k_dequantize<QR_Q5_1>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
-    case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
-    case QR_Q6_0: hipLaunchKernelGGL(k_dequantize<QR_Q6_0>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
-    default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_units, out); break;
+    case QR_Q4_0: hipLaunchKernelGGL(k_dequantize<QR_Q4_0>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q4_1: hipLaunchKernelGGL(k_dequantize<QR_Q4_1>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q5_0: hipLaunchKernelGGL(k_dequantize<QR_Q5_0>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q5_1: hipLaunchKernelGGL(k_dequantize<QR_Q5_1>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q6_0: hipLaunchKernelGGL(k_dequantize<QR_Q6_0>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q8_K64: hipLaunchKernelGGL(k_dequantize<QR_Q8_K64>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q8_K16: hipLaunchKernelGGL(k_dequantize<QR_Q8_K16>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
   }
   return qr_check_launch("k_dequantize");
 }

@@ -65,10 +65,16 @@ __device__ __forceinline__ float half_bits(uint32_t h) {
 // row, with the decoders' arithmetic (qr_dequantize_rows).
 template <int TYPE>
 __device__ __forceinline__ void decode4(const uint8_t* __restrict__ row, int gin, int k, float (&xh)[4]) {
-  if (TYPE == QR_Q8_K128) {
-    const uint8_t* b = row + (int64_t)(gin >> 2) * 140;
+  if (TYPE == QR_Q8_K128 || TYPE == QR_Q8_K64 || TYPE == QR_Q8_K16) {
+    // block of values 32*gin + 4k .. +3 and the offset of their code word
+    const uint8_t* b = TYPE == QR_Q8_K128 ? row + (int64_t)(gin >> 2) * 140
+                     : TYPE == QR_Q8_K64  ? row + (int64_t)(gin >> 1) * 72
+                                          : row + (int64_t)(2 * gin + (k >> 2)) * 24;
+    const int off = TYPE == QR_Q8_K128 ? 4 + 32 * (gin & 3) + 4 * k
+                  : TYPE == QR_Q8_K64  ? 4 + 32 * (gin & 1) + 4 * k
+                                       : 4 + 4 * (k & 3);
     const float d = f32_bits(ld32(b));
-    const uint32_t w = ld32(b + 4 + 32 * (gin & 3) + 4 * k);
+    const uint32_t w = ld32(b + off);
 #pragma unroll
     for (int e = 0; e < 4; ++e) xh[e] = d * (float)(int8_t)(uint8_t)(w >> (8 * e));
   } else if (TYPE == QR_Q4_K) {
@@ -329,6 +335,8 @@ int dispatch_stats(int t, const void* x, const uint8_t* packed, const float* q, 
     case QR_Q5_1: return run_stats<QR_Q5_1, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     case QR_Q4_K: return run_stats<QR_Q4_K, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     case QR_Q6_0: return run_stats<QR_Q6_0, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
+    case QR_Q8_K64: return run_stats<QR_Q8_K64, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
+    case QR_Q8_K16: return run_stats<QR_Q8_K16, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     default: return run_stats<QR_Q8_K128, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
   }
 }
@@ -345,11 +353,11 @@ size_t qr_stats_workspace_bytes(int64_t n_rows, int64_t n_per_row) {
 int qr_quantize_stats(int t, int src, const void* x, const void* packed, const float* imatrix, int64_t n_rows,
                       int64_t n_per_row, qr_stats* out, void* workspace, size_t workspace_bytes, void* stream) {
   qr_clear_error();
-  if (t < QR_Q4_0 || t > QR_Q6_0) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
+  if (t < QR_Q4_0 || t > QR_Q8_K16) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
   if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
   const size_t rb = qr_row_bytes(t, n_per_row);
-  if (n_rows < 0 || n_per_row <= 0 || rb == 0)
-    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld is not a positive multiple of the block length",
+  if (n_rows < 0 || n_per_row <= 0 || rb == 0 || n_per_row % 32 != 0)
+    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld is not a positive multiple of the block length and of 32",
                    (long long)n_per_row);
   if (n_rows == 0) return QR_OK;
   if (n_per_row > INT32_MAX || n_rows > (int64_t)UINT32_MAX / n_per_row)

@@ -1,7 +1,8 @@
 """Python binding of libqrow.so (argument marshalling only).
 
 Every function has the name of the C entry point it calls (see
-include/qrow.h, include/qrow_imatrix.h and include/qrow_matmul.h) and takes torch tensors that live on the GPU; all arithmetic
+include/qrow.h, include/qrow_imatrix.h, include/qrow_matmul.h and
+include/qrow_stats.h) and takes torch tensors that live on the GPU; all arithmetic
 runs in the library's HIP kernels. torch provides device memory and the
 stream. There is no CPU fallback: without the built library or a GPU the
 calls raise.
@@ -17,13 +18,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # QROW_LIBRARY may name another build of the same library (A/B timing).
 LIB_PATH = os.environ.get("QROW_LIBRARY") or os.path.join(HERE, "libqrow.so")
 
-QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q4_K, QR_Q8_K128, QR_Q6_0 = range(7)
+QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q4_K, QR_Q8_K128, QR_Q6_0, QR_Q8_K64, QR_Q8_K16 = range(9)
 QR_F32, QR_BF16 = 0, 1
 # element-importance weightings (qr_weighting)
 WEIGHTINGS = {"sqrt_sigma2_x2": 0, "x2": 1, "abs_x": 2, "sigma2_plus_x2": 3,
               "sigma_plus_abs_x": 4, "imatrix_only": 5}
 TYPES = {"q4_0": QR_Q4_0, "q4_1": QR_Q4_1, "q5_0": QR_Q5_0, "q5_1": QR_Q5_1,
-         "q4_k": QR_Q4_K, "q8_k128": QR_Q8_K128, "q6_0": QR_Q6_0}
+         "q4_k": QR_Q4_K, "q8_k128": QR_Q8_K128, "q6_0": QR_Q6_0,
+         "q8_k64": QR_Q8_K64, "q8_k16": QR_Q8_K16}
+ACT_TYPES = ("q8_k128", "q8_k64", "q8_k16")
 ERRORS = {-1: "QR_EINVAL_TYPE", -2: "QR_EINVAL_SHAPE", -3: "QR_EINVAL_PTR",
           -4: "QR_EOVERFLOW", -5: "QR_EDEVICE"}
 
@@ -35,7 +38,7 @@ EXPORTS = ("qr_quantize_rows", "qr_quantize_rows_grouped",
            "qr_imatrix_accumulate", "qr_imatrix_merge",
            "qr_imatrix_finalize", "qr_matmul_q8k128",
            "qr_quantize_rows_weighted", "qr_stats_workspace_bytes",
-           "qr_quantize_stats")
+           "qr_quantize_stats", "qr_quantize_activations_q8k", "qr_matmul_q8k")
 IMX_MAX_EXPERTS, IMX_MAX_TOP_K = 1024, 64
 
 
@@ -75,6 +78,8 @@ def load_library(path: str = LIB_PATH):
         L.qr_imatrix_merge.argtypes = [vp, vp, vp, vp, i64, i64, vp]
         L.qr_imatrix_finalize.argtypes = [vp, vp, i64, i64, vp, vp]
         L.qr_matmul_q8k128.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp]
+        L.qr_matmul_q8k.argtypes = [i32, i32, vp, vp, i64, i64, i64, vp, vp]
+        L.qr_quantize_activations_q8k.argtypes = [i32, i32, vp, i64, i64, vp, vp]
         L.qr_quantize_rows_weighted.argtypes = [i32, i32, vp, vp, i64, i64, i32, vp, vp]
         L.qr_stats_workspace_bytes.argtypes = [i64, i64]
         L.qr_stats_workspace_bytes.restype = C.c_size_t
@@ -220,6 +225,19 @@ def qr_quantize_activations_q8k128(x: torch.Tensor, out=None, stream=None):
     return out
 
 
+def qr_quantize_activations_q8k(t, x: torch.Tensor, out=None, stream=None):
+    """x: [n_rows, n_per_row] fp32/bf16 to the Q8_K format t (q8_k128,
+    q8_k64 or q8_k16); n_per_row a multiple of its block length."""
+    _dev2d(x, "x")
+    tid = _tid(t)
+    n_rows, n = x.shape
+    out = _out(out, (n_rows, qr_row_bytes(tid, n)), torch.uint8, x.device)
+    _check(load_library().qr_quantize_activations_q8k(
+        tid, _src_dtype(x), C.c_void_p(x.data_ptr()), n_rows, n,
+        C.c_void_p(out.data_ptr()), _stream(x, stream)))
+    return out
+
+
 def qr_dequantize_rows(t, packed: torch.Tensor, n_rows: int, n_per_row: int,
                        out=None, stream=None):
     """packed: uint8 [n_rows, qr_row_bytes]; returns fp32 [n_rows, n_per_row]."""
@@ -327,6 +345,24 @@ def qr_imatrix_finalize(sums, counts, out=None, stream=None):
 
 # --------------------------------------------------------------------------
 # product with Q8_K_128 activations (include/qrow_matmul.h)
+
+def qr_matmul_q8k(t, act, w: torch.Tensor, x: torch.Tensor, n_in: int, out=None, stream=None):
+    """y [n_tok, n_out] fp32 = W @ A.T for packed weight rows w (uint8
+    [n_out, qr_row_bytes(t, n_in)]) and packed activation rows x of the
+    Q8_K format act (uint8 [n_tok, qr_row_bytes(act, n_in)]), both on the GPU."""
+    tid, aid = _tid(t), _tid(act)
+    for name, a in (("w", w), ("x", x)):
+        if (not isinstance(a, torch.Tensor) or not a.is_cuda or a.dtype != torch.uint8
+                or a.dim() != 2 or not a.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous 2-D CUDA uint8 tensor")
+    if w.shape[1] != qr_row_bytes(tid, n_in) or x.shape[1] != qr_row_bytes(aid, n_in):
+        raise ValueError("packed row lengths do not match n_in")
+    n_out, n_tok = w.shape[0], x.shape[0]
+    out = _out(out, (n_tok, n_out), torch.float32, w.device)
+    _check(load_library().qr_matmul_q8k(
+        tid, aid, _ptr(w), _ptr(x), n_out, n_tok, n_in, _ptr(out), _stream(w, stream)))
+    return out
+
 
 def qr_matmul_q8k128(t, w: torch.Tensor, x: torch.Tensor, n_in: int, out=None, stream=None):
     """y [n_tok, n_out] fp32 = W @ A.T for packed weight rows w (uint8

@@ -32,14 +32,14 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(HEADERS) == 4 and len(names) == 16
+    assert len(HEADERS) == 4 and len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(qrow.EXPORTS) == names
 
 
 def test_formats_agree_with_the_oracle(lib):
-    for t in range(7):
+    for t in range(9):
         assert lib.qr_block_elems(t) == oracle.block_elems(t)
         for n in (0, 32, 128, 256, 4096, 7168, 11008, 100):
             assert lib.qr_row_bytes(t, n) == oracle.row_bytes(t, n)
@@ -70,7 +70,7 @@ def test_argument_validation_without_a_gpu(lib):
     assert lib.qr_quantize_rows(0, 0, fake, None, 4, 65536, fake, None) == -2
     assert lib.qr_quantize_activations_q8k128(0, fake, 4, 100, fake, None) == -2
     assert lib.qr_dequantize_rows(4, fake, 4, 32, fake, None) == -2
-    assert lib.qr_dequantize_rows(8, fake, 4, 32, fake, None) == -1
+    assert lib.qr_dequantize_rows(9, fake, 4, 32, fake, None) == -1
     # n_rows == 0 is a no-op even with NULL pointers
     assert lib.qr_quantize_rows(0, 0, None, None, 0, 256, None, None) == 0
     assert lib.qr_quantize_activations_q8k128(0, None, 0, 128, None, None) == 0
@@ -159,6 +159,27 @@ def test_matmul_argument_validation_without_a_gpu(lib):
     assert mm(0, fake, fake, 4, 2 ** 30, 32768, fake, None) == -4   # too many token tiles
 
 
+def test_q8k_family_argument_validation_without_a_gpu(lib):
+    fake = C.c_void_p(0x10000)       # never dereferenced: calls fail first
+    qa = lib.qr_quantize_activations_q8k
+    assert qa(0, 0, fake, 4, 128, fake, None) == -1            # not a Q8_K type
+    assert qa(6, 0, fake, 4, 128, fake, None) == -1
+    assert qa(7, 2, fake, 4, 128, fake, None) == -1            # bad source dtype
+    assert qa(7, 0, fake, 4, 96, fake, None) == -2             # not whole 64-blocks
+    assert qa(8, 0, fake, 4, 40, fake, None) == -2             # not whole 16-blocks
+    assert qa(8, 0, None, 0, 48, None, None) == 0              # no rows
+    assert qa(8, 0, fake, 4, 48, None, None) == -3
+    assert qa(8, 0, C.c_void_p(0x10008), 4, 48, fake, None) == -3
+    mm = lib.qr_matmul_q8k
+    assert mm(0, 0, fake, fake, 4, 2, 256, fake, None) == -1    # activations not Q8_K
+    assert mm(5, 7, fake, fake, 4, 2, 256, fake, None) == -1    # weights not a weight type
+    assert mm(0, 7, fake, fake, 4, 2, 96, fake, None) == -2     # not whole 64-blocks
+    assert mm(0, 8, fake, fake, 4, 2, 48, fake, None) == -2     # not whole 32-weight groups
+    assert mm(4, 8, fake, fake, 4, 2, 128, fake, None) == -2    # Q4_K needs 256
+    assert mm(0, 8, None, None, 0, 2, 64, None, None) == 0      # empty: no-op
+    assert mm(0, 8, None, fake, 4, 2, 64, fake, None) == -3
+
+
 def test_weighting_enum_agrees_with_the_oracle_and_is_validated(lib):
     assert qrow.WEIGHTINGS == oracle.WEIGHTINGS
     fake = C.c_void_p(0x10000)
@@ -174,7 +195,8 @@ def test_stats_argument_validation_without_a_gpu(lib):
     ws = lib.qr_stats_workspace_bytes(4, 256)
     assert ws > 0 and lib.qr_stats_workspace_bytes(4, 0) == 0
     st = lib.qr_quantize_stats
-    assert st(7, 0, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
+    assert st(9, 0, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
+    assert st(8, 0, fake, fake, None, 4, 48, fake, fake, ws, None) == -2     # whole 32-groups
     assert st(0, 2, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
     assert st(4, 0, fake, fake, None, 4, 128, fake, fake, ws, None) == -2    # Q4_K: 256
     assert st(0, 0, None, None, None, 0, 256, None, None, 0, None) == 0       # no rows
