@@ -33,6 +33,7 @@ TYPE_NAMES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1,
               "q4_k": Q4_K, "q8_k128": Q8_K128, "q6_0": Q6_0,
               "q8_k64": Q8_K64, "q8_k16": Q8_K16}
 ACT_TYPES = ("q8_k128", "q8_k64", "q8_k16")
+FITS = {"max": 0, "weighted": 1}   # Q4_K sub-scale choice
 
 _lib = None
 _lock = threading.Lock()
@@ -110,6 +111,8 @@ def _load(path):
                                           C.c_float, u8p]
     L.orc_quantize_q8k128.argtypes = [vp, i64, i64, vp]
     L.orc_quantize_q8k.argtypes = [C.c_int, vp, i64, i64, vp]
+    L.orc_fit_levels_pos.argtypes = [C.c_int, f32p, f32p, C.c_int, C.c_int, C.c_int, u8p, f32p, i32p]
+    L.orc_quantize_rows_ex.argtypes = [C.c_int, vp, vp, i64, i64, i64, C.c_int, C.c_int, vp]
     L.orc_row_weights_mode.argtypes = [f32p, vp, i64, C.c_float, C.c_int, f32p]
     L.orc_quantize_rows_weighted.argtypes = [C.c_int, vp, vp, i64, i64, C.c_int, vp]
     L.orc_quantize_row_sigma2_mode.argtypes = [C.c_int, f32p, vp, i64, C.c_float,
@@ -198,6 +201,22 @@ def solve_sym(x, w, nmax, K=None, F=None):
     return l, d[0], info
 
 
+def fit_levels_pos(v, W, nmax=63, K=None, F=None):
+    """Weighted fit of non-negative values v ~ d*l, l in 0..nmax (the Q4_K
+    sub-scale fit); returns (levels uint8, d, info)."""
+    c = solver_constants()
+    K = c["sym_cand"] if K is None else K
+    F = c["sym_flip_passes"] if F is None else F
+    v, W = _f32(v), _f32(W)
+    l = np.zeros(v.size, np.uint8)
+    d = np.zeros(1, np.float32)
+    info = np.zeros(4, np.int32)
+    rc = lib().orc_fit_levels_pos(v.size, v, W, nmax, K, F, l, d, info)
+    if rc != 0:
+        raise ValueError("orc_fit_levels_pos: invalid arguments")
+    return l, d[0], info
+
+
 def solve_asym(x, w, nmax, K=None, F=None, k4=False):
     """Returns (levels uint8 in [0, nmax], d, m, info)."""
     c = solver_constants()
@@ -244,6 +263,37 @@ def quantize_rows_weighted(t, x, imatrix, mode, threads: int = 1) -> np.ndarray:
                 raise ValueError("orc_quantize_rows_weighted failed")
 
     _rows_parallel(n_rows, run, threads)
+    return out
+
+
+def quantize_rows_ex(t, x, imatrix=None, mode=0, fit="max", threads: int = 1) -> np.ndarray:
+    """Rows x [n_rows, n] with a weighting and a Q4_K sub-scale fit ("max"
+    or "weighted"). imatrix is None, [n], or [n_groups, n] for n_groups
+    equal runs of rows (row r uses group r // (n_rows / n_groups))."""
+    t = _tid(t)
+    x = _f32(x)
+    n_rows, n = x.shape
+    rb = row_bytes(t, n)
+    q = None if imatrix is None else _f32(imatrix).reshape(-1, n)
+    G = 1 if q is None else q.shape[0]
+    if n_rows % G:
+        raise ValueError("imatrix groups do not divide the rows")
+    rpg = n_rows // G
+    out = np.zeros((n_rows, rb), np.uint8)
+    m = _wid(mode)
+    f = FITS[fit] if isinstance(fit, str) else int(fit)
+    for g in range(G):
+        qg = None if q is None else q[g]
+
+        def run(r0, r1, g=g, qg=qg):
+            if r1 > r0:
+                a, b = g * rpg + r0, g * rpg + r1
+                rc = lib().orc_quantize_rows_ex(t, _ptr(x[a:b]), _ptr(qg), 1, b - a, n, m, f,
+                                                _ptr(out[a:b]))
+                if rc != 0:
+                    raise ValueError("orc_quantize_rows_ex failed")
+
+        _rows_parallel(rpg, run, threads)
     return out
 
 

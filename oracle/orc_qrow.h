@@ -118,6 +118,21 @@ int orc_quantize_rows_grouped(int type, const float *x, const float *imatrix,
 int orc_quantize_row_sigma2(int type, const float *x, const float *q,
                             int64_t n_per_row, float sigma2, uint8_t *out);
 
+/* How the Q4_K 6-bit sub-scales and sub-offsets are chosen (other types
+ * have none and ignore it). */
+enum {
+    ORC_FIT_MAX = 0,       /* fp16(max/63), each rounded to the nearest level */
+    ORC_FIT_WEIGHTED = 1   /* weighted least-squares fit of the eight values   */
+};
+/* Weighted fit v_j ~ d * l_j, l_j in 0..nmax, of n values v_j >= 0 with
+ * weights W_j: K trial scales, F flip passes (the sub-scale fit). */
+int orc_fit_levels_pos(int n, const float *v, const float *W, int nmax, int K,
+                       int F, uint8_t *l_out, float *d_out, int32_t *info);
+/* Grouped rows with a weighting and a sub-scale fit. */
+int orc_quantize_rows_ex(int type, const float *x, const float *imatrix,
+                         int64_t n_groups, int64_t rows_per_group,
+                         int64_t n_per_row, int mode, int fit, uint8_t *out);
+
 /* Q8_K_128 activation quantizer. */
 int orc_quantize_q8k128(const float *x, int64_t n_rows, int64_t n_per_row,
                         uint8_t *out);

@@ -336,6 +336,94 @@ int orc_solve_sym(int n, const float *x, const float *w, int nmax, int K, int F,
 }
 
 /* ------------------------------------------------------------------------ */
+/* non-negative values, levels 0 .. nmax, one scale: the Q4_K sub-scales      */
+
+/* Weighted fit of n values v_j >= 0 as v_j ~ d * l_j, l_j in 0..nmax, with
+ * weights W_j: the least-squares scale and greedy flips of [WT 一] applied
+ * to the eight sub-scales (or sub-offsets) of a Q4_K super-block.
+ * Readings (the pages fix the sub-scales' width, not how they are chosen):
+ * the trial scales map the largest value to the top of the level range,
+ * is = c / max v with c = nmax + 0.25*k, k in the order 0, -1, +1, -2, +2
+ * (the symmetric blocks' schedule, mirrored to the positive end); each
+ * trial rounds v_j * is to the nearest level in float and clamps. Because
+ * one sub-block can carry most of the weight, the fit's error is a small
+ * difference of large scores, so the sums sumlx = sum W v l and
+ * suml2 = sum W l^2, the score comparisons (by cross multiplication, an
+ * earlier trial winning ties) and the flips (the rule of flip_passes(),
+ * element by element in order) are evaluated in double; d = sumlx/suml2
+ * rounded once to float. All-zero values, a scale that is not finite or no
+ * weight give levels 0 and d = 0. */
+int orc_fit_levels_pos(int n, const float *v, const float *W, int nmax, int K,
+                       int F, uint8_t *l_out, float *d_out, int32_t *info)
+{
+    if (n < 1 || n > MAXN || nmax < 1 || K < 1 || K > 5 || F < 0) return ORC_EINVAL;
+    float L[MAXN];
+    double Wv[MAXN];
+    const float hi_level = (float)nmax;
+    int32_t inf_local[4] = {-1, 0, 0, 1};
+    float vmax = v[0];
+    for (int i = 1; i < n; ++i) vmax = fmaxf(vmax, v[i]);
+    for (int i = 0; i < n; ++i) Wv[i] = (double)W[i] * (double)v[i];   /* exact */
+
+    int best = -1;
+    double bS1 = 0.0, bS2 = 0.0;
+    float bis = 0.0f;
+    if (vmax > 0.0f) {
+        for (int k = 0; k < K; ++k) {
+            float c = (float)nmax + ORC_CAND_STEP * (float)cand_offset[k];
+            float is = c / vmax;
+            if (!isfinite(is)) continue;
+            double S1 = 0.0, S2 = 0.0;
+            for (int i = 0; i < n; ++i) {
+                double l = (double)clampf(rintf(v[i] * is), 0.0f, hi_level);
+                S1 = fma(Wv[i], l, S1);
+                S2 = fma((double)W[i] * l, l, S2);
+            }
+            if (!(S2 > 0.0)) continue;
+            if (best < 0 || (S1 * S1) * bS2 > (bS1 * bS1) * S2) {
+                best = k; bS1 = S1; bS2 = S2; bis = is;
+            }
+        }
+    }
+    if (best < 0) {
+        for (int i = 0; i < n; ++i) l_out[i] = 0;
+        *d_out = 0.0f;
+        if (info) { info[0] = -1; info[1] = 0; info[2] = 0; info[3] = 1; }
+        return ORC_OK;
+    }
+    for (int i = 0; i < n; ++i) L[i] = clampf(rintf(v[i] * bis), 0.0f, hi_level);
+    double A = bS1, B = bS2;
+    int accepted = 0, passes = 0, converged = 0;
+    for (int p = 0; p < F; ++p) {
+        int changed = 0;
+        ++passes;
+        for (int j = 0; j < n; ++j) {
+            double e = fma((double)v[j], B, -((double)L[j] * A));
+            double s = ((signbit(A) != 0) != (signbit(e) != 0)) ? -1.0 : 1.0;
+            double lp = (double)L[j] + s;
+            double A1 = fma(s, Wv[j], A);
+            double B1 = fma((double)W[j], fma(2.0 * s, (double)L[j], 1.0), B);
+            if ((A1 * A1) * B > (A * A) * B1 && B1 > 0.0 && lp >= 0.0 && lp <= (double)nmax) {
+                A = A1;
+                B = B1;
+                L[j] = (float)lp;
+                changed = 1;
+                ++accepted;
+            }
+        }
+        if (!changed) { converged = 1; break; }
+    }
+    inf_local[0] = best;
+    inf_local[1] = accepted;
+    inf_local[2] = passes;
+    inf_local[3] = converged;
+    *d_out = (float)(A / B);
+    for (int i = 0; i < n; ++i) l_out[i] = (uint8_t)L[i];
+    if (info) memcpy(info, inf_local, sizeof inf_local);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* asymmetric block: levels 0 .. nmax, scale and offset, x ~ d*l + m          */
 
 /* Weighted least squares for (d, m) from the five block sums, in double.
@@ -553,14 +641,19 @@ static void unpack6x8(const uint8_t *p, uint8_t *v)
 }
 
 /* Q4_K super-block [KQ §一]: 8 sub-blocks of 32, each fitted as
- * x ~ a_j * l - b_j with levels 0..15. Readings: the super-scales are
- * d = fp16(max a_j / 63) and dmin = fp16(max b_j / 63) (round to nearest
- * even, subnormals kept); sub-scales are sc_j = rint(a_j / d) and
- * mn_j = rint(b_j / dmin) clamped to 0..63; the levels are then re-rounded
- * against the stored scales so that the decoder reproduces the fit. */
-static void quantize_q4k(const float *x, const float *w, uint8_t *out)
+ * x ~ a_j * l - b_j with levels 0..15. Readings, fit == ORC_FIT_MAX (the
+ * default): the super-scales are d = fp16(max a_j / 63) and
+ * dmin = fp16(max b_j / 63) (round to nearest even, subnormals kept);
+ * sub-scales are sc_j = rint(a_j / d) and mn_j = rint(b_j / dmin) clamped to
+ * 0..63. fit == ORC_FIT_WEIGHTED: the 6-bit sub-scales and sub-offsets are
+ * each fitted by orc_fit_levels_pos() with weight W_j = the sum of the
+ * sub-block's 32 importances (ascending order), d and dmin = fp16 of the
+ * fitted scales, sc_j and mn_j = the fitted levels (0 where the fp16 scale
+ * is 0). Either way the levels are then re-rounded against the stored
+ * scales so that the decoder reproduces the fit. */
+static void quantize_q4k(const float *x, const float *w, int fit, uint8_t *out)
 {
-    float a[8], b[8];
+    float a[8], b[8], W[8];
     for (int j = 0; j < 8; ++j) {
         uint8_t l[32];
         float d, m;
@@ -568,18 +661,34 @@ static void quantize_q4k(const float *x, const float *w, uint8_t *out)
                        ORC_ASYM_FLIP_PASSES, 1, l, &d, &m, NULL);
         a[j] = d > 0.0f ? d : 0.0f;
         b[j] = -m > 0.0f ? -m : 0.0f;
+        float sw = 0.0f;
+        for (int i = 0; i < 32; ++i) sw = sw + w[32 * j + i];
+        W[j] = sw;
     }
-    float amx = a[0], bmx = b[0];
-    for (int j = 1; j < 8; ++j) { amx = fmaxf(amx, a[j]); bmx = fmaxf(bmx, b[j]); }
-    uint16_t d16 = orc_f32_to_f16(amx / 63.0f);
-    uint16_t m16 = orc_f32_to_f16(bmx / 63.0f);
-    float dA = orc_f16_to_f32(d16), dB = orc_f16_to_f32(m16);
-
+    uint16_t d16, m16;
     uint8_t sc[8], mn[8];
-    for (int j = 0; j < 8; ++j) {
-        sc[j] = dA > 0.0f ? (uint8_t)clampf(rintf(a[j] / dA), 0.0f, 63.0f) : 0;
-        mn[j] = dB > 0.0f ? (uint8_t)clampf(rintf(b[j] / dB), 0.0f, 63.0f) : 0;
+    if (fit == ORC_FIT_WEIGHTED) {
+        float da, db;
+        orc_fit_levels_pos(8, a, W, 63, ORC_SYM_CAND, ORC_SYM_FLIP_PASSES, sc, &da, NULL);
+        orc_fit_levels_pos(8, b, W, 63, ORC_SYM_CAND, ORC_SYM_FLIP_PASSES, mn, &db, NULL);
+        d16 = orc_f32_to_f16(da);
+        m16 = orc_f32_to_f16(db);
+        for (int j = 0; j < 8; ++j) {
+            if (orc_f16_to_f32(d16) == 0.0f) sc[j] = 0;
+            if (orc_f16_to_f32(m16) == 0.0f) mn[j] = 0;
+        }
+    } else {
+        float amx = a[0], bmx = b[0];
+        for (int j = 1; j < 8; ++j) { amx = fmaxf(amx, a[j]); bmx = fmaxf(bmx, b[j]); }
+        d16 = orc_f32_to_f16(amx / 63.0f);
+        m16 = orc_f32_to_f16(bmx / 63.0f);
+        float dA0 = orc_f16_to_f32(d16), dB0 = orc_f16_to_f32(m16);
+        for (int j = 0; j < 8; ++j) {
+            sc[j] = dA0 > 0.0f ? (uint8_t)clampf(rintf(a[j] / dA0), 0.0f, 63.0f) : 0;
+            mn[j] = dB0 > 0.0f ? (uint8_t)clampf(rintf(b[j] / dB0), 0.0f, 63.0f) : 0;
+        }
     }
+    float dA = orc_f16_to_f32(d16), dB = orc_f16_to_f32(m16);
     out[0] = (uint8_t)d16; out[1] = (uint8_t)(d16 >> 8);
     out[2] = (uint8_t)m16; out[3] = (uint8_t)(m16 >> 8);
     pack6x8(sc, out + 4);
@@ -603,8 +712,8 @@ static void quantize_q4k(const float *x, const float *w, uint8_t *out)
 /* row drivers                                                                */
 
 static int quantize_row_impl(int type, const float *x, const float *q,
-                             int64_t n, float sigma2, int mode, float *w,
-                             uint8_t *out)
+                             int64_t n, float sigma2, int mode, int fit,
+                             float *w, uint8_t *out)
 {
     const int be = orc_block_elems(type);
     const size_t bb = orc_block_bytes(type);
@@ -620,7 +729,7 @@ static int quantize_row_impl(int type, const float *x, const float *q,
     for (int64_t ib = 0; ib < n / be; ++ib) {
         const float *xb = x + ib * be;
         float *wb = w + ib * be;
-        if (type == ORC_Q4_K) quantize_q4k(xb, wb, out + ib * bb);
+        if (type == ORC_Q4_K) quantize_q4k(xb, wb, fit, out + ib * bb);
         else quantize_block32(type, xb, wb, out + ib * bb);
     }
     return ORC_OK;
@@ -640,7 +749,7 @@ int orc_quantize_row_sigma2_mode(int type, const float *x, const float *q,
         mode < 0 || mode > ORC_W_IMATRIX_ONLY) return ORC_EINVAL;
     float *w = (float *)malloc(sizeof(float) * (size_t)n_per_row);
     if (!w) return ORC_EINVAL;
-    int rc = quantize_row_impl(type, x, q, n_per_row, sigma2, mode, w, out);
+    int rc = quantize_row_impl(type, x, q, n_per_row, sigma2, mode, ORC_FIT_MAX, w, out);
     free(w);
     return rc;
 }
@@ -654,10 +763,11 @@ int orc_quantize_row_sigma2(int type, const float *x, const float *q,
 
 static int quantize_rows_mode(int type, const float *x, const float *imatrix,
                               int64_t n_groups, int64_t rows_per_group,
-                              int64_t n_per_row, int mode, uint8_t *out)
+                              int64_t n_per_row, int mode, int fit, uint8_t *out)
 {
     if (!weight_type_ok(type) || n_groups < 0 || rows_per_group < 0 ||
-        mode < 0 || mode > ORC_W_IMATRIX_ONLY) return ORC_EINVAL;
+        mode < 0 || mode > ORC_W_IMATRIX_ONLY ||
+        (fit != ORC_FIT_MAX && fit != ORC_FIT_WEIGHTED)) return ORC_EINVAL;
     size_t rb = orc_row_bytes(type, n_per_row);
     if (rb == 0) return ORC_EINVAL;
     float *w = (float *)malloc(sizeof(float) * (size_t)n_per_row);
@@ -666,7 +776,7 @@ static int quantize_rows_mode(int type, const float *x, const float *imatrix,
         const float *xr = x + r * n_per_row;
         const float *q = imatrix ? imatrix + (r / rows_per_group) * n_per_row : NULL;
         quantize_row_impl(type, xr, q, n_per_row, orc_row_sigma2(xr, n_per_row),
-                          mode, w, out + (size_t)r * rb);
+                          mode, fit, w, out + (size_t)r * rb);
     }
     free(w);
     return ORC_OK;
@@ -677,7 +787,15 @@ int orc_quantize_rows_grouped(int type, const float *x, const float *imatrix,
                               int64_t n_per_row, uint8_t *out)
 {
     return quantize_rows_mode(type, x, imatrix, n_groups, rows_per_group,
-                              n_per_row, ORC_W_SQRT_SIGMA2_X2, out);
+                              n_per_row, ORC_W_SQRT_SIGMA2_X2, ORC_FIT_MAX, out);
+}
+
+int orc_quantize_rows_ex(int type, const float *x, const float *imatrix,
+                         int64_t n_groups, int64_t rows_per_group,
+                         int64_t n_per_row, int mode, int fit, uint8_t *out)
+{
+    return quantize_rows_mode(type, x, imatrix, n_groups, rows_per_group,
+                              n_per_row, mode, fit, out);
 }
 
 int orc_quantize_rows_weighted(int type, const float *x, const float *imatrix,
@@ -685,7 +803,7 @@ int orc_quantize_rows_weighted(int type, const float *x, const float *imatrix,
                                uint8_t *out)
 {
     if (n_rows == 0) return weight_type_ok(type) && orc_row_bytes(type, n_per_row) ? ORC_OK : ORC_EINVAL;
-    return quantize_rows_mode(type, x, imatrix, 1, n_rows, n_per_row, mode, out);
+    return quantize_rows_mode(type, x, imatrix, 1, n_rows, n_per_row, mode, ORC_FIT_MAX, out);
 }
 
 int orc_quantize_rows(int type, const float *x, const float *imatrix,

@@ -33,7 +33,8 @@ MUTANTS = [
     # flips
     ("flip: direction reversed", "? -1.0f : 1.0f;", "? 1.0f : -1.0f;"),
     ("flip: +1 dropped from suml2 update", "fmaf(2.0f * s, L[j], 1.0f)", "fmaf(2.0f * s, L[j], 0.0f)"),
-    ("flip: operands of the test transposed", "(A1 * A1) * B > (A * A) * B1", "(A1 * A1) * B1 > (A * A) * B"),
+    ("flip: operands of the test transposed", "int better = (A1 * A1) * B > (A * A) * B1;",
+     "int better = (A1 * A1) * B1 > (A * A) * B;"),
     ("flip: every move kept", "if (better && B1 > 0.0f && lp >= lo_level && lp <= hi_level) {",
      "if (B1 > 0.0f && lp >= lo_level && lp <= hi_level) {"),
     # asymmetric solver
@@ -42,7 +43,7 @@ MUTANTS = [
     ("asym: flips start from Slx + m*Sl", "float A = fmaf(-mf, bSl, bSlx), B = bSll;", "float A = fmaf(mf, bSl, bSlx), B = bSll;"),
     ("asym: Q4_K offset may be positive", "if (k4 && mm > 0.0) {", "if (0 && k4 && mm > 0.0) {"),
     # Q4_K super-block
-    ("q4k: sub-scale multiplied by d16", "rintf(a[j] / dA)", "rintf(a[j] * dA)"),
+    ("q4k: sub-scale multiplied by d16", "rintf(a[j] / dA0)", "rintf(a[j] * dA0)"),
     ("q4k: re-round with +dm sign flipped", "rintf((x[32 * j + i] + dm) * id)", "rintf((x[32 * j + i] - dm) * id)"),
     ("q4k: super-scale over 64", "orc_f32_to_f16(amx / 63.0f)", "orc_f32_to_f16(amx / 64.0f)"),
     ("f16: subnormals flushed", "if (e < -14) e = -14;", "if (e < -14) return sign;"),
@@ -92,6 +93,13 @@ MUTANTS = [
     ("q6_0: decode offset 31", "o[i] = d * (float)((int)u[i] - 32);", "o[i] = d * (float)((int)u[i] - 31);"),
     ("matmul: Q6_0 offset 16", "bv = sym ? d * (type == ORC_Q6_0 ? 32 : five ? 16 : 8) : -m;",
      "bv = sym ? d * (type == ORC_Q6_0 ? 16 : five ? 16 : 8) : -m;"),
+    # weighted Q4_K sub-scale fit
+    ("fit: largest value below the top level", "float is = c / vmax;", "float is = (c - 1.0f) / vmax;"),
+    ("fit: trials scored without the weights", "S2 = fma((double)W[i] * l, l, S2);", "S2 = fma(l, l, S2);"),
+    ("fit: flips move against the residual", "double s = ((signbit(A) != 0) != (signbit(e) != 0)) ? -1.0 : 1.0;",
+     "double s = ((signbit(A) != 0) != (signbit(e) != 0)) ? 1.0 : -1.0;"),
+    ("fit: sub-block weights all one", "W[j] = sw;", "W[j] = 1.0f;"),
+    ("fit: offsets fitted from the scales", "orc_fit_levels_pos(8, b, W, 63,", "orc_fit_levels_pos(8, a, W, 63,"),
     # error statistics
     ("stats: percentile rank rounded down", "const int64_t k = (95 * n + 99) / 100;",
      "const int64_t k = (95 * n) / 100;"),
@@ -103,7 +111,8 @@ MUTANTS = [
 
 
 PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py", "test_matmul_oracle_pins.py",
-             "test_weighting_oracle_pins.py", "test_stats_oracle_pins.py", "test_q8k_family_oracle_pins.py")
+             "test_weighting_oracle_pins.py", "test_stats_oracle_pins.py", "test_q8k_family_oracle_pins.py",
+             "test_subscale_fit_oracle_pins.py")
 
 
 def _pins_modules():
