@@ -98,6 +98,12 @@ def _setup(name, dev):
         out = torch.empty((11008, qrow.qr_row_bytes("q4_k", 4096)), dtype=torch.uint8, device=dev)
         return (lambda: qrow.qr_quantize_rows("q4_k", x, q, out=out),
                 x.numel() * 4 + q.numel() * 4 + out.numel(), x.numel())
+    if name == "q4_k_fit_11008x4096":
+        # the same matrix with the weighted fit of the 6-bit sub-scales
+        x, q = synth.torch_q4_k_matrix(dev)
+        out = torch.empty((11008, qrow.qr_row_bytes("q4_k", 4096)), dtype=torch.uint8, device=dev)
+        return (lambda: qrow.qr_quantize_rows_ex("q4_k", x, q, subscale_fit="weighted", out=out),
+                x.numel() * 4 + q.numel() * 4 + out.numel(), x.numel())
     if name == "q4_0_2048x2048":
         x, q = synth.q4_0_matrix()
         xd, qd = torch.from_numpy(x).to(dev), torch.from_numpy(q).to(dev)
@@ -235,7 +241,7 @@ ACT_WORKLOADS = ("q8_k64_8192x7168", "q8_k16_8192x7168")
 STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "copy_1gib", "mix_q4_k_m_stack_7b") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
+                  "moe_256x2048x7168", "copy_1gib", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -276,6 +282,22 @@ def activation_block_ablation(dev, flush):
         rows[act] = {"ms": round(ms, 5), "bytes_per_value": round(out.numel() / x.size, 4),
                      "rel_rmse": round(st["rel_rmse"], 6),
                      "product_rel_err": round(float(torch.linalg.norm(y - exact) / torch.linalg.norm(exact)), 6)}
+    return rows
+
+
+def subscale_fit_comparison(x, q, flush):
+    """The two choices of the Q4_K 6-bit sub-scales on the Q4_K matrix:
+    quantization time and the error statistics of each output."""
+    from post_weight_quantization_row_amd import qrow
+    rows = {}
+    for fit in qrow.FITS:
+        out = qrow.qr_quantize_rows_ex("q4_k", x, q, subscale_fit=fit)
+        ms, _, _ = timed_steps(lambda: qrow.qr_quantize_rows_ex("q4_k", x, q, subscale_fit=fit, out=out), 5, 1,
+                               flush)
+        st = qrow.qr_quantize_stats("q4_k", x, out, q)
+        rows[fit] = {"ms": round(ms, 5), "rel_rmse": round(st["rel_rmse"], 6),
+                     "weighted_rel_rmse": round(st["weighted_rel_rmse"], 6),
+                     "max_abs_err": st["max_abs_err"], "p95_abs_err": st["p95_abs_err"]}
     return rows
 
 
@@ -430,6 +452,7 @@ def main():
                            "GB/s": round(nb / (mi * 1e-3) / 1e9, 1),
                            "hbm_frac": round(nb / (mi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         extra["weighting_ablation_q4_k_11008x4096"] = weighting_ablation(x, q, flush)
+        extra["subscale_fit_q4_k_11008x4096"] = subscale_fit_comparison(x, q, flush)
         extra["mix_q4_k_m_stack_7b"] = mix_stack_entry(dev, flush)
         extra["activation_block_ablation_calib_8192x7168"] = activation_block_ablation(dev, flush)
         result["extra"] = extra

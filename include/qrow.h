@@ -147,6 +147,35 @@ int qr_quantize_rows_weighted(int t, int src, const void *x,
                               int64_t n_per_row, int weighting, void *out,
                               void *stream);
 
+/* How the Q4_K 6-bit sub-scales and sub-offsets are chosen (types without
+ * sub-scales ignore it). */
+typedef enum {
+    QR_FIT_MAX = 0,       /* d = fp16(max a_j / 63), sc_j = rint(a_j / d): the default */
+    QR_FIT_WEIGHTED = 1   /* weighted least-squares fit of the eight values */
+} qr_subscale_fit;
+
+/*
+ * qr_quantize_rows_ex -- the row quantizer with every option: grouped
+ * importances (as qr_quantize_rows_grouped), a weighting (as
+ * qr_quantize_rows_weighted) and the Q4_K sub-scale fit. [KQ 一] fixes eight
+ * 6-bit sub-scales and sub-offsets under fp16 super-scales but not how they
+ * are chosen. With QR_FIT_WEIGHTED the sub-blocks' least-squares scales a_j
+ * (and offsets b_j) are fitted as a_j ~ d * sc_j, sc_j in 0..63, by the
+ * weighted least squares with trial scales and greedy flips of [WT 一],
+ * each sub-block weighted by the sum of its 32 importances: trial scales
+ * put the largest value on 63 + 0.25k (k = 0, -1, +1, -2, +2), levels are
+ * rounded in float, the sums, comparisons and flips are evaluated in double
+ * and d = sumlx/suml2 is stored as fp16 (sub-scales 0 if that is 0). The
+ * element codes are then re-rounded against the stored scales as in the
+ * default. Errors as qr_quantize_rows_grouped, and QR_EINVAL_TYPE for an
+ * unknown weighting or subscale_fit. The default choices (QR_W_SQRT_SIGMA2_X2,
+ * QR_FIT_MAX) give the bytes of qr_quantize_rows_grouped.
+ */
+int qr_quantize_rows_ex(int t, int src, const void *x, const float *imatrix,
+                        int64_t n_groups, int64_t rows_per_group,
+                        int64_t n_per_row, int weighting, int subscale_fit,
+                        void *out, void *stream);
+
 /*
  * qr_quantize_activations_q8k128 -- the Q8_K_128 activation quantizer
  * [Q8 修复方案]. Per 128 values: amax = max |x|; codes q = rint(x * (127/amax))

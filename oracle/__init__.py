@@ -113,6 +113,7 @@ def _load(path):
     L.orc_quantize_q8k.argtypes = [C.c_int, vp, i64, i64, vp]
     L.orc_fit_levels_pos.argtypes = [C.c_int, f32p, f32p, C.c_int, C.c_int, C.c_int, u8p, f32p, i32p]
     L.orc_quantize_rows_ex.argtypes = [C.c_int, vp, vp, i64, i64, i64, C.c_int, C.c_int, vp]
+    L.orc_quantize_row_sigma2_ex.argtypes = [C.c_int, f32p, vp, i64, C.c_float, C.c_int, C.c_int, u8p]
     L.orc_row_weights_mode.argtypes = [f32p, vp, i64, C.c_float, C.c_int, f32p]
     L.orc_quantize_rows_weighted.argtypes = [C.c_int, vp, vp, i64, i64, C.c_int, vp]
     L.orc_quantize_row_sigma2_mode.argtypes = [C.c_int, f32p, vp, i64, C.c_float,
@@ -294,6 +295,18 @@ def quantize_rows_ex(t, x, imatrix=None, mode=0, fit="max", threads: int = 1) ->
                     raise ValueError("orc_quantize_rows_ex failed")
 
         _rows_parallel(rpg, run, threads)
+    return out
+
+
+def quantize_row_sigma2_ex(t, x, q, sigma2, mode=0, fit="max") -> np.ndarray:
+    t = _tid(t)
+    x = _f32(x).ravel()
+    qq = None if q is None else _f32(q)
+    out = np.zeros(row_bytes(t, x.size), np.uint8)
+    f = FITS[fit] if isinstance(fit, str) else int(fit)
+    rc = lib().orc_quantize_row_sigma2_ex(t, x, _ptr(qq), x.size, np.float32(sigma2), _wid(mode), f, out)
+    if rc != 0:
+        raise ValueError("orc_quantize_row_sigma2_ex failed")
     return out
 
 

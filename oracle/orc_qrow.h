@@ -128,6 +128,10 @@ enum {
  * weights W_j: K trial scales, F flip passes (the sub-scale fit). */
 int orc_fit_levels_pos(int n, const float *v, const float *W, int nmax, int K,
                        int F, uint8_t *l_out, float *d_out, int32_t *info);
+/* One row with the row statistic supplied, a weighting and a sub-scale fit. */
+int orc_quantize_row_sigma2_ex(int type, const float *x, const float *q,
+                               int64_t n_per_row, float sigma2, int mode,
+                               int fit, uint8_t *out);
 /* Grouped rows with a weighting and a sub-scale fit. */
 int orc_quantize_rows_ex(int type, const float *x, const float *imatrix,
                          int64_t n_groups, int64_t rows_per_group,

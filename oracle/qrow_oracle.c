@@ -741,17 +741,26 @@ static int weight_type_ok(int type)
            type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0;
 }
 
+int orc_quantize_row_sigma2_ex(int type, const float *x, const float *q,
+                               int64_t n_per_row, float sigma2, int mode,
+                               int fit, uint8_t *out)
+{
+    if (!weight_type_ok(type) || orc_row_bytes(type, n_per_row) == 0 ||
+        mode < 0 || mode > ORC_W_IMATRIX_ONLY ||
+        (fit != ORC_FIT_MAX && fit != ORC_FIT_WEIGHTED)) return ORC_EINVAL;
+    float *w = (float *)malloc(sizeof(float) * (size_t)n_per_row);
+    if (!w) return ORC_EINVAL;
+    int rc = quantize_row_impl(type, x, q, n_per_row, sigma2, mode, fit, w, out);
+    free(w);
+    return rc;
+}
+
 int orc_quantize_row_sigma2_mode(int type, const float *x, const float *q,
                                  int64_t n_per_row, float sigma2, int mode,
                                  uint8_t *out)
 {
-    if (!weight_type_ok(type) || orc_row_bytes(type, n_per_row) == 0 ||
-        mode < 0 || mode > ORC_W_IMATRIX_ONLY) return ORC_EINVAL;
-    float *w = (float *)malloc(sizeof(float) * (size_t)n_per_row);
-    if (!w) return ORC_EINVAL;
-    int rc = quantize_row_impl(type, x, q, n_per_row, sigma2, mode, ORC_FIT_MAX, w, out);
-    free(w);
-    return rc;
+    return orc_quantize_row_sigma2_ex(type, x, q, n_per_row, sigma2, mode,
+                                      ORC_FIT_MAX, out);
 }
 
 int orc_quantize_row_sigma2(int type, const float *x, const float *q,

@@ -388,7 +388,7 @@ __device__ __forceinline__ void fit_dm(float Sw_, float Sx_, float Sl_, float Sl
 // (w: importances; x: overwritten).
 template <int NMAX, bool K4, bool BF16, bool VAR>
 __device__ __forceinline__ void solve_asym(const void* lds, int g, const float* __restrict__ q, const RowImp& imp,
-                                           float (&L)[QK], float& d_out, float& m_out) {
+                                           float (&L)[QK], float& d_out, float& m_out, float& sw_out) {
   constexpr float HI = (float)NMAX;
   float x[QK], w[QK];
   load_group<BF16>(lds, g, x);
@@ -408,6 +408,7 @@ __device__ __forceinline__ void solve_asym(const void* lds, int g, const float* 
   lo = lo + 0.0f;   // a zero bound is +0 whichever zero min/max returned
   hi = hi + 0.0f;
   if (K4) lo = fminf(lo, 0.0f);
+  sw_out = Sw;      // the group's total importance (after any fallback)
 
   if (hi == lo || !(Sw > 0.0f)) {   // constant group, or importances that underflow to 0
 #pragma unroll
@@ -481,6 +482,73 @@ __device__ __forceinline__ void solve_asym(const void* lds, int g, const float* 
 }
 
 // -------------------------------------------------------------------------
+// weighted fit of the eight Q4_K sub-scales (or sub-offsets) [WT 一 applied
+// to the values of a super-block]: v_j ~ d * l_j, l_j in 0..63, weights W_j.
+// Trial scales map the largest value to 63 + step*k; levels are rounded in
+// float; the sums, the score comparisons and the flips run in double (one
+// sub-block can carry most of the weight, and the fit's error is then a
+// small difference of large scores); d = sumlx/suml2 rounded to float.
+
+__device__ __forceinline__ void fit_levels_pos8(const float (&v)[8], const float (&W)[8], float (&L)[8],
+                                                float& d_out) {
+  float vmax = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) vmax = fmaxf(vmax, v[i]);
+  double Wv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Wv[i] = (double)W[i] * (double)v[i];   // exact
+  bool have = false;
+  double bS1 = 0.0, bS2 = 0.0;
+  float bis = 0.0f;
+  if (vmax > 0.0f) {
+#pragma unroll
+    for (int k = 0; k < SYM_CAND; ++k) {
+      const float c = 63.0f + CAND_STEP * (float)cand_offset(k);
+      const float is = c / vmax;
+      double S1 = 0.0, S2 = 0.0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double l = (double)med3(rne(v[i] * is), 0.0f, 63.0f);
+        S1 = __builtin_fma(Wv[i], l, S1);
+        S2 = __builtin_fma((double)W[i] * l, l, S2);
+      }
+      const bool ok = __builtin_isfinite(is) && (S2 > 0.0);
+      if (ok && (!have || (S1 * S1) * bS2 > (bS1 * bS1) * S2)) {
+        have = true; bS1 = S1; bS2 = S2; bis = is;
+      }
+    }
+  }
+  if (!have) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) L[i] = 0.0f;
+    d_out = 0.0f;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) L[i] = med3(rne(v[i] * bis), 0.0f, 63.0f);
+  double A = bS1, B = bS2;
+#pragma unroll 1
+  for (int p = 0; p < SYM_FLIP_PASSES; ++p) {
+    bool changed = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double e = __builtin_fma((double)v[j], B, -((double)L[j] * A));
+      const double sg = (__builtin_signbit(A) != __builtin_signbit(e)) ? -1.0 : 1.0;
+      const double lp = (double)L[j] + sg;
+      const double A1 = __builtin_fma(sg, Wv[j], A);
+      const double B1 = __builtin_fma((double)W[j], __builtin_fma(2.0 * sg, (double)L[j], 1.0), B);
+      const bool keep = ((A1 * A1) * B > (A * A) * B1) && (B1 > 0.0) && (lp >= 0.0) && (lp <= 63.0);
+      A = keep ? A1 : A;
+      B = keep ? B1 : B;
+      L[j] = keep ? (float)lp : L[j];
+      changed |= keep;
+    }
+    if (!changed) break;
+  }
+  d_out = (float)(A / B);
+}
+
+// -------------------------------------------------------------------------
 // packers
 
 // 32 codes in [0, 15] -> 16 bytes: byte i = u_i | u_{i+16} << 4.
@@ -536,7 +604,8 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
                                                                         const float* __restrict__ imatrix,
                                                                         int n_per_row, int64_t rows_per_group,
                                                                         uint8_t* __restrict__ out,
-                                                                        int64_t row_bytes, int weighting) {
+                                                                        int64_t row_bytes, int weighting,
+                                                                        int fit) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
@@ -609,7 +678,8 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
     } else if constexpr (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
       constexpr int NMAX = TYPE == QR_Q4_1 ? 15 : 31;
       float d, m;
-      solve_asym<NMAX, false, BF16, VAR>(lds_raw, g, qg, imp, L, d, m);
+      float sw;
+      solve_asym<NMAX, false, BF16, VAR>(lds_raw, g, qg, imp, L, d, m, sw);
       if constexpr (TYPE == QR_Q4_1) {
         const uint4 qs = pack_nibbles_f(L);
         uint8_t* p = orow + (size_t)g * 24;
@@ -626,21 +696,55 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
         store_u32(p + 12, qs.x); store_u32(p + 16, qs.y); store_u32(p + 20, qs.z); store_u32(p + 24, qs.w);
       }
     } else {  // QR_Q4_K: lanes 8s .. 8s+7 hold the sub-blocks of one super-block [KQ 一]
-      float d, m;
-      solve_asym<15, true, BF16, VAR>(lds_raw, g, qg, imp, L, d, m);
+      float d, m, sw;
+      solve_asym<15, true, BF16, VAR>(lds_raw, g, qg, imp, L, d, m, sw);
       const float a = d > 0.0f ? d : 0.0f;
       const float b = -m > 0.0f ? -m : 0.0f;
-      float A = a, Bm = b;
+      const int j = g & 7;
+      _Float16 d16, m16;
+      float sc, mn;
+      if (VAR && fit == QR_FIT_WEIGHTED) {
+        // lanes 0-3 of the super-block fit the eight scales, lanes 4-7 the
+        // eight offsets (the same instructions on other data); lanes 0 and
+        // 4 then hand out their levels, four to a word, and their scales
+        const bool offs = (j & 4) != 0;
+        float vv[8], wv[8], lv[8], dv;
 #pragma unroll
-      for (int off = 1; off < 8; off <<= 1) {
-        A = fmaxf(A, __shfl_xor(A, off, 8));
-        Bm = fmaxf(Bm, __shfl_xor(Bm, off, 8));
+        for (int k = 0; k < 8; ++k) {
+          const float ak = __shfl(a, k, 8), bk = __shfl(b, k, 8);
+          vv[k] = offs ? bk : ak;
+          wv[k] = __shfl(sw, k, 8);
+        }
+        fit_levels_pos8(vv, wv, lv, dv);
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          w0 |= (uint32_t)lv[k] << (8 * k);
+          w1 |= (uint32_t)lv[4 + k] << (8 * k);
+        }
+        const uint32_t sw0 = __shfl(w0, 0, 8), sw1 = __shfl(w1, 0, 8);
+        const uint32_t mw0 = __shfl(w0, 4, 8), mw1 = __shfl(w1, 4, 8);
+        const float da = __shfl(dv, 0, 8), db = __shfl(dv, 4, 8);
+        d16 = (_Float16)da;
+        m16 = (_Float16)db;
+        sc = (float)(((j < 4 ? sw0 : sw1) >> (8 * (j & 3))) & 255u);
+        mn = (float)(((j < 4 ? mw0 : mw1) >> (8 * (j & 3))) & 255u);
+        if ((float)d16 == 0.0f) sc = 0.0f;
+        if ((float)m16 == 0.0f) mn = 0.0f;
+      } else {
+        float A = a, Bm = b;
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+          A = fmaxf(A, __shfl_xor(A, off, 8));
+          Bm = fmaxf(Bm, __shfl_xor(Bm, off, 8));
+        }
+        d16 = (_Float16)(A / 63.0f);
+        m16 = (_Float16)(Bm / 63.0f);
+        const float dA0 = (float)d16, dB0 = (float)m16;
+        sc = dA0 > 0.0f ? med3(rne(a / dA0), 0.0f, 63.0f) : 0.0f;
+        mn = dB0 > 0.0f ? med3(rne(b / dB0), 0.0f, 63.0f) : 0.0f;
       }
-      const _Float16 d16 = (_Float16)(A / 63.0f);
-      const _Float16 m16 = (_Float16)(Bm / 63.0f);
       const float dA = (float)d16, dB = (float)m16;
-      const float sc = dA > 0.0f ? med3(rne(a / dA), 0.0f, 63.0f) : 0.0f;
-      const float mn = dB > 0.0f ? med3(rne(b / dB), 0.0f, 63.0f) : 0.0f;
       const float ds = dA * sc, dm = dB * mn;
       float u[QK];
       if (ds == 0.0f) {
@@ -653,7 +757,6 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
         for (int i = 0; i < QK; ++i) u[i] = med3(rne((u[i] + dm) * id), 0.0f, 15.0f);
       }
       const uint4 qs = pack_nibbles_f(u);
-      const int j = g & 7;
       uint64_t scb = (uint64_t)(uint32_t)sc << (6 * j);
       uint64_t mnb = (uint64_t)(uint32_t)mn << (6 * j);
 #pragma unroll
@@ -968,7 +1071,7 @@ bool aligned16(const void* p) { return qr_aligned(p, 16); }
 
 template <int TYPE, bool BF16, bool VAR>
 int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_row, int64_t rows_per_group,
-                void* out, size_t row_bytes, int weighting, hipStream_t stream) {
+                void* out, size_t row_bytes, int weighting, int fit, hipStream_t stream) {
   auto kern = k_quantize_rows<TYPE, BF16, VAR>;
   const int n_groups = n_per_row / QK;
   int waves = (n_groups + WAVE - 1) / WAVE;
@@ -982,15 +1085,15 @@ int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_r
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE * waves), lds, stream, x, imatrix, n_per_row,
-                     rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes, weighting);
+                     rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes, weighting, fit);
   return qr_check_launch("k_quantize_rows");
 }
 
 template <bool BF16, bool VAR>
 int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, int n_per_row,
-                  int64_t rows_per_group, void* out, size_t row_bytes, int weighting, hipStream_t s) {
+                  int64_t rows_per_group, void* out, size_t row_bytes, int weighting, int fit, hipStream_t s) {
 #define QR_ROWS_LAUNCH(T) \
-  launch_rows<T, BF16, VAR>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, weighting, s)
+  launch_rows<T, BF16, VAR>(x, imatrix, n_rows, n_per_row, rows_per_group, out, row_bytes, weighting, fit, s)
   switch (t) {
     case QR_Q4_0: return QR_ROWS_LAUNCH(QR_Q4_0);
     case QR_Q4_1: return QR_ROWS_LAUNCH(QR_Q4_1);
@@ -1004,13 +1107,17 @@ int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, in
 }
 
 // Validation and launch shared by the row quantizers. The pages' weighting
-// runs in the kernels compiled for it alone; the others in the variants.
+// with the default sub-scales runs in the kernels compiled for it alone;
+// every other choice in the variants.
 int quantize_rows_common(int t, int src, const void* x, const float* imatrix, int64_t n_groups,
-                         int64_t rows_per_group, int64_t n_per_row, int weighting, void* out, void* stream) {
+                         int64_t rows_per_group, int64_t n_per_row, int weighting, int fit, void* out,
+                         void* stream) {
   if (!qr_is_weight_type(t)) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
   if (weighting < QR_W_SQRT_SIGMA2_X2 || weighting > QR_W_IMATRIX_ONLY)
     return qr_fail(QR_EINVAL_TYPE, "weighting %d is not a qr_weighting", weighting);
+  if (fit != QR_FIT_MAX && fit != QR_FIT_WEIGHTED)
+    return qr_fail(QR_EINVAL_TYPE, "subscale_fit %d is not a qr_subscale_fit", fit);
   if (n_groups < 0 || rows_per_group < 0) return qr_fail(QR_EINVAL_SHAPE, "negative row count");
   const int be = block_elems(t);
   const int64_t max_row = src == QR_F32 ? QR_MAX_ROW_F32 : QR_MAX_ROW_BF16;
@@ -1030,11 +1137,13 @@ int quantize_rows_common(int t, int src, const void* x, const float* imatrix, in
     return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int n = (int)n_per_row;
-  if (weighting == QR_W_SQRT_SIGMA2_X2)
-    return src == QR_F32 ? dispatch_rows<false, false>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, 0, s)
-                         : dispatch_rows<true, false>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, 0, s);
-  return src == QR_F32 ? dispatch_rows<false, true>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, weighting, s)
-                       : dispatch_rows<true, true>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, weighting, s);
+  if (t != QR_Q4_K) fit = QR_FIT_MAX;   // no sub-scales to fit
+  if (weighting == QR_W_SQRT_SIGMA2_X2 && fit == QR_FIT_MAX)
+    return src == QR_F32 ? dispatch_rows<false, false>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, 0, 0, s)
+                         : dispatch_rows<true, false>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, 0, 0, s);
+  return src == QR_F32
+             ? dispatch_rows<false, true>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, weighting, fit, s)
+             : dispatch_rows<true, true>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, weighting, fit, s);
 }
 
 int grid_for(int64_t work_items, int per_block) {
@@ -1088,15 +1197,23 @@ void qr_solver_constants(int32_t* c) {
 int qr_quantize_rows_grouped(int t, int src, const void* x, const float* imatrix, int64_t n_groups,
                              int64_t rows_per_group, int64_t n_per_row, void* out, void* stream) {
   qr_clear_error();
-  return quantize_rows_common(t, src, x, imatrix, n_groups, rows_per_group, n_per_row, QR_W_SQRT_SIGMA2_X2, out,
-                              stream);
+  return quantize_rows_common(t, src, x, imatrix, n_groups, rows_per_group, n_per_row, QR_W_SQRT_SIGMA2_X2,
+                              QR_FIT_MAX, out, stream);
+}
+
+int qr_quantize_rows_ex(int t, int src, const void* x, const float* imatrix, int64_t n_groups,
+                        int64_t rows_per_group, int64_t n_per_row, int weighting, int subscale_fit, void* out,
+                        void* stream) {
+  qr_clear_error();
+  return quantize_rows_common(t, src, x, imatrix, n_groups, rows_per_group, n_per_row, weighting, subscale_fit,
+                              out, stream);
 }
 
 int qr_quantize_rows_weighted(int t, int src, const void* x, const float* imatrix, int64_t n_rows,
                               int64_t n_per_row, int weighting, void* out, void* stream) {
   qr_clear_error();
   if (n_rows < 0) return qr_fail(QR_EINVAL_SHAPE, "negative row count");
-  return quantize_rows_common(t, src, x, imatrix, 1, n_rows, n_per_row, weighting, out, stream);
+  return quantize_rows_common(t, src, x, imatrix, 1, n_rows, n_per_row, weighting, QR_FIT_MAX, out, stream);
 }
 
 int qr_quantize_rows(int t, int src, const void* x, const float* imatrix, int64_t n_rows, int64_t n_per_row,

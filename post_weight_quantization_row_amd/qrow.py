@@ -27,6 +27,7 @@ TYPES = {"q4_0": QR_Q4_0, "q4_1": QR_Q4_1, "q5_0": QR_Q5_0, "q5_1": QR_Q5_1,
          "q4_k": QR_Q4_K, "q8_k128": QR_Q8_K128, "q6_0": QR_Q6_0,
          "q8_k64": QR_Q8_K64, "q8_k16": QR_Q8_K16}
 ACT_TYPES = ("q8_k128", "q8_k64", "q8_k16")
+FITS = {"max": 0, "weighted": 1}   # qr_subscale_fit
 ERRORS = {-1: "QR_EINVAL_TYPE", -2: "QR_EINVAL_SHAPE", -3: "QR_EINVAL_PTR",
           -4: "QR_EOVERFLOW", -5: "QR_EDEVICE"}
 
@@ -38,7 +39,8 @@ EXPORTS = ("qr_quantize_rows", "qr_quantize_rows_grouped",
            "qr_imatrix_accumulate", "qr_imatrix_merge",
            "qr_imatrix_finalize", "qr_matmul_q8k128",
            "qr_quantize_rows_weighted", "qr_stats_workspace_bytes",
-           "qr_quantize_stats", "qr_quantize_activations_q8k", "qr_matmul_q8k")
+           "qr_quantize_stats", "qr_quantize_activations_q8k", "qr_matmul_q8k",
+           "qr_quantize_rows_ex")
 IMX_MAX_EXPERTS, IMX_MAX_TOP_K = 1024, 64
 
 
@@ -81,6 +83,7 @@ def load_library(path: str = LIB_PATH):
         L.qr_matmul_q8k.argtypes = [i32, i32, vp, vp, i64, i64, i64, vp, vp]
         L.qr_quantize_activations_q8k.argtypes = [i32, i32, vp, i64, i64, vp, vp]
         L.qr_quantize_rows_weighted.argtypes = [i32, i32, vp, vp, i64, i64, i32, vp, vp]
+        L.qr_quantize_rows_ex.argtypes = [i32, i32, vp, vp, i64, i64, i64, i32, i32, vp, vp]
         L.qr_stats_workspace_bytes.argtypes = [i64, i64]
         L.qr_stats_workspace_bytes.restype = C.c_size_t
         L.qr_quantize_stats.argtypes = [i32, i32, vp, vp, vp, i64, i64, vp, vp, C.c_size_t, vp]
@@ -211,6 +214,38 @@ def qr_quantize_rows_grouped(t, x: torch.Tensor, imatrix, rows_per_group: int,
         tid, _src_dtype(x), C.c_void_p(x.data_ptr()),
         None if q is None else C.c_void_p(q.data_ptr()), n_groups,
         rows_per_group, n, C.c_void_p(out.data_ptr()), _stream(x, stream)))
+    return out
+
+
+def qr_quantize_rows_ex(t, x: torch.Tensor, imatrix=None, rows_per_group=None, weighting=0,
+                        subscale_fit="max", out=None, stream=None):
+    """Every option of the row quantizer: imatrix is None, [n] or
+    [n_groups, n] (rows_per_group = n_rows / n_groups when not given);
+    weighting a name of WEIGHTINGS or its number; subscale_fit "max" or
+    "weighted" (Q4_K sub-scales)."""
+    _dev2d(x, "x")
+    tid = _tid(t)
+    n_rows, n = x.shape
+    wid = WEIGHTINGS[weighting] if isinstance(weighting, str) else int(weighting)
+    fid = FITS[subscale_fit] if isinstance(subscale_fit, str) else int(subscale_fit)
+    q = None
+    n_groups = 1
+    if imatrix is not None:
+        if imatrix.dtype != torch.float32 or not imatrix.is_cuda or imatrix.numel() % n:
+            raise ValueError("imatrix must be a CUDA float32 tensor of whole rows of n_per_row")
+        q = imatrix.contiguous()
+        n_groups = q.numel() // n
+    if rows_per_group is None:
+        if n_rows % n_groups:
+            raise ValueError("the imatrix groups do not divide the rows")
+        rows_per_group = n_rows // n_groups
+    if n_groups * rows_per_group != n_rows:
+        raise ValueError("n_groups * rows_per_group must equal n_rows")
+    out = _out(out, (n_rows, qr_row_bytes(tid, n)), torch.uint8, x.device)
+    _check(load_library().qr_quantize_rows_ex(
+        tid, _src_dtype(x), C.c_void_p(x.data_ptr()),
+        None if q is None else C.c_void_p(q.data_ptr()), n_groups, rows_per_group, n, wid, fid,
+        C.c_void_p(out.data_ptr()), _stream(x, stream)))
     return out
 
 

@@ -32,7 +32,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(HEADERS) == 4 and len(names) == 18
+    assert len(HEADERS) == 4 and len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(qrow.EXPORTS) == names
@@ -178,6 +178,21 @@ def test_q8k_family_argument_validation_without_a_gpu(lib):
     assert mm(4, 8, fake, fake, 4, 2, 128, fake, None) == -2    # Q4_K needs 256
     assert mm(0, 8, None, None, 0, 2, 64, None, None) == 0      # empty: no-op
     assert mm(0, 8, None, fake, 4, 2, 64, fake, None) == -3
+
+
+def test_quantize_rows_ex_validation_without_a_gpu(lib):
+    assert qrow.FITS == oracle.FITS
+    fake = C.c_void_p(0x10000)
+    ex = lib.qr_quantize_rows_ex
+    assert ex(4, 0, fake, None, 1, 4, 256, 0, 2, fake, None) == -1      # unknown fit
+    assert "subscale_fit" in qrow.qr_last_error()
+    assert ex(4, 0, fake, None, 1, 4, 256, 6, 1, fake, None) == -1      # unknown weighting
+    assert ex(5, 0, fake, None, 1, 4, 256, 0, 1, fake, None) == -1      # not a weight type
+    assert ex(4, 0, fake, None, 1, 4, 128, 0, 1, fake, None) == -2      # Q4_K needs 256
+    assert ex(4, 0, fake, None, -1, 4, 256, 0, 1, fake, None) == -2
+    assert ex(4, 0, None, None, 0, 4, 256, 0, 1, None, None) == 0       # no rows
+    assert ex(4, 0, None, None, 1, 4, 256, 0, 1, fake, None) == -3
+    assert ex(4, 0, fake, None, 2 ** 40, 2 ** 40, 256, 0, 1, fake, None) == -4
 
 
 def test_weighting_enum_agrees_with_the_oracle_and_is_validated(lib):

@@ -1,0 +1,122 @@
+"""GPU parity of the weighted Q4_K sub-scale fit (qr_quantize_rows_ex with
+QR_FIT_WEIGHTED) against the CPU oracle, through the C-ABI.
+
+Bar: byte-identical packed rows, as for the default Q4_K; the one tolerated
+difference is a row whose double sum of x^2 lies at a float rounding
+midpoint, which must then equal the oracle run with the neighbouring
+sigma2 under the same options.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from post_weight_quantization_row_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def qr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from post_weight_quantization_row_amd import qrow
+    qrow.load_library()
+    return qrow
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(x, bf16):
+    if bf16:
+        return torch.from_numpy(synth.f32_to_bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, F32)).cuda()
+
+
+def sigma2_ambiguous(row):
+    s64 = oracle.row_sigma2_f64(row)
+    s32 = F32(s64)
+    for nb in (np.nextafter(s32, F32(np.inf)), np.nextafter(s32, F32(-np.inf))):
+        if abs((float(s32) + float(nb)) / 2 - s64) <= 1e-11 * abs(s64):
+            return True
+    return False
+
+
+def assert_rows_equal(gpu, ref, x, q_of_row, mode, fit):
+    for r in np.nonzero((gpu != ref).any(axis=1))[0]:
+        ok = False
+        if sigma2_ambiguous(x[r]):
+            s32 = F32(oracle.row_sigma2_f64(x[r]))
+            for s in (np.nextafter(s32, F32(np.inf)), np.nextafter(s32, F32(-np.inf))):
+                ok |= np.array_equal(gpu[r], oracle.quantize_row_sigma2_ex("q4_k", x[r], q_of_row(r), s,
+                                                                           mode, fit))
+        assert ok, f"row {r} differs at bytes {np.nonzero(gpu[r] != ref[r])[0][:16]}"
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("with_q", [True, False])
+@pytest.mark.parametrize("n_rows,n", [(1, 256), (7, 1024), (33, 4096), (3, 11008 // 256 * 256), (2, 16384)])
+def test_weighted_fit_rows(qr, bf16, with_q, n_rows, n):
+    say(f"q4_k weighted fit bf16={bf16} q={with_q} ({n_rows},{n})")
+    x, q = synth.q4_k_matrix(n_rows, n, seed=700 + n_rows + n)
+    if bf16:
+        x = synth.round_to_bf16(x)
+    q = q if with_q else None
+    got = qr.qr_quantize_rows_ex("q4_k", to_dev(x, bf16), None if q is None else torch.from_numpy(q).cuda(),
+                                 subscale_fit="weighted").cpu().numpy()
+    ref = oracle.quantize_rows_ex("q4_k", x, q, fit="weighted")
+    assert_rows_equal(got, ref, x, lambda r: q, 0, "weighted")
+
+
+@pytest.mark.parametrize("mode", ["x2", "abs_x", "imatrix_only"])
+def test_weighted_fit_with_other_weightings(qr, mode):
+    x, q = synth.q4_k_matrix(16, 2048, seed=710)
+    got = qr.qr_quantize_rows_ex("q4_k", to_dev(x, False), torch.from_numpy(q).cuda(), weighting=mode,
+                                 subscale_fit="weighted").cpu().numpy()
+    ref = oracle.quantize_rows_ex("q4_k", x, q, mode=mode, fit="weighted")
+    assert_rows_equal(got, ref, x, lambda r: q, mode, "weighted")
+
+
+def test_weighted_fit_grouped(qr):
+    # a stack of 6 experts x 8 rows, each expert with its own importances
+    x, _ = synth.q4_k_matrix(48, 1024, seed=720)
+    q = np.exp(np.random.default_rng(721).standard_normal((6, 1024))).astype(F32)
+    got = qr.qr_quantize_rows_ex("q4_k", to_dev(x, False), torch.from_numpy(q).cuda(),
+                                 subscale_fit="weighted").cpu().numpy()
+    ref = oracle.quantize_rows_ex("q4_k", x, q, fit="weighted")
+    assert_rows_equal(got, ref, x, lambda r: q[r // 8], 0, "weighted")
+
+
+def test_degenerate_rows(qr):
+    x = np.zeros((4, 512), F32)
+    x[1, :256] = 1.0                              # constant super-block
+    x[2, ::7] = F32(1e-30)                        # tiny values, fp16 scales underflow
+    x[3, 300] = 5.0                               # a single spike
+    q = np.ones(512, F32)
+    q[:32] = 0.0                                  # one sub-block with no importance
+    got = qr.qr_quantize_rows_ex("q4_k", to_dev(x, False), torch.from_numpy(q).cuda(),
+                                 subscale_fit="weighted").cpu().numpy()
+    assert np.array_equal(got, oracle.quantize_rows_ex("q4_k", x, q, fit="weighted"))
+
+
+def test_default_options_match_the_other_entry_points(qr):
+    x, q = synth.q4_k_matrix(20, 4096, seed=730)
+    xd, qd = to_dev(x, False), torch.from_numpy(q).cuda()
+    a = qr.qr_quantize_rows_ex("q4_k", xd, qd)
+    assert torch.equal(a, qr.qr_quantize_rows("q4_k", xd, qd))
+    b = qr.qr_quantize_rows_ex("q4_0", xd, qd, weighting="x2", subscale_fit="weighted")
+    assert torch.equal(b, qr.qr_quantize_rows_weighted("q4_0", xd, qd, "x2"))   # no sub-scales: fit ignored
+
+
+def test_full_size_q4_k(qr):
+    x, q = synth.q4_k_matrix()
+    say("full size q4_k weighted fit")
+    got = qr.qr_quantize_rows_ex("q4_k", to_dev(x, False), torch.from_numpy(q).cuda(),
+                                 subscale_fit="weighted").cpu().numpy()
+    rows = np.r_[0:64, 5000:5064, 10944:11008]
+    ref = oracle.quantize_rows_ex("q4_k", x[rows], q, fit="weighted")
+    assert_rows_equal(got[rows], ref, x[rows], lambda r: q, 0, "weighted")
