@@ -15,7 +15,8 @@
  *
  * The product is defined plainly: y[t][r] = sum_i w[r][i] * a[t][i], with w
  * and a the exact values the packed blocks encode (Q4_0: d*(u-8); Q5_0:
- * d*(u-16); Q4_1, Q5_1: d*u + m; Q4_K: (d*sc_j)*u - dmin*mn_j; Q8_K_128 and
+ * d*(u-16); Q4_1, Q5_1: d*u + m; Q4_K: (d*sc_j)*u - dmin*mn_j; Q6_K:
+ * (d*s_j)*(u-32); Q8_K_128 and
  * its 64- and 16-value siblings: d*q), taken in double in ascending i. Each part is exact in double; only
  * the products and the sum round. The oracle also returns
  * S = sum_i (|scale part| + |offset part|) * |a_i|, the magnitude that bounds
@@ -80,7 +81,15 @@ static void weight_parts(int type, const uint8_t *row, int64_t n, double *a,
         const uint8_t *p = row + blk * bb;
         for (int i = 0; i < be; ++i) {
             double av = 0.0, bv = 0.0;
-            if (type == ORC_Q4_K) {
+            if (type == ORC_Q6_K) {
+                const int g = i / 32, k = i % 32;
+                const uint8_t *qs = p + 20 + 16 * g;
+                int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);
+                u |= ((p[148 + 8 * g + k / 4] >> (2 * (k % 4))) & 3) << 4;
+                const double ds = rd_f16(p) * (double)(int8_t)p[4 + i / 16];
+                av = ds * u;
+                bv = ds * 32;
+            } else if (type == ORC_Q4_K) {
                 const int j = i / 32, k = i % 32;
                 const uint8_t *qs = p + 16 + 16 * j;
                 const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);
@@ -116,7 +125,8 @@ static void act_values(int act_type, const uint8_t *row, int64_t n, double *x)
 static int is_weight_type(int type)
 {
     return type == ORC_Q4_0 || type == ORC_Q4_1 || type == ORC_Q5_0 ||
-           type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0;
+           type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0 ||
+           type == ORC_Q6_K;
 }
 
 int orc_matmul_q8k128(int type, const uint8_t *w, const uint8_t *x,

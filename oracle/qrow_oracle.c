@@ -59,7 +59,7 @@ int orc_block_elems(int type)
 {
     switch (type) {
     case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0: case ORC_Q5_1: case ORC_Q6_0: return 32;
-    case ORC_Q4_K: return 256;
+    case ORC_Q4_K: case ORC_Q6_K: return 256;
     case ORC_Q8_K128: return 128;
     case ORC_Q8_K64: return 64;
     case ORC_Q8_K16: return 16;
@@ -79,6 +79,7 @@ size_t orc_block_bytes(int type)
     case ORC_Q6_0: return 4 + 8 + 16;        /* d, 2-bit plane, nibbles  */
     case ORC_Q8_K64: return 4 + 64 + 4;      /* d, int8 x64, int16 x2    */
     case ORC_Q8_K16: return 4 + 16 + 2 + 2;  /* d, int8 x16, int16, pad  */
+    case ORC_Q6_K: return 2 + 2 + 16 + 128 + 64; /* d16, pad, sc, nibbles, planes */
     default: return 0;
     }
 }
@@ -708,6 +709,53 @@ static void quantize_q4k(const float *x, const float *w, int fit, uint8_t *out)
     }
 }
 
+/* Q6_K super-block: the two-level scaling of [KQ 一] for 6-bit levels.
+ * Readings (the pages describe the K-quant structure through Q4_K and name
+ * the 6-bit tier without its layout): 256 weights in 16 sub-blocks of 16;
+ * each sub-block fitted by the symmetric routine [WT 一] on levels
+ * -32..31, giving a signed scale d_j; the super-scale d = fp16(max |d_j| /
+ * 127) (round to nearest even, subnormals kept); signed 8-bit sub-scales
+ * s_j = rint(d_j / d) clamped to -127..127 (0 when d is 0); the levels are
+ * then re-rounded against the stored scale d*s_j (exact in float) and
+ * stored as u = l + 32. Layout: f16 d | 2 zero bytes | i8 s[16] | nibbles
+ * of the eight 32-weight groups (16 B each, u_i low, u_{i+16} high) | the
+ * 2-bit planes of the eight groups (8 B each, bits 2i, 2i+1 = bits 4, 5 of
+ * u_i). */
+static void quantize_q6k(const float *x, const float *w, uint8_t *out)
+{
+    float dj[16];
+    for (int j = 0; j < 16; ++j) {
+        int8_t l[16];
+        orc_solve_sym(16, x + 16 * j, w + 16 * j, 32, ORC_SYM_CAND,
+                      ORC_SYM_FLIP_PASSES, l, &dj[j], NULL);
+    }
+    float amx = 0.0f;
+    for (int j = 0; j < 16; ++j) amx = fmaxf(amx, fabsf(dj[j]));
+    uint16_t d16 = orc_f32_to_f16(amx / 127.0f);
+    float dA = orc_f16_to_f32(d16);
+    int8_t sc[16];
+    for (int j = 0; j < 16; ++j)
+        sc[j] = dA > 0.0f ? (int8_t)clampf(rintf(dj[j] / dA), -127.0f, 127.0f) : 0;
+    uint8_t u[256];
+    for (int j = 0; j < 16; ++j) {
+        float ds = dA * (float)sc[j];   /* exact: 11-bit times 8-bit */
+        if (ds == 0.0f) {
+            memset(u + 16 * j, 32, 16);
+        } else {
+            float id = 1.0f / ds;
+            for (int i = 0; i < 16; ++i)
+                u[16 * j + i] = (uint8_t)(clampf(rintf(x[16 * j + i] * id), -32.0f, 31.0f) + 32.0f);
+        }
+    }
+    out[0] = (uint8_t)d16; out[1] = (uint8_t)(d16 >> 8);
+    out[2] = 0; out[3] = 0;
+    memcpy(out + 4, sc, 16);
+    for (int g = 0; g < 8; ++g) {
+        pack_nibbles32(u + 32 * g, out + 20 + 16 * g);
+        pack_plane2(u + 32 * g, out + 148 + 8 * g);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* row drivers                                                                */
 
@@ -730,6 +778,7 @@ static int quantize_row_impl(int type, const float *x, const float *q,
         const float *xb = x + ib * be;
         float *wb = w + ib * be;
         if (type == ORC_Q4_K) quantize_q4k(xb, wb, fit, out + ib * bb);
+        else if (type == ORC_Q6_K) quantize_q6k(xb, wb, out + ib * bb);
         else quantize_block32(type, xb, wb, out + ib * bb);
     }
     return ORC_OK;
@@ -738,7 +787,8 @@ static int quantize_row_impl(int type, const float *x, const float *q,
 static int weight_type_ok(int type)
 {
     return type == ORC_Q4_0 || type == ORC_Q4_1 || type == ORC_Q5_0 ||
-           type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0;
+           type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0 ||
+           type == ORC_Q6_K;
 }
 
 int orc_quantize_row_sigma2_ex(int type, const float *x, const float *q,
@@ -939,6 +989,20 @@ int orc_dequantize_rows(int type, const uint8_t *in, int64_t n_rows,
             case ORC_Q8_K128: case ORC_Q8_K64: case ORC_Q8_K16: {
                 float d = get_f32(p);
                 for (int i = 0; i < be; ++i) o[i] = d * (float)(int8_t)p[4 + i];
+                break;
+            }
+            case ORC_Q6_K: {
+                float dA = orc_f16_to_f32((uint16_t)(p[0] | (p[1] << 8)));
+                for (int g = 0; g < 8; ++g) {
+                    uint64_t plane = 0;
+                    for (int k = 0; k < 8; ++k) plane |= (uint64_t)p[148 + 8 * g + k] << (8 * k);
+                    unpack_nibbles32(p + 20 + 16 * g, u);
+                    for (int i = 0; i < 32; ++i) {
+                        int uu = u[i] | (int)(((plane >> (2 * i)) & 3) << 4);
+                        float ds = dA * (float)(int8_t)p[4 + 2 * g + i / 16];
+                        o[32 * g + i] = ds * (float)(uu - 32);
+                    }
+                }
                 break;
             }
             case ORC_Q6_0: {

@@ -100,6 +100,14 @@ MUTANTS = [
      "double s = ((signbit(A) != 0) != (signbit(e) != 0)) ? 1.0 : -1.0;"),
     ("fit: sub-block weights all one", "W[j] = sw;", "W[j] = 1.0f;"),
     ("fit: offsets fitted from the scales", "orc_fit_levels_pos(8, b, W, 63,", "orc_fit_levels_pos(8, a, W, 63,"),
+    # Q6_K super-block
+    ("q6k: super-scale over 128", "orc_f32_to_f16(amx / 127.0f)", "orc_f32_to_f16(amx / 128.0f)"),
+    ("q6k: sub-scale sign dropped", "(int8_t)clampf(rintf(dj[j] / dA), -127.0f, 127.0f)",
+     "(int8_t)clampf(rintf(fabsf(dj[j]) / dA), -127.0f, 127.0f)"),
+    ("q6k: level -32 clamped away", "clampf(rintf(x[16 * j + i] * id), -32.0f, 31.0f)",
+     "clampf(rintf(x[16 * j + i] * id), -31.0f, 31.0f)"),
+    ("q6k: decoder takes the group's first sub-scale", "(int8_t)p[4 + 2 * g + i / 16];", "(int8_t)p[4 + 2 * g];"),
+    ("matmul: Q6_K offset 31", "bv = ds * 32;", "bv = ds * 31;"),
     # error statistics
     ("stats: percentile rank rounded down", "const int64_t k = (95 * n + 99) / 100;",
      "const int64_t k = (95 * n) / 100;"),
@@ -112,7 +120,7 @@ MUTANTS = [
 
 PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py", "test_matmul_oracle_pins.py",
              "test_weighting_oracle_pins.py", "test_stats_oracle_pins.py", "test_q8k_family_oracle_pins.py",
-             "test_subscale_fit_oracle_pins.py")
+             "test_subscale_fit_oracle_pins.py", "test_q6k_oracle_pins.py")
 
 
 def _pins_modules():
@@ -145,6 +153,7 @@ def _pin_calls(mods):
         "test_block_bytes_by_hand": dict(t="q8_k16"),
         "test_error_within_half_a_step_of_the_block_maximum": dict(t="q8_k16"),
         "test_family_product_equals_library_matmul": dict(t="q4_1", act="q8_k16"),
+        "test_product_with_q6_k_weights": dict(act="q8_k16"),
     }
     calls = []
     for mod in mods:
