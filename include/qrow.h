@@ -43,6 +43,11 @@
  *  Q6_0  28 B: f32 d | u8 qh[8] | u8 qs[16]  levels -32..31,     u = l+32
  *     qs as above holds the low 4 bits; bits 2i and 2i+1 of the 64-bit
  *     little-endian qh are bits 4 and 5 of u_i.
+ *  Q6_K 212 B per 256: f16 d | 2 zero bytes | i8 s[16] | qs[8][16] | qh[8][8]
+ *     16 sub-blocks of 16 weights, levels -32..31 (u = l+32) decoding to
+ *     (f32(d)*s_j)*(u - 32); 32-weight group g uses qs[g] (nibbles as above:
+ *     the low nibbles are sub-block 2g, the high ones 2g+1) and the 2-bit
+ *     plane qh[g] as in Q6_0.
  *  Q4_K 144 B per 256: f16 d | f16 dmin | sc[8] as 6-bit fields in 6 B |
  *     mn[8] as 6-bit fields in 6 B | u8 qs[128]; field j sits at bit 6j;
  *     sub-block j (32 weights) uses qs[16j .. 16j+15] as above and decodes
@@ -71,7 +76,8 @@ typedef enum {
     QR_Q8_K128 = 5,
     QR_Q6_0 = 6,
     QR_Q8_K64 = 7,
-    QR_Q8_K16 = 8
+    QR_Q8_K16 = 8,
+    QR_Q6_K = 9
 } qr_type;
 
 typedef enum { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
@@ -104,8 +110,8 @@ typedef enum {
 /*
  * qr_quantize_rows -- importance-weighted quantization of weight rows [WT 一],
  * [KQ 一], [LQ 2.1].
- *  t        QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q6_0 or QR_Q4_K (else
- *           EINVAL_TYPE).
+ *  t        QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q6_0, QR_Q4_K or QR_Q6_K
+ *           (else EINVAL_TYPE).
  *  src      QR_F32 or QR_BF16: element type of x.
  *  x        [n_rows, n_per_row] weights, row-major.
  *  imatrix  [n_per_row] fp32 importances shared by all rows, or NULL for
@@ -117,7 +123,11 @@ typedef enum {
  * sub-block) is fitted by a trial-scale search, the weighted least-squares
  * scale (and offset), and greedy flip passes; Q4_K then quantizes the eight
  * sub-scales and offsets to 6 bits under fp16 super-scales and re-rounds the
- * levels. The results are bit-identical to the CPU oracle of this project.
+ * levels. Q6_K fits each 16-weight sub-block with the symmetric routine on
+ * levels -32..31, sets d = fp16(max |d_j| / 127) and s_j = rint(d_j / d)
+ * in -127..127, and re-rounds the levels against d*s_j ([KQ 一]'s two-level
+ * scaling at 6 bits; the layout is this library's). The results are
+ * bit-identical to the CPU oracle of this project.
  */
 int qr_quantize_rows(int t, int src, const void *x, const float *imatrix,
                      int64_t n_rows, int64_t n_per_row, void *out,

@@ -80,8 +80,9 @@ __device__ __forceinline__ float half_bits(uint32_t h) {
 // bytes (lo: elements 0..15, hi: 16..31) and the float parts of the decode.
 struct Group {
   uint32_t lo[4], hi[4];
-  float sa;  // scale part:  d (legacy) or d*sc (Q4_K)
+  float sa;  // scale part:  d (legacy), d*sc (Q4_K), d*s of the first 16 (Q6_K)
   float sb;  // offset part: the level offset 8/16 (symmetric), m (Q4_1/Q5_1) or dmin*mn (Q4_K)
+  float sa1; // Q6_K: d*s of the second 16 (its codes are signed levels, no offset)
 };
 
 // The packed bytes of one group as loaded (up to eight words), kept apart
@@ -93,7 +94,18 @@ struct RawGroup {
 template <int TYPE>
 __device__ __forceinline__ RawGroup load_raw(const uint8_t* __restrict__ row, int g) {
   RawGroup R;
-  if (TYPE == QR_Q4_K) {
+  if (TYPE == QR_Q6_K) {
+    // d | the sub-scale word | 16 nibble bytes | the 8-byte plane (212-byte
+    // blocks are only 4-byte aligned)
+    const uint8_t* sb = row + (int64_t)(g >> 3) * 212;
+    const int j = g & 7;
+    R.v[0] = ld32(sb);
+    R.v[1] = ld32(sb + 4 + 4 * (j >> 1));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) R.v[2 + k] = ld32(sb + 20 + 16 * j + 4 * k);
+    R.v[6] = ld32(sb + 148 + 8 * j);
+    R.v[7] = ld32(sb + 152 + 8 * j);
+  } else if (TYPE == QR_Q4_K) {
     const uint8_t* sb = row + (int64_t)(g >> 3) * 144;
     const u32x4 h = *reinterpret_cast<const u32x4*>(sb);
     const u32x4 c = *reinterpret_cast<const u32x4*>(sb + 16 + 16 * (g & 7));
@@ -153,6 +165,27 @@ __device__ __forceinline__ RawAct load_act(const uint8_t* __restrict__ xrow, int
 template <int TYPE>
 __device__ __forceinline__ Group unpack(const RawGroup& R, int g) {
   Group G;
+  G.sa1 = 0.0f;
+  if (TYPE == QR_Q6_K) {
+    // codes u = nibble | plane bits << 4, turned into signed levels u - 32:
+    // per byte, x = u ^ 32 sign-extended from bit 5
+    const int j = g & 7;
+    const float dA = half_bits(R.v[0]);
+    const uint32_t sw = R.v[1] >> (16 * (j & 1));
+    G.sa = dA * (float)(int)(int8_t)(uint8_t)(sw & 255u);
+    G.sa1 = dA * (float)(int)(int8_t)(uint8_t)((sw >> 8) & 255u);
+    G.sb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t wk = R.v[2 + k];
+      const uint32_t lo = (wk & 0x0f0f0f0fu) | (spread2((R.v[6] >> (8 * k)) & 255u) << 4);
+      const uint32_t hi = ((wk >> 4) & 0x0f0f0f0fu) | (spread2((R.v[7] >> (8 * k)) & 255u) << 4);
+      const uint32_t xl = lo ^ 0x20202020u, xh = hi ^ 0x20202020u;
+      G.lo[k] = xl | ((xl & 0x20202020u) * 6u);
+      G.hi[k] = xh | ((xh & 0x20202020u) * 6u);
+    }
+    return G;
+  }
   uint32_t qh = 0;
   int qs0;  // first word of the 16 code bytes
   if (TYPE == QR_Q4_K) {
@@ -367,7 +400,13 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k(const uint8_t* __res
         int ilo = 0, ihi = 0;
 #pragma unroll
         for (int c = 0; c < 4; ++c) ilo = __builtin_amdgcn_sdot4((int)G.lo[c], (int)a[c], ilo, false);
-        if (SPLIT) {
+        if (TYPE == QR_Q6_K) {
+          // signed levels: sum(l*q) per 16-weight half, each with its scale
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ihi = __builtin_amdgcn_sdot4((int)G.hi[c], (int)a[4 + c], ihi, false);
+          acc[t] = __builtin_fmaf(G.sa * da, (float)ilo, acc[t]);
+          acc[t] = __builtin_fmaf(G.sa1 * (SPLIT ? da1 : da), (float)ihi, acc[t]);
+        } else if (SPLIT) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) ihi = __builtin_amdgcn_sdot4((int)G.hi[c], (int)a[4 + c], ihi, false);
           acc[t] = add_term<TYPE>(G, ilo, bs, da, acc[t]);
@@ -425,6 +464,7 @@ int launch_act(int t, int tt, const uint8_t* w, const uint8_t* x, int64_t n_out,
     case QR_Q5_0: return launch_type<QR_Q5_0, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
     case QR_Q5_1: return launch_type<QR_Q5_1, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
     case QR_Q6_0: return launch_type<QR_Q6_0, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q6_K: return launch_type<QR_Q6_K, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
     default: return launch_type<QR_Q4_K, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
   }
 }
@@ -439,7 +479,7 @@ int qr_matmul_q8k(int t, int act, const void* w, const void* x, int64_t n_out, i
   if (!qr_is_weight_type(t)) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   if (act != QR_Q8_K128 && act != QR_Q8_K64 && act != QR_Q8_K16)
     return qr_fail(QR_EINVAL_TYPE, "activation type %d is not a Q8_K type", act);
-  const int64_t wb = t == QR_Q4_K ? 256 : 32;
+  const int64_t wb = (t == QR_Q4_K || t == QR_Q6_K) ? 256 : 32;
   const int64_t mult = wb > act_block(act) ? wb : act_block(act);
   if (n_in <= 0 || n_in % mult != 0 || n_in > QR_MATMUL_MAX_IN)
     return qr_fail(QR_EINVAL_SHAPE, "n_in=%lld must be a positive multiple of %lld and at most %d", (long long)n_in,

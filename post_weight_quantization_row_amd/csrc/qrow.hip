@@ -355,6 +355,75 @@ __device__ __forceinline__ float solve_sym(const void* lds, int g, const float* 
   return A / B;
 }
 
+// Symmetric fit of elements OFF .. OFF+N-1 of a group (the 16-weight
+// sub-blocks of Q6_K): the steps of solve_sym on that part alone, the
+// importances computed once for the whole group.
+template <int NMAX, int OFF, int N>
+__device__ __forceinline__ float sym_fit_part(const float (&x)[QK], const float (&w)[QK], const float (&wx)[QK],
+                                              float (&L)[QK]) {
+  constexpr float LO = (float)-NMAX, HI = (float)(NMAX - 1);
+  float xmax = x[OFF], xmin = x[OFF];
+#pragma unroll
+  for (int i = OFF + 1; i < OFF + N; ++i) { xmax = fmaxf(xmax, x[i]); xmin = fminf(xmin, x[i]); }
+  const float amax = fmaxf(xmax, -xmin);
+  float xm = (xmax > -xmin) ? xmax : xmin;
+  if (xmax == -xmin) {
+    xm = x[OFF + N - 1];
+#pragma unroll
+    for (int i = OFF + N - 2; i >= OFF; --i) xm = (fabsf(x[i]) == amax) ? x[i] : xm;
+  }
+  bool have = false;
+  float bS1 = 0.0f, bS2 = 0.0f, bis = 0.0f;
+  if (amax > 0.0f) {
+#pragma unroll
+    for (int k = 0; k < SYM_CAND; ++k) {
+      const float c = (float)NMAX + CAND_STEP * (float)cand_offset(k);
+      const float is = -c / xm;
+      float S1 = 0.0f, S2 = 0.0f;
+#pragma unroll
+      for (int i = OFF; i < OFF + N; ++i) {
+        const float l = med3(rne(x[i] * is), LO, HI);
+        S1 = fma_(wx[i], l, S1);
+        S2 = fma_(w[i] * l, l, S2);
+      }
+      const bool ok = __builtin_isfinite(is) && (S2 > 0.0f);
+      const bool better = ok && (!have || ((double)S1 * (double)S1) * (double)bS2 >
+                                              ((double)bS1 * (double)bS1) * (double)S2);
+      if (better) { have = true; bS1 = S1; bS2 = S2; bis = is; }
+    }
+  }
+  if (!have) {
+#pragma unroll
+    for (int i = OFF; i < OFF + N; ++i) L[i] = 0.0f;
+    return 0.0f;
+  }
+#pragma unroll
+  for (int i = OFF; i < OFF + N; ++i) L[i] = med3(rne(x[i] * bis), LO, HI);
+  float A = bS1, B = bS2;
+#pragma unroll 1
+  for (int p = 0; p < SYM_FLIP_PASSES; ++p) {
+    bool changed = false;
+#pragma unroll
+    for (int j = OFF; j < OFF + N; ++j) {
+      const float t = L[j] * A;
+      const float e = fma_(x[j], B, -t);
+      const uint32_t sg = (fbits(A) ^ fbits(e)) & 0x80000000u;
+      const float sv = __builtin_bit_cast(float, 0x3f800000u | sg);
+      const float s2 = __builtin_bit_cast(float, 0x40000000u | sg);
+      const float lp = L[j] + sv;
+      const float A1 = fma_(sv, wx[j], A);
+      const float B1 = fma_(w[j], fma_(s2, L[j], 1.0f), B);
+      const bool keep = ((A1 * A1) * B > (A * A) * B1) && (B1 > 0.0f) && (lp >= LO) && (lp <= HI);
+      A = keep ? A1 : A;
+      B = keep ? B1 : B;
+      L[j] = keep ? lp : L[j];
+      changed |= keep;
+    }
+    if (!__any(changed)) break;
+  }
+  return A / B;
+}
+
 // -------------------------------------------------------------------------
 // asymmetric group: levels 0 .. NMAX, x ~ d*l + m
 
@@ -638,7 +707,55 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
     const float* qg = q ? q + g * QK : nullptr;
     float L[QK];
 
-    if constexpr (TYPE == QR_Q6_0) {
+    if constexpr (TYPE == QR_Q6_K) {  // lanes 8s .. 8s+7: the eight 32-weight groups of a super-block
+      float x[QK], w[QK], wx[QK];
+      load_group<BF16>(lds_raw, g, x);
+      group_importances<VAR>(x, qg, imp, w);
+      {  // a group with no importance at all falls back to q = 1
+        uint32_t any = 0;
+#pragma unroll
+        for (int i = 0; i < QK; ++i) any |= fbits(w[i]) & 0x7fffffffu;
+        if (any == 0) group_importances<VAR>(x, nullptr, imp, w);
+      }
+#pragma unroll
+      for (int i = 0; i < QK; ++i) wx[i] = w[i] * x[i];
+      const float d0 = sym_fit_part<32, 0, 16>(x, w, wx, L);    // sub-block 2j
+      const float d1 = sym_fit_part<32, 16, 16>(x, w, wx, L);   // sub-block 2j+1
+      float amx = fmaxf(fabsf(d0), fabsf(d1));
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) amx = fmaxf(amx, __shfl_xor(amx, off, 8));
+      const _Float16 d16 = (_Float16)(amx / 127.0f);
+      const float dA = (float)d16;
+      const float s0 = dA > 0.0f ? med3(rne(d0 / dA), -127.0f, 127.0f) : 0.0f;
+      const float s1 = dA > 0.0f ? med3(rne(d1 / dA), -127.0f, 127.0f) : 0.0f;
+      const float ds0 = dA * s0, ds1 = dA * s1;   // exact: 11-bit times 8-bit
+      const float id0 = ds0 == 0.0f ? 0.0f : 1.0f / ds0;
+      const float id1 = ds1 == 0.0f ? 0.0f : 1.0f / ds1;
+      uint32_t u[QK];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        u[i] = ds0 == 0.0f ? 32u : (uint32_t)(int32_t)(med3(rne(x[i] * id0), -32.0f, 31.0f) + 32.0f);
+        u[16 + i] = ds1 == 0.0f ? 32u : (uint32_t)(int32_t)(med3(rne(x[16 + i] * id1), -32.0f, 31.0f) + 32.0f);
+      }
+      uint32_t h0 = 0, h1 = 0;  // bits 4 and 5 of each code, two bits apiece
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        h0 |= ((u[i] >> 4) & 3u) << (2 * i);
+        h1 |= ((u[16 + i] >> 4) & 3u) << (2 * i);
+      }
+      const uint4 qs = pack_nibbles(u);
+      const int j = g & 7;
+      uint8_t* p = orow + (size_t)(g >> 3) * 212;
+      // sub-scales: lane j holds bytes 2j, 2j+1; even lanes write a word
+      const uint32_t v16 = ((uint32_t)(int32_t)s0 & 255u) | (((uint32_t)(int32_t)s1 & 255u) << 8);
+      const uint32_t pair = __shfl_xor(v16, 1, 8);
+      if ((j & 1) == 0) store_u32(p + 4 + 2 * j, v16 | (pair << 16));
+      if (j == 0) store_u32(p, (uint32_t)__builtin_bit_cast(uint16_t, d16));   // d16, then the zero pad
+      uint8_t* pq = p + 20 + 16 * j;
+      store_u32(pq, qs.x); store_u32(pq + 4, qs.y); store_u32(pq + 8, qs.z); store_u32(pq + 12, qs.w);
+      store_u32(p + 148 + 8 * j, h0);
+      store_u32(p + 152 + 8 * j, h1);
+    } else if constexpr (TYPE == QR_Q6_0) {
       const float d = solve_sym<32, BF16, VAR>(lds_raw, g, qg, imp, L);
       uint32_t u[QK];
 #pragma unroll
@@ -980,6 +1097,21 @@ __device__ __forceinline__ void decode4(const uint8_t* __restrict__ in, int64_t 
     const int sh = (k >> 2) * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = fma_(ds, (float)((bytes >> (8 * i + sh)) & 15u), -dm);
+  } else if constexpr (TYPE == QR_Q6_K) {
+    const uint8_t* p = in + (U >> 3) * 212;
+    const int j = (int)(U & 7);
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(p);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(p + 4 + 4 * (j >> 1));
+    const uint32_t qh = *reinterpret_cast<const uint32_t*>(p + 148 + 8 * j + 4 * (k >> 2));
+    const uint32_t bytes = *reinterpret_cast<const uint32_t*>(p + 20 + 16 * j + 4 * (k & 3));
+    const float dA = (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 & 0xffffu));
+    const float ds = dA * (float)(int32_t)(int8_t)(uint8_t)(sw >> (8 * (2 * (j & 1) + (k >> 2))));
+    const int sh = (k >> 2) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = ((bytes >> (8 * i + sh)) & 15u) | (((qh >> (2 * (4 * (k & 3) + i))) & 3u) << 4);
+      o[i] = ds * (float)((int32_t)u - 32);
+    }
   } else if constexpr (TYPE == QR_Q6_0) {
     const uint8_t* p = in + U * 28;
     const uint32_t w0 = *reinterpret_cast<const uint32_t*>(p);
@@ -1043,7 +1175,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 int block_elems(int t) {
   switch (t) {
     case QR_Q4_0: case QR_Q4_1: case QR_Q5_0: case QR_Q5_1: case QR_Q6_0: return 32;
-    case QR_Q4_K: return 256;
+    case QR_Q4_K: case QR_Q6_K: return 256;
     case QR_Q8_K128: return 128;
     case QR_Q8_K64: return 64;
     case QR_Q8_K16: return 16;
@@ -1062,6 +1194,7 @@ size_t block_bytes(int t) {
     case QR_Q6_0: return 28;
     case QR_Q8_K64: return 72;
     case QR_Q8_K16: return 24;
+    case QR_Q6_K: return 212;
     default: return 0;
   }
 }
@@ -1101,6 +1234,7 @@ int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, in
     case QR_Q5_1: return QR_ROWS_LAUNCH(QR_Q5_1);
     case QR_Q4_K: return QR_ROWS_LAUNCH(QR_Q4_K);
     case QR_Q6_0: return QR_ROWS_LAUNCH(QR_Q6_0);
+    case QR_Q6_K: return QR_ROWS_LAUNCH(QR_Q6_K);
     default: return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   }
 #undef QR_ROWS_LAUNCH
@@ -1289,6 +1423,7 @@ int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row,
     case QR_Q5_1: hipLaunchKernelGGL(k_dequantize<QR_Q5_1>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     case QR_Q6_0: hipLaunchKernelGGL(k_dequantize<QR_Q6_0>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q6_K: hipLaunchKernelGGL(k_dequantize<QR_Q6_K>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     case QR_Q8_K64: hipLaunchKernelGGL(k_dequantize<QR_Q8_K64>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     case QR_Q8_K16: hipLaunchKernelGGL(k_dequantize<QR_Q8_K16>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;

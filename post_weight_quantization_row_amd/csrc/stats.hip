@@ -89,6 +89,20 @@ __device__ __forceinline__ void decode4(const uint8_t* __restrict__ row, int gin
     const uint32_t nib = k < 4 ? (w & 0x0f0f0f0fu) : ((w >> 4) & 0x0f0f0f0fu);
 #pragma unroll
     for (int e = 0; e < 4; ++e) xh[e] = __builtin_fmaf(ds, (float)((nib >> (8 * e)) & 0xffu), -dm);
+  } else if (TYPE == QR_Q6_K) {
+    const uint8_t* p = row + (int64_t)(gin >> 3) * 212;
+    const int j = gin & 7;
+    const float dA = half_bits(ld32(p));
+    const uint32_t sw = ld32(p + 4 + 4 * (j >> 1));
+    const float ds = dA * (float)(int)(int8_t)(uint8_t)(sw >> (8 * (2 * (j & 1) + (k >> 2))));
+    const uint32_t qh = ld32(p + 148 + 8 * j + 4 * (k >> 2));
+    const uint32_t w = ld32(p + 20 + 16 * j + 4 * (k & 3));
+    const uint32_t nib = k < 4 ? (w & 0x0f0f0f0fu) : ((w >> 4) & 0x0f0f0f0fu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = ((nib >> (8 * e)) & 0xffu) | (((qh >> (2 * (4 * (k & 3) + e))) & 3u) << 4);
+      xh[e] = ds * (float)((int)u - 32);
+    }
   } else if (TYPE == QR_Q6_0) {
     const uint8_t* p = row + (int64_t)gin * 28;
     const float d = f32_bits(ld32(p));
@@ -337,6 +351,7 @@ int dispatch_stats(int t, const void* x, const uint8_t* packed, const float* q, 
     case QR_Q6_0: return run_stats<QR_Q6_0, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     case QR_Q8_K64: return run_stats<QR_Q8_K64, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     case QR_Q8_K16: return run_stats<QR_Q8_K16, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
+    case QR_Q6_K: return run_stats<QR_Q6_K, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     default: return run_stats<QR_Q8_K128, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
   }
 }
@@ -353,7 +368,7 @@ size_t qr_stats_workspace_bytes(int64_t n_rows, int64_t n_per_row) {
 int qr_quantize_stats(int t, int src, const void* x, const void* packed, const float* imatrix, int64_t n_rows,
                       int64_t n_per_row, qr_stats* out, void* workspace, size_t workspace_bytes, void* stream) {
   qr_clear_error();
-  if (t < QR_Q4_0 || t > QR_Q8_K16) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
+  if (t < QR_Q4_0 || t > QR_Q6_K) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
   if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
   const size_t rb = qr_row_bytes(t, n_per_row);
   if (n_rows < 0 || n_per_row <= 0 || rb == 0 || n_per_row % 32 != 0)

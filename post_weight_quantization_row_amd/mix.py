@@ -12,7 +12,9 @@ sensitive tensors differs by architecture. Readings taken here:
 * the share promoted is set by a size budget: the promoted tensors are those roles in
   as many layers as fit in the budget (default +10% over the all-base
   plan), the layers spread evenly over the depth;
-* the base type is Q4_K and the 6-bit type this library's Q6_0.
+* the base type is Q4_K and the 6-bit type this library's Q6_K, the same
+  two-level K-quant scaling at 6 bits (Q6_0, the 32-weight 6-bit block,
+  can be chosen instead).
 
 ``plan_stack`` builds a plan (pure host arithmetic on row sizes),
 ``describe`` prints it (the dry run), and ``run`` quantizes every tensor on
@@ -79,7 +81,7 @@ def _spread(k: int, n: int) -> list:
     return sorted({round(i * (n - 1) / (k - 1)) for i in range(k)})
 
 
-def plan_stack(n_layers: int = 32, base: str = "q4_k", high: str = "q6_0",
+def plan_stack(n_layers: int = 32, base: str = "q4_k", high: str = "q6_k",
                roles=("attn_v", "ffn_down"), budget: float = 0.10) -> Plan:
     """A type for every tensor of the 7B-shaped stack (synth.STACK_LAYER per
     layer): `roles` get `high` in the largest evenly spread set of layers
@@ -143,7 +145,7 @@ def _main(argv=None) -> int:
     ap.add_argument("--dry-run", action="store_true", help="print the plan only")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--base", default="q4_k")
-    ap.add_argument("--high", default="q6_0")
+    ap.add_argument("--high", default="q6_k")
     ap.add_argument("--roles", default="attn_v,ffn_down")
     ap.add_argument("--budget", type=float, default=0.10)
     args = ap.parse_args(argv)

@@ -49,7 +49,7 @@ def test_two_layer_plan(qr):
             assert np.float32(st["p95_abs_err"]) == o["p95_abs_err"]
             for k in ("sum_err2", "sum_x2", "sum_werr2", "sum_wx2"):
                 assert abs(st[k] - o[k]) <= 2.0 * o["n"] * 2.0 ** -53 * o[k], k
-    assert seen == {"q4_k", "q6_0"}
+    assert seen == {"q4_k", "q6_k"}
     # six bits cut the error of the promoted tensors well below their 4-bit neighbours
     assert errs["blk.1.attn_v"] < 0.5 * errs["blk.0.attn_v"]
     assert errs["blk.1.ffn_down"] < 0.5 * errs["blk.0.ffn_down"]

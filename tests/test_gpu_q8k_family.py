@@ -7,7 +7,8 @@ Product bound: as for Q8_K_128 activations (the integer parts exact, at
 most three fp32 roundings per term, a fixed order of additions), with the
 number of sequential fp32 additions per lane doubled for 16-value blocks
 (two terms per 32-weight group): (n_in/1024 + 9) * 2^-24 * S for Q8_K64 and
-(n_in/512 + 9) * 2^-24 * S for Q8_K16, S the oracle's magnitude sum.
+(n_in/512 + 9) * 2^-24 * S for Q8_K16 or Q6_K weights (whose two 16-weight
+halves carry their own scales), S the oracle's magnitude sum.
 """
 import numpy as np
 import pytest
@@ -20,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 F32 = np.float32
 ACTS = ["q8_k64", "q8_k16"]
-WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0"]
+WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k"]
 
 
 @pytest.fixture(scope="module")
@@ -109,7 +110,7 @@ def product_check(qr, t, act, w, xa, n_in):
     y = qr.qr_matmul_q8k(t, act, torch.from_numpy(w).cuda(), torch.from_numpy(xa).cuda(), n_in)
     yg = y.cpu().numpy().astype(np.float64)
     yo, S = oracle.matmul_q8k128(t, w, xa, n_out, n_tok, n_in, with_magnitude=True, act=act)
-    per_lane = n_in / (512 if act == "q8_k16" else 1024)
+    per_lane = n_in / (512 if act == "q8_k16" or t == "q6_k" else 1024)
     bound = (per_lane + 9) * 2.0 ** -24 * S
     err = np.abs(yg - yo)
     assert np.all(np.isfinite(yg))
@@ -122,7 +123,7 @@ def product_check(qr, t, act, w, xa, n_in):
 @pytest.mark.parametrize("n_out,n_tok,n_in", [(37, 1, 256), (16, 3, 768), (100, 8, 1024), (33, 13, 2048),
                                               (5, 2, 8192), (9, 5, 1280)])
 def test_product(qr, t, act, n_out, n_tok, n_in):
-    if t == "q4_k" and n_in % 256:
+    if t in ("q4_k", "q6_k") and n_in % 256:
         n_in = 256 * (n_in // 256 + 1)
     say(f"product {t} x {act} ({n_out},{n_tok},{n_in})")
     x, q = synth.q4_0_matrix(n_out, n_in, seed=n_out + n_in)

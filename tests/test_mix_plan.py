@@ -29,7 +29,7 @@ def test_default_plan_is_q4_k_m_shaped():
     assert 4.5 < 8 * p.bytes / p.weights < 5.0
     for t in p.tensors:
         role = t.name.split(".", 2)[2]
-        want = "q6_0" if (t.layer in p.promoted_layers and role in ("attn_v", "ffn_down")) else "q4_k"
+        want = "q6_k" if (t.layer in p.promoted_layers and role in ("attn_v", "ffn_down")) else "q4_k"
         assert t.type == want, t.name
 
 
@@ -63,7 +63,7 @@ def test_zero_and_large_budgets():
     assert all(t.type == "q4_k" for t in mix.plan_stack(4, budget=0.0).tensors)
     p = mix.plan_stack(4, budget=5.0)
     assert p.promoted_layers == [0, 1, 2, 3]
-    assert sum(t.type == "q6_0" for t in p.tensors) == 8
+    assert sum(t.type == "q6_k" for t in p.tensors) == 8
 
 
 def test_other_roles_and_types():
@@ -92,4 +92,4 @@ def test_dry_run_command_line():
                           "--layers", "4"], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
     assert "promoted layers" in out.stdout and "total:" in out.stdout
-    assert "q6_0" in out.stdout
+    assert "q6_k" in out.stdout
