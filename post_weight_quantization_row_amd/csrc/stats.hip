@@ -47,12 +47,17 @@ struct StatsState {
   uint32_t prefix;  // leading bits of the value selected so far
 };
 
+// The global histograms are kept in ST_REP copies, workgroup b adding into
+// copy b % ST_REP, so that thousands of workgroups do not queue on the same
+// few counters; the select kernels add the copies up.
+constexpr int ST_REP = 16;
+
 // workspace layout
 constexpr size_t WS_STATE = 0;
 constexpr size_t WS_HIST0 = 256;
-constexpr size_t WS_HIST1 = WS_HIST0 + ST_BINS0 * 4;
-constexpr size_t WS_HIST2 = WS_HIST1 + ST_BINS1 * 4;
-constexpr size_t WS_PART = (WS_HIST2 + ST_BINS2 * 4 + 255) & ~(size_t)255;
+constexpr size_t WS_HIST1 = WS_HIST0 + (size_t)ST_REP * ST_BINS0 * 4;
+constexpr size_t WS_HIST2 = WS_HIST1 + (size_t)ST_REP * ST_BINS1 * 4;
+constexpr size_t WS_PART = (WS_HIST2 + (size_t)ST_REP * ST_BINS2 * 4 + 255) & ~(size_t)255;
 constexpr size_t WS_BYTES = WS_PART + (size_t)ST_MAX_WGS * ST_PART * 8;
 
 __device__ __forceinline__ uint32_t ld32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
@@ -151,10 +156,16 @@ __device__ __forceinline__ void load_x4(const void* __restrict__ x, int64_t elem
   }
 }
 
+// One workgroup per histogram copy clears it; the first sets the state.
 __global__ __launch_bounds__(ST_THREADS) void k_stats_init(uint8_t* __restrict__ ws, uint32_t k) {
-  uint32_t* h = reinterpret_cast<uint32_t*>(ws + WS_HIST0);
-  for (int i = threadIdx.x; i < ST_BINS0 + ST_BINS1 + ST_BINS2; i += ST_THREADS) h[i] = 0;
-  if (threadIdx.x == 0) {
+  const int r = blockIdx.x;
+  uint32_t* h0 = reinterpret_cast<uint32_t*>(ws + WS_HIST0) + r * ST_BINS0;
+  uint32_t* h1 = reinterpret_cast<uint32_t*>(ws + WS_HIST1) + r * ST_BINS1;
+  uint32_t* h2 = reinterpret_cast<uint32_t*>(ws + WS_HIST2) + r * ST_BINS2;
+  for (int i = threadIdx.x; i < ST_BINS0; i += ST_THREADS) h0[i] = 0;
+  for (int i = threadIdx.x; i < ST_BINS1; i += ST_THREADS) h1[i] = 0;
+  for (int i = threadIdx.x; i < ST_BINS2; i += ST_THREADS) h2[i] = 0;
+  if (r == 0 && threadIdx.x == 0) {
     StatsState* st = reinterpret_cast<StatsState*>(ws + WS_STATE);
     st->k = k;
     st->prefix = 0;
@@ -209,7 +220,8 @@ __global__ __launch_bounds__(ST_THREADS) void k_stats_pass(const void* __restric
     }
   }
   __syncthreads();
-  uint32_t* gh = reinterpret_cast<uint32_t*>(ws + (PASS == 0 ? WS_HIST0 : PASS == 1 ? WS_HIST1 : WS_HIST2));
+  uint32_t* gh = reinterpret_cast<uint32_t*>(ws + (PASS == 0 ? WS_HIST0 : PASS == 1 ? WS_HIST1 : WS_HIST2)) +
+                 (blockIdx.x % ST_REP) * NB;
   for (int i = threadIdx.x; i < NB; i += ST_THREADS)
     if (h[i]) atomicAdd(&gh[i], h[i]);
   if (PASS != 0) return;
@@ -250,33 +262,40 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t v, int lane) {
   return v;
 }
 
-// One wave: the bin of the histogram that holds rank k; appends its index
-// (BITS bits) to the prefix and leaves the rank within the bin.
+// One workgroup: the bin of the histogram (the sum of its copies) that
+// holds rank k; appends its index (BITS bits) to the prefix and leaves the
+// rank within the bin.
 template <int NB, int BITS, int PASS>
-__global__ __launch_bounds__(WAVE) void k_stats_select(uint8_t* __restrict__ ws) {
-  constexpr int PER = NB / WAVE;
+__global__ __launch_bounds__(ST_THREADS) void k_stats_select(uint8_t* __restrict__ ws) {
+  constexpr int PER = NB / ST_THREADS;
+  __shared__ uint32_t wave_tot[ST_THREADS / WAVE];
   const uint32_t* h = reinterpret_cast<const uint32_t*>(ws + (PASS == 0 ? WS_HIST0 : PASS == 1 ? WS_HIST1 : WS_HIST2));
   StatsState* st = reinterpret_cast<StatsState*>(ws + WS_STATE);
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x, lane = t & (WAVE - 1), wave = t / WAVE;
   uint32_t c[PER];
   uint32_t local = 0;
 #pragma unroll
   for (int b = 0; b < PER; ++b) {
-    c[b] = h[lane * PER + b];
-    local += c[b];
+    uint32_t v = 0;
+#pragma unroll
+    for (int r = 0; r < ST_REP; ++r) v += h[r * NB + t * PER + b];
+    c[b] = v;
+    local += v;
   }
-  const uint32_t incl = wave_scan(local, lane);
-  const uint32_t excl = incl - local;
+  uint32_t incl = wave_scan(local, lane);
+  if (lane == WAVE - 1) wave_tot[wave] = incl;
   const uint32_t k = st->k;
-  __syncthreads();  // every lane has read k before one of them rewrites it
+  __syncthreads();  // the wave totals are in place and every thread has read k
+  for (int w = 0; w < wave; ++w) incl += wave_tot[w];
+  const uint32_t excl = incl - local;
   if (excl < k && k <= incl) {
     uint32_t cum = excl;
-    int bin = lane * PER + PER - 1;
+    int bin = t * PER + PER - 1;
     uint32_t rem = k - cum;
 #pragma unroll
     for (int b = 0; b < PER; ++b) {
       if (cum + c[b] >= k) {
-        bin = lane * PER + b;
+        bin = t * PER + b;
         rem = k - cum;
         break;
       }
@@ -287,30 +306,37 @@ __global__ __launch_bounds__(WAVE) void k_stats_select(uint8_t* __restrict__ ws)
   }
 }
 
-// Sums of the per-workgroup partials in workgroup order, then the output.
-__global__ __launch_bounds__(WAVE) void k_stats_final(const uint8_t* __restrict__ ws, int n_wgs, int64_t n,
-                                                      qr_stats* __restrict__ out) {
+// Sums of the per-workgroup partials in a fixed order (thread t takes
+// partials t, t + 256, ..., then a tree over the threads), then the output.
+__global__ __launch_bounds__(ST_THREADS) void k_stats_final(const uint8_t* __restrict__ ws, int n_wgs, int64_t n,
+                                                            qr_stats* __restrict__ out) {
+  __shared__ double red[ST_PART][ST_THREADS];
   const double* part = reinterpret_cast<const double*>(ws + WS_PART);
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x;
   double v[ST_PART] = {0.0, 0.0, 0.0, 0.0, 0.0};
-  for (int w = lane; w < n_wgs; w += WAVE) {
+  for (int w = t; w < n_wgs; w += ST_THREADS) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] += part[(int64_t)w * ST_PART + c];
     v[4] = fmax(v[4], part[(int64_t)w * ST_PART + 4]);
   }
 #pragma unroll
-  for (int m = WAVE / 2; m >= 1; m >>= 1) {
+  for (int c = 0; c < ST_PART; ++c) red[c][t] = v[c];
+  __syncthreads();
+  for (int m = ST_THREADS / 2; m >= 1; m >>= 1) {
+    if (t < m) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] += __shfl_xor(v[c], m, WAVE);
-    v[4] = fmax(v[4], __shfl_xor(v[4], m, WAVE));
+      for (int c = 0; c < 4; ++c) red[c][t] += red[c][t + m];
+      red[4][t] = fmax(red[4][t], red[4][t + m]);
+    }
+    __syncthreads();
   }
-  if (lane == 0) {
+  if (t == 0) {
     const StatsState* st = reinterpret_cast<const StatsState*>(ws + WS_STATE);
-    out->sum_err2 = v[0];
-    out->sum_x2 = v[1];
-    out->sum_werr2 = v[2];
-    out->sum_wx2 = v[3];
-    out->max_abs_err = (float)v[4];
+    out->sum_err2 = red[0][0];
+    out->sum_x2 = red[1][0];
+    out->sum_werr2 = red[2][0];
+    out->sum_wx2 = red[3][0];
+    out->max_abs_err = (float)red[4][0];
     out->p95_abs_err = __builtin_bit_cast(float, st->prefix);
     out->n = n;
   }
@@ -325,17 +351,17 @@ int run_stats(const void* x, const uint8_t* packed, const float* q, int64_t n_ro
   if (grid > ST_MAX_WGS) grid = ST_MAX_WGS;
   const uint32_t k = (uint32_t)((95 * n + 99) / 100);
   const int gpr = n_per_row / 32;
-  hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(ST_THREADS), 0, s, ws, k);
+  hipLaunchKernelGGL(k_stats_init, dim3(ST_REP), dim3(ST_THREADS), 0, s, ws, k);
   hipLaunchKernelGGL((k_stats_pass<TYPE, BF16, 0>), dim3((uint32_t)grid), dim3(ST_THREADS), 0, s, x, packed, q,
                      n_groups, gpr, n_per_row, rb, ws);
-  hipLaunchKernelGGL((k_stats_select<ST_BINS0, 11, 0>), dim3(1), dim3(WAVE), 0, s, ws);
+  hipLaunchKernelGGL((k_stats_select<ST_BINS0, 11, 0>), dim3(1), dim3(ST_THREADS), 0, s, ws);
   hipLaunchKernelGGL((k_stats_pass<TYPE, BF16, 1>), dim3((uint32_t)grid), dim3(ST_THREADS), 0, s, x, packed, q,
                      n_groups, gpr, n_per_row, rb, ws);
-  hipLaunchKernelGGL((k_stats_select<ST_BINS1, 11, 1>), dim3(1), dim3(WAVE), 0, s, ws);
+  hipLaunchKernelGGL((k_stats_select<ST_BINS1, 11, 1>), dim3(1), dim3(ST_THREADS), 0, s, ws);
   hipLaunchKernelGGL((k_stats_pass<TYPE, BF16, 2>), dim3((uint32_t)grid), dim3(ST_THREADS), 0, s, x, packed, q,
                      n_groups, gpr, n_per_row, rb, ws);
-  hipLaunchKernelGGL((k_stats_select<ST_BINS2, 9, 2>), dim3(1), dim3(WAVE), 0, s, ws);
-  hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(WAVE), 0, s, ws, (int)grid, n, out);
+  hipLaunchKernelGGL((k_stats_select<ST_BINS2, 9, 2>), dim3(1), dim3(ST_THREADS), 0, s, ws);
+  hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(ST_THREADS), 0, s, ws, (int)grid, n, out);
   return qr_check_launch("k_stats");
 }
 
