@@ -102,10 +102,11 @@ typedef enum {
 #define QR_EOVERFLOW    -4  /* a size computation overflows                  */
 #define QR_EDEVICE      -5  /* the HIP runtime reported an error            */
 
-/* Largest supported row: the row is staged on chip while its blocks are
- * solved. */
+/* Largest supported row: the row is staged in LDS while its blocks are
+ * solved (32-value groups padded to 144 bytes for fp32 and 80 for bf16, plus
+ * the cross-wave partial sums, within the 160 KiB of one workgroup). */
 #define QR_MAX_ROW_F32   32768
-#define QR_MAX_ROW_BF16  65536
+#define QR_MAX_ROW_BF16  32768
 
 /*
  * qr_quantize_rows -- importance-weighted quantization of weight rows [WT 一],

@@ -667,6 +667,10 @@ __device__ __forceinline__ void store_u32(uint8_t* p, uint32_t v) { *reinterpret
 // at most MAX_ROW_WAVES); every lane solves groups tid, tid + 64W, ...
 
 constexpr int MAX_ROW_WAVES = 8;
+constexpr int LDS_PER_WORKGROUP = 160 * 1024;
+static_assert((size_t)QR_MAX_ROW_F32 / QK * LDS_F32_STRIDE * 4 + 8 * MAX_ROW_WAVES <= LDS_PER_WORKGROUP &&
+                  (size_t)QR_MAX_ROW_BF16 / QK * LDS_BF16_STRIDE * 2 + 8 * MAX_ROW_WAVES <= LDS_PER_WORKGROUP,
+              "the longest row and the partial sums fit in one workgroup's LDS");
 
 template <int TYPE, bool BF16, bool VAR>
 __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(3))) void k_quantize_rows(const void* __restrict__ x,
@@ -1213,7 +1217,7 @@ int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_r
   static bool attr_set = false;
   if (lds > 65536 && !attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WORKGROUP);
     if (e != hipSuccess) return qr_fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     attr_set = true;
   }

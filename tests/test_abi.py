@@ -68,6 +68,8 @@ def test_argument_validation_without_a_gpu(lib):
     assert lib.qr_quantize_rows(0, 0, fake, None, -1, 256, fake, None) == -2
     assert lib.qr_quantize_rows(0, 0, fake, None, 4, 0, fake, None) == -2
     assert lib.qr_quantize_rows(0, 0, fake, None, 4, 65536, fake, None) == -2
+    assert lib.qr_quantize_rows(4, 0, fake, None, 4, 32768 + 256, fake, None) == -2   # longest row: 32768
+    assert lib.qr_quantize_rows(4, 1, fake, None, 4, 32768 + 256, fake, None) == -2   # bf16 too
     assert lib.qr_quantize_activations_q8k128(0, fake, 4, 100, fake, None) == -2
     assert lib.qr_dequantize_rows(4, fake, 4, 32, fake, None) == -2
     assert lib.qr_dequantize_rows(10, fake, 4, 32, fake, None) == -1

@@ -88,6 +88,16 @@ def test_long_rows_use_smaller_token_tiles(qr):
     check(qr, "q4_0", w, xa, 16384)
 
 
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q5_1"])
+@pytest.mark.parametrize("n_tok", [1, 8])
+def test_longest_rows(qr, t, n_tok):
+    # n_in = QR_MATMUL_MAX_IN: one token per tile (the staged tile would not
+    # fit the activation budget), several groups per lane
+    say(f"longest rows {t} n_tok={n_tok}")
+    w, xa = inputs(t, 24, n_tok, 32768, seed=95 + n_tok)
+    check(qr, t, w, xa, 32768)
+
+
 def test_reproducible(qr):
     w, xa = inputs("q4_k", 64, 8, 4096, seed=93)
     wd, xd = torch.from_numpy(w).cuda(), torch.from_numpy(xa).cuda()

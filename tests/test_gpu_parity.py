@@ -103,6 +103,30 @@ def test_weight_rows_small(qr, t, bf16, qkind):
         assert_rows_equal(t, got, ref, xh, lambda r: q)
 
 
+@pytest.mark.parametrize("t", WEIGHT_TYPES)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_longest_rows(qr, t, bf16):
+    # rows of QR_MAX_ROW values: the whole row staged in LDS, eight waves
+    # each solving several groups
+    n = 32768
+    rng = np.random.default_rng(zlib.crc32(f"max/{t}/{bf16}".encode()))
+    x = (0.02 * rng.standard_t(5, (3, n))).astype(F32)
+    q = np.exp(1.5 * rng.standard_normal(n)).astype(F32)
+    say(f"case {t} bf16={bf16} longest rows (3,{n})")
+    got = qr.qr_quantize_rows(t, to_dev(x, bf16), torch.from_numpy(q).cuda()).cpu().numpy()
+    xh = host_values(x, bf16)
+    assert_rows_equal(t, got, oracle.quantize_rows(t, xh, q), xh, lambda r: q)
+    y = qr.qr_dequantize_rows(t, torch.from_numpy(got).cuda(), 3, n).cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), oracle.dequantize_rows(t, got, 3, n).view(np.uint32))
+
+
+def test_rows_beyond_the_longest_are_rejected(qr):
+    for bf16 in (False, True):
+        x = torch.zeros((1, 32768 + 256), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+        with pytest.raises(qr.QrowError):
+            qr.qr_quantize_rows("q4_k", x, None)
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_q8k128_small(qr, bf16):
     rng = np.random.default_rng(7 + bf16)
