@@ -114,6 +114,7 @@ def test_dense(qr, bf16, T, C):
     (10000, 4096, 128, 2, 1),    # one slab of three 4096-token windows
     (2048, 512, 1024, 8, 1),     # the largest expert count (64 KB routing LDS)
     (9000, 64, 4, 2, 2),         # many slabs, per-slot rows
+    (600, 256, 128, 64, 1),      # the largest top_k (64 experts per token)
 ])
 def test_routed(qr, T, C, E, K, S):
     say(f"routed T={T} C={C} E={E} K={K} S={S}")
