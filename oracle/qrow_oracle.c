@@ -766,13 +766,14 @@ static int quantize_row_impl(int type, const float *x, const float *q,
     const int be = orc_block_elems(type);
     const size_t bb = orc_block_bytes(type);
     orc_row_weights_mode(x, q, n, sigma2, mode, w);
-    /* A 32-weight group (the unit every fit works on: a legacy block or a
-     * Q4_K sub-block) whose importances are all zero -- an imatrix with no
+    /* A fitted unit (a legacy block or Q4_K sub-block of 32 weights, a Q6_K
+     * sub-block of 16) whose importances are all zero -- an imatrix with no
      * data on those columns -- falls back to unit importances (reading). */
-    for (int64_t g = 0; g < n / 32; ++g) {
+    const int unit = type == ORC_Q6_K ? 16 : 32;
+    for (int64_t g = 0; g < n / unit; ++g) {
         int all_zero = 1;
-        for (int i = 0; i < 32; ++i) if (w[32 * g + i] != 0.0f) { all_zero = 0; break; }
-        if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, mode, w + 32 * g);
+        for (int i = 0; i < unit; ++i) if (w[unit * g + i] != 0.0f) { all_zero = 0; break; }
+        if (all_zero) orc_row_weights_mode(x + unit * g, NULL, unit, sigma2, mode, w + unit * g);
     }
     for (int64_t ib = 0; ib < n / be; ++ib) {
         const float *xb = x + ib * be;

@@ -715,11 +715,22 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
       float x[QK], w[QK], wx[QK];
       load_group<BF16>(lds_raw, g, x);
       group_importances<VAR>(x, qg, imp, w);
-      {  // a group with no importance at all falls back to q = 1
-        uint32_t any = 0;
+      {  // a sub-block (16 weights) with no importance at all falls back to q = 1
+        uint32_t any0 = 0, any1 = 0;
 #pragma unroll
-        for (int i = 0; i < QK; ++i) any |= fbits(w[i]) & 0x7fffffffu;
-        if (any == 0) group_importances<VAR>(x, nullptr, imp, w);
+        for (int i = 0; i < 16; ++i) {
+          any0 |= fbits(w[i]) & 0x7fffffffu;
+          any1 |= fbits(w[16 + i]) & 0x7fffffffu;
+        }
+        if (any0 == 0 || any1 == 0) {
+          float wu[QK];
+          group_importances<VAR>(x, nullptr, imp, wu);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            w[i] = any0 == 0 ? wu[i] : w[i];
+            w[16 + i] = any1 == 0 ? wu[16 + i] : w[16 + i];
+          }
+        }
       }
 #pragma unroll
       for (int i = 0; i < QK; ++i) wx[i] = w[i] * x[i];

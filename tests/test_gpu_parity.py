@@ -120,6 +120,20 @@ def test_longest_rows(qr, t, bf16):
     assert np.array_equal(y.view(np.uint32), oracle.dequantize_rows(t, got, 3, n).view(np.uint32))
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_q6_k_sub_blocks_without_importance(qr, bf16):
+    # zero importances on single 16-weight halves of 32-weight groups: each
+    # such Q6_K sub-block falls back to unit importances on its own
+    rng = np.random.default_rng(61 + bf16)
+    x = (0.02 * rng.standard_t(5, (9, 2048))).astype(F32)
+    q = np.exp(rng.standard_normal(2048)).astype(F32)
+    for lo in (0, 48, 272, 1040, 2032):
+        q[lo:lo + 16] = 0.0
+    got = qr.qr_quantize_rows("q6_k", to_dev(x, bf16), torch.from_numpy(q).cuda()).cpu().numpy()
+    xh = host_values(x, bf16)
+    assert_rows_equal("q6_k", got, oracle.quantize_rows("q6_k", xh, q), xh, lambda r: q)
+
+
 def test_rows_beyond_the_longest_are_rejected(qr):
     for bf16 in (False, True):
         x = torch.zeros((1, 32768 + 256), dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")

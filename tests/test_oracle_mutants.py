@@ -84,8 +84,10 @@ MUTANTS = [
      "case ORC_W_ABS_X:           return x;"),
     ("weighting: sigma not rooted", "const float sigma = sqrtf(sigma2);", "const float sigma = sigma2;"),
     ("weighting: fallback ignores the mode",
-     "if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, mode, w + 32 * g);",
-     "if (all_zero) orc_row_weights_mode(x + 32 * g, NULL, 32, sigma2, 0, w + 32 * g);"),
+     "if (all_zero) orc_row_weights_mode(x + unit * g, NULL, unit, sigma2, mode, w + unit * g);",
+     "if (all_zero) orc_row_weights_mode(x + unit * g, NULL, unit, sigma2, 0, w + unit * g);"),
+    ("q6k: importance fallback per 32 weights", "const int unit = type == ORC_Q6_K ? 16 : 32;",
+     "const int unit = 32;"),
     ("weighting: imatrix dropped", "w[j] = q ? q[j] * m : m;", "w[j] = m;"),
     # Q6_0
     ("q6_0: plane bits shifted by one", "v |= (uint64_t)((u[i] >> 4) & 3) << (2 * i);",

@@ -140,6 +140,24 @@ def test_zero_rows_and_k_quant_gain():
     assert oracle.row_bytes("q6_k", 4096) < oracle.row_bytes("q6_0", 4096)
 
 
+def test_sub_blocks_without_importance_fall_back_to_unit_importances():
+    # zero importances on one 16-weight half of a 32-weight group: that
+    # sub-block is fitted as if its importances were 1 (the imatrix has no
+    # data there), exactly as a wholly zero group is for the 32-weight types
+    x, q = synth.q4_k_matrix(4, 512, seed=49)
+    qz, q1 = q.copy(), q.copy()
+    for lo, hi in ((0, 16), (48, 64), (272, 288)):
+        qz[lo:hi], q1[lo:hi] = 0.0, 1.0
+    a = oracle.quantize_rows("q6_k", x, qz)
+    assert np.array_equal(a, oracle.quantize_rows("q6_k", x, q1))
+    assert np.all(oracle.dequantize_rows("q6_k", a, 4, 512)[:, 0:16] != 0)
+    # the 32-weight types take the fallback per whole group only
+    qz2, q12 = q.copy(), q.copy()
+    qz2[0:32], q12[0:32] = 0.0, 1.0
+    for t in ("q4_0", "q4_k", "q6_k"):
+        assert np.array_equal(oracle.quantize_rows(t, x, qz2), oracle.quantize_rows(t, x, q12)), t
+
+
 @pytest.mark.parametrize("act", ["q8_k128", "q8_k16"])
 def test_product_with_q6_k_weights(act):
     x, q = synth.q4_0_matrix(20, 1024, seed=46)
