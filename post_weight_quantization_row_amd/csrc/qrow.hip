@@ -672,8 +672,17 @@ static_assert((size_t)QR_MAX_ROW_F32 / QK * LDS_F32_STRIDE * 4 + 8 * MAX_ROW_WAV
                   (size_t)QR_MAX_ROW_BF16 / QK * LDS_BF16_STRIDE * 2 + 8 * MAX_ROW_WAVES <= LDS_PER_WORKGROUP,
               "the longest row and the partial sums fit in one workgroup's LDS");
 
+// Waves per SIMD the register allocation aims at: the symmetric types fit
+// 128 VGPRs and run fastest at 4 (the LDS limit of a 4096-value fp32 row);
+// the asymmetric solver needs more registers and runs fastest at 3
+// (measured: at 4, Q4_1/Q5_1 spill and take 2.9x as long, Q4_K 10% longer;
+// at 3, Q6_K takes 5-10% longer).
+__host__ __device__ constexpr int row_waves_per_eu(int t) {
+  return (t == QR_Q4_1 || t == QR_Q5_1 || t == QR_Q4_K) ? 3 : 4;
+}
+
 template <int TYPE, bool BF16, bool VAR>
-__global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(3))) void k_quantize_rows(const void* __restrict__ x,
+__global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(row_waves_per_eu(TYPE)))) void k_quantize_rows(const void* __restrict__ x,
                                                                         const float* __restrict__ imatrix,
                                                                         int n_per_row, int64_t rows_per_group,
                                                                         uint8_t* __restrict__ out,
