@@ -95,6 +95,35 @@ __device__ __forceinline__ float sqrt_cr(float t, bool normal_range) {
 }
 
 // -------------------------------------------------------------------------
+// DPP helpers (gfx9 encodings): quad_perm, row_half_mirror, row_mirror, row_shl:8
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_SHL8 = 0x108;
+
+// max and bitwise or over each group of 8 lanes (8s .. 8s+7): two quad
+// swaps, then the mirror within the half row joins the two quads
+__device__ __forceinline__ float oct_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+  return fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+}
+__device__ __forceinline__ uint32_t oct_or(uint32_t v) {
+  v |= (uint32_t)dpp_i<DPP_QUAD_XOR1>((int)v);
+  v |= (uint32_t)dpp_i<DPP_QUAD_XOR2>((int)v);
+  return v | (uint32_t)dpp_i<DPP_ROW_HALF_MIRROR>((int)v);
+}
+
+// -------------------------------------------------------------------------
 // row staging and the row statistic [WT 一]
 
 // The workgroup streams its row into LDS (16-byte coalesced loads; groups of
@@ -745,9 +774,7 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
       for (int i = 0; i < QK; ++i) wx[i] = w[i] * x[i];
       const float d0 = sym_fit_part<32, 0, 16>(x, w, wx, L);    // sub-block 2j
       const float d1 = sym_fit_part<32, 16, 16>(x, w, wx, L);   // sub-block 2j+1
-      float amx = fmaxf(fabsf(d0), fabsf(d1));
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) amx = fmaxf(amx, __shfl_xor(amx, off, 8));
+      const float amx = oct_max(fmaxf(fabsf(d0), fabsf(d1)));   // over the super-block's 16 sub-blocks
       const _Float16 d16 = (_Float16)(amx / 127.0f);
       const float dA = (float)d16;
       const float s0 = dA > 0.0f ? med3(rne(d0 / dA), -127.0f, 127.0f) : 0.0f;
@@ -772,7 +799,7 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
       uint8_t* p = orow + (size_t)(g >> 3) * 212;
       // sub-scales: lane j holds bytes 2j, 2j+1; even lanes write a word
       const uint32_t v16 = ((uint32_t)(int32_t)s0 & 255u) | (((uint32_t)(int32_t)s1 & 255u) << 8);
-      const uint32_t pair = __shfl_xor(v16, 1, 8);
+      const uint32_t pair = (uint32_t)dpp_i<DPP_QUAD_XOR1>((int)v16);
       if ((j & 1) == 0) store_u32(p + 4 + 2 * j, v16 | (pair << 16));
       if (j == 0) store_u32(p, (uint32_t)__builtin_bit_cast(uint16_t, d16));   // d16, then the zero pad
       uint8_t* pq = p + 20 + 16 * j;
@@ -873,12 +900,7 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
         if ((float)d16 == 0.0f) sc = 0.0f;
         if ((float)m16 == 0.0f) mn = 0.0f;
       } else {
-        float A = a, Bm = b;
-#pragma unroll
-        for (int off = 1; off < 8; off <<= 1) {
-          A = fmaxf(A, __shfl_xor(A, off, 8));
-          Bm = fmaxf(Bm, __shfl_xor(Bm, off, 8));
-        }
+        const float A = oct_max(a), Bm = oct_max(b);   // the super-block's largest scale and offset
         d16 = (_Float16)(A / 63.0f);
         m16 = (_Float16)(Bm / 63.0f);
         const float dA0 = (float)d16, dB0 = (float)m16;
@@ -898,13 +920,11 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
         for (int i = 0; i < QK; ++i) u[i] = med3(rne((u[i] + dm) * id), 0.0f, 15.0f);
       }
       const uint4 qs = pack_nibbles_f(u);
-      uint64_t scb = (uint64_t)(uint32_t)sc << (6 * j);
-      uint64_t mnb = (uint64_t)(uint32_t)mn << (6 * j);
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) {
-        scb |= __shfl_xor(scb, off, 8);
-        mnb |= __shfl_xor(mnb, off, 8);
-      }
+      // the eight 6-bit fields, merged over the super-block's lanes
+      const uint64_t scj = (uint64_t)(uint32_t)sc << (6 * j);
+      const uint64_t mnj = (uint64_t)(uint32_t)mn << (6 * j);
+      const uint64_t scb = (uint64_t)oct_or((uint32_t)scj) | ((uint64_t)oct_or((uint32_t)(scj >> 32)) << 32);
+      const uint64_t mnb = (uint64_t)oct_or((uint32_t)mnj) | ((uint64_t)oct_or((uint32_t)(mnj >> 32)) << 32);
       uint8_t* p = orow + (size_t)(g >> 3) * 144;
       *reinterpret_cast<uint4*>(p + 16 + 16 * j) = qs;
       if (j == 0) {
@@ -935,21 +955,6 @@ constexpr int Q8_STEPS = 8;                      // wave steps per iteration
 
 __host__ __device__ constexpr int q8_block_bytes(int b) { return b == 128 ? 140 : b == 64 ? 72 : 24; }
 __host__ __device__ constexpr int q8_chunk_blocks(int b) { return (256 / b) * Q8_STEPS; }
-
-// DPP helpers (gfx9 encodings): quad_perm, row_half_mirror, row_mirror, row_shl:8
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
-}
-constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int DPP_ROW_HALF_MIRROR = 0x141;
-constexpr int DPP_ROW_MIRROR = 0x140;
-constexpr int DPP_ROW_SHL8 = 0x108;
 
 // max over each 32-lane half of the wave
 __device__ __forceinline__ float half_wave_max(float v) {
