@@ -1239,12 +1239,19 @@ int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_r
   int waves = (n_groups + WAVE - 1) / WAVE;
   if (waves > MAX_ROW_WAVES) waves = MAX_ROW_WAVES;
   const size_t lds = (size_t)n_groups * (BF16 ? LDS_BF16_STRIDE * 2 : LDS_F32_STRIDE * 4) + 8 * (size_t)waves;
-  static bool attr_set = false;
-  if (lds > 65536 && !attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WORKGROUP);
-    if (e != hipSuccess) return qr_fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-    attr_set = true;
+  // Rows above 64 KB of LDS need the kernel's dynamic-LDS limit raised, once
+  // per device (the attribute belongs to the device the call runs on).
+  constexpr int MAX_DEVICES = 64;
+  static bool attr_set[MAX_DEVICES] = {};
+  if (lds > 65536) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipGetDevice failed");
+    if (dev < 0 || dev >= MAX_DEVICES || !attr_set[dev]) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WORKGROUP);
+      if (e != hipSuccess) return qr_fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+      if (dev >= 0 && dev < MAX_DEVICES) attr_set[dev] = true;
+    }
   }
   hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE * waves), lds, stream, x, imatrix, n_per_row,
                      rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes, weighting, fit);
