@@ -78,6 +78,14 @@ __device__ __forceinline__ float med3(float v, float lo, float hi) {
 }
 __device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
 
+// The same value, opaque to the optimizer (no instruction is emitted): an
+// expression formed again from it is computed afresh instead of being kept
+// live, as a 32-wide array of registers, from its first evaluation.
+__device__ __forceinline__ float fresh(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Correctly rounded square root for t in [2^-96, FLT_MAX]: the hardware
 // square root (within one ulp) is corrected to the nearest float by testing
 // the residuals against its two neighbours (Tuckerman's test, exact with
@@ -278,6 +286,29 @@ __device__ __forceinline__ void group_importances(const float (&x)[QK], const fl
   else group_importances_<false>(x, q, r.sigma2, w);
 }
 
+// Importances with q = 1 for elements OFF .. OFF+N-1 only, written in place
+// (the fallback of a sub-block that has no importance at all): the values
+// group_importances gives those elements without an imatrix.
+template <bool VAR, int OFF, int N>
+__device__ __forceinline__ void unit_importances(const float (&x)[QK], const RowImp& r, float (&w)[QK]) {
+  auto fill = [&](auto m) {
+#pragma unroll
+    for (int i = OFF; i < OFF + N; ++i) w[i] = m(x[i]);
+  };
+  if (VAR && r.mode != QR_W_SQRT_SIGMA2_X2) {
+    switch (r.mode) {
+      case QR_W_X2: fill([&](float v) { return magnitude<QR_W_X2>(v, r); }); break;
+      case QR_W_ABS_X: fill([&](float v) { return magnitude<QR_W_ABS_X>(v, r); }); break;
+      case QR_W_SIGMA2_PLUS_X2: fill([&](float v) { return magnitude<QR_W_SIGMA2_PLUS_X2>(v, r); }); break;
+      case QR_W_SIGMA_PLUS_ABS_X: fill([&](float v) { return magnitude<QR_W_SIGMA_PLUS_ABS_X>(v, r); }); break;
+      default: fill([&](float v) { return magnitude<QR_W_IMATRIX_ONLY>(v, r); }); break;
+    }
+    return;
+  }
+  if (r.normal) fill([&](float v) { return sqrt_cr(fma_(v, v, r.sigma2), true); });
+  else fill([&](float v) { return sqrt_cr(fma_(v, v, r.sigma2), false); });
+}
+
 // -------------------------------------------------------------------------
 // greedy flip pass [WT 一]
 //
@@ -287,22 +318,28 @@ __device__ __forceinline__ void group_importances(const float (&x)[QK], const fl
 // A' = A + s*w_j*y_j and B' = B + w_j*(2*s*l_j + 1). A pass that keeps no
 // move ends the loop for the wave; lanes that kept none repeat a pass whose
 // every decision is unchanged, so their result is the same.
-template <int F, bool ZERO_LO>
-__device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&w)[QK], const float (&wy)[QK],
-                                            float lo, float hi, float (&L)[QK], float& A_io, float& B_io) {
+//
+// The pass covers elements OFF .. OFF+N-1. yw(j, y, wy) gives y_j and the
+// product w_j*y_j: the solvers form them from arrays they hold anyway, so no
+// 32-wide array of either stays live (that is what keeps the solvers within
+// 128 VGPRs, four waves per SIMD).
+template <int F, bool ZERO_LO, int OFF = 0, int N = QK, class YW>
+__device__ __forceinline__ void flip_passes(YW yw, const float (&w)[QK], float lo, float hi, float (&L)[QK],
+                                            float& A_io, float& B_io) {
   float A = A_io, B = B_io;
-#pragma unroll 1
-  for (int p = 0; p < F; ++p) {
+  auto pass = [&]() {
     bool changed = false;
 #pragma unroll
-    for (int j = 0; j < QK; ++j) {
+    for (int j = OFF; j < OFF + N; ++j) {
+      float y, wy;
+      yw(j, y, wy);
       const float t = L[j] * A;
-      const float e = fma_(y[j], B, -t);
+      const float e = fma_(y, B, -t);
       const uint32_t sg = (fbits(A) ^ fbits(e)) & 0x80000000u;
       const float s = __builtin_bit_cast(float, 0x3f800000u | sg);    // +-1
       const float s2 = __builtin_bit_cast(float, 0x40000000u | sg);   // +-2
       const float lp = L[j] + s;
-      const float A1 = fma_(s, wy[j], A);
+      const float A1 = fma_(s, wy, A);
       const float B1 = fma_(w[j], fma_(s2, L[j], 1.0f), B);
       // levels [0, hi]: lp >= +0 and lp <= hi is one unsigned compare of
       // the bit patterns (lp is never -0 here; negative values compare high)
@@ -313,7 +350,16 @@ __device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&
       L[j] = keep ? lp : L[j];
       changed |= keep;
     }
-    if (!__any(changed)) break;
+    return changed;
+  };
+  if constexpr (F == 1) {
+    // one pass, straight-line: no loop out of which y_j and w_j*y_j could be
+    // hoisted into 32-wide arrays
+    pass();
+  } else {
+#pragma unroll 1
+    for (int p = 0; p < F; ++p)
+      if (!__any(pass())) break;
   }
   A_io = A;
   B_io = B;
@@ -322,75 +368,16 @@ __device__ __forceinline__ void flip_passes(const float (&y)[QK], const float (&
 // -------------------------------------------------------------------------
 // symmetric group: levels -NMAX .. NMAX-1, one scale
 
-template <int NMAX, bool BF16, bool VAR>
-__device__ __forceinline__ float solve_sym(const void* lds, int g, const float* __restrict__ q, const RowImp& imp,
-                                           float (&L)[QK]) {
+// Symmetric fit of elements OFF .. OFF+N-1 of a group: the whole group for
+// the 32-weight types, a 16-weight sub-block of Q6_K.
+//
+// The products w*x live only while the trials run; the flip pass forms them
+// again rather than keeping that array live next to the levels.
+template <int NMAX, int OFF, int N>
+__device__ __forceinline__ float sym_fit_part(const float (&x)[QK], const float (&w)[QK], float (&L)[QK]) {
   constexpr float LO = (float)-NMAX, HI = (float)(NMAX - 1);
-  float x[QK], w[QK], wx[QK];
-  load_group<BF16>(lds, g, x);
-  group_importances<VAR>(x, q, imp, w);
-  {  // a group with no importance at all falls back to q = 1
-    uint32_t any = 0;
-#pragma unroll
-    for (int i = 0; i < QK; ++i) any |= fbits(w[i]) & 0x7fffffffu;
-    if (any == 0) group_importances<VAR>(x, nullptr, imp, w);
-  }
   // element of largest magnitude, first one on ties: from max and min, with
   // a scan only when +a and -a are both present
-  float xmax = x[0], xmin = x[0];
-#pragma unroll
-  for (int i = 1; i < QK; ++i) { xmax = fmaxf(xmax, x[i]); xmin = fminf(xmin, x[i]); }
-  const float amax = fmaxf(xmax, -xmin);
-  float xm = (xmax > -xmin) ? xmax : xmin;
-  if (xmax == -xmin) {
-    xm = x[QK - 1];
-#pragma unroll
-    for (int i = QK - 2; i >= 0; --i) xm = (fabsf(x[i]) == amax) ? x[i] : xm;
-  }
-#pragma unroll
-  for (int i = 0; i < QK; ++i) wx[i] = w[i] * x[i];
-
-  // Trial scales: the largest element maps to -(NMAX + step*k); each trial
-  // is scored by sumlx^2/suml2, compared by cross multiplication in double.
-  bool have = false;
-  float bS1 = 0.0f, bS2 = 0.0f, bis = 0.0f;
-  if (amax > 0.0f) {
-#pragma unroll
-    for (int k = 0; k < SYM_CAND; ++k) {
-      const float c = (float)NMAX + CAND_STEP * (float)cand_offset(k);
-      const float is = -c / xm;
-      float S1 = 0.0f, S2 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < QK; ++i) {
-        const float l = med3(rne(x[i] * is), LO, HI);
-        S1 = fma_(wx[i], l, S1);
-        S2 = fma_(w[i] * l, l, S2);
-      }
-      const bool ok = __builtin_isfinite(is) && (S2 > 0.0f);
-      const bool better = ok && (!have || ((double)S1 * (double)S1) * (double)bS2 >
-                                              ((double)bS1 * (double)bS1) * (double)S2);
-      if (better) { have = true; bS1 = S1; bS2 = S2; bis = is; }
-    }
-  }
-  if (!have) {
-#pragma unroll
-    for (int i = 0; i < QK; ++i) L[i] = 0.0f;
-    return 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < QK; ++i) L[i] = med3(rne(x[i] * bis), LO, HI);
-  float A = bS1, B = bS2;
-  flip_passes<SYM_FLIP_PASSES, false>(x, w, wx, LO, HI, L, A, B);
-  return A / B;
-}
-
-// Symmetric fit of elements OFF .. OFF+N-1 of a group (the 16-weight
-// sub-blocks of Q6_K): the steps of solve_sym on that part alone, the
-// importances computed once for the whole group.
-template <int NMAX, int OFF, int N>
-__device__ __forceinline__ float sym_fit_part(const float (&x)[QK], const float (&w)[QK], const float (&wx)[QK],
-                                              float (&L)[QK]) {
-  constexpr float LO = (float)-NMAX, HI = (float)(NMAX - 1);
   float xmax = x[OFF], xmin = x[OFF];
 #pragma unroll
   for (int i = OFF + 1; i < OFF + N; ++i) { xmax = fmaxf(xmax, x[i]); xmin = fminf(xmin, x[i]); }
@@ -401,13 +388,17 @@ __device__ __forceinline__ float sym_fit_part(const float (&x)[QK], const float 
 #pragma unroll
     for (int i = OFF + N - 2; i >= OFF; --i) xm = (fabsf(x[i]) == amax) ? x[i] : xm;
   }
+  // Trial scales: the largest element maps to -(NMAX + step*k); each trial
+  // is scored by sumlx^2/suml2, compared by cross multiplication in double.
   bool have = false;
   float bS1 = 0.0f, bS2 = 0.0f, bis = 0.0f;
   if (amax > 0.0f) {
+    float wx[QK];
+#pragma unroll
+    for (int i = OFF; i < OFF + N; ++i) wx[i] = w[i] * x[i];
 #pragma unroll
     for (int k = 0; k < SYM_CAND; ++k) {
-      const float c = (float)NMAX + CAND_STEP * (float)cand_offset(k);
-      const float is = -c / xm;
+      const float is = -((float)NMAX + CAND_STEP * (float)cand_offset(k)) / xm;
       float S1 = 0.0f, S2 = 0.0f;
 #pragma unroll
       for (int i = OFF; i < OFF + N; ++i) {
@@ -421,36 +412,31 @@ __device__ __forceinline__ float sym_fit_part(const float (&x)[QK], const float 
       if (better) { have = true; bS1 = S1; bS2 = S2; bis = is; }
     }
   }
-  if (!have) {
-#pragma unroll
-    for (int i = OFF; i < OFF + N; ++i) L[i] = 0.0f;
-    return 0.0f;
-  }
+  // Without a usable trial, bis = 0 gives zero levels (x is finite) and
+  // A = B = 0 lets the flip pass keep no move; the scale is then 0.
 #pragma unroll
   for (int i = OFF; i < OFF + N; ++i) L[i] = med3(rne(x[i] * bis), LO, HI);
   float A = bS1, B = bS2;
-#pragma unroll 1
-  for (int p = 0; p < SYM_FLIP_PASSES; ++p) {
-    bool changed = false;
+  flip_passes<SYM_FLIP_PASSES, false, OFF, N>(
+      [&](int j, float& y, float& wy) { y = x[j]; wy = w[j] * fresh(x[j]); }, w, LO, HI, L, A, B);
+  return have ? A / B : 0.0f;
+}
+
+// A whole 32-weight group: importances (with the fallback to q = 1 for a
+// group that has none), then the fit.
+template <int NMAX, bool BF16, bool VAR>
+__device__ __forceinline__ float solve_sym(const void* lds, int g, const float* __restrict__ q, const RowImp& imp,
+                                           float (&L)[QK]) {
+  float x[QK], w[QK];
+  load_group<BF16>(lds, g, x);
+  group_importances<VAR>(x, q, imp, w);
+  {  // a group with no importance at all falls back to q = 1
+    uint32_t any = 0;
 #pragma unroll
-    for (int j = OFF; j < OFF + N; ++j) {
-      const float t = L[j] * A;
-      const float e = fma_(x[j], B, -t);
-      const uint32_t sg = (fbits(A) ^ fbits(e)) & 0x80000000u;
-      const float sv = __builtin_bit_cast(float, 0x3f800000u | sg);
-      const float s2 = __builtin_bit_cast(float, 0x40000000u | sg);
-      const float lp = L[j] + sv;
-      const float A1 = fma_(sv, wx[j], A);
-      const float B1 = fma_(w[j], fma_(s2, L[j], 1.0f), B);
-      const bool keep = ((A1 * A1) * B > (A * A) * B1) && (B1 > 0.0f) && (lp >= LO) && (lp <= HI);
-      A = keep ? A1 : A;
-      B = keep ? B1 : B;
-      L[j] = keep ? lp : L[j];
-      changed |= keep;
-    }
-    if (!__any(changed)) break;
+    for (int i = 0; i < QK; ++i) any |= fbits(w[i]) & 0x7fffffffu;
+    if (any == 0) group_importances<VAR>(x, nullptr, imp, w);
   }
-  return A / B;
+  return sym_fit_part<NMAX, 0, QK>(x, w, L);
 }
 
 // -------------------------------------------------------------------------
@@ -482,8 +468,10 @@ __device__ __forceinline__ void fit_dm(float Sw_, float Sx_, float Sl_, float Sl
   score = dd * Slx + mm * Sx;
 }
 
-// Returns (d, m) and the levels; x, w are left in the arrays for the caller
-// (w: importances; x: overwritten).
+// Returns (d, m) and the levels. The trials run in one sweep over the
+// elements with one set of sums per trial (each sum still in ascending
+// element order); only x, w and the levels are held as 32-wide arrays, w*x,
+// x - lo and x - m being formed again where needed, with the same roundings.
 template <int NMAX, bool K4, bool BF16, bool VAR>
 __device__ __forceinline__ void solve_asym(const void* lds, int g, const float* __restrict__ q, const RowImp& imp,
                                            float (&L)[QK], float& d_out, float& m_out, float& sw_out) {
@@ -508,75 +496,75 @@ __device__ __forceinline__ void solve_asym(const void* lds, int g, const float* 
   if (K4) lo = fminf(lo, 0.0f);
   sw_out = Sw;      // the group's total importance (after any fallback)
 
-  if (hi == lo || !(Sw > 0.0f)) {   // constant group, or importances that underflow to 0
+  // A constant group (range 0: no finite trial) or importances that
+  // underflow to 0 have no usable trial; they take the path below with zero
+  // levels and return d = 0, m = lo.
+  const float range = hi - lo;
+  float is[ASYM_CAND], Sl[ASYM_CAND], Sll[ASYM_CAND], Slx[ASYM_CAND];
 #pragma unroll
-    for (int i = 0; i < QK; ++i) L[i] = 0.0f;
-    d_out = 0.0f;
-    m_out = lo;
-    return;
+  for (int k = 0; k < ASYM_CAND; ++k) {
+    is[k] = ((float)NMAX + CAND_STEP * (float)cand_offset(k)) / range;
+    Sl[k] = 0.0f;
+    Sll[k] = 0.0f;
+    Slx[k] = 0.0f;
   }
-  float wx[QK], xs[QK];
   float Sx = 0.0f;
 #pragma unroll
   for (int i = 0; i < QK; ++i) {
-    wx[i] = w[i] * x[i];
-    xs[i] = x[i] - lo;
-    Sx = Sx + wx[i];
+    const float wx = w[i] * x[i];
+    const float xs = x[i] - lo;
+    Sx = Sx + wx;
+    // 0 <= xs <= range, so rint(xs * is) lies in [0, NMAX] for these
+    // trials and the clamp to the level range never acts.
+#pragma unroll
+    for (int k = 0; k < ASYM_CAND; ++k) {
+      const float l = rne(xs * is[k]);
+      const float wl = w[i] * l;
+      Sl[k] = Sl[k] + wl;
+      Sll[k] = fma_(wl, l, Sll[k]);
+      Slx[k] = fma_(wx, l, Slx[k]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // element by element: no 32-wide temporaries
   }
-  const float range = hi - lo;
+  // all sums complete here, before the branches of the fits below
+  Sx = fresh(Sx);
+#pragma unroll
+  for (int k = 0; k < ASYM_CAND; ++k) {
+    Sl[k] = fresh(Sl[k]);
+    Sll[k] = fresh(Sll[k]);
+    Slx[k] = fresh(Slx[k]);
+  }
   bool have = false;
   float bis = 0.0f, bSl = 0.0f, bSll = 0.0f, bSlx = 0.0f;
   double bm = 0.0, bscore = 0.0;
 #pragma unroll
   for (int k = 0; k < ASYM_CAND; ++k) {
-    const float is = ((float)NMAX + CAND_STEP * (float)cand_offset(k)) / range;
-    // 0 <= xs <= range, so rint(xs * is) lies in [0, NMAX] for these
-    // trials and the clamp to the level range never acts.
-    float Sl = 0.0f, Sll = 0.0f, Slx = 0.0f;
-#pragma unroll
-    for (int i = 0; i < QK; ++i) {
-      const float l = rne(xs[i] * is);
-      const float wl = w[i] * l;
-      Sl = Sl + wl;
-      Sll = fma_(wl, l, Sll);
-      Slx = fma_(wx[i], l, Slx);
-    }
     double d, m, score;
-    fit_dm<K4>(Sw, Sx, Sl, Sll, Slx, d, m, score);
-    const bool ok = __builtin_isfinite(is);
+    fit_dm<K4>(Sw, Sx, Sl[k], Sll[k], Slx[k], d, m, score);
+    const bool ok = __builtin_isfinite(is[k]) && (Sw > 0.0f);
     if (ok && (!have || score > bscore)) {
-      have = true; bis = is; bm = m; bscore = score; bSl = Sl; bSll = Sll; bSlx = Slx;
+      have = true; bis = is[k]; bm = m; bscore = score; bSl = Sl[k]; bSll = Sll[k]; bSlx = Slx[k];
     }
   }
-  if (!have) {
+  // Without a usable trial, bis = 0 gives zero levels (0 <= x - lo, finite)
+  // and A = B = 0 lets the flip pass keep no move.
+  const float lo_ = fresh(lo);
 #pragma unroll
-    for (int i = 0; i < QK; ++i) L[i] = 0.0f;
-    d_out = 0.0f;
-    m_out = lo;
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < QK; ++i) L[i] = rne(xs[i] * bis);
+  for (int i = 0; i < QK; ++i) L[i] = rne((x[i] - lo_) * bis);
 
   // flips with the offset of the winning trial held fixed, then a joint refit
   const float mf = (float)bm;
-  float y[QK], wy[QK];
-  load_group<BF16>(lds, g, x);
-#pragma unroll
-  for (int i = 0; i < QK; ++i) {
-    y[i] = x[i] - mf;
-    wy[i] = w[i] * y[i];
-  }
   float A = fma_(-mf, bSl, bSlx), B = bSll;
-  flip_passes<ASYM_FLIP_PASSES, true>(y, w, wy, 0.0f, HI, L, A, B);
+  flip_passes<ASYM_FLIP_PASSES, true>(
+      [&](int j, float& y, float& wy) { y = x[j] - mf; wy = w[j] * y; }, w, 0.0f, HI, L, A, B);
 
-  float Sl = 0.0f;
+  float Slf = 0.0f;
 #pragma unroll
-  for (int i = 0; i < QK; ++i) Sl = Sl + w[i] * L[i];
+  for (int i = 0; i < QK; ++i) Slf = Slf + w[i] * L[i];
   double d, m, score;
-  fit_dm<K4>(Sw, Sx, Sl, B, fma_(mf, Sl, A), d, m, score);
-  d_out = (float)d;
-  m_out = (float)m;
+  fit_dm<K4>(Sw, Sx, Slf, B, fma_(mf, Slf, A), d, m, score);
+  d_out = have ? (float)d : 0.0f;
+  m_out = have ? (float)m : lo;
 }
 
 // -------------------------------------------------------------------------
@@ -701,14 +689,10 @@ static_assert((size_t)QR_MAX_ROW_F32 / QK * LDS_F32_STRIDE * 4 + 8 * MAX_ROW_WAV
                   (size_t)QR_MAX_ROW_BF16 / QK * LDS_BF16_STRIDE * 2 + 8 * MAX_ROW_WAVES <= LDS_PER_WORKGROUP,
               "the longest row and the partial sums fit in one workgroup's LDS");
 
-// Waves per SIMD the register allocation aims at: the symmetric types fit
-// 128 VGPRs and run fastest at 4 (the LDS limit of a 4096-value fp32 row);
-// the asymmetric solver needs more registers and runs fastest at 3
-// (measured: at 4, Q4_1/Q5_1 spill and take 2.9x as long, Q4_K 10% longer;
-// at 3, Q6_K takes 5-10% longer).
-__host__ __device__ constexpr int row_waves_per_eu(int t) {
-  return (t == QR_Q4_1 || t == QR_Q5_1 || t == QR_Q4_K) ? 3 : 4;
-}
+// Waves per SIMD the register allocation aims at: four (the LDS limit of a
+// 4096-value fp32 row). The solvers keep three 32-wide arrays live (x, w and
+// the levels), which fits in 128 VGPRs without spills.
+__host__ __device__ constexpr int row_waves_per_eu(int) { return 4; }
 
 template <int TYPE, bool BF16, bool VAR>
 __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(row_waves_per_eu(TYPE)))) void k_quantize_rows(const void* __restrict__ x,
@@ -750,7 +734,7 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
     float L[QK];
 
     if constexpr (TYPE == QR_Q6_K) {  // lanes 8s .. 8s+7: the eight 32-weight groups of a super-block
-      float x[QK], w[QK], wx[QK];
+      float x[QK], w[QK];
       load_group<BF16>(lds_raw, g, x);
       group_importances<VAR>(x, qg, imp, w);
       {  // a sub-block (16 weights) with no importance at all falls back to q = 1
@@ -760,20 +744,11 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
           any0 |= fbits(w[i]) & 0x7fffffffu;
           any1 |= fbits(w[16 + i]) & 0x7fffffffu;
         }
-        if (any0 == 0 || any1 == 0) {
-          float wu[QK];
-          group_importances<VAR>(x, nullptr, imp, wu);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            w[i] = any0 == 0 ? wu[i] : w[i];
-            w[16 + i] = any1 == 0 ? wu[16 + i] : w[16 + i];
-          }
-        }
+        if (any0 == 0) unit_importances<VAR, 0, 16>(x, imp, w);
+        if (any1 == 0) unit_importances<VAR, 16, 16>(x, imp, w);
       }
-#pragma unroll
-      for (int i = 0; i < QK; ++i) wx[i] = w[i] * x[i];
-      const float d0 = sym_fit_part<32, 0, 16>(x, w, wx, L);    // sub-block 2j
-      const float d1 = sym_fit_part<32, 16, 16>(x, w, wx, L);   // sub-block 2j+1
+      const float d0 = sym_fit_part<32, 0, 16>(x, w, L);    // sub-block 2j
+      const float d1 = sym_fit_part<32, 16, 16>(x, w, L);   // sub-block 2j+1
       const float amx = oct_max(fmaxf(fabsf(d0), fabsf(d1)));   // over the super-block's 16 sub-blocks
       const _Float16 d16 = (_Float16)(amx / 127.0f);
       const float dA = (float)d16;
