@@ -87,19 +87,19 @@ __device__ __forceinline__ float fresh(float v) {
 }
 
 // Correctly rounded square root for t in [2^-96, FLT_MAX]: the hardware
-// square root (within one ulp) is corrected to the nearest float by testing
-// the residuals against its two neighbours (Tuckerman's test, exact with
-// fused multiply-adds). Outside that range the library sqrtf is used.
+// square root s (within one ulp) is corrected to the nearest float by
+// Tuckerman's test, exact with fused multiply-adds. The sign of the exact
+// residual t - s*s says on which side of sqrt(t) s lies, so only the
+// neighbour n on the other side can be nearer: n replaces s iff
+// t - n*s > 0 (n above s) or t - n*s <= 0 (n below s). Outside that range
+// the library sqrtf is used.
 __device__ __forceinline__ float sqrt_cr(float t, bool normal_range) {
   if (!normal_range) return sqrtf(t);
-  float s = __builtin_amdgcn_sqrtf(t);
-  float sdn = __builtin_bit_cast(float, __builtin_bit_cast(int32_t, s) - 1);
-  float sup = __builtin_bit_cast(float, __builtin_bit_cast(int32_t, s) + 1);
-  float rdn = fma_(-sdn, s, t);
-  float rup = fma_(-sup, s, t);
-  s = (rdn <= 0.0f) ? sdn : s;
-  s = (rup > 0.0f) ? sup : s;
-  return s;
+  const float s = __builtin_amdgcn_sqrtf(t);
+  const bool up = fma_(-s, s, t) > 0.0f;   // s < sqrt(t)
+  const float n = __builtin_bit_cast(float, __builtin_bit_cast(int32_t, s) + (up ? 1 : -1));
+  const bool pos = fma_(-n, s, t) > 0.0f;
+  return pos == up ? n : s;
 }
 
 // -------------------------------------------------------------------------
@@ -139,30 +139,38 @@ __device__ __forceinline__ uint32_t oct_or(uint32_t v) {
 // double, reduced across the wave.
 template <bool BF16>
 __device__ __forceinline__ double stage_row(const void* __restrict__ xrow, int n, void* lds, int tid, int nthreads) {
+  // Thread tid moves 16-byte vectors tid, tid + nthreads, ... As nthreads is
+  // a multiple of 64, each step advances the vector by nthreads/8 (fp32) or
+  // nthreads/4 (bf16) whole groups and keeps its place inside the group, so
+  // both addresses advance by a fixed stride.
   double acc = 0.0;
   if (!BF16) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(xrow);
-    float* dst = reinterpret_cast<float*>(lds);
     const int n4 = n >> 2;
+    const f32x4* src = reinterpret_cast<const f32x4*>(xrow) + tid;
+    float* dst = reinterpret_cast<float*>(lds) + (tid >> 3) * LDS_F32_STRIDE + (tid & 7) * 4;
+    const int dstep = (nthreads >> 3) * LDS_F32_STRIDE;
 #pragma unroll 8
     for (int i = tid; i < n4; i += nthreads) {
-      f32x4 v = __builtin_nontemporal_load(src + i);
-      const int e = i << 2;
-      *reinterpret_cast<f32x4*>(dst + (e >> 5) * LDS_F32_STRIDE + (e & 31)) = v;
+      f32x4 v = __builtin_nontemporal_load(src);
+      *reinterpret_cast<f32x4*>(dst) = v;
+      src += nthreads;
+      dst += dstep;
       acc = __builtin_fma((double)v.x, (double)v.x, acc);
       acc = __builtin_fma((double)v.y, (double)v.y, acc);
       acc = __builtin_fma((double)v.z, (double)v.z, acc);
       acc = __builtin_fma((double)v.w, (double)v.w, acc);
     }
   } else {
-    const u32x4* src = reinterpret_cast<const u32x4*>(xrow);
-    uint16_t* dst = reinterpret_cast<uint16_t*>(lds);
     const int n8 = n >> 3;
+    const u32x4* src = reinterpret_cast<const u32x4*>(xrow) + tid;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(lds) + (tid >> 2) * LDS_BF16_STRIDE + (tid & 3) * 8;
+    const int dstep = (nthreads >> 2) * LDS_BF16_STRIDE;
 #pragma unroll 8
     for (int i = tid; i < n8; i += nthreads) {
-      u32x4 v = __builtin_nontemporal_load(src + i);
-      const int e = i << 3;
-      *reinterpret_cast<u32x4*>(dst + (e >> 5) * LDS_BF16_STRIDE + (e & 31)) = v;
+      u32x4 v = __builtin_nontemporal_load(src);
+      *reinterpret_cast<u32x4*>(dst) = v;
+      src += nthreads;
+      dst += dstep;
       const uint32_t p[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -335,9 +343,9 @@ __device__ __forceinline__ void flip_passes(YW yw, const float (&w)[QK], float l
       yw(j, y, wy);
       const float t = L[j] * A;
       const float e = fma_(y, B, -t);
-      const uint32_t sg = (fbits(A) ^ fbits(e)) & 0x80000000u;
-      const float s = __builtin_bit_cast(float, 0x3f800000u | sg);    // +-1
-      const float s2 = __builtin_bit_cast(float, 0x40000000u | sg);   // +-2
+      const float sg = __builtin_bit_cast(float, fbits(A) ^ fbits(e));   // sign: sign(A) * sign(e)
+      const float s = __builtin_copysignf(1.0f, sg);    // +-1
+      const float s2 = __builtin_copysignf(2.0f, sg);   // +-2
       const float lp = L[j] + s;
       const float A1 = fma_(s, wy, A);
       const float B1 = fma_(w[j], fma_(s2, L[j], 1.0f), B);
