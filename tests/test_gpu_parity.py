@@ -105,6 +105,26 @@ def test_weight_rows_small(qr, t, bf16, qkind):
 
 @pytest.mark.parametrize("t", WEIGHT_TYPES)
 @pytest.mark.parametrize("bf16", [False, True])
+def test_grouped_rows_with_odd_group_sizes(qr, t, bf16):
+    # rows whose groups leave part of the last wave idle (224, 72 and 32
+    # groups), an odd number of rows per imatrix group and in all, and one
+    # imatrix group whose importances are all zero
+    rng = np.random.default_rng(zlib.crc32(f"odd-groups/{t}/{bf16}".encode()))
+    for n, rows_per_group, n_groups in ((7168, 3, 3), (2304, 1, 5), (1024, 5, 3)):
+        x = (0.02 * rng.standard_t(5, (n_groups * rows_per_group, n))).astype(F32)
+        x *= np.exp(0.3 * rng.standard_normal((x.shape[0], 1))).astype(F32)
+        q = np.exp(1.5 * rng.standard_normal((n_groups, n))).astype(F32)
+        q[1] = 0.0
+        say(f"case {t} bf16={bf16} grouped shape={x.shape} rows_per_group={rows_per_group}")
+        got = qr.qr_quantize_rows_grouped(t, to_dev(x, bf16), torch.from_numpy(q).cuda(),
+                                          rows_per_group).cpu().numpy()
+        xh = host_values(x, bf16)
+        ref = oracle.quantize_rows_grouped(t, xh, q, rows_per_group, threads=8)
+        assert_rows_equal(t, got, ref, xh, lambda r: q[r // rows_per_group])
+
+
+@pytest.mark.parametrize("t", WEIGHT_TYPES)
+@pytest.mark.parametrize("bf16", [False, True])
 def test_longest_rows(qr, t, bf16):
     # rows of QR_MAX_ROW values: the whole row staged in LDS, eight waves
     # each solving several groups
