@@ -44,6 +44,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "qrow.h"
 #include "qr_internal.h"
 
@@ -1226,17 +1228,24 @@ int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_r
   if (waves > MAX_ROW_WAVES) waves = MAX_ROW_WAVES;
   const size_t lds = (size_t)n_groups * (BF16 ? LDS_BF16_STRIDE * 2 : LDS_F32_STRIDE * 4) + 8 * (size_t)waves;
   // Rows above 64 KB of LDS need the kernel's dynamic-LDS limit raised, once
-  // per device (the attribute belongs to the device the call runs on).
+  // per device. The attribute is set on the current device, so for a stream
+  // of another device that device is made current for the call. The flags
+  // may be read and set by several host threads at once.
   constexpr int MAX_DEVICES = 64;
-  static bool attr_set[MAX_DEVICES] = {};
+  static std::atomic<bool> attr_set[MAX_DEVICES];
   if (lds > 65536) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipGetDevice failed");
-    if (dev < 0 || dev >= MAX_DEVICES || !attr_set[dev]) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WORKGROUP);
+    int sdev = dev;
+    if (stream && hipStreamGetDevice(stream, &sdev) != hipSuccess)
+      return qr_fail(QR_EDEVICE, "hipStreamGetDevice failed");
+    if (sdev < 0 || sdev >= MAX_DEVICES || !attr_set[sdev].load(std::memory_order_acquire)) {
+      if (sdev != dev && hipSetDevice(sdev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipSetDevice failed");
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WORKGROUP);
+      if (sdev != dev && hipSetDevice(dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipSetDevice failed");
       if (e != hipSuccess) return qr_fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-      if (dev >= 0 && dev < MAX_DEVICES) attr_set[dev] = true;
+      if (sdev >= 0 && sdev < MAX_DEVICES) attr_set[sdev].store(true, std::memory_order_release);
     }
   }
   hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE * waves), lds, stream, x, imatrix, n_per_row,
