@@ -32,11 +32,12 @@ HBM_PEAK_GBS = 8000.0
 # (packed fp32 instructions are not used, so one instruction = one op/lane)
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # Operations of the method per Q4_K weight (3 trial scales, 1 flip pass),
-# counted from the oracle's loops: see the operation table in the design
-# notes (row statistic 2, importance + zero test 4, range 2, w*x etc. 4,
-# trials 24, block solves 2.5, winner codes 4, flip setup 2, flip pass 19,
-# refit sums 2, Q4_K re-round and scales 5.5).
+# counted from the oracle's loops: row statistic 2, importance + zero test 4,
+# range 2, w*x etc. 4, trials 24, block solves 2.5, winner codes 4, flip
+# setup 2, flip pass 19, refit sums 2, Q4_K re-round and scales 5.5.
 ALG_OPS_PER_WEIGHT_Q4K = 71.0
+# MI355X dense int8 matrix-core peak (no sparsity), Tera-ops per second
+INT8_PEAK_TOPS = 5000.0
 METRIC = "Gweights/s quantized (Q4_0, Q4_K) + achieved HBM GB/s fraction"
 COUNTERS = os.path.join(ROOT, "profiles", "q4_k_11008x4096_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "post_weight_quantization_row_amd", "csrc", "qrow.hip")
@@ -242,7 +243,8 @@ def mix_stack_entry(dev, flush):
 IMATRIX_WORKLOADS = ("imatrix_moe_256x8_4096x7168", "imatrix_moe_slots_256x8_4096x2048",
                      "imatrix_dense_4096x4096")
 MATMUL_WORKLOADS = ("mmq_q4_k_11008x4096_t1", "mmq_q4_0_4096x4096_t8",
-                    "mmq_q4_k_11008x4096_t1_q8_k16", "mmq_q4_0_4096x4096_t8_q8_k16")
+                    "mmq_q4_k_11008x4096_t1_q8_k16", "mmq_q4_0_4096x4096_t8_q8_k16",
+                    "mmq_q4_k_11008x4096_t512")
 ACT_WORKLOADS = ("q8_k64_8192x7168", "q8_k16_8192x7168")
 STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
@@ -462,6 +464,16 @@ def main():
             extra[name] = {"ms": round(mi, 5), "alg_bytes": nb, "G_elements_per_s": round(n_el / mi / 1e6, 3),
                            "GB/s": round(nb / (mi * 1e-3) / 1e9, 1),
                            "hbm_frac": round(nb / (mi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if name.startswith("mmq_"):
+                # integer multiply-adds against the dense int8 matrix-core peak
+                base = name
+                for suffix in ("_q8_k64", "_q8_k16"):
+                    if base.endswith(suffix):
+                        base = base[:-len(suffix)]
+                wl = synth.WORKLOADS[base]
+                tops = 2.0 * wl["n_out"] * wl["n_tok"] * wl["n_in"] / (mi * 1e-3) / 1e12
+                extra[name]["int8_Tops"] = round(tops, 2)
+                extra[name]["int8_mfma_frac"] = round(tops / INT8_PEAK_TOPS, 4)
         extra["weighting_ablation_q4_k_11008x4096"] = weighting_ablation(x, q, flush)
         extra["subscale_fit_q4_k_11008x4096"] = subscale_fit_comparison(x, q, flush)
         extra["mix_q4_k_m_stack_7b"] = mix_stack_entry(dev, flush)

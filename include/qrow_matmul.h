@@ -44,7 +44,10 @@ extern "C" {
  * dmin*mn_j * bsum_j), and the scales are applied in fp32. The fp32 sums are
  * taken in a fixed order (reproducible bit for bit); against the exact
  * product each output is within (n_in/1024 + 9) * 2^-24 of
- * sum_i (|scale part_i| + |offset part_i|) * |A[t][i]|.
+ * S = sum_i (|scale part_i| + |offset part_i|) * |A[t][i]|. From 17 tokens
+ * on, the integer products run on the int8 matrix cores (tiles of 64 tokens
+ * x 64 rows) and the per-block sums are accumulated in double: each output
+ * is then within 2^-24 |y| + 8 * 2^-24 S, inside the same bound.
  * Limits: n_in a positive multiple of 128 (256 for Q4_K), at most
  * QR_MATMUL_MAX_IN. n_out == 0 or n_tok == 0 is a no-op.
  */

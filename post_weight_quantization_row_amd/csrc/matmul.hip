@@ -440,6 +440,242 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k(const uint8_t* __res
   }
 }
 
+// -------------------------------------------------------------------------
+// Many tokens: int8 matrix cores [Q8 修复方案: the same integer dot products
+// and code-sum fold].
+//
+// With Q8_K_128 activations and at least MF_MIN_TOK tokens, a workgroup
+// of four waves owns a tile of 64 tokens x 64 weight rows. K advances one
+// activation block (128 values, four 32-weight groups) per step:
+//  * each of the 256 threads decodes one (row, group) of the tile to 32 int8
+//    codes in LDS -- the symmetric types as signed levels, so that they need
+//    no offset fold -- with its scale parts; the tile's activation blocks
+//    (codes, scale, int16 code sums) are staged beside them. The global
+//    loads for the next step are issued before this step's products.
+//  * each wave owns 32 tokens x 32 rows (2 x 2 tiles of 16 x 16): per group
+//    one v_mfma_i32_16x16x32_i8 per tile (activations as A, weights as B)
+//    gives the exact int32 dot products; they take the group's scale parts
+//    with fp32 fused multiply-adds, and per activation block the sum takes
+//    the activation scale and is added to a double accumulator. Q6_K's two
+//    16-weight halves, each with its own scale, are two products with the
+//    other half's codes zeroed.
+// A block's sum has at most eight roundings, the accumulation is nearly
+// exact and the result is rounded once: each output is within
+// 2^-24 |y| + 8 * 2^-24 S of the exact product (S = sum of the terms'
+// magnitudes), whatever n_in: inside the bound of the lane-parallel path.
+//
+// Output layout of the 16 x 16 x 32 product (checked on the device): lane l
+// holds D[4 (l / 16) + v][l % 16], v = 0..3; A[i][k] and B[k][j] come from
+// lane l with i or j = l % 16 and k = 8 (l / 16) + byte.
+
+constexpr int MF_TOK = 64, MF_ROWS = 64, MF_THREADS = 256;
+constexpr int MF_ROW_WORDS = 36;         // LDS words per token or row: 4 groups x 8 code words + 4 pad
+// Fewer tokens: the lane-parallel kernel. Measured on the 11008x4096 Q4_K
+// matrix: 51 against 51 us at 16 tokens, 50 against 70 at 24, 50 against 86
+// at 32; at 8 tokens the lane-parallel kernel takes 11 us.
+constexpr int MF_MIN_TOK = 17;
+constexpr int MF_ACT_BYTES = 140;        // a Q8_K_128 block: d, 128 codes, 4 int16 sums
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// per byte: a code u in [0, 2 off) to the signed level u - off (off = 8, 16, 32)
+template <int TYPE>
+__device__ __forceinline__ uint32_t signed_levels(uint32_t u) {
+  constexpr uint32_t OFF = TYPE == QR_Q4_0 ? 0x08080808u : TYPE == QR_Q5_0 ? 0x10101010u : 0x20202020u;
+  constexpr uint32_t EXT = TYPE == QR_Q4_0 ? 0x1eu : TYPE == QR_Q5_0 ? 0x0eu : 0x06u;   // sign extension
+  const uint32_t v = u ^ OFF;
+  return v | ((v & OFF) * EXT);
+}
+
+// One K step of a tile in LDS. Rows of 36 words (word 8 g + k: code word k
+// of group g) make the operand reads conflict free: the 16 tokens or rows of
+// a product start 36 words apart, in distinct banks.
+struct MfStage {
+  uint32_t aq[MF_TOK][MF_ROW_WORDS];    // activation codes
+  uint32_t wq[MF_ROWS][MF_ROW_WORDS];   // weight codes (symmetric types: signed levels)
+  float wsa[4][MF_ROWS];                // scale part (Q6_K: of the first half)
+  float wsb[4][MF_ROWS];                // offset part, signed (Q6_K: scale of the second half)
+  float ad[MF_TOK];                     // activation scales
+  int32_t asum[4][MF_TOK];              // activation code sums per group
+};
+
+template <int TYPE>
+__global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_matmul_mfma(
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ x, int64_t n_out, int64_t n_tok, int n_in,
+    int64_t w_row_bytes, float* __restrict__ y) {
+  constexpr bool SYM = TYPE == QR_Q4_0 || TYPE == QR_Q5_0 || TYPE == QR_Q6_0;
+  constexpr bool Q6K = TYPE == QR_Q6_K;
+  __shared__ __align__(16) MfStage stage[2];   // double buffer: one barrier per K step
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * MF_ROWS;
+  const int64_t t0 = (int64_t)blockIdx.y * MF_TOK;
+  const int nsteps = n_in / 128;
+  const int64_t x_row_bytes = (int64_t)nsteps * MF_ACT_BYTES;
+
+  // Staging roles: thread tid decodes group tid & 3 of row tid >> 2, and
+  // moves quarter tid & 3 (32 code bytes) of token tid >> 2's block plus one
+  // more word of it: the scale (quarter 0) or a word of code sums (1, 2).
+  const int srow = tid >> 2, sq = tid & 3;
+  const int64_t grow = r0 + srow < n_out ? r0 + srow : n_out - 1;   // rows past the end: unused
+  const uint8_t* wrow = w + grow * w_row_bytes;
+  const bool tok_ok = t0 + srow < n_tok;                            // tokens past the end: zeros
+  const uint8_t* xrow = x + (tok_ok ? t0 + srow : n_tok - 1) * x_row_bytes;
+  const int extra = sq == 0 ? 0 : sq == 1 ? 132 : 136;              // quarter 3 repeats quarter 2's word
+  RawGroup rg;
+  uint32_t av[9];
+  auto load_step = [&](int s) {
+    rg = load_raw<TYPE>(wrow, 4 * s + sq);
+    const uint8_t* blk = xrow + (int64_t)s * MF_ACT_BYTES;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) av[k] = ld32(blk + 4 + 32 * sq + 4 * k);
+    av[8] = ld32(blk + extra);
+  };
+  auto store_step = [&](int s, MfStage& st) {
+    const Group G = unpack<TYPE>(rg, 4 * s + sq);
+    uint4 c0, c1;
+    c0.x = SYM ? signed_levels<TYPE>(G.lo[0]) : G.lo[0];
+    c0.y = SYM ? signed_levels<TYPE>(G.lo[1]) : G.lo[1];
+    c0.z = SYM ? signed_levels<TYPE>(G.lo[2]) : G.lo[2];
+    c0.w = SYM ? signed_levels<TYPE>(G.lo[3]) : G.lo[3];
+    c1.x = SYM ? signed_levels<TYPE>(G.hi[0]) : G.hi[0];
+    c1.y = SYM ? signed_levels<TYPE>(G.hi[1]) : G.hi[1];
+    c1.z = SYM ? signed_levels<TYPE>(G.hi[2]) : G.hi[2];
+    c1.w = SYM ? signed_levels<TYPE>(G.hi[3]) : G.hi[3];
+    *reinterpret_cast<uint4*>(&st.wq[srow][8 * sq]) = c0;
+    *reinterpret_cast<uint4*>(&st.wq[srow][8 * sq + 4]) = c1;
+    st.wsa[sq][srow] = G.sa;
+    st.wsb[sq][srow] = Q6K ? G.sa1 : TYPE == QR_Q4_K ? -G.sb : G.sb;
+    uint4 a0, a1;
+    a0.x = tok_ok ? av[0] : 0u; a0.y = tok_ok ? av[1] : 0u; a0.z = tok_ok ? av[2] : 0u; a0.w = tok_ok ? av[3] : 0u;
+    a1.x = tok_ok ? av[4] : 0u; a1.y = tok_ok ? av[5] : 0u; a1.z = tok_ok ? av[6] : 0u; a1.w = tok_ok ? av[7] : 0u;
+    *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq]) = a0;
+    *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq + 4]) = a1;
+    const uint32_t v = tok_ok ? av[8] : 0u;
+    if (sq == 0) {
+      st.ad[srow] = __builtin_bit_cast(float, v);
+    } else if (sq < 3) {
+      const int g = 2 * (sq - 1);
+      st.asum[g][srow] = (int32_t)(int16_t)(v & 0xffffu);
+      st.asum[g + 1][srow] = (int32_t)(int16_t)(v >> 16);
+    }
+  };
+
+  const int wt = (wave & 1) * 32, wr = (wave >> 1) * 32;   // this wave's tokens and rows in the tile
+  const int li = lane & 15, lk = lane >> 4;
+  double acc[2][2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[a][b][v] = 0.0;
+
+  load_step(0);
+  store_step(0, stage[0]);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) load_step(s + 1);   // in flight during this step's products
+    const MfStage& st = stage[s & 1];
+    // the four groups' terms of the block, summed in fp32 (at most four
+    // roundings of terms of the block), then scaled and added in double
+    float inner[2][2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) inner[a][b][v] = 0.0f;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      long aop[2], bop[2];
+      float sa[2], sb[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        aop[tt] = *reinterpret_cast<const long*>(&st.aq[wt + 16 * tt + li][8 * gi + 2 * lk]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        bop[rt] = *reinterpret_cast<const long*>(&st.wq[wr + 16 * rt + li][8 * gi + 2 * lk]);
+        sa[rt] = st.wsa[gi][wr + 16 * rt + li];
+        sb[rt] = st.wsb[gi][wr + 16 * rt + li];
+      }
+      i32x4 bs[2];
+      if (!SYM && !Q6K) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) bs[tt] = *reinterpret_cast<const i32x4*>(&st.asum[gi][wt + 16 * tt + 4 * lk]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const i32x4 zero = {0, 0, 0, 0};
+          if (Q6K) {
+            const long blo = lk < 2 ? bop[rt] : 0, bhi = lk < 2 ? 0 : bop[rt];
+            const i32x4 dlo = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[tt], blo, zero, 0, 0, 0);
+            const i32x4 dhi = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[tt], bhi, zero, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              inner[tt][rt][v] = __builtin_fmaf(sb[rt], (float)dhi[v], __builtin_fmaf(sa[rt], (float)dlo[v], inner[tt][rt][v]));
+          } else {
+            const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[tt], bop[rt], zero, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float t = __builtin_fmaf(sa[rt], (float)d[v], inner[tt][rt][v]);
+              if (!SYM) t = __builtin_fmaf(sb[rt], (float)bs[tt][v], t);
+              inner[tt][rt][v] = t;
+            }
+          }
+        }
+      }
+    }
+    // the step's activation scales
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const float4 d4 = *reinterpret_cast<const float4*>(&st.ad[wt + 16 * tt + 4 * lk]);
+      const double dv[4] = {(double)d4.x, (double)d4.y, (double)d4.z, (double)d4.w};
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[tt][rt][v] = __builtin_fma(dv[v], (double)inner[tt][rt][v], acc[tt][rt][v]);
+    }
+    if (s + 1 < nsteps) store_step(s + 1, stage[(s + 1) & 1]);
+    __syncthreads();   // the next step's tile is staged; this one is free again
+  }
+  // lanes 16k .. 16k+15 hold consecutive rows of one token: 64-byte runs
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t tok = t0 + wt + 16 * tt + 4 * lk + v;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int64_t row = r0 + wr + 16 * rt + li;
+        if (tok < n_tok && row < n_out) y[tok * n_out + row] = (float)acc[tt][rt][v];
+      }
+    }
+}
+
+template <int TYPE>
+int launch_mfma(const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in, int64_t w_row_bytes,
+                float* y, hipStream_t s) {
+  const dim3 grid((uint32_t)((n_out + MF_ROWS - 1) / MF_ROWS), (uint32_t)((n_tok + MF_TOK - 1) / MF_TOK));
+  hipLaunchKernelGGL(k_matmul_mfma<TYPE>, grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in, w_row_bytes, y);
+  return qr_check_launch("k_matmul_mfma");
+}
+
+int launch_mfma_type(int t, const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in,
+                     int64_t wrb, float* y, hipStream_t s) {
+  switch (t) {
+    case QR_Q4_0: return launch_mfma<QR_Q4_0>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q4_1: return launch_mfma<QR_Q4_1>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q5_0: return launch_mfma<QR_Q5_0>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q5_1: return launch_mfma<QR_Q5_1>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q6_0: return launch_mfma<QR_Q6_0>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q6_K: return launch_mfma<QR_Q6_K>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    default: return launch_mfma<QR_Q4_K>(w, x, n_out, n_tok, n_in, wrb, y, s);
+  }
+}
+
 template <int TYPE, int ACT>
 int launch_type(int tt, const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in,
                 int64_t w_row_bytes, float* y, hipStream_t s) {
@@ -491,6 +727,13 @@ int qr_matmul_q8k(int t, int act, const void* w, const void* x, int64_t n_out, i
   if (!w || !x || !y) return qr_fail(QR_EINVAL_PTR, "w, x and y must be non-NULL");
   if (!qr_aligned(w, 16) || !qr_aligned(x, 16) || !qr_aligned(y, 16))
     return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
+  const int64_t wrb0 = (int64_t)qr_row_bytes(t, n_in);
+  if (act == QR_Q8_K128 && n_tok >= MF_MIN_TOK) {
+    if ((n_tok + MF_TOK - 1) / MF_TOK > 65535)
+      return qr_fail(QR_EOVERFLOW, "n_tok=%lld needs too many token tiles", (long long)n_tok);
+    return launch_mfma_type(t, reinterpret_cast<const uint8_t*>(w), reinterpret_cast<const uint8_t*>(x), n_out,
+                            n_tok, (int)n_in, wrb0, y, reinterpret_cast<hipStream_t>(stream));
+  }
   // tokens per tile: as many as fit (up to 8) in the activation budget
   int tt = n_tok >= 8 ? 8 : n_tok >= 4 ? 4 : n_tok >= 2 ? 2 : 1;
   while (tt > 1 && mmq_lds_bytes(tt, n_in, act) > MMQ_LDS_BUDGET) tt >>= 1;

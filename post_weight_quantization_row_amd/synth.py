@@ -38,6 +38,8 @@ available here). Their shapes and value distributions are:
   Q8_K_128 (a decode step).
 * ``mmq_q4_0_4096x4096_t8``: product of the Q4_0-quantized first attention
   matrix of ``stack_7b_32x7`` with 8 such tokens.
+* ``mmq_q4_k_11008x4096_t512``: the Q4_K matrix of ``mmq_q4_k_11008x4096_t1``
+  with 512 such tokens (a prompt processed at once).
 
 Two back-ends draw the same recipes: numpy (CPU, used by the CPU tests and by
 small GPU tests) and torch on the GPU (used for the multi-GB stacks). The two
@@ -75,6 +77,9 @@ WORKLOADS = {
     "mmq_q4_0_4096x4096_t8": dict(type="matmul", wtype="q4_0", n_out=4096,
                                   n_in=4096, n_tok=8, weights="stack_7b_32x7",
                                   seed=1010),
+    "mmq_q4_k_11008x4096_t512": dict(type="matmul", wtype="q4_k", n_out=11008,
+                                     n_in=4096, n_tok=512, weights="q4_k_11008x4096",
+                                     seed=1013),
     "imatrix_dense_4096x4096": dict(type="imatrix", dtype="bf16",
                                     n_tokens=4096, n_cols=4096, n_experts=1,
                                     top_k=0, n_slots=1, n_dead=0, seed=1007),

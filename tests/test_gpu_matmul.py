@@ -98,6 +98,68 @@ def test_longest_rows(qr, t, n_tok):
     check(qr, t, w, xa, 32768)
 
 
+# ---------------------------------------------------------------------------
+# 17 tokens or more with Q8_K_128 activations: the int8 matrix-core kernel
+# (tiles of 64 tokens x 64 rows; block sums in fp32, accumulation in double)
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("n_out,n_tok,n_in", [(64, 64, 256), (100, 33, 768), (37, 130, 1024),
+                                              (130, 64, 2048), (16, 257, 512), (20, 17, 512)])
+def test_many_tokens(qr, t, n_out, n_tok, n_in):
+    say(f"many tokens {t} n_out={n_out} n_tok={n_tok} n_in={n_in}")
+    w, xa = inputs(t, n_out, n_tok, n_in, seed=3 * n_out + n_tok + n_in)
+    y = check(qr, t, w, xa, n_in).cpu().numpy().astype(np.float64)
+    # the integer products are exact; the (at most eight) scaled terms of an
+    # activation block are summed with fp32 fused multiply-adds, the blocks
+    # in double, and the result rounded once to fp32: within
+    # 2^-24 |y| + 8 * 2^-24 S of the exact product whatever n_in, plus the
+    # double roundings of both sides (the oracle sums n_in terms)
+    yo, S = oracle.matmul_q8k128(t, w, xa, n_out, n_tok, n_in, with_magnitude=True)
+    tight = 2.0 ** -24 * np.abs(yo) + 8 * 2.0 ** -24 * S + (2 * n_in + 64) * 2.0 ** -52 * S
+    assert np.all(np.abs(y - yo) <= tight)
+
+
+@pytest.mark.parametrize("t", ["q4_1", "q4_k", "q6_k"])
+def test_many_tokens_outlier_activations(qr, t):
+    say(f"many tokens, outliers {t}")
+    w, xa = inputs(t, 40, 70, 4096, seed=97, outliers=True)
+    check(qr, t, w, xa, 4096)
+
+
+def test_many_tokens_longest_rows(qr):
+    say("many tokens, longest rows")
+    w, xa = inputs("q5_1", 20, 40, 32768, seed=98)
+    check(qr, "q5_1", w, xa, 32768)
+
+
+def test_many_tokens_reproducible_and_independent_of_the_tiling(qr):
+    # the same rows and tokens give the same outputs whatever the tile they
+    # fall in: tokens 0..39 alone, and as part of 100 tokens
+    w, xa = inputs("q4_k", 70, 100, 2048, seed=99)
+    wd, xd = torch.from_numpy(w).cuda(), torch.from_numpy(xa).cuda()
+    y1 = qr.qr_matmul_q8k128("q4_k", wd, xd, 2048)
+    y2 = qr.qr_matmul_q8k128("q4_k", wd, xd, 2048)
+    y3 = qr.qr_matmul_q8k128("q4_k", wd, xd[:40].contiguous(), 2048)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(y1[:40], y3)
+
+
+@pytest.mark.parametrize("act", ["q8_k64", "q8_k16"])
+def test_many_tokens_other_activation_blocks(qr, act):
+    # the other Q8_K formats keep the lane-parallel kernel at any token count
+    say(f"many tokens {act}")
+    x, q = synth.q4_0_matrix(48, 1024, seed=96)
+    w = oracle.quantize_rows("q4_k", x, q)
+    a = synth.calib_activations(40, 1024, seed=196, bf16=False)
+    xa = oracle.quantize_q8k(act, a)
+    y = qr.qr_matmul_q8k("q4_k", act, torch.from_numpy(w).cuda(), torch.from_numpy(xa).cuda(), 1024)
+    torch.cuda.synchronize()
+    yo, S = oracle.matmul_q8k128("q4_k", w, xa, 48, 40, 1024, with_magnitude=True, act=act)
+    bound = (1024 / 512 + 9) * 2.0 ** -24 * S
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - yo) <= bound)
+
+
 def test_reproducible(qr):
     w, xa = inputs("q4_k", 64, 8, 4096, seed=93)
     wd, xd = torch.from_numpy(w).cuda(), torch.from_numpy(xa).cuda()
@@ -121,3 +183,22 @@ def test_full_size_workloads(qr, name):
     w = oracle.quantize_rows(t, x, q, threads=8)
     xa = oracle.quantize_q8k128(a)
     check(qr, t, w, xa, x.shape[1])
+
+
+def test_full_size_512_tokens_sampled(qr):
+    # the 11008x4096 Q4_K matrix with 512 tokens, quantized on the GPU in the
+    # launch configuration the benchmark times; 96 rows x all tokens checked
+    # against the oracle's product of the same packed bytes
+    say("full size mmq_q4_k_11008x4096_t512 (sampled rows)")
+    t, x, q, a = synth.matmul_sources("mmq_q4_k_11008x4096_t512")
+    xd, qd, ad = (torch.from_numpy(v).cuda() for v in (x, q, a))
+    w = qr.qr_quantize_rows(t, xd, qd)
+    xa = qr.qr_quantize_activations_q8k("q8_k128", ad)
+    y = qr.qr_matmul_q8k128(t, w, xa, x.shape[1]).cpu().numpy().astype(np.float64)
+    rows = np.sort(np.random.default_rng(1014).choice(x.shape[0], 96, replace=False))
+    rows[-1] = x.shape[0] - 1
+    ws = w.cpu().numpy()[rows]
+    yo, S = oracle.matmul_q8k128(t, ws, xa.cpu().numpy(), len(rows), a.shape[0], x.shape[1],
+                                 with_magnitude=True)
+    bound = (x.shape[1] / 1024 + 9) * 2.0 ** -24 * S
+    assert np.all(np.abs(y[:, rows] - yo) <= bound)
