@@ -496,7 +496,7 @@ struct MfStage {
   float wsa[4][MF_ROWS];                // scale part (Q6_K: of the first half)
   float wsb[4][MF_ROWS];                // offset part, signed (Q6_K: scale of the second half)
   float ad[MF_TOK];                     // activation scales
-  int32_t asum[4][MF_TOK];              // activation code sums per group
+  float asum[4][MF_TOK];                // activation code sums per group (exact in fp32)
 };
 
 template <int TYPE>
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
       st.ad[srow] = __builtin_bit_cast(float, v);
     } else if (sq < 3) {
       const int g = 2 * (sq - 1);
-      st.asum[g][srow] = (int32_t)(int16_t)(v & 0xffffu);
-      st.asum[g + 1][srow] = (int32_t)(int16_t)(v >> 16);
+      st.asum[g][srow] = (float)(int16_t)(v & 0xffffu);
+      st.asum[g + 1][srow] = (float)(int16_t)(v >> 16);
     }
   };
 
@@ -599,10 +599,10 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
         sa[rt] = st.wsa[gi][wr + 16 * rt + li];
         sb[rt] = st.wsb[gi][wr + 16 * rt + li];
       }
-      i32x4 bs[2];
+      float4 bs[2];
       if (!SYM && !Q6K) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) bs[tt] = *reinterpret_cast<const i32x4*>(&st.asum[gi][wt + 16 * tt + 4 * lk]);
+        for (int tt = 0; tt < 2; ++tt) bs[tt] = *reinterpret_cast<const float4*>(&st.asum[gi][wt + 16 * tt + 4 * lk]);
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               float t = __builtin_fmaf(sa[rt], (float)d[v], inner[tt][rt][v]);
-              if (!SYM) t = __builtin_fmaf(sb[rt], (float)bs[tt][v], t);
+              if (!SYM) t = __builtin_fmaf(sb[rt], v == 0 ? bs[tt].x : v == 1 ? bs[tt].y : v == 2 ? bs[tt].z : bs[tt].w, t);
               inner[tt][rt][v] = t;
             }
           }
