@@ -499,23 +499,27 @@ struct MfStage {
   float asum[4][MF_TOK];                // activation code sums per group (exact in fp32)
 };
 
-template <int TYPE>
+// RT row tiles of 16 per wave: tiles of 64 tokens x 64 rows (RT = 2), or
+// x 32 rows (RT = 1) when the first would leave CUs without two workgroups.
+template <int TYPE, int RT>
 __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_matmul_mfma(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ x, int64_t n_out, int64_t n_tok, int n_in,
     int64_t w_row_bytes, float* __restrict__ y) {
   constexpr bool SYM = TYPE == QR_Q4_0 || TYPE == QR_Q5_0 || TYPE == QR_Q6_0;
   constexpr bool Q6K = TYPE == QR_Q6_K;
+  constexpr int ROWS = 32 * RT;   // rows of the tile
   __shared__ __align__(16) MfStage stage[2];   // double buffer: one barrier per K step
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * MF_ROWS;
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
   const int64_t t0 = (int64_t)blockIdx.y * MF_TOK;
   const int nsteps = n_in / 128;
   const int64_t x_row_bytes = (int64_t)nsteps * MF_ACT_BYTES;
 
-  // Staging roles: thread tid decodes group tid & 3 of row tid >> 2, and
-  // moves quarter tid & 3 (32 code bytes) of token tid >> 2's block plus one
-  // more word of it: the scale (quarter 0) or a word of code sums (1, 2).
+  // Staging roles: thread tid decodes group tid & 3 of row tid >> 2 (rows
+  // of the tile only: with 32 rows, waves 0 and 1), and moves quarter tid & 3
+  // (32 code bytes) of token tid >> 2's block plus one more word of it: the
+  // scale (quarter 0) or a word of code sums (1, 2).
   const int srow = tid >> 2, sq = tid & 3;
   const int64_t grow = r0 + srow < n_out ? r0 + srow : n_out - 1;   // rows past the end: unused
   const uint8_t* wrow = w + grow * w_row_bytes;
@@ -524,28 +528,31 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
   const int extra = sq == 0 ? 0 : sq == 1 ? 132 : 136;              // quarter 3 repeats quarter 2's word
   RawGroup rg;
   uint32_t av[9];
+  const bool wstage = srow < ROWS;   // uniform over each wave
   auto load_step = [&](int s) {
-    rg = load_raw<TYPE>(wrow, 4 * s + sq);
+    if (wstage) rg = load_raw<TYPE>(wrow, 4 * s + sq);
     const uint8_t* blk = xrow + (int64_t)s * MF_ACT_BYTES;
 #pragma unroll
     for (int k = 0; k < 8; ++k) av[k] = ld32(blk + 4 + 32 * sq + 4 * k);
     av[8] = ld32(blk + extra);
   };
   auto store_step = [&](int s, MfStage& st) {
-    const Group G = unpack<TYPE>(rg, 4 * s + sq);
-    uint4 c0, c1;
-    c0.x = SYM ? signed_levels<TYPE>(G.lo[0]) : G.lo[0];
-    c0.y = SYM ? signed_levels<TYPE>(G.lo[1]) : G.lo[1];
-    c0.z = SYM ? signed_levels<TYPE>(G.lo[2]) : G.lo[2];
-    c0.w = SYM ? signed_levels<TYPE>(G.lo[3]) : G.lo[3];
-    c1.x = SYM ? signed_levels<TYPE>(G.hi[0]) : G.hi[0];
-    c1.y = SYM ? signed_levels<TYPE>(G.hi[1]) : G.hi[1];
-    c1.z = SYM ? signed_levels<TYPE>(G.hi[2]) : G.hi[2];
-    c1.w = SYM ? signed_levels<TYPE>(G.hi[3]) : G.hi[3];
-    *reinterpret_cast<uint4*>(&st.wq[srow][8 * sq]) = c0;
-    *reinterpret_cast<uint4*>(&st.wq[srow][8 * sq + 4]) = c1;
-    st.wsa[sq][srow] = G.sa;
-    st.wsb[sq][srow] = Q6K ? G.sa1 : TYPE == QR_Q4_K ? -G.sb : G.sb;
+    if (wstage) {
+      const Group G = unpack<TYPE>(rg, 4 * s + sq);
+      uint4 c0, c1;
+      c0.x = SYM ? signed_levels<TYPE>(G.lo[0]) : G.lo[0];
+      c0.y = SYM ? signed_levels<TYPE>(G.lo[1]) : G.lo[1];
+      c0.z = SYM ? signed_levels<TYPE>(G.lo[2]) : G.lo[2];
+      c0.w = SYM ? signed_levels<TYPE>(G.lo[3]) : G.lo[3];
+      c1.x = SYM ? signed_levels<TYPE>(G.hi[0]) : G.hi[0];
+      c1.y = SYM ? signed_levels<TYPE>(G.hi[1]) : G.hi[1];
+      c1.z = SYM ? signed_levels<TYPE>(G.hi[2]) : G.hi[2];
+      c1.w = SYM ? signed_levels<TYPE>(G.hi[3]) : G.hi[3];
+      *reinterpret_cast<uint4*>(&st.wq[srow][8 * sq]) = c0;
+      *reinterpret_cast<uint4*>(&st.wq[srow][8 * sq + 4]) = c1;
+      st.wsa[sq][srow] = G.sa;
+      st.wsb[sq][srow] = Q6K ? G.sa1 : TYPE == QR_Q4_K ? -G.sb : G.sb;
+    }
     uint4 a0, a1;
     a0.x = tok_ok ? av[0] : 0u; a0.y = tok_ok ? av[1] : 0u; a0.z = tok_ok ? av[2] : 0u; a0.w = tok_ok ? av[3] : 0u;
     a1.x = tok_ok ? av[4] : 0u; a1.y = tok_ok ? av[5] : 0u; a1.z = tok_ok ? av[6] : 0u; a1.w = tok_ok ? av[7] : 0u;
@@ -561,40 +568,36 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
 
-  const int wt = (wave & 1) * 32, wr = (wave >> 1) * 32;   // this wave's tokens and rows in the tile
+  const int wt = (wave & 1) * 32, wr = (wave >> 1) * 16 * RT;   // this wave's tokens and rows in the tile
   const int li = lane & 15, lk = lane >> 4;
-  double acc[2][2][4];
+  double acc[2][RT][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < RT; ++b)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[a][b][v] = 0.0;
 
-  load_step(0);
-  store_step(0, stage[0]);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) load_step(s + 1);   // in flight during this step's products
-    const MfStage& st = stage[s & 1];
-    // the four groups' terms of the block, summed in fp32 (at most four
+  // one step's products from a staged tile
+  auto compute = [&](const MfStage& st) {
+    // the four groups' terms of the block, summed in fp32 (at most eight
     // roundings of terms of the block), then scaled and added in double
-    float inner[2][2][4];
+    float inner[2][RT][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < RT; ++b)
 #pragma unroll
         for (int v = 0; v < 4; ++v) inner[a][b][v] = 0.0f;
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      long aop[2], bop[2];
-      float sa[2], sb[2];
+      long aop[2], bop[RT];
+      float sa[RT], sb[RT];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         aop[tt] = *reinterpret_cast<const long*>(&st.aq[wt + 16 * tt + li][8 * gi + 2 * lk]);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         bop[rt] = *reinterpret_cast<const long*>(&st.wq[wr + 16 * rt + li][8 * gi + 2 * lk]);
         sa[rt] = st.wsa[gi][wr + 16 * rt + li];
         sb[rt] = st.wsb[gi][wr + 16 * rt + li];
@@ -607,7 +610,7 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
           const i32x4 zero = {0, 0, 0, 0};
           if (Q6K) {
             const long blo = lk < 2 ? bop[rt] : 0, bhi = lk < 2 ? 0 : bop[rt];
@@ -634,10 +637,20 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
       const float4 d4 = *reinterpret_cast<const float4*>(&st.ad[wt + 16 * tt + 4 * lk]);
       const double dv[4] = {(double)d4.x, (double)d4.y, (double)d4.z, (double)d4.w};
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[tt][rt][v] = __builtin_fma(dv[v], (double)inner[tt][rt][v], acc[tt][rt][v]);
     }
+  };
+
+  // Step s is computed from tile s & 1 while the words of step s + 1 load
+  // into registers; they are staged into the other tile afterwards.
+  load_step(0);
+  store_step(0, stage[0]);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) load_step(s + 1);   // in flight during this step's products
+    compute(stage[s & 1]);
     if (s + 1 < nsteps) store_step(s + 1, stage[(s + 1) & 1]);
     __syncthreads();   // the next step's tile is staged; this one is free again
   }
@@ -648,7 +661,7 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     for (int v = 0; v < 4; ++v) {
       const int64_t tok = t0 + wt + 16 * tt + 4 * lk + v;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         const int64_t row = r0 + wr + 16 * rt + li;
         if (tok < n_tok && row < n_out) y[tok * n_out + row] = (float)acc[tt][rt][v];
       }
@@ -658,8 +671,16 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 template <int TYPE>
 int launch_mfma(const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in, int64_t w_row_bytes,
                 float* y, hipStream_t s) {
-  const dim3 grid((uint32_t)((n_out + MF_ROWS - 1) / MF_ROWS), (uint32_t)((n_tok + MF_TOK - 1) / MF_TOK));
-  hipLaunchKernelGGL(k_matmul_mfma<TYPE>, grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in, w_row_bytes, y);
+  const int64_t tok_tiles = (n_tok + MF_TOK - 1) / MF_TOK;
+  // 64-row tiles unless that leaves fewer than two workgroups per CU
+  // (256 CUs): then 32-row tiles, twice as many
+  if (((n_out + 63) / 64) * tok_tiles >= 512) {
+    const dim3 grid((uint32_t)((n_out + 63) / 64), (uint32_t)tok_tiles);
+    hipLaunchKernelGGL((k_matmul_mfma<TYPE, 2>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in, w_row_bytes, y);
+  } else {
+    const dim3 grid((uint32_t)((n_out + 31) / 32), (uint32_t)tok_tiles);
+    hipLaunchKernelGGL((k_matmul_mfma<TYPE, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in, w_row_bytes, y);
+  }
   return qr_check_launch("k_matmul_mfma");
 }
 

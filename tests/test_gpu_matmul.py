@@ -119,6 +119,16 @@ def test_many_tokens(qr, t, n_out, n_tok, n_in):
     assert np.all(np.abs(y - yo) <= tight)
 
 
+@pytest.mark.parametrize("t", ["q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("n_out,n_tok", [(4096, 512), (4033, 449)])
+def test_many_tokens_large_tiles(qr, t, n_out, n_tok):
+    # enough 64 x 64 tiles (512) for the kernel's 64-row tiles; the smaller
+    # cases above take its 32-row tiles
+    say(f"many tokens, 64-row tiles {t} n_out={n_out} n_tok={n_tok}")
+    w, xa = inputs(t, n_out, n_tok, 256, seed=n_out + n_tok)
+    check(qr, t, w, xa, 256)
+
+
 @pytest.mark.parametrize("t", ["q4_1", "q4_k", "q6_k"])
 def test_many_tokens_outlier_activations(qr, t):
     say(f"many tokens, outliers {t}")
