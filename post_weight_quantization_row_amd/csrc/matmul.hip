@@ -445,14 +445,16 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k(const uint8_t* __res
 // and code-sum fold].
 //
 // With Q8_K_128 activations and at least MF_MIN_TOK tokens, a workgroup
-// of four waves owns a tile of 64 tokens x 64 weight rows. K advances one
+// of four waves owns a tile of 64 tokens x 64 weight rows (x 32 rows when
+// 64-row tiles would leave CUs without two workgroups). K advances one
 // activation block (128 values, four 32-weight groups) per step:
-//  * each of the 256 threads decodes one (row, group) of the tile to 32 int8
-//    codes in LDS -- the symmetric types as signed levels, so that they need
-//    no offset fold -- with its scale parts; the tile's activation blocks
+//  * each thread decodes one (row, group) of the tile to 32 int8 codes in
+//    LDS -- the symmetric types as signed levels, so that they need no
+//    offset fold -- with its scale parts; the tile's activation blocks
 //    (codes, scale, int16 code sums) are staged beside them. The global
 //    loads for the next step are issued before this step's products.
-//  * each wave owns 32 tokens x 32 rows (2 x 2 tiles of 16 x 16): per group
+//  * each wave owns 32 tokens x 32 (or 16) rows, 2 x 2 (or 2 x 1) tiles of
+//    16 x 16: per group
 //    one v_mfma_i32_16x16x32_i8 per tile (activations as A, weights as B)
 //    gives the exact int32 dot products; they take the group's scale parts
 //    with fp32 fused multiply-adds, and per activation block the sum takes
