@@ -63,9 +63,11 @@ int qr_matmul_q8k128(int t, const void *w, const void *x, int64_t n_out,
  * activation blocks: the integer dot product and the offset fold are taken
  * per 16 values and the two scaled terms added in that order, which doubles
  * the fp32 additions per lane: the bound becomes (n_in/512 + 9) * 2^-24 of
- * the same magnitude. Limits: n_in a positive multiple of the larger of the
- * two block lengths (32 or 256 for the weights), at most QR_MATMUL_MAX_IN;
- * QR_EINVAL_TYPE for an act outside the family.
+ * the same magnitude. From 17 tokens on, Q8_K64 activations take the int8
+ * matrix cores like Q8_K_128 (with the same tighter error); Q8_K16 stays
+ * on the lane-parallel path. Limits: n_in a positive multiple of the larger
+ * of the two block lengths (32 or 256 for the weights), at most
+ * QR_MATMUL_MAX_IN; QR_EINVAL_TYPE for an act outside the family.
  */
 int qr_matmul_q8k(int t, int act, const void *w, const void *x, int64_t n_out,
                   int64_t n_tok, int64_t n_in, float *y, void *stream);

@@ -444,7 +444,7 @@ __global__ __launch_bounds__(MMQ_THREADS) void k_matmul_q8k(const uint8_t* __res
 // Many tokens: int8 matrix cores [Q8 修复方案: the same integer dot products
 // and code-sum fold].
 //
-// With Q8_K_128 activations and at least MF_MIN_TOK tokens, a workgroup
+// With Q8_K_128 or Q8_K64 activations and at least MF_MIN_TOK tokens, a workgroup
 // of four waves owns a tile of 64 tokens x 64 weight rows (x 32 rows when
 // 64-row tiles would leave CUs without two workgroups). K advances one
 // activation block (128 values, four 32-weight groups) per step:
@@ -476,7 +476,9 @@ constexpr int MF_ROW_WORDS = 36;         // LDS words per token or row: 4 groups
 // matrix: 51 against 51 us at 16 tokens, 50 against 70 at 24, 50 against 86
 // at 32; at 8 tokens the lane-parallel kernel takes 11 us.
 constexpr int MF_MIN_TOK = 17;
-constexpr int MF_ACT_BYTES = 140;        // a Q8_K_128 block: d, 128 codes, 4 int16 sums
+// Bytes of activations per 128-value step: one Q8_K_128 block (d, 128 codes,
+// 4 int16 sums) or two Q8_K64 blocks (d, 64 codes, 2 int16 sums each).
+__host__ __device__ constexpr int mf_step_bytes(int act) { return act == QR_Q8_K128 ? 140 : 144; }
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -497,45 +499,52 @@ struct MfStage {
   uint32_t wq[MF_ROWS][MF_ROW_WORDS];   // weight codes (symmetric types: signed levels)
   float wsa[4][MF_ROWS];                // scale part (Q6_K: of the first half)
   float wsb[4][MF_ROWS];                // offset part, signed (Q6_K: scale of the second half)
-  float ad[MF_TOK];                     // activation scales
+  float ad[2][MF_TOK];                  // activation scales (of each 64-value block for Q8_K64)
   float asum[4][MF_TOK];                // activation code sums per group (exact in fp32)
 };
 
 // RT row tiles of 16 per wave: tiles of 64 tokens x 64 rows (RT = 2), or
 // x 32 rows (RT = 1) when the first would leave CUs without two workgroups.
-template <int TYPE, int RT>
+// ACT: Q8_K_128 or Q8_K64 activations (a 64-value block holds two groups).
+template <int TYPE, int ACT, int RT>
 __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_matmul_mfma(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ x, int64_t n_out, int64_t n_tok, int n_in,
     int64_t w_row_bytes, float* __restrict__ y) {
   constexpr bool SYM = TYPE == QR_Q4_0 || TYPE == QR_Q5_0 || TYPE == QR_Q6_0;
   constexpr bool Q6K = TYPE == QR_Q6_K;
   constexpr int ROWS = 32 * RT;   // rows of the tile
+  constexpr int SB = mf_step_bytes(ACT);
+  constexpr int GPB = ACT == QR_Q8_K128 ? 4 : 2;   // groups per activation block
   __shared__ __align__(16) MfStage stage[2];   // double buffer: one barrier per K step
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t r0 = (int64_t)blockIdx.x * ROWS;
   const int64_t t0 = (int64_t)blockIdx.y * MF_TOK;
   const int nsteps = n_in / 128;
-  const int64_t x_row_bytes = (int64_t)nsteps * MF_ACT_BYTES;
+  const int64_t x_row_bytes = (int64_t)nsteps * SB;
 
   // Staging roles: thread tid decodes group tid & 3 of row tid >> 2 (rows
   // of the tile only: with 32 rows, waves 0 and 1), and moves quarter tid & 3
-  // (32 code bytes) of token tid >> 2's block plus one more word of it: the
-  // scale (quarter 0) or a word of code sums (1, 2).
+  // (32 code bytes, group tid & 3) of token tid >> 2's step plus one more
+  // word of it: Q8_K_128 the scale (quarter 0) or a word of code sums (1,
+  // 2); Q8_K64 block 0's scale and sums (0, 1), block 1's (2, 3).
   const int srow = tid >> 2, sq = tid & 3;
   const int64_t grow = r0 + srow < n_out ? r0 + srow : n_out - 1;   // rows past the end: unused
   const uint8_t* wrow = w + grow * w_row_bytes;
   const bool tok_ok = t0 + srow < n_tok;                            // tokens past the end: zeros
   const uint8_t* xrow = x + (tok_ok ? t0 + srow : n_tok - 1) * x_row_bytes;
-  const int extra = sq == 0 ? 0 : sq == 1 ? 132 : 136;              // quarter 3 repeats quarter 2's word
+  // code bytes of group sq, and the extra word (Q8_K_128: quarter 3 repeats 2's)
+  const int code_off = ACT == QR_Q8_K128 ? 4 + 32 * sq : 72 * (sq >> 1) + 4 + 32 * (sq & 1);
+  const int extra = ACT == QR_Q8_K128 ? (sq == 0 ? 0 : sq == 1 ? 132 : 136)
+                                      : (sq == 0 ? 0 : sq == 1 ? 68 : sq == 2 ? 72 : 140);
   RawGroup rg;
   uint32_t av[9];
   const bool wstage = srow < ROWS;   // uniform over each wave
   auto load_step = [&](int s) {
     if (wstage) rg = load_raw<TYPE>(wrow, 4 * s + sq);
-    const uint8_t* blk = xrow + (int64_t)s * MF_ACT_BYTES;
+    const uint8_t* blk = xrow + (int64_t)s * SB;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) av[k] = ld32(blk + 4 + 32 * sq + 4 * k);
+    for (int k = 0; k < 8; ++k) av[k] = ld32(blk + code_off + 4 * k);
     av[8] = ld32(blk + extra);
   };
   auto store_step = [&](int s, MfStage& st) {
@@ -561,10 +570,11 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq]) = a0;
     *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq + 4]) = a1;
     const uint32_t v = tok_ok ? av[8] : 0u;
-    if (sq == 0) {
-      st.ad[srow] = __builtin_bit_cast(float, v);
-    } else if (sq < 3) {
-      const int g = 2 * (sq - 1);
+    const bool is_scale = ACT == QR_Q8_K128 ? sq == 0 : (sq & 1) == 0;
+    if (is_scale) {
+      st.ad[sq >> 1][srow] = __builtin_bit_cast(float, v);
+    } else if (ACT != QR_Q8_K128 || sq < 3) {
+      const int g = ACT == QR_Q8_K128 ? 2 * (sq - 1) : sq - 1;   // first of the word's two groups
       st.asum[g][srow] = (float)(int16_t)(v & 0xffffu);
       st.asum[g + 1][srow] = (float)(int16_t)(v >> 16);
     }
@@ -582,17 +592,19 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 
   // one step's products from a staged tile
   auto compute = [&](const MfStage& st) {
-    // the four groups' terms of the block, summed in fp32 (at most eight
-    // roundings of terms of the block), then scaled and added in double
+    // the groups' terms of an activation block, summed in fp32 (at most
+    // eight roundings of terms of the block), then scaled and added in double
     float inner[2][RT][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < RT; ++b)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) inner[a][b][v] = 0.0f;
-#pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
+      if (gi % GPB == 0) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < RT; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) inner[a][b][v] = 0.0f;
+      }
       long aop[2], bop[RT];
       float sa[RT], sb[RT];
 #pragma unroll
@@ -632,16 +644,18 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
           }
         }
       }
-    }
-    // the step's activation scales
+      // the block's activation scale
+      if (gi % GPB == GPB - 1) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const float4 d4 = *reinterpret_cast<const float4*>(&st.ad[wt + 16 * tt + 4 * lk]);
-      const double dv[4] = {(double)d4.x, (double)d4.y, (double)d4.z, (double)d4.w};
+        for (int tt = 0; tt < 2; ++tt) {
+          const float4 d4 = *reinterpret_cast<const float4*>(&st.ad[gi / GPB][wt + 16 * tt + 4 * lk]);
+          const double dv[4] = {(double)d4.x, (double)d4.y, (double)d4.z, (double)d4.w};
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+          for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[tt][rt][v] = __builtin_fma(dv[v], (double)inner[tt][rt][v], acc[tt][rt][v]);
+            for (int v = 0; v < 4; ++v) acc[tt][rt][v] = __builtin_fma(dv[v], (double)inner[tt][rt][v], acc[tt][rt][v]);
+        }
+      }
     }
   };
 
@@ -670,7 +684,7 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     }
 }
 
-template <int TYPE>
+template <int TYPE, int ACT>
 int launch_mfma(const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in, int64_t w_row_bytes,
                 float* y, hipStream_t s) {
   const int64_t tok_tiles = (n_tok + MF_TOK - 1) / MF_TOK;
@@ -678,24 +692,27 @@ int launch_mfma(const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok
   // (256 CUs): then 32-row tiles, twice as many
   if (((n_out + 63) / 64) * tok_tiles >= 512) {
     const dim3 grid((uint32_t)((n_out + 63) / 64), (uint32_t)tok_tiles);
-    hipLaunchKernelGGL((k_matmul_mfma<TYPE, 2>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in, w_row_bytes, y);
+    hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 2>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
+                       w_row_bytes, y);
   } else {
     const dim3 grid((uint32_t)((n_out + 31) / 32), (uint32_t)tok_tiles);
-    hipLaunchKernelGGL((k_matmul_mfma<TYPE, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in, w_row_bytes, y);
+    hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
+                       w_row_bytes, y);
   }
   return qr_check_launch("k_matmul_mfma");
 }
 
+template <int ACT>
 int launch_mfma_type(int t, const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in,
                      int64_t wrb, float* y, hipStream_t s) {
   switch (t) {
-    case QR_Q4_0: return launch_mfma<QR_Q4_0>(w, x, n_out, n_tok, n_in, wrb, y, s);
-    case QR_Q4_1: return launch_mfma<QR_Q4_1>(w, x, n_out, n_tok, n_in, wrb, y, s);
-    case QR_Q5_0: return launch_mfma<QR_Q5_0>(w, x, n_out, n_tok, n_in, wrb, y, s);
-    case QR_Q5_1: return launch_mfma<QR_Q5_1>(w, x, n_out, n_tok, n_in, wrb, y, s);
-    case QR_Q6_0: return launch_mfma<QR_Q6_0>(w, x, n_out, n_tok, n_in, wrb, y, s);
-    case QR_Q6_K: return launch_mfma<QR_Q6_K>(w, x, n_out, n_tok, n_in, wrb, y, s);
-    default: return launch_mfma<QR_Q4_K>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q4_0: return launch_mfma<QR_Q4_0, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q4_1: return launch_mfma<QR_Q4_1, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q5_0: return launch_mfma<QR_Q5_0, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q5_1: return launch_mfma<QR_Q5_1, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q6_0: return launch_mfma<QR_Q6_0, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q6_K: return launch_mfma<QR_Q6_K, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    default: return launch_mfma<QR_Q4_K, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
   }
 }
 
@@ -751,11 +768,14 @@ int qr_matmul_q8k(int t, int act, const void* w, const void* x, int64_t n_out, i
   if (!qr_aligned(w, 16) || !qr_aligned(x, 16) || !qr_aligned(y, 16))
     return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
   const int64_t wrb0 = (int64_t)qr_row_bytes(t, n_in);
-  if (act == QR_Q8_K128 && n_tok >= MF_MIN_TOK) {
+  if (act != QR_Q8_K16 && n_tok >= MF_MIN_TOK) {   // Q8_K_128 or Q8_K64: the matrix cores
     if ((n_tok + MF_TOK - 1) / MF_TOK > 65535)
       return qr_fail(QR_EOVERFLOW, "n_tok=%lld needs too many token tiles", (long long)n_tok);
-    return launch_mfma_type(t, reinterpret_cast<const uint8_t*>(w), reinterpret_cast<const uint8_t*>(x), n_out,
-                            n_tok, (int)n_in, wrb0, y, reinterpret_cast<hipStream_t>(stream));
+    const uint8_t* pw0 = reinterpret_cast<const uint8_t*>(w);
+    const uint8_t* px0 = reinterpret_cast<const uint8_t*>(x);
+    hipStream_t s0 = reinterpret_cast<hipStream_t>(stream);
+    return act == QR_Q8_K128 ? launch_mfma_type<QR_Q8_K128>(t, pw0, px0, n_out, n_tok, (int)n_in, wrb0, y, s0)
+                             : launch_mfma_type<QR_Q8_K64>(t, pw0, px0, n_out, n_tok, (int)n_in, wrb0, y, s0);
   }
   // tokens per tile: as many as fit (up to 8) in the activation budget
   int tt = n_tok >= 8 ? 8 : n_tok >= 4 ? 4 : n_tok >= 2 ? 2 : 1;

@@ -99,7 +99,7 @@ def test_longest_rows(qr, t, n_tok):
 
 
 # ---------------------------------------------------------------------------
-# 17 tokens or more with Q8_K_128 activations: the int8 matrix-core kernel
+# 17 tokens or more with Q8_K_128 or Q8_K64 activations: the int8 matrix-core kernel
 # (tiles of 64 tokens x 64 rows; block sums in fp32, accumulation in double)
 
 @pytest.mark.parametrize("t", TYPES)
@@ -155,9 +155,34 @@ def test_many_tokens_reproducible_and_independent_of_the_tiling(qr):
     assert torch.equal(y1[:40], y3)
 
 
+def k64_inputs(t, n_out, n_tok, n_in, seed):
+    x, q = synth.q4_0_matrix(n_out, n_in, seed=seed)
+    w = oracle.quantize_rows(t, x, q)
+    a = synth.calib_activations(n_tok, n_in, seed=seed + 1, bf16=False)
+    return w, oracle.quantize_q8k("q8_k64", a)
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("n_out,n_tok,n_in", [(100, 33, 768), (37, 130, 1024), (20, 17, 512), (4033, 449, 256)])
+def test_many_tokens_q8_k64(qr, t, n_out, n_tok, n_in):
+    # Q8_K64 activations on the matrix cores: a 128-value step holds two
+    # blocks, each scaling its two groups (32- and 64-row tiles)
+    say(f"many tokens q8_k64 {t} n_out={n_out} n_tok={n_tok} n_in={n_in}")
+    w, xa = k64_inputs(t, n_out, n_tok, n_in, seed=5 * n_out + n_tok + n_in)
+    y = qr.qr_matmul_q8k(t, "q8_k64", torch.from_numpy(w).cuda(), torch.from_numpy(xa).cuda(), n_in)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    yo, S = oracle.matmul_q8k128(t, w, xa, n_out, n_tok, n_in, with_magnitude=True, act="q8_k64")
+    bound = (n_in / (512 if t == "q6_k" else 1024) + 9) * 2.0 ** -24 * S
+    tight = 2.0 ** -24 * np.abs(yo) + 8 * 2.0 ** -24 * S + (2 * n_in + 64) * 2.0 ** -52 * S
+    assert np.all(np.abs(y - yo) <= bound)
+    assert np.all(np.abs(y - yo) <= tight)
+
+
 @pytest.mark.parametrize("act", ["q8_k64", "q8_k16"])
 def test_many_tokens_other_activation_blocks(qr, act):
-    # the other Q8_K formats keep the lane-parallel kernel at any token count
+    # Q8_K16 keeps the lane-parallel kernel at any token count (a group
+    # spans two of its blocks); Q8_K64 takes the matrix cores
     say(f"many tokens {act}")
     x, q = synth.q4_0_matrix(48, 1024, seed=96)
     w = oracle.quantize_rows("q4_k", x, q)
