@@ -206,10 +206,11 @@ __global__ __launch_bounds__(ST_THREADS) void k_stats_pass(const void* __restric
       const uint32_t bits = __builtin_bit_cast(uint32_t, ae);
       if (PASS == 0) {
         const double ed = (double)err, xd = (double)xv[e], qd = (double)qv[e];
-        s_e2 = __builtin_fma(ed, ed, s_e2);       // ed*ed exact: one rounding
-        s_x2 = __builtin_fma(xd, xd, s_x2);
-        s_qe2 += qd * (ed * ed);
-        s_qx2 += qd * (xd * xd);
+        const double e2 = ed * ed, x2 = xd * xd;  // squares of floats: exact in double
+        s_e2 += e2;                               // one rounding per term
+        s_x2 += x2;
+        s_qe2 = __builtin_fma(qd, e2, s_qe2);     // one rounding per term
+        s_qx2 = __builtin_fma(qd, x2, s_qx2);
         mx = fmaxf(mx, ae);
         atomicAdd(&h[bits >> 20], 1u);
       } else if (PASS == 1) {
