@@ -340,7 +340,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
-              "is not supported (rows are independent, see the sharding notes)",
+              "is not supported (rows and experts are independent: several GPUs "
+              "would each quantize their own share with the same kernel)",
               file=sys.stderr)
         sys.exit(2)
 
