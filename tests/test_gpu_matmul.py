@@ -104,7 +104,7 @@ def test_longest_rows(qr, t, n_tok):
 
 @pytest.mark.parametrize("t", TYPES)
 @pytest.mark.parametrize("n_out,n_tok,n_in", [(64, 64, 256), (100, 33, 768), (37, 130, 1024),
-                                              (130, 64, 2048), (16, 257, 512), (20, 17, 512)])
+                                              (130, 64, 2048), (16, 257, 512), (20, 17, 512), (1, 40, 256)])
 def test_many_tokens(qr, t, n_out, n_tok, n_in):
     say(f"many tokens {t} n_out={n_out} n_tok={n_tok} n_in={n_in}")
     w, xa = inputs(t, n_out, n_tok, n_in, seed=3 * n_out + n_tok + n_in)
