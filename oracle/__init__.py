@@ -26,12 +26,12 @@ SOURCES = [SRC, os.path.join(HERE, "imatrix_oracle.c"),
            os.path.join(HERE, "stats_oracle.c")]
 LIB = os.path.join(HERE, "liborc_qrow.so")
 
-Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128, Q6_0, Q8_K64, Q8_K16, Q6_K = range(10)
+Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q8_K128, Q6_0, Q8_K64, Q8_K16, Q6_K, Q5_K = range(11)
 WEIGHTINGS = {"sqrt_sigma2_x2": 0, "x2": 1, "abs_x": 2, "sigma2_plus_x2": 3,
               "sigma_plus_abs_x": 4, "imatrix_only": 5}
 TYPE_NAMES = {"q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1,
               "q4_k": Q4_K, "q8_k128": Q8_K128, "q6_0": Q6_0,
-              "q8_k64": Q8_K64, "q8_k16": Q8_K16, "q6_k": Q6_K}
+              "q8_k64": Q8_K64, "q8_k16": Q8_K16, "q6_k": Q6_K, "q5_k": Q5_K}
 ACT_TYPES = ("q8_k128", "q8_k64", "q8_k16")
 FITS = {"max": 0, "weighted": 1}   # Q4_K sub-scale choice
 

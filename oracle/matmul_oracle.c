@@ -89,10 +89,11 @@ static void weight_parts(int type, const uint8_t *row, int64_t n, double *a,
                 const double ds = rd_f16(p) * (double)(int8_t)p[4 + i / 16];
                 av = ds * u;
                 bv = ds * 32;
-            } else if (type == ORC_Q4_K) {
+            } else if (type == ORC_Q4_K || type == ORC_Q5_K) {
                 const int j = i / 32, k = i % 32;
-                const uint8_t *qs = p + 16 + 16 * j;
-                const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);
+                const uint8_t *qs = p + (type == ORC_Q4_K ? 16 : 48) + 16 * j;
+                int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);
+                if (type == ORC_Q5_K) u |= ((p[16 + 4 * j + k / 8] >> (k % 8)) & 1) << 4;
                 av = rd_f16(p) * field6(p + 4, j) * u;
                 bv = rd_f16(p + 2) * field6(p + 10, j);
             } else {
@@ -126,7 +127,7 @@ static int is_weight_type(int type)
 {
     return type == ORC_Q4_0 || type == ORC_Q4_1 || type == ORC_Q5_0 ||
            type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0 ||
-           type == ORC_Q6_K;
+           type == ORC_Q6_K || type == ORC_Q5_K;
 }
 
 int orc_matmul_q8k128(int type, const uint8_t *w, const uint8_t *x,

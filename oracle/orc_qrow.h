@@ -33,7 +33,8 @@ enum {
     ORC_Q6_0 = 6,    /* 32 weights, levels -32..31, fp32 scale, 2-bit plane 28 B */
     ORC_Q8_K64 = 7,  /* 64 activations, fp32 d, int8, int16 sums/32       72 B */
     ORC_Q8_K16 = 8,  /* 16 activations, fp32 d, int8, int16 sum, 2 B pad   24 B */
-    ORC_Q6_K = 9     /* 256 weights, 16x16 sub-blocks, int8 sc, fp16 d, levels -32..31 212 B */
+    ORC_Q6_K = 9,    /* 256 weights, 16x16 sub-blocks, int8 sc, fp16 d, levels -32..31 212 B */
+    ORC_Q5_K = 10    /* 256 weights, 8x32 sub-blocks, 6-bit sc/mn, fp16 d, levels 0..31 176 B */
 };
 
 /* Solver constants (the oracle's own copy). */

@@ -59,7 +59,7 @@ int orc_block_elems(int type)
 {
     switch (type) {
     case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0: case ORC_Q5_1: case ORC_Q6_0: return 32;
-    case ORC_Q4_K: case ORC_Q6_K: return 256;
+    case ORC_Q4_K: case ORC_Q5_K: case ORC_Q6_K: return 256;
     case ORC_Q8_K128: return 128;
     case ORC_Q8_K64: return 64;
     case ORC_Q8_K16: return 16;
@@ -80,6 +80,7 @@ size_t orc_block_bytes(int type)
     case ORC_Q8_K64: return 4 + 64 + 4;      /* d, int8 x64, int16 x2    */
     case ORC_Q8_K16: return 4 + 16 + 2 + 2;  /* d, int8 x16, int16, pad  */
     case ORC_Q6_K: return 2 + 2 + 16 + 128 + 64; /* d16, pad, sc, nibbles, planes */
+    case ORC_Q5_K: return 2 + 2 + 6 + 6 + 32 + 128; /* d16, dmin16, sc6, mn6, 5th bits, qs */
     default: return 0;
     }
 }
@@ -642,7 +643,13 @@ static void unpack6x8(const uint8_t *p, uint8_t *v)
 }
 
 /* Q4_K super-block [KQ §一]: 8 sub-blocks of 32, each fitted as
- * x ~ a_j * l - b_j with levels 0..15. Readings, fit == ORC_FIT_MAX (the
+ * x ~ a_j * l - b_j with levels 0..nmax (15). Q5_K is the same
+ * super-block with levels 0..31 (nmax = 31; [LQ] 2.2 lists Q5_K among the
+ * K-quants and [KQ] names Q5_K_M among the 4-bit-and-above K choices, with
+ * no layout; the layout is this library's): the fifth bit
+ * of the levels of sub-block j is a 32-bit word at byte 16 + 4 j (bit i for
+ * element i) and the low nibbles follow at byte 48 + 16 j.
+ * Readings, fit == ORC_FIT_MAX (the
  * default): the super-scales are d = fp16(max a_j / 63) and
  * dmin = fp16(max b_j / 63) (round to nearest even, subnormals kept);
  * sub-scales are sc_j = rint(a_j / d) and mn_j = rint(b_j / dmin) clamped to
@@ -652,13 +659,13 @@ static void unpack6x8(const uint8_t *p, uint8_t *v)
  * fitted scales, sc_j and mn_j = the fitted levels (0 where the fp16 scale
  * is 0). Either way the levels are then re-rounded against the stored
  * scales so that the decoder reproduces the fit. */
-static void quantize_q4k(const float *x, const float *w, int fit, uint8_t *out)
+static void quantize_kquant(const float *x, const float *w, int fit, int nmax, uint8_t *out)
 {
     float a[8], b[8], W[8];
     for (int j = 0; j < 8; ++j) {
         uint8_t l[32];
         float d, m;
-        orc_solve_asym(32, x + 32 * j, w + 32 * j, 15, ORC_ASYM_CAND,
+        orc_solve_asym(32, x + 32 * j, w + 32 * j, nmax, ORC_ASYM_CAND,
                        ORC_ASYM_FLIP_PASSES, 1, l, &d, &m, NULL);
         a[j] = d > 0.0f ? d : 0.0f;
         b[j] = -m > 0.0f ? -m : 0.0f;
@@ -703,9 +710,18 @@ static void quantize_q4k(const float *x, const float *w, int fit, uint8_t *out)
         } else {
             float id = 1.0f / ds;
             for (int i = 0; i < 32; ++i)
-                u[i] = (uint8_t)clampf(rintf((x[32 * j + i] + dm) * id), 0.0f, 15.0f);
+                u[i] = (uint8_t)clampf(rintf((x[32 * j + i] + dm) * id), 0.0f, (float)nmax);
         }
-        pack_nibbles32(u, out + 16 + 16 * j);
+        if (nmax == 15) {
+            pack_nibbles32(u, out + 16 + 16 * j);
+        } else {
+            uint32_t qh = 0;
+            for (int i = 0; i < 32; ++i) qh |= (uint32_t)((u[i] >> 4) & 1) << i;
+            for (int k = 0; k < 4; ++k) out[16 + 4 * j + k] = (uint8_t)(qh >> (8 * k));
+            uint8_t lo[32];
+            for (int i = 0; i < 32; ++i) lo[i] = u[i] & 15;
+            pack_nibbles32(lo, out + 48 + 16 * j);
+        }
     }
 }
 
@@ -778,7 +794,8 @@ static int quantize_row_impl(int type, const float *x, const float *q,
     for (int64_t ib = 0; ib < n / be; ++ib) {
         const float *xb = x + ib * be;
         float *wb = w + ib * be;
-        if (type == ORC_Q4_K) quantize_q4k(xb, wb, fit, out + ib * bb);
+        if (type == ORC_Q4_K) quantize_kquant(xb, wb, fit, 15, out + ib * bb);
+        else if (type == ORC_Q5_K) quantize_kquant(xb, wb, fit, 31, out + ib * bb);
         else if (type == ORC_Q6_K) quantize_q6k(xb, wb, out + ib * bb);
         else quantize_block32(type, xb, wb, out + ib * bb);
     }
@@ -789,7 +806,7 @@ static int weight_type_ok(int type)
 {
     return type == ORC_Q4_0 || type == ORC_Q4_1 || type == ORC_Q5_0 ||
            type == ORC_Q5_1 || type == ORC_Q4_K || type == ORC_Q6_0 ||
-           type == ORC_Q6_K;
+           type == ORC_Q6_K || type == ORC_Q5_K;
 }
 
 int orc_quantize_row_sigma2_ex(int type, const float *x, const float *q,
@@ -974,7 +991,7 @@ int orc_dequantize_rows(int type, const uint8_t *in, int64_t n_rows,
                 for (int i = 0; i < 32; ++i) o[i] = fmaf(d, (float)u[i], m);
                 break;
             }
-            case ORC_Q4_K: {
+            case ORC_Q4_K: case ORC_Q5_K: {
                 float dA = orc_f16_to_f32((uint16_t)(p[0] | (p[1] << 8)));
                 float dB = orc_f16_to_f32((uint16_t)(p[2] | (p[3] << 8)));
                 uint8_t sc[8], mn[8];
@@ -982,7 +999,13 @@ int orc_dequantize_rows(int type, const uint8_t *in, int64_t n_rows,
                 unpack6x8(p + 10, mn);
                 for (int j = 0; j < 8; ++j) {
                     float ds = dA * (float)sc[j], dm = dB * (float)mn[j];
-                    unpack_nibbles32(p + 16 + 16 * j, u);
+                    if (type == ORC_Q4_K) {
+                        unpack_nibbles32(p + 16 + 16 * j, u);
+                    } else {
+                        uint32_t qh = get_u32(p + 16 + 4 * j);
+                        unpack_nibbles32(p + 48 + 16 * j, u);
+                        for (int i = 0; i < 32; ++i) u[i] |= (uint8_t)(((qh >> i) & 1) << 4);
+                    }
                     for (int i = 0; i < 32; ++i) o[32 * j + i] = fmaf(ds, (float)u[i], -dm);
                 }
                 break;

@@ -74,8 +74,8 @@ MUTANTS = [
      "bv = sym ? d * (type == ORC_Q6_0 ? 32 : five ? 16 : 7) : -m;"),
     ("matmul: Q4_K scale from the offset field", "av = rd_f16(p) * field6(p + 4, j) * u;",
      "av = rd_f16(p) * field6(p + 10, j) * u;"),
-    ("matmul: Q4_K high nibble", "const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);",
-     "const int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] & 15);"),
+    ("matmul: Q4_K high nibble", "int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] >> 4);\n                if (type",
+     "int u = k < 16 ? (qs[k] & 15) : (qs[k - 16] & 15);\n                if (type"),
     ("matmul: activation block stride", "const uint8_t *p = row + blk * ab;", "const uint8_t *p = row + blk * (ab - 4);"),
     ("matmul: offset sign", "acc += (a[i] - b[i]) * xt[i];", "acc += (a[i] + b[i]) * xt[i];"),
     ("q8_1: s without d", "orc_f32_to_f16(d * (float)sum)", "orc_f32_to_f16((float)sum)"),
@@ -110,6 +110,16 @@ MUTANTS = [
      "clampf(rintf(x[16 * j + i] * id), -31.0f, 31.0f)"),
     ("q6k: decoder takes the group's first sub-scale", "(int8_t)p[4 + 2 * g + i / 16];", "(int8_t)p[4 + 2 * g];"),
     ("matmul: Q6_K offset 31", "bv = ds * 32;", "bv = ds * 31;"),
+    # Q5_K super-block
+    ("q5k: fifth-bit words in reverse order", "out[16 + 4 * j + k] = (uint8_t)(qh >> (8 * k));",
+     "out[16 + 4 * (7 - j) + k] = (uint8_t)(qh >> (8 * k));"),
+    ("q5k: decoder reads the first fifth-bit word", "uint32_t qh = get_u32(p + 16 + 4 * j);",
+     "uint32_t qh = get_u32(p + 16);"),
+    ("q5k: levels clamped to 0..15", "0.0f, (float)nmax);", "0.0f, 15.0f);"),
+    ("matmul: Q5_K nibbles at the Q4_K offset", "p + (type == ORC_Q4_K ? 16 : 48) + 16 * j;",
+     "p + 16 + 16 * j;"),
+    ("matmul: Q5_K fifth bit of the wrong word", "u |= ((p[16 + 4 * j + k / 8] >> (k % 8)) & 1) << 4;",
+     "u |= ((p[16 + k / 8] >> (k % 8)) & 1) << 4;"),
     # error statistics
     ("stats: percentile rank rounded down", "const int64_t k = (95 * n + 99) / 100;",
      "const int64_t k = (95 * n) / 100;"),
@@ -122,7 +132,8 @@ MUTANTS = [
 
 PIN_FILES = ("test_oracle_pins.py", "test_imatrix_oracle_pins.py", "test_matmul_oracle_pins.py",
              "test_weighting_oracle_pins.py", "test_stats_oracle_pins.py", "test_q8k_family_oracle_pins.py",
-             "test_subscale_fit_oracle_pins.py", "test_q6k_oracle_pins.py")
+             "test_subscale_fit_oracle_pins.py", "test_q6k_oracle_pins.py",
+             "test_q5k_oracle_pins.py")
 
 
 def _pins_modules():
