@@ -9,9 +9,11 @@
  *       (diagonal Hessian estimate) entry of its column; each block's scale is
  *       the weighted least-squares value sumlx/suml2, refined by greedy level
  *       flips along g = scale*w*(x - scale*l).
- *  [KQ] "3.2 K-quants 与重要性矩阵：量化兵器谱", section 一: the Q4_K super-block.
+ *  [KQ] "3.2 K-quants 与重要性矩阵：量化兵器谱", section 一: the Q4_K super-block
+ *       (fp16 super-scale over 6-bit sub-scales); Q5_K_M among the K types.
  *  [LQ] "从零理解 LLM 量化 PTQ、QAT 与 ik_llama.cpp 量化体系的源码级导学",
- *       section 2.1: the legacy 32-weight blocks Q4_0, Q4_1, Q5_0, Q5_1.
+ *       section 2.1: the legacy 32-weight blocks Q4_0, Q4_1, Q5_0, Q5_1;
+ *       section 2.2: the K-quant family, Q5_K among it.
  *  [Q8] "ik_llama.cpp 量化精度修复实录：用 Q8_K_128 替代 Q8_1 …", section 修复方案:
  *       the Q8_K_128 activation block; the row length must be a multiple of
  *       128.
@@ -52,6 +54,11 @@
  *     mn[8] as 6-bit fields in 6 B | u8 qs[128]; field j sits at bit 6j;
  *     sub-block j (32 weights) uses qs[16j .. 16j+15] as above and decodes
  *     to (d*sc_j)*u - dmin*mn_j.
+ *  Q5_K 176 B per 256: the Q4_K header (16 B) | qh[8] as u32 | u8 qs[128];
+ *     levels 0..31: sub-block j takes bit 4 of u_i from bit i of qh[j] and
+ *     the low 4 bits from qs[16j .. 16j+15] (nibbles as above); decodes as
+ *     Q4_K. (The pages name Q5_K but give no layout: it is Q4_K's
+ *     super-block with one more bit per weight, 5.5 bits per weight.)
  *  Q8_K128 140 B per 128: f32 d | i8 q[128] | i16 bsum[4]; bsum[g] is the
  *     plain sum of q[32g .. 32g+31], not multiplied by d.
  *  Q8_K64   72 B per 64:  f32 d | i8 q[64] | i16 bsum[2] (sums of 32 codes).
@@ -77,7 +84,8 @@ typedef enum {
     QR_Q6_0 = 6,
     QR_Q8_K64 = 7,
     QR_Q8_K16 = 8,
-    QR_Q6_K = 9
+    QR_Q6_K = 9,
+    QR_Q5_K = 10
 } qr_type;
 
 typedef enum { QR_F32 = 0, QR_BF16 = 1 } qr_dtype;
@@ -111,8 +119,8 @@ typedef enum {
 /*
  * qr_quantize_rows -- importance-weighted quantization of weight rows [WT 一],
  * [KQ 一], [LQ 2.1].
- *  t        QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q6_0, QR_Q4_K or QR_Q6_K
- *           (else EINVAL_TYPE).
+ *  t        QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q6_0, QR_Q4_K, QR_Q5_K or
+ *           QR_Q6_K (else EINVAL_TYPE).
  *  src      QR_F32 or QR_BF16: element type of x.
  *  x        [n_rows, n_per_row] weights, row-major.
  *  imatrix  [n_per_row] fp32 importances shared by all rows, or NULL for
@@ -122,9 +130,9 @@ typedef enum {
  * float; w_j = imatrix[j] * sqrtf(fmaf(x_j, x_j, sigma2)); a 32-weight group
  * whose w are all zero uses imatrix = 1 instead. Each 32-weight block (Q4_K:
  * sub-block) is fitted by a trial-scale search, the weighted least-squares
- * scale (and offset), and greedy flip passes; Q4_K then quantizes the eight
- * sub-scales and offsets to 6 bits under fp16 super-scales and re-rounds the
- * levels. Q6_K fits each 16-weight sub-block with the symmetric routine on
+ * scale (and offset), and greedy flip passes; Q4_K (levels 0..15) and Q5_K
+ * (0..31) then quantize the eight sub-scales and offsets to 6 bits under
+ * fp16 super-scales and re-round the levels. Q6_K fits each 16-weight sub-block with the symmetric routine on
  * levels -32..31, sets d = fp16(max |d_j| / 127) and s_j = rint(d_j / d)
  * in -127..127, and re-rounds the levels against d*s_j ([KQ 一]'s two-level
  * scaling at 6 bits; the layout is this library's). The results are
@@ -158,8 +166,8 @@ int qr_quantize_rows_weighted(int t, int src, const void *x,
                               int64_t n_per_row, int weighting, void *out,
                               void *stream);
 
-/* How the Q4_K 6-bit sub-scales and sub-offsets are chosen (types without
- * sub-scales ignore it). */
+/* How the Q4_K and Q5_K 6-bit sub-scales and sub-offsets are chosen (types
+ * without them ignore it). */
 typedef enum {
     QR_FIT_MAX = 0,       /* d = fp16(max a_j / 63), sc_j = rint(a_j / d): the default */
     QR_FIT_WEIGHTED = 1   /* weighted least-squares fit of the eight values */
@@ -168,7 +176,7 @@ typedef enum {
 /*
  * qr_quantize_rows_ex -- the row quantizer with every option: grouped
  * importances (as qr_quantize_rows_grouped), a weighting (as
- * qr_quantize_rows_weighted) and the Q4_K sub-scale fit. [KQ 一] fixes eight
+ * qr_quantize_rows_weighted) and the Q4_K/Q5_K sub-scale fit. [KQ 一] fixes eight
  * 6-bit sub-scales and sub-offsets under fp16 super-scales but not how they
  * are chosen. With QR_FIT_WEIGHTED the sub-blocks' least-squares scales a_j
  * (and offsets b_j) are fitted as a_j ~ d * sc_j, sc_j in 0..63, by the
@@ -220,7 +228,7 @@ int qr_quantize_activations_q8k(int t, int src, const void *x, int64_t n_rows,
  * qr_dequantize_rows -- decoder for every type above. in is the packed
  * [n_rows, qr_row_bytes(t, n_per_row)] buffer; out is fp32
  * [n_rows, n_per_row]. Symmetric blocks decode to d*(u - nmax), asymmetric
- * ones to fmaf(d, u, m), Q4_K to fmaf(f32(d)*sc, u, -(f32(dmin)*mn)), the
+ * ones to fmaf(d, u, m), Q4_K and Q5_K to fmaf(f32(d)*sc, u, -(f32(dmin)*mn)), the
  * Q8_K family to d*q.
  */
 int qr_dequantize_rows(int t, const void *in, int64_t n_rows,

@@ -31,7 +31,8 @@ extern "C" {
 
 /*
  * qr_matmul_q8k128 -- y[t][r] = sum_i W[r][i] * A[t][i] [Q8 修复方案].
- *  t      weight type: QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1 or QR_Q4_K.
+ *  t      weight type: QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q6_0, QR_Q4_K,
+ *         QR_Q5_K or QR_Q6_K.
  *  w      packed weight rows [n_out, qr_row_bytes(t, n_in)] (the output of
  *         qr_quantize_rows).
  *  x      packed Q8_K_128 activation rows [n_tok, qr_row_bytes(QR_Q8_K128,
@@ -40,15 +41,17 @@ extern "C" {
  * W and A are the values the blocks encode. Per 32 weights the codes are
  * multiplied with the activation codes in int32 (four products per
  * instruction), the weight offset is folded in with the block's int16 code
- * sum (Q4_0, Q5_0: sum(u*q) - 8 or 16 * bsum; Q4_1, Q5_1: m * bsum; Q4_K:
- * dmin*mn_j * bsum_j), and the scales are applied in fp32. The fp32 sums are
+ * sum (Q4_0, Q5_0, Q6_0: sum(u*q) - 8, 16 or 32 * bsum; Q4_1, Q5_1:
+ * m * bsum; Q4_K, Q5_K: dmin*mn_j * bsum_j; Q6_K: the levels are signed,
+ * no offset), and the scales are applied in fp32. The fp32 sums are
  * taken in a fixed order (reproducible bit for bit); against the exact
  * product each output is within (n_in/1024 + 9) * 2^-24 of
- * S = sum_i (|scale part_i| + |offset part_i|) * |A[t][i]|. From 17 tokens
+ * S = sum_i (|scale part_i| + |offset part_i|) * |A[t][i]| ((n_in/512 + 9)
+ * for Q6_K, whose 16-weight sub-blocks add two scaled terms per group). From 17 tokens
  * on, the integer products run on the int8 matrix cores (tiles of 64 tokens
  * x 64 rows) and the per-block sums are accumulated in double: each output
  * is then within 2^-24 |y| + 8 * 2^-24 S, inside the same bound.
- * Limits: n_in a positive multiple of 128 (256 for Q4_K), at most
+ * Limits: n_in a positive multiple of 128 (256 for the K types), at most
  * QR_MATMUL_MAX_IN. n_out == 0 or n_tok == 0 is a no-op.
  */
 int qr_matmul_q8k128(int t, const void *w, const void *x, int64_t n_out,

@@ -80,15 +80,15 @@ __device__ __forceinline__ float half_bits(uint32_t h) {
 // bytes (lo: elements 0..15, hi: 16..31) and the float parts of the decode.
 struct Group {
   uint32_t lo[4], hi[4];
-  float sa;  // scale part:  d (legacy), d*sc (Q4_K), d*s of the first 16 (Q6_K)
-  float sb;  // offset part: the level offset 8/16 (symmetric), m (Q4_1/Q5_1) or dmin*mn (Q4_K)
+  float sa;  // scale part:  d (legacy), d*sc (Q4_K, Q5_K), d*s of the first 16 (Q6_K)
+  float sb;  // offset part: the level offset 8/16 (symmetric), m (Q4_1/Q5_1) or dmin*mn (Q4_K, Q5_K)
   float sa1; // Q6_K: d*s of the second 16 (its codes are signed levels, no offset)
 };
 
-// The packed bytes of one group as loaded (up to eight words), kept apart
+// The packed bytes of one group as loaded (up to nine words), kept apart
 // from the decoding so that a batch of loads can be in flight at once.
 struct RawGroup {
-  uint32_t v[8];
+  uint32_t v[9];
 };
 
 template <int TYPE>
@@ -105,15 +105,18 @@ __device__ __forceinline__ RawGroup load_raw(const uint8_t* __restrict__ row, in
     for (int k = 0; k < 4; ++k) R.v[2 + k] = ld32(sb + 20 + 16 * j + 4 * k);
     R.v[6] = ld32(sb + 148 + 8 * j);
     R.v[7] = ld32(sb + 152 + 8 * j);
-  } else if (TYPE == QR_Q4_K) {
-    const uint8_t* sb = row + (int64_t)(g >> 3) * 144;
+  } else if (TYPE == QR_Q4_K || TYPE == QR_Q5_K) {
+    // header | (Q5_K: the group's fifth-bit word) | its 16 nibble bytes
+    constexpr bool Q5 = TYPE == QR_Q5_K;
+    const uint8_t* sb = row + (int64_t)(g >> 3) * (Q5 ? 176 : 144);
     const u32x4 h = *reinterpret_cast<const u32x4*>(sb);
-    const u32x4 c = *reinterpret_cast<const u32x4*>(sb + 16 + 16 * (g & 7));
+    const u32x4 c = *reinterpret_cast<const u32x4*>(sb + (Q5 ? 48 : 16) + 16 * (g & 7));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       R.v[k] = h[k];
       R.v[4 + k] = c[k];
     }
+    if (Q5) R.v[8] = ld32(sb + 16 + 4 * (g & 7));
   } else {
     constexpr int WORDS = TYPE == QR_Q4_0 ? 5 : (TYPE == QR_Q5_1 || TYPE == QR_Q6_0) ? 7 : 6;
     const uint8_t* p = row + (int64_t)g * (WORDS * 4);
@@ -188,7 +191,7 @@ __device__ __forceinline__ Group unpack(const RawGroup& R, int g) {
   }
   uint32_t qh = 0;
   int qs0;  // first word of the 16 code bytes
-  if (TYPE == QR_Q4_K) {
+  if (TYPE == QR_Q4_K || TYPE == QR_Q5_K) {
     const int j = g & 7;
     const uint32_t h1 = R.v[1], h2 = R.v[2], h3 = R.v[3];
     const uint64_t sc6 = (uint64_t)h1 | ((uint64_t)(h2 & 0xffffu) << 32);
@@ -196,6 +199,7 @@ __device__ __forceinline__ Group unpack(const RawGroup& R, int g) {
     const float d = half_bits(R.v[0]), dmin = half_bits(R.v[0] >> 16);
     G.sa = d * (float)((sc6 >> (6 * j)) & 63);     // exact: 11-bit times 6-bit
     G.sb = dmin * (float)((mn6 >> (6 * j)) & 63);
+    if (TYPE == QR_Q5_K) qh = R.v[8];
     qs0 = 4;
   } else if (TYPE == QR_Q6_0) {
     G.sa = __builtin_bit_cast(float, R.v[0]);
@@ -214,7 +218,7 @@ __device__ __forceinline__ Group unpack(const RawGroup& R, int g) {
     const uint32_t wk = R.v[qs0 + k];
     G.lo[k] = wk & 0x0f0f0f0fu;
     G.hi[k] = (wk >> 4) & 0x0f0f0f0fu;
-    if (TYPE == QR_Q5_0 || TYPE == QR_Q5_1) {
+    if (TYPE == QR_Q5_0 || TYPE == QR_Q5_1 || TYPE == QR_Q5_K) {
       G.lo[k] |= spread4((qh >> (4 * k)) & 15u) << 4;
       G.hi[k] |= spread4((qh >> (16 + 4 * k)) & 15u) << 4;
     }
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
       *reinterpret_cast<uint4*>(&st.wq[srow][8 * sq]) = c0;
       *reinterpret_cast<uint4*>(&st.wq[srow][8 * sq + 4]) = c1;
       st.wsa[sq][srow] = G.sa;
-      st.wsb[sq][srow] = Q6K ? G.sa1 : TYPE == QR_Q4_K ? -G.sb : G.sb;
+      st.wsb[sq][srow] = Q6K ? G.sa1 : (TYPE == QR_Q4_K || TYPE == QR_Q5_K) ? -G.sb : G.sb;
     }
     uint4 a0, a1;
     a0.x = tok_ok ? av[0] : 0u; a0.y = tok_ok ? av[1] : 0u; a0.z = tok_ok ? av[2] : 0u; a0.w = tok_ok ? av[3] : 0u;
@@ -712,6 +716,7 @@ int launch_mfma_type(int t, const uint8_t* w, const uint8_t* x, int64_t n_out, i
     case QR_Q5_1: return launch_mfma<QR_Q5_1, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
     case QR_Q6_0: return launch_mfma<QR_Q6_0, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
     case QR_Q6_K: return launch_mfma<QR_Q6_K, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q5_K: return launch_mfma<QR_Q5_K, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
     default: return launch_mfma<QR_Q4_K, ACT>(w, x, n_out, n_tok, n_in, wrb, y, s);
   }
 }
@@ -741,6 +746,7 @@ int launch_act(int t, int tt, const uint8_t* w, const uint8_t* x, int64_t n_out,
     case QR_Q5_1: return launch_type<QR_Q5_1, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
     case QR_Q6_0: return launch_type<QR_Q6_0, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
     case QR_Q6_K: return launch_type<QR_Q6_K, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
+    case QR_Q5_K: return launch_type<QR_Q5_K, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
     default: return launch_type<QR_Q4_K, ACT>(tt, w, x, n_out, n_tok, n_in, wrb, y, s);
   }
 }
@@ -755,7 +761,7 @@ int qr_matmul_q8k(int t, int act, const void* w, const void* x, int64_t n_out, i
   if (!qr_is_weight_type(t)) return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   if (act != QR_Q8_K128 && act != QR_Q8_K64 && act != QR_Q8_K16)
     return qr_fail(QR_EINVAL_TYPE, "activation type %d is not a Q8_K type", act);
-  const int64_t wb = (t == QR_Q4_K || t == QR_Q6_K) ? 256 : 32;
+  const int64_t wb = (t == QR_Q4_K || t == QR_Q5_K || t == QR_Q6_K) ? 256 : 32;
   const int64_t mult = wb > act_block(act) ? wb : act_block(act);
   if (n_in <= 0 || n_in % mult != 0 || n_in > QR_MATMUL_MAX_IN)
     return qr_fail(QR_EINVAL_SHAPE, "n_in=%lld must be a positive multiple of %lld and at most %d", (long long)n_in,

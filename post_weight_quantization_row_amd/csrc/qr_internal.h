@@ -18,4 +18,4 @@ QR_HIDDEN int qr_check_launch(const char* what);
 inline bool qr_aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // The weight-row types (everything but the Q8_K_128 activation format).
-inline bool qr_is_weight_type(int t) { return (t >= 0 && t <= 4) || t == 6 || t == 9; }
+inline bool qr_is_weight_type(int t) { return (t >= 0 && t <= 4) || t == 6 || t == 9 || t == 10; }

@@ -848,9 +848,11 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
         store_u32(p + 8, pack_high_bits(u));
         store_u32(p + 12, qs.x); store_u32(p + 16, qs.y); store_u32(p + 20, qs.z); store_u32(p + 24, qs.w);
       }
-    } else {  // QR_Q4_K: lanes 8s .. 8s+7 hold the sub-blocks of one super-block [KQ 一]
+    } else {  // QR_Q4_K, QR_Q5_K: lanes 8s .. 8s+7 hold the sub-blocks of one super-block [KQ 一]
+      constexpr int KMAX = TYPE == QR_Q5_K ? 31 : 15;    // levels 0..KMAX
+      constexpr int KBYTES = TYPE == QR_Q5_K ? 176 : 144;
       float d, m, sw;
-      solve_asym<15, true, BF16, VAR>(lds_raw, g, qg, imp, L, d, m, sw);
+      solve_asym<KMAX, true, BF16, VAR>(lds_raw, g, qg, imp, L, d, m, sw);
       const float a = d > 0.0f ? d : 0.0f;
       const float b = -m > 0.0f ? -m : 0.0f;
       const int j = g & 7;
@@ -902,16 +904,23 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
         const float id = 1.0f / ds;
         load_group<BF16>(lds_raw, g, u);
 #pragma unroll
-        for (int i = 0; i < QK; ++i) u[i] = med3(rne((u[i] + dm) * id), 0.0f, 15.0f);
+        for (int i = 0; i < QK; ++i) u[i] = med3(rne((u[i] + dm) * id), 0.0f, (float)KMAX);
       }
-      const uint4 qs = pack_nibbles_f(u);
+      uint8_t* p = orow + (size_t)(g >> 3) * KBYTES;
+      if constexpr (TYPE == QR_Q5_K) {   // fifth bits at 16 + 4j, low nibbles at 48 + 16j
+        uint32_t ui[QK];
+#pragma unroll
+        for (int i = 0; i < QK; ++i) ui[i] = (uint32_t)u[i];
+        store_u32(p + 16 + 4 * j, pack_high_bits(ui));
+        *reinterpret_cast<uint4*>(p + 48 + 16 * j) = pack_nibbles(ui);
+      } else {
+        *reinterpret_cast<uint4*>(p + 16 + 16 * j) = pack_nibbles_f(u);
+      }
       // the eight 6-bit fields, merged over the super-block's lanes
       const uint64_t scj = (uint64_t)(uint32_t)sc << (6 * j);
       const uint64_t mnj = (uint64_t)(uint32_t)mn << (6 * j);
       const uint64_t scb = (uint64_t)oct_or((uint32_t)scj) | ((uint64_t)oct_or((uint32_t)(scj >> 32)) << 32);
       const uint64_t mnb = (uint64_t)oct_or((uint32_t)mnj) | ((uint64_t)oct_or((uint32_t)(mnj >> 32)) << 32);
-      uint8_t* p = orow + (size_t)(g >> 3) * 144;
-      *reinterpret_cast<uint4*>(p + 16 + 16 * j) = qs;
       if (j == 0) {
         const uint32_t h0 = (uint32_t)__builtin_bit_cast(uint16_t, d16) |
                             ((uint32_t)__builtin_bit_cast(uint16_t, m16) << 16);
@@ -1100,11 +1109,13 @@ __device__ __forceinline__ void decode4(const uint8_t* __restrict__ in, int64_t 
     const float d = __builtin_bit_cast(float, dbits);
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = d * (float)(int8_t)(qv >> (8 * i));
-  } else if constexpr (TYPE == QR_Q4_K) {
-    const uint8_t* p = in + (U >> 3) * 144;
+  } else if constexpr (TYPE == QR_Q4_K || TYPE == QR_Q5_K) {
+    constexpr bool Q5 = TYPE == QR_Q5_K;
+    const uint8_t* p = in + (U >> 3) * (Q5 ? 176 : 144);
     const int j = (int)(U & 7);
-    const u32x4 h = *reinterpret_cast<const u32x4*>(p);       // 144*B is 16-byte aligned
-    const uint32_t bytes = *reinterpret_cast<const uint32_t*>(p + 16 + 16 * j + 4 * (k & 3));
+    const u32x4 h = *reinterpret_cast<const u32x4*>(p);       // 144*B and 176*B are 16-byte aligned
+    const uint32_t bytes = *reinterpret_cast<const uint32_t*>(p + (Q5 ? 48 : 16) + 16 * j + 4 * (k & 3));
+    const uint32_t qh = Q5 ? *reinterpret_cast<const uint32_t*>(p + 16 + 4 * j) >> (4 * k) : 0u;
     const uint64_t scb = (uint64_t)h.y | ((uint64_t)(h.z & 0xffffu) << 32);
     const uint64_t mnb = (uint64_t)(h.z >> 16) | ((uint64_t)h.w << 16);
     const float dA = (float)__builtin_bit_cast(_Float16, (uint16_t)(h.x & 0xffffu));
@@ -1113,7 +1124,8 @@ __device__ __forceinline__ void decode4(const uint8_t* __restrict__ in, int64_t 
     const float dm = dB * (float)(uint32_t)((mnb >> (6 * j)) & 63u);
     const int sh = (k >> 2) * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = fma_(ds, (float)((bytes >> (8 * i + sh)) & 15u), -dm);
+    for (int i = 0; i < 4; ++i)
+      o[i] = fma_(ds, (float)(((bytes >> (8 * i + sh)) & 15u) | (((qh >> i) & 1u) << 4)), -dm);
   } else if constexpr (TYPE == QR_Q6_K) {
     const uint8_t* p = in + (U >> 3) * 212;
     const int j = (int)(U & 7);
@@ -1192,7 +1204,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 int block_elems(int t) {
   switch (t) {
     case QR_Q4_0: case QR_Q4_1: case QR_Q5_0: case QR_Q5_1: case QR_Q6_0: return 32;
-    case QR_Q4_K: case QR_Q6_K: return 256;
+    case QR_Q4_K: case QR_Q5_K: case QR_Q6_K: return 256;
     case QR_Q8_K128: return 128;
     case QR_Q8_K64: return 64;
     case QR_Q8_K16: return 16;
@@ -1212,6 +1224,7 @@ size_t block_bytes(int t) {
     case QR_Q8_K64: return 72;
     case QR_Q8_K16: return 24;
     case QR_Q6_K: return 212;
+    case QR_Q5_K: return 176;
     default: return 0;
   }
 }
@@ -1266,6 +1279,7 @@ int dispatch_rows(int t, const void* x, const float* imatrix, int64_t n_rows, in
     case QR_Q4_K: return QR_ROWS_LAUNCH(QR_Q4_K);
     case QR_Q6_0: return QR_ROWS_LAUNCH(QR_Q6_0);
     case QR_Q6_K: return QR_ROWS_LAUNCH(QR_Q6_K);
+    case QR_Q5_K: return QR_ROWS_LAUNCH(QR_Q5_K);
     default: return qr_fail(QR_EINVAL_TYPE, "type %d is not a weight-row type", t);
   }
 #undef QR_ROWS_LAUNCH
@@ -1302,7 +1316,7 @@ int quantize_rows_common(int t, int src, const void* x, const float* imatrix, in
     return qr_fail(QR_EINVAL_PTR, "device pointers must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int n = (int)n_per_row;
-  if (t != QR_Q4_K) fit = QR_FIT_MAX;   // no sub-scales to fit
+  if (t != QR_Q4_K && t != QR_Q5_K) fit = QR_FIT_MAX;   // no 6-bit sub-scales to fit
   if (weighting == QR_W_SQRT_SIGMA2_X2 && fit == QR_FIT_MAX)
     return src == QR_F32 ? dispatch_rows<false, false>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, 0, 0, s)
                          : dispatch_rows<true, false>(t, x, imatrix, n_rows, n, rows_per_group, out, rb, 0, 0, s);
@@ -1455,6 +1469,7 @@ int qr_dequantize_rows(int t, const void* in, int64_t n_rows, int64_t n_per_row,
     case QR_Q4_K: hipLaunchKernelGGL(k_dequantize<QR_Q4_K>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     case QR_Q6_0: hipLaunchKernelGGL(k_dequantize<QR_Q6_0>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     case QR_Q6_K: hipLaunchKernelGGL(k_dequantize<QR_Q6_K>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
+    case QR_Q5_K: hipLaunchKernelGGL(k_dequantize<QR_Q5_K>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     case QR_Q8_K64: hipLaunchKernelGGL(k_dequantize<QR_Q8_K64>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     case QR_Q8_K16: hipLaunchKernelGGL(k_dequantize<QR_Q8_K16>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;
     default: hipLaunchKernelGGL(k_dequantize<QR_Q8_K128>, dim3(grid), dim3(256), 0, s, p, n_items, out); break;

@@ -82,18 +82,21 @@ __device__ __forceinline__ void decode4(const uint8_t* __restrict__ row, int gin
     const uint32_t w = ld32(b + off);
 #pragma unroll
     for (int e = 0; e < 4; ++e) xh[e] = d * (float)(int8_t)(uint8_t)(w >> (8 * e));
-  } else if (TYPE == QR_Q4_K) {
-    const uint8_t* sb = row + (int64_t)(gin >> 3) * 144;
+  } else if (TYPE == QR_Q4_K || TYPE == QR_Q5_K) {
+    constexpr bool Q5 = TYPE == QR_Q5_K;
+    const uint8_t* sb = row + (int64_t)(gin >> 3) * (Q5 ? 176 : 144);
     const int j = gin & 7;
     const uint32_t h0 = ld32(sb), h1 = ld32(sb + 4), h2 = ld32(sb + 8), h3 = ld32(sb + 12);
     const uint64_t sc6 = (uint64_t)h1 | ((uint64_t)(h2 & 0xffffu) << 32);
     const uint64_t mn6 = (uint64_t)(h2 >> 16) | ((uint64_t)h3 << 16);
     const float ds = half_bits(h0) * (float)((sc6 >> (6 * j)) & 63);
     const float dm = half_bits(h0 >> 16) * (float)((mn6 >> (6 * j)) & 63);
-    const uint32_t w = ld32(sb + 16 + 16 * j + 4 * (k & 3));
+    const uint32_t w = ld32(sb + (Q5 ? 48 : 16) + 16 * j + 4 * (k & 3));
     const uint32_t nib = k < 4 ? (w & 0x0f0f0f0fu) : ((w >> 4) & 0x0f0f0f0fu);
+    const uint32_t qh = Q5 ? ld32(sb + 16 + 4 * j) >> (4 * k) : 0u;   // fifth bits of elements 4k ..
 #pragma unroll
-    for (int e = 0; e < 4; ++e) xh[e] = __builtin_fmaf(ds, (float)((nib >> (8 * e)) & 0xffu), -dm);
+    for (int e = 0; e < 4; ++e)
+      xh[e] = __builtin_fmaf(ds, (float)(((nib >> (8 * e)) & 0xffu) | (((qh >> e) & 1u) << 4)), -dm);
   } else if (TYPE == QR_Q6_K) {
     const uint8_t* p = row + (int64_t)(gin >> 3) * 212;
     const int j = gin & 7;
@@ -379,6 +382,7 @@ int dispatch_stats(int t, const void* x, const uint8_t* packed, const float* q, 
     case QR_Q8_K64: return run_stats<QR_Q8_K64, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     case QR_Q8_K16: return run_stats<QR_Q8_K16, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     case QR_Q6_K: return run_stats<QR_Q6_K, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
+    case QR_Q5_K: return run_stats<QR_Q5_K, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
     default: return run_stats<QR_Q8_K128, BF16>(x, packed, q, n_rows, n_per_row, rb, out, ws, s);
   }
 }
@@ -395,7 +399,7 @@ size_t qr_stats_workspace_bytes(int64_t n_rows, int64_t n_per_row) {
 int qr_quantize_stats(int t, int src, const void* x, const void* packed, const float* imatrix, int64_t n_rows,
                       int64_t n_per_row, qr_stats* out, void* workspace, size_t workspace_bytes, void* stream) {
   qr_clear_error();
-  if (t < QR_Q4_0 || t > QR_Q6_K) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
+  if (t < QR_Q4_0 || t > QR_Q5_K) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
   if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
   const size_t rb = qr_row_bytes(t, n_per_row);
   if (n_rows < 0 || n_per_row <= 0 || rb == 0 || n_per_row % 32 != 0)

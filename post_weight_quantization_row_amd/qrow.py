@@ -18,14 +18,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # QROW_LIBRARY may name another build of the same library (A/B timing).
 LIB_PATH = os.environ.get("QROW_LIBRARY") or os.path.join(HERE, "libqrow.so")
 
-QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q4_K, QR_Q8_K128, QR_Q6_0, QR_Q8_K64, QR_Q8_K16, QR_Q6_K = range(10)
+QR_Q4_0, QR_Q4_1, QR_Q5_0, QR_Q5_1, QR_Q4_K, QR_Q8_K128, QR_Q6_0, QR_Q8_K64, QR_Q8_K16, QR_Q6_K, QR_Q5_K = range(11)
 QR_F32, QR_BF16 = 0, 1
 # element-importance weightings (qr_weighting)
 WEIGHTINGS = {"sqrt_sigma2_x2": 0, "x2": 1, "abs_x": 2, "sigma2_plus_x2": 3,
               "sigma_plus_abs_x": 4, "imatrix_only": 5}
 TYPES = {"q4_0": QR_Q4_0, "q4_1": QR_Q4_1, "q5_0": QR_Q5_0, "q5_1": QR_Q5_1,
          "q4_k": QR_Q4_K, "q8_k128": QR_Q8_K128, "q6_0": QR_Q6_0,
-         "q8_k64": QR_Q8_K64, "q8_k16": QR_Q8_K16, "q6_k": QR_Q6_K}
+         "q8_k64": QR_Q8_K64, "q8_k16": QR_Q8_K16, "q6_k": QR_Q6_K, "q5_k": QR_Q5_K}
 ACT_TYPES = ("q8_k128", "q8_k64", "q8_k16")
 FITS = {"max": 0, "weighted": 1}   # qr_subscale_fit
 ERRORS = {-1: "QR_EINVAL_TYPE", -2: "QR_EINVAL_SHAPE", -3: "QR_EINVAL_PTR",

@@ -39,11 +39,11 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_formats_agree_with_the_oracle(lib):
-    for t in range(10):
+    for t in range(11):
         assert lib.qr_block_elems(t) == oracle.block_elems(t)
         for n in (0, 32, 128, 256, 4096, 7168, 11008, 100):
             assert lib.qr_row_bytes(t, n) == oracle.row_bytes(t, n)
-    assert lib.qr_block_elems(10) == 0 and lib.qr_row_bytes(10, 256) == 0
+    assert lib.qr_block_elems(11) == 0 and lib.qr_row_bytes(11, 256) == 0
 
 
 def test_solver_constants_agree_with_the_oracle():
@@ -72,7 +72,8 @@ def test_argument_validation_without_a_gpu(lib):
     assert lib.qr_quantize_rows(4, 1, fake, None, 4, 32768 + 256, fake, None) == -2   # bf16 too
     assert lib.qr_quantize_activations_q8k128(0, fake, 4, 100, fake, None) == -2
     assert lib.qr_dequantize_rows(4, fake, 4, 32, fake, None) == -2
-    assert lib.qr_dequantize_rows(10, fake, 4, 32, fake, None) == -1
+    assert lib.qr_dequantize_rows(11, fake, 4, 32, fake, None) == -1
+    assert lib.qr_quantize_rows(10, 0, fake, None, 4, 128, fake, None) == -2    # Q5_K: whole 256-blocks
     # n_rows == 0 is a no-op even with NULL pointers
     assert lib.qr_quantize_rows(0, 0, None, None, 0, 256, None, None) == 0
     assert lib.qr_quantize_activations_q8k128(0, None, 0, 128, None, None) == 0
@@ -212,7 +213,7 @@ def test_stats_argument_validation_without_a_gpu(lib):
     ws = lib.qr_stats_workspace_bytes(4, 256)
     assert ws > 0 and lib.qr_stats_workspace_bytes(4, 0) == 0
     st = lib.qr_quantize_stats
-    assert st(10, 0, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
+    assert st(11, 0, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
     assert st(8, 0, fake, fake, None, 4, 48, fake, fake, ws, None) == -2     # whole 32-groups
     assert st(0, 2, fake, fake, None, 4, 256, fake, fake, ws, None) == -1
     assert st(4, 0, fake, fake, None, 4, 128, fake, fake, ws, None) == -2    # Q4_K: 256

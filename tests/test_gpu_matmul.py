@@ -22,7 +22,7 @@ from post_weight_quantization_row_amd import synth
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k"]
+TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k", "q5_k"]
 
 
 @pytest.fixture(scope="module")
@@ -88,7 +88,7 @@ def test_long_rows_use_smaller_token_tiles(qr):
     check(qr, "q4_0", w, xa, 16384)
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q5_1"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q5_1", "q5_k"])
 @pytest.mark.parametrize("n_tok", [1, 8])
 def test_longest_rows(qr, t, n_tok):
     # n_in = QR_MATMUL_MAX_IN: one token per tile (the staged tile would not
@@ -119,7 +119,7 @@ def test_many_tokens(qr, t, n_out, n_tok, n_in):
     assert np.all(np.abs(y - yo) <= tight)
 
 
-@pytest.mark.parametrize("t", ["q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("t", ["q4_0", "q4_k", "q6_k", "q5_k"])
 @pytest.mark.parametrize("n_out,n_tok", [(4096, 512), (4033, 449)])
 def test_many_tokens_large_tiles(qr, t, n_out, n_tok):
     # enough 64 x 64 tiles (512) for the kernel's 64-row tiles; the smaller

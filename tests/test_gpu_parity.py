@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
-WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k"]
+WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k", "q5_k"]
 
 
 @pytest.fixture(scope="module")
@@ -84,7 +84,7 @@ SHAPES = [(1, 256), (5, 2304), (3, 4096), (33, 512), (2, 7168), (2, 11008 // 32 
 def test_weight_rows_small(qr, t, bf16, qkind):
     rng = np.random.default_rng(zlib.crc32(f"{t}/{bf16}/{qkind}".encode()))
     for n_rows, n in SHAPES:
-        if t in ("q4_k", "q6_k") and n % 256:
+        if t in ("q4_k", "q5_k", "q6_k") and n % 256:
             n = n // 256 * 256
         x = (0.02 * rng.standard_t(5, (n_rows, n))).astype(F32)
         x[:, ::97] *= 30                              # sparse outliers

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 F32 = np.float32
 ACTS = ["q8_k64", "q8_k16"]
-WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k"]
+WEIGHT_TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k", "q5_k"]
 
 
 @pytest.fixture(scope="module")
@@ -123,7 +123,7 @@ def product_check(qr, t, act, w, xa, n_in):
 @pytest.mark.parametrize("n_out,n_tok,n_in", [(37, 1, 256), (16, 3, 768), (100, 8, 1024), (33, 13, 2048),
                                               (5, 2, 8192), (9, 5, 1280)])
 def test_product(qr, t, act, n_out, n_tok, n_in):
-    if t in ("q4_k", "q6_k") and n_in % 256:
+    if t in ("q4_k", "q5_k", "q6_k") and n_in % 256:
         n_in = 256 * (n_in // 256 + 1)
     say(f"product {t} x {act} ({n_out},{n_tok},{n_in})")
     x, q = synth.q4_0_matrix(n_out, n_in, seed=n_out + n_in)

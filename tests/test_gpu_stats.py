@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
-TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q8_k128", "q6_0", "q6_k"]
+TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q8_k128", "q6_0", "q6_k", "q5_k"]
 
 
 @pytest.fixture(scope="module")

@@ -46,13 +46,13 @@ def sigma2_ambiguous(row):
     return False
 
 
-def assert_rows_equal(gpu, ref, x, q_of_row, mode, fit):
+def assert_rows_equal(gpu, ref, x, q_of_row, mode, fit, t="q4_k"):
     for r in np.nonzero((gpu != ref).any(axis=1))[0]:
         ok = False
         if sigma2_ambiguous(x[r]):
             s32 = F32(oracle.row_sigma2_f64(x[r]))
             for s in (np.nextafter(s32, F32(np.inf)), np.nextafter(s32, F32(-np.inf))):
-                ok |= np.array_equal(gpu[r], oracle.quantize_row_sigma2_ex("q4_k", x[r], q_of_row(r), s,
+                ok |= np.array_equal(gpu[r], oracle.quantize_row_sigma2_ex(t, x[r], q_of_row(r), s,
                                                                            mode, fit))
         assert ok, f"row {r} differs at bytes {np.nonzero(gpu[r] != ref[r])[0][:16]}"
 
@@ -70,6 +70,20 @@ def test_weighted_fit_rows(qr, bf16, with_q, n_rows, n):
                                  subscale_fit="weighted").cpu().numpy()
     ref = oracle.quantize_rows_ex("q4_k", x, q, fit="weighted")
     assert_rows_equal(got, ref, x, lambda r: q, 0, "weighted")
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("n_rows,n", [(5, 256), (9, 2048), (4, 16384)])
+def test_q5_k_weighted_fit_rows(qr, bf16, n_rows, n):
+    # the same sub-scale fit over Q5_K's 5-bit sub-block fits
+    say(f"q5_k weighted fit bf16={bf16} ({n_rows},{n})")
+    x, q = synth.q4_k_matrix(n_rows, n, seed=740 + n_rows + n)
+    if bf16:
+        x = synth.round_to_bf16(x)
+    got = qr.qr_quantize_rows_ex("q5_k", to_dev(x, bf16), torch.from_numpy(q).cuda(),
+                                 subscale_fit="weighted").cpu().numpy()
+    ref = oracle.quantize_rows_ex("q5_k", x, q, fit="weighted")
+    assert_rows_equal(got, ref, x, lambda r: q, 0, "weighted", t="q5_k")
 
 
 @pytest.mark.parametrize("mode", ["x2", "abs_x", "imatrix_only"])

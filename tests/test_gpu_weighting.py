@@ -19,7 +19,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
-TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k"]
+TYPES = ["q4_0", "q4_1", "q5_0", "q5_1", "q4_k", "q6_0", "q6_k", "q5_k"]
 MODES = list(oracle.WEIGHTINGS)
 
 
@@ -67,7 +67,7 @@ def test_weighting(qr, t, mode):
     rng = np.random.default_rng(zlib.crc32(f"{t}/{mode}".encode()))
     for bf16, (n_rows, n), qkind in [(False, (5, 2304), "lognormal"), (True, (3, 4096), "none"),
                                      (False, (33, 512), "zero-columns"), (True, (2, 7168), "lognormal")]:
-        if t in ("q4_k", "q6_k") and n % 256:
+        if t in ("q4_k", "q5_k", "q6_k") and n % 256:
             n = n // 256 * 256
         x = (0.02 * rng.standard_t(5, (n_rows, n))).astype(F32)
         x[:, ::97] *= 30
