@@ -99,11 +99,12 @@ def _setup(name, dev):
         out = torch.empty((11008, qrow.qr_row_bytes("q4_k", 4096)), dtype=torch.uint8, device=dev)
         return (lambda: qrow.qr_quantize_rows("q4_k", x, q, out=out),
                 x.numel() * 4 + q.numel() * 4 + out.numel(), x.numel())
-    if name == "q6_k_11008x4096":
-        # the same matrix in the 6-bit K-quant
+    if name in ("q6_k_11008x4096", "q5_k_11008x4096"):
+        # the same matrix in the 6-bit or 5-bit K-quant
+        t = name[:4]
         x, q = synth.torch_q4_k_matrix(dev)
-        out = torch.empty((11008, qrow.qr_row_bytes("q6_k", 4096)), dtype=torch.uint8, device=dev)
-        return (lambda: qrow.qr_quantize_rows("q6_k", x, q, out=out),
+        out = torch.empty((11008, qrow.qr_row_bytes(t, 4096)), dtype=torch.uint8, device=dev)
+        return (lambda: qrow.qr_quantize_rows(t, x, q, out=out),
                 x.numel() * 4 + q.numel() * 4 + out.numel(), x.numel())
     if name == "q4_k_fit_11008x4096":
         # the same matrix with the weighted fit of the 6-bit sub-scales
@@ -249,7 +250,7 @@ ACT_WORKLOADS = ("q8_k64_8192x7168", "q8_k16_8192x7168")
 STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "copy_1gib", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096", "q6_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
+                  "moe_256x2048x7168", "copy_1gib", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096", "q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -459,7 +460,7 @@ def main():
                                                "hbm_frac": round(bd / (md * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # importance-matrix accumulation (the step that produces the imatrix)
         # and the product with Q8_K_128 activations (the step that consumes both)
-        for name in ("q6_k_11008x4096",) + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS:
+        for name in ("q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS:
             fn, nb, n_el = _setup(name, dev)
             mi, _, _ = timed_steps(fn, 10, 2, flush)
             extra[name] = {"ms": round(mi, 5), "alg_bytes": nb, "G_elements_per_s": round(n_el / mi / 1e6, 3),

@@ -14,7 +14,8 @@ sensitive tensors differs by architecture. Readings taken here:
   plan), the layers spread evenly over the depth;
 * the base type is Q4_K and the 6-bit type this library's Q6_K, the same
   two-level K-quant scaling at 6 bits (Q6_0, the 32-weight 6-bit block,
-  can be chosen instead).
+  can be chosen instead); ``base="q5_k"`` gives the Q5_K_M-shaped plan the
+  page names beside Q4_K_M.
 
 ``plan_stack`` builds a plan (pure host arithmetic on row sizes),
 ``describe`` prints it (the dry run), and ``run`` quantizes every tensor on

@@ -78,6 +78,18 @@ def test_other_roles_and_types():
         mix.plan_stack(2, high="q8_k128")
 
 
+def test_q5_k_m_shaped_plan():
+    # the 5-bit K type as the base (Q5_K_M): 176 B per 256 weights, the
+    # sensitive roles at Q6_K within the budget
+    p = mix.plan_stack(base="q5_k")
+    assert p.bytes == recount(p)
+    base = sum(r * n for _, _, r, n in synth.STACK_LAYER) * 32 * 176 // 256
+    assert p.base_bytes() == base
+    assert 0 < p.bytes / base - 1 <= 0.10
+    assert 5.5 < 8 * p.bytes / p.weights < 6.0
+    assert {t.type for t in p.tensors} == {"q5_k", "q6_k"}
+
+
 def test_summary_totals():
     p = mix.plan_stack(2)
     s = mix.summary(p, {"sum_err2": 1.0, "sum_x2": 4.0, "sum_werr2": 9.0, "sum_wx2": 16.0},
