@@ -6,7 +6,8 @@
 //       的由来与原理", section 一: row statistic sigma2, element importance
 //       qw*sqrt(sigma2 + x^2), least-squares block scale sumlx/suml2 and
 //       greedy level flips along g = scale*w*(x - scale*l).
-//  [KQ] "3.2 K-quants 与重要性矩阵：量化兵器谱", section 一: Q4_K super-block.
+//  [KQ] "3.2 K-quants 与重要性矩阵：量化兵器谱", section 一: Q4_K super-block
+//       (Q5_K: the same super-block with 5-bit levels; the layout is ours).
 //  [LQ] "从零理解 LLM 量化 PTQ、QAT 与 ik_llama.cpp 量化体系的源码级导学", 2.1:
 //       legacy 32-weight blocks.
 //  [Q8] "ik_llama.cpp 量化精度修复实录：用 Q8_K_128 替代 Q8_1 …", 修复方案:
@@ -21,8 +22,8 @@
 //    sigma2. Each lane then owns one 32-element group at a
 //    time and solves it entirely in VGPRs: importances, trial scales,
 //    least-squares sums, the sequential flip passes (sequential within a
-//    lane, parallel across the 64 lanes), packing. For Q4_K, eight
-//    consecutive lanes hold the eight sub-blocks of one super-block and
+//    lane, parallel across the 64 lanes), packing. For the K types, eight
+//    consecutive lanes hold the eight 32-weight parts of one super-block and
 //    combine their scales with cross-lane shuffles.
 //  * Activations (Q8_K_128) and the decoders are streaming kernels: 32 lanes
 //    per 128-value block (one float4 each), several blocks in flight per
@@ -578,7 +579,7 @@ __device__ __forceinline__ void solve_asym(const void* lds, int g, const float* 
 }
 
 // -------------------------------------------------------------------------
-// weighted fit of the eight Q4_K sub-scales (or sub-offsets) [WT 一 applied
+// weighted fit of the eight Q4_K/Q5_K sub-scales (or sub-offsets) [WT 一 applied
 // to the values of a super-block]: v_j ~ d * l_j, l_j in 0..63, weights W_j.
 // Trial scales map the largest value to 63 + step*k; levels are rounded in
 // float; the sums, the score comparisons and the flips run in double (one

@@ -222,7 +222,7 @@ def qr_quantize_rows_ex(t, x: torch.Tensor, imatrix=None, rows_per_group=None, w
     """Every option of the row quantizer: imatrix is None, [n] or
     [n_groups, n] (rows_per_group = n_rows / n_groups when not given);
     weighting a name of WEIGHTINGS or its number; subscale_fit "max" or
-    "weighted" (Q4_K sub-scales)."""
+    "weighted" (the Q4_K and Q5_K sub-scales)."""
     _dev2d(x, "x")
     tid = _tid(t)
     n_rows, n = x.shape

@@ -261,6 +261,18 @@ def test_full_q4_k_11008x4096(qr):
     say(f"rows resolved by a neighbouring sigma2: {n_alt}")
 
 
+@pytest.mark.parametrize("t", ["q5_k", "q6_k"])
+def test_full_11008x4096_other_k_types_sampled(qr, t):
+    # the headline matrix in the 5- and 6-bit K types, quantized whole as
+    # the benchmark launches it; 256 sampled rows against the oracle
+    x, q = synth.q4_k_matrix()
+    say(f"case {t}_11008x4096 full (sampled rows)")
+    got = qr.qr_quantize_rows(t, to_dev(x, False), torch.from_numpy(q).cuda()).cpu().numpy()
+    rows = np.sort(np.random.default_rng(1021).choice(x.shape[0], 256, replace=False))
+    ref = oracle.quantize_rows(t, x[rows], q, threads=16)
+    assert_rows_equal(t, got[rows], ref, x[rows], lambda r: q)
+
+
 def test_full_q8_k128_8192x7168(qr):
     x, ch = synth.q8_k128_activations()
     say("case q8_k128_8192x7168 full")
