@@ -5,6 +5,8 @@ import ctypes as C
 import glob
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -222,3 +224,24 @@ def test_stats_argument_validation_without_a_gpu(lib):
     assert st(0, 0, fake, fake, None, 4, 256, None, fake, ws, None) == -3
     assert st(0, 0, fake, fake, None, 4, 256, fake, C.c_void_p(0x10010), ws, None) == -3
     assert st(0, 0, fake, fake, None, 4, 256, fake, fake, ws - 1, None) == -2
+
+
+def test_no_fallback_without_the_library_or_a_gpu():
+    # a missing library is an error, not a silent CPU path; so is a host tensor
+    code = (
+        "import os, torch\n"
+        "os.environ['QROW_LIBRARY'] = '/nonexistent/libqrow.so'\n"
+        "from post_weight_quantization_row_amd import qrow\n"
+        "try:\n"
+        "    qrow.load_library()\n"
+        "    raise SystemExit('loaded a missing library')\n"
+        "except RuntimeError as e:\n"
+        "    assert 'missing' in str(e)\n"
+        "try:\n"
+        "    qrow.qr_quantize_rows('q4_k', torch.zeros((2, 256)))\n"
+        "    raise SystemExit('quantized a host tensor')\n"
+        "except (TypeError, RuntimeError) as e:\n"
+        "    print('refused:', type(e).__name__)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "refused" in r.stdout
