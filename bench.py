@@ -207,7 +207,7 @@ def _setup(name, dev):
 
 def _mix_stack(dev):
     """The 32-layer 7B-shaped stack (bf16, resident) with its Q4_K_M-style
-    plan: Q4_K everywhere, Q6_0 for attn_v and ffn_down in the layers that
+    plan: Q4_K everywhere, Q6_K for attn_v and ffn_down in the layers that
     fit a +10% size budget."""
     import torch
     from post_weight_quantization_row_amd import mix, qrow, synth

@@ -105,7 +105,8 @@ typedef enum {
 #define QR_EINVAL_TYPE  -1  /* unknown type, or a type the call does not take */
 #define QR_EINVAL_SHAPE -2  /* n_per_row not a positive multiple of the block
                                length (32, 256 or 128), above the supported
-                               maximum, or a negative count                   */
+                               maximum, a negative count, or more rows than
+                               one launch holds (row quantizers: see below)  */
 #define QR_EINVAL_PTR   -3  /* NULL or misaligned pointer with n_rows > 0    */
 #define QR_EOVERFLOW    -4  /* a size computation overflows                  */
 #define QR_EDEVICE      -5  /* the HIP runtime reported an error            */
@@ -137,6 +138,12 @@ typedef enum {
  * in -127..127, and re-rounds the levels against d*s_j ([KQ 一]'s two-level
  * scaling at 6 bits; the layout is this library's). The results are
  * bit-identical to the CPU oracle of this project.
+ * Row limit: each row is one workgroup of 64 * min(8, ceil(n_per_row / 2048))
+ * threads, and one launch holds fewer than 2^32 threads, so n_rows must be
+ * at most (2^32 - 1) / that thread count (67108863 rows of 2048 values,
+ * 8388607 rows of 16384 or more); larger calls return QR_EINVAL_SHAPE
+ * before anything is launched (split them). This applies to every row
+ * quantizer below (for the grouped forms, to n_groups * rows_per_group).
  */
 int qr_quantize_rows(int t, int src, const void *x, const float *imatrix,
                      int64_t n_rows, int64_t n_per_row, void *out,

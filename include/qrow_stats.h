@@ -25,7 +25,7 @@
 extern "C" {
 #endif
 
-/* Written by qr_quantize_stats (device memory, 48 bytes). With e_i = x_i -
+/* Written by qr_quantize_stats (device memory, 72 bytes). With e_i = x_i -
  * xhat_i in float (xhat from qr_dequantize_rows) and q_i the imatrix entry
  * of the element's column (1 without an imatrix): */
 typedef struct {
@@ -36,6 +36,9 @@ typedef struct {
     float max_abs_err;   /* max |e_i|                                       */
     float p95_abs_err;   /* the ceil(0.95 N)-th smallest |e_i| (exact)      */
     int64_t n;           /* N = n_rows * n_per_row                          */
+    double rmse;         /* sqrt(sum_err2 / N)                              */
+    double rel_rmse;     /* sqrt(sum_err2 / sum_x2), 0 if sum_x2 is 0       */
+    double weighted_rel_rmse; /* sqrt(sum_werr2 / sum_wx2), 0 if that is 0  */
 } qr_stats;
 
 /* Device scratch bytes that qr_quantize_stats needs (a few hundred KB; 0
@@ -47,7 +50,8 @@ size_t qr_stats_workspace_bytes(int64_t n_rows, int64_t n_per_row);
  * [n_rows, qr_row_bytes(t, n_per_row)]) against `x` (src fp32 or bf16,
  * [n_rows, n_per_row]), weighted by `imatrix` ([n_per_row] fp32 or NULL).
  * RMSE = sqrt(sum_err2 / n); relative RMSE = sqrt(sum_err2 / sum_x2);
- * importance-weighted relative RMSE = sqrt(sum_werr2 / sum_wx2). max and
+ * importance-weighted relative RMSE = sqrt(sum_werr2 / sum_wx2), all three
+ * computed on the device in double from the sums. max and
  * p95 are exact (the percentile by a radix selection over the bits of |e|,
  * in three counting passes); the sums are double, added in a fixed order
  * (reproducible bit for bit), each within n * 2^-52 of its exact value,

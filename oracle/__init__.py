@@ -530,7 +530,8 @@ def matmul_q8_1(t, w_packed, x, n_out: int):
 def quantize_stats(t, x, packed, imatrix=None) -> dict:
     """Error statistics of packed rows against x (float32 [n_rows, n]):
     sums of e^2, x^2, q e^2, q x^2 (double), max |e| and the nearest-rank
-    95th percentile of |e|, e = x - decoded in float."""
+    95th percentile of |e|, e = x - decoded in float, and the RMSE, relative
+    RMSE and importance-weighted relative RMSE."""
     t = _tid(t)
     xv = _f32(x)
     n_rows, n = xv.shape
@@ -538,7 +539,7 @@ def quantize_stats(t, x, packed, imatrix=None) -> dict:
     if p.size != n_rows * row_bytes(t, n):
         raise ValueError("packed buffer has the wrong size")
     q = None if imatrix is None else _f32(imatrix)
-    sums = np.zeros(4, np.float64)
+    sums = np.zeros(7, np.float64)
     mx = np.zeros(1, np.float32)
     p95 = np.zeros(1, np.float32)
     rc = lib().orc_quantize_stats(t, xv, p, _ptr(q), n_rows, n, sums, mx, p95)
@@ -546,7 +547,8 @@ def quantize_stats(t, x, packed, imatrix=None) -> dict:
         raise ValueError("orc_quantize_stats: invalid arguments")
     return {"sum_err2": sums[0], "sum_x2": sums[1], "sum_werr2": sums[2],
             "sum_wx2": sums[3], "max_abs_err": mx[0], "p95_abs_err": p95[0],
-            "n": n_rows * n}
+            "n": n_rows * n, "rmse": sums[4], "rel_rmse": sums[5],
+            "weighted_rel_rmse": sums[6]}
 
 
 def f32_to_f16_bits(v: float) -> int:

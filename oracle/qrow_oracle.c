@@ -431,8 +431,10 @@ int orc_fit_levels_pos(int n, const float *v, const float *W, int nmax, int K,
 /* Weighted least squares for (d, m) from the five block sums, in double.
  * The reconstruction error is sum w x^2 minus the returned score.
  * Reading: codes whose weighted spread is below 2^-16 of sum w l^2 are
- * treated as constant (d = 0, m = weighted mean); with k4, a positive offset
- * is replaced by the best fit with m = 0. */
+ * treated as constant (d = 0, m = weighted mean). The sums arrive as floats,
+ * so D = Sw*Sll - Sl^2 carries an error of a few 2^-24 of Sw*Sll; below
+ * 2^-16 of it the solved (d, m) would rest on fewer than six good bits.
+ * With k4, a positive offset is replaced by the best fit with m = 0. */
 static void fit_dm(float Sw_, float Sx_, float Sl_, float Sll_, float Slx_,
                    int k4, double *d, double *m, double *score)
 {
@@ -536,8 +538,10 @@ int orc_solve_asym(int n, const float *x, const float *w, int nmax, int K,
     /* Flips (reading): the offset m of the winning trial is held fixed and
      * the scale-only rule of flip_passes() is applied to y = x - m, starting
      * from A = sum w y l = Slx - m*Sl and B = sum w l^2 = Sll of that trial;
-     * then (d, m) are refitted jointly on the final levels, with
-     * Sll = B and Slx = A + m*Sl. */
+     * the pass keeps A and B as running sums, move by move. Then (d, m) are
+     * refitted jointly on the final levels from the sums the pass kept:
+     * Sll = B and Slx = A + m*Sl (equal, in exact arithmetic, to the sums
+     * recomputed from the final codes), with Sl summed again. */
     const float mf = (float)bm;
     for (int i = 0; i < n; ++i) {
         y[i] = x[i] - mf;

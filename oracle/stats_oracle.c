@@ -15,7 +15,9 @@
  * (orc_dequantize_rows); the 95th percentile is the nearest-rank one, the
  * k-th smallest |e_i| with k = ceil(0.95 N); the sums are in double, in
  * element order: sum e^2, sum x^2, sum q e^2 and sum q x^2 (q the imatrix
- * entry of the element's column, 1 without an imatrix).
+ * entry of the element's column, 1 without an imatrix). From the sums:
+ * RMSE = sqrt(sum e^2 / N), relative RMSE = sqrt(sum e^2 / sum x^2) and the
+ * importance-weighted relative RMSE = sqrt(sum q e^2 / sum q x^2).
  */
 #include "orc_qrow.h"
 
@@ -62,6 +64,11 @@ int orc_quantize_stats(int type, const float *x, const uint8_t *packed,
     sums[1] = x2;
     sums[2] = qe2;
     sums[3] = qx2;
+    /* [LR 3.2]: RMSE = sqrt(total error / number of samples); the relative
+     * forms divide by the signal instead (0 when that is 0). */
+    sums[4] = sqrt(e2 / (double)n);
+    sums[5] = x2 > 0.0 ? sqrt(e2 / x2) : 0.0;
+    sums[6] = qx2 > 0.0 ? sqrt(qe2 / qx2) : 0.0;
     *max_abs = mx;
     *p95_abs = ae[k - 1];
     free(xh);

@@ -1236,13 +1236,18 @@ size_t block_bytes(int t) {
 bool aligned16(const void* p) { return qr_aligned(p, 16); }
 
 
+// Waves of the workgroup that quantizes one row of n_per_row values.
+int row_waves(int n_per_row) {
+  const int waves = (n_per_row / QK + WAVE - 1) / WAVE;
+  return waves > MAX_ROW_WAVES ? MAX_ROW_WAVES : waves;
+}
+
 template <int TYPE, bool BF16, bool VAR>
 int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_row, int64_t rows_per_group,
                 void* out, size_t row_bytes, int weighting, int fit, hipStream_t stream) {
   auto kern = k_quantize_rows<TYPE, BF16, VAR>;
   const int n_groups = n_per_row / QK;
-  int waves = (n_groups + WAVE - 1) / WAVE;
-  if (waves > MAX_ROW_WAVES) waves = MAX_ROW_WAVES;
+  const int waves = row_waves(n_per_row);
   const size_t lds = (size_t)n_groups * (BF16 ? LDS_BF16_STRIDE * 2 : LDS_F32_STRIDE * 4) + 8 * (size_t)waves;
   // Rows above 64 KB of LDS need the kernel's dynamic-LDS limit raised, once
   // per device. The attribute is set on the current device, so for a stream
@@ -1312,6 +1317,11 @@ int quantize_rows_common(int t, int src, const void* x, const float* imatrix, in
   const int64_t n_rows = n_groups * rows_per_group;
   if (n_rows == 0) return QR_OK;
   if (n_rows > (int64_t)UINT32_MAX) return qr_fail(QR_EOVERFLOW, "n_rows=%lld exceeds 2^32-1", (long long)n_rows);
+  // one workgroup per row: the launch's work items must stay below 2^32
+  const int64_t row_threads = (int64_t)WAVE * row_waves((int)n_per_row);
+  if (n_rows > (int64_t)UINT32_MAX / row_threads)
+    return qr_fail(QR_EINVAL_SHAPE, "n_rows=%lld rows of %d threads exceed one launch (at most %lld rows)",
+                   (long long)n_rows, (int)row_threads, (long long)((int64_t)UINT32_MAX / row_threads));
   const size_t rb = qr_row_bytes(t, n_per_row);
   if ((uint64_t)n_rows > SIZE_MAX / rb || (uint64_t)n_rows > SIZE_MAX / ((uint64_t)n_per_row * 4))
     return qr_fail(QR_EOVERFLOW, "buffer size overflows");

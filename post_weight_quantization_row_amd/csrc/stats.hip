@@ -343,6 +343,9 @@ __global__ __launch_bounds__(ST_THREADS) void k_stats_final(const uint8_t* __res
     out->max_abs_err = (float)red[4][0];
     out->p95_abs_err = __builtin_bit_cast(float, st->prefix);
     out->n = n;
+    out->rmse = sqrt(red[0][0] / (double)n);
+    out->rel_rmse = red[1][0] > 0.0 ? sqrt(red[0][0] / red[1][0]) : 0.0;
+    out->weighted_rel_rmse = red[3][0] > 0.0 ? sqrt(red[2][0] / red[3][0]) : 0.0;
   }
 }
 

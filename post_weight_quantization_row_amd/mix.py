@@ -193,7 +193,9 @@ def evaluate(plan: Plan, tensor_fn, on_tensor=None) -> dict:
 
 def summary(plan: Plan, tot: dict, tot_base: dict) -> dict:
     """Stack-wide relative errors of the plan and of the all-base stack,
-    from per-tensor sums of squared errors and squared values."""
+    from per-tensor sums of squared errors and squared values (report
+    arithmetic over the library's per-tensor sums; the per-tensor ratios
+    come from the library itself)."""
     def rel(d, e, x):
         return (d[e] / d[x]) ** 0.5 if d[x] > 0 else 0.0
     return {"stack": "total", "bytes": plan.bytes, "base_bytes": plan.base_bytes(),

@@ -127,6 +127,33 @@ def _dev2d(x: torch.Tensor, name: str):
         raise ValueError(f"{name} must be a contiguous 2-D tensor")
 
 
+def _cuda_device(t, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    return t.device
+
+
+def _on(t, name: str, device):
+    """Refuses anything but a tensor in the memory of `device`: the kernels
+    take raw device addresses, and a host address would reach a kernel as
+    one."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.device != torch.device(device):
+        raise TypeError(f"{name} is on {t.device}, not on {device}")
+    return t
+
+
+def _imatrix(imatrix, n: int, device):
+    """A per-column imatrix of n values (or None) on `device`, contiguous."""
+    if imatrix is None:
+        return None
+    _on(imatrix, "imatrix", device)
+    if imatrix.dtype != torch.float32 or imatrix.numel() != n:
+        raise ValueError("imatrix must be a CUDA float32 tensor of n_per_row values")
+    return imatrix.contiguous()
+
+
 def qr_last_error() -> str:
     return load_library().qr_last_error().decode()
 
@@ -149,6 +176,7 @@ def qr_solver_constants() -> dict:
 def _out(out, shape, dtype, device):
     if out is None:
         return torch.empty(shape, dtype=dtype, device=device)
+    _on(out, "out", device)
     if out.shape != torch.Size(shape) or out.dtype != dtype or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous {dtype} tensor of shape {shape}")
     return out
@@ -163,11 +191,7 @@ def qr_quantize_rows(t, x: torch.Tensor, imatrix=None, out=None, stream=None):
     n_rows, n = x.shape
     rb = qr_row_bytes(tid, n)
     out = _out(out, (n_rows, rb), torch.uint8, x.device)
-    q = None
-    if imatrix is not None:
-        if imatrix.dtype != torch.float32 or imatrix.numel() != n or not imatrix.is_cuda:
-            raise ValueError("imatrix must be a CUDA float32 tensor of n_per_row values")
-        q = imatrix.contiguous()
+    q = _imatrix(imatrix, n, x.device)
     _check(load_library().qr_quantize_rows(
         tid, _src_dtype(x), C.c_void_p(x.data_ptr()),
         None if q is None else C.c_void_p(q.data_ptr()), n_rows, n,
@@ -183,11 +207,7 @@ def qr_quantize_rows_weighted(t, x: torch.Tensor, imatrix, weighting, out=None, 
     wid = WEIGHTINGS[weighting] if isinstance(weighting, str) else int(weighting)
     n_rows, n = x.shape
     out = _out(out, (n_rows, qr_row_bytes(tid, n)), torch.uint8, x.device)
-    q = None
-    if imatrix is not None:
-        if imatrix.dtype != torch.float32 or imatrix.numel() != n or not imatrix.is_cuda:
-            raise ValueError("imatrix must be a CUDA float32 tensor of n_per_row values")
-        q = imatrix.contiguous()
+    q = _imatrix(imatrix, n, x.device)
     _check(load_library().qr_quantize_rows_weighted(
         tid, _src_dtype(x), C.c_void_p(x.data_ptr()),
         None if q is None else C.c_void_p(q.data_ptr()), n_rows, n, wid,
@@ -206,6 +226,7 @@ def qr_quantize_rows_grouped(t, x: torch.Tensor, imatrix, rows_per_group: int,
     n_groups = n_rows // rows_per_group
     q = None
     if imatrix is not None:
+        _on(imatrix, "imatrix", x.device)
         if imatrix.dtype != torch.float32 or tuple(imatrix.shape) != (n_groups, n):
             raise ValueError("imatrix must be float32 [n_groups, n_per_row]")
         q = imatrix.contiguous()
@@ -231,7 +252,8 @@ def qr_quantize_rows_ex(t, x: torch.Tensor, imatrix=None, rows_per_group=None, w
     q = None
     n_groups = 1
     if imatrix is not None:
-        if imatrix.dtype != torch.float32 or not imatrix.is_cuda or imatrix.numel() % n:
+        _on(imatrix, "imatrix", x.device)
+        if imatrix.dtype != torch.float32 or imatrix.numel() % n:
             raise ValueError("imatrix must be a CUDA float32 tensor of whole rows of n_per_row")
         q = imatrix.contiguous()
         n_groups = q.numel() // n
@@ -277,7 +299,8 @@ def qr_dequantize_rows(t, packed: torch.Tensor, n_rows: int, n_per_row: int,
                        out=None, stream=None):
     """packed: uint8 [n_rows, qr_row_bytes]; returns fp32 [n_rows, n_per_row]."""
     tid = _tid(t)
-    if not packed.is_cuda or packed.dtype != torch.uint8 or not packed.is_contiguous():
+    _on(packed, "packed", _cuda_device(packed, "packed"))
+    if packed.dtype != torch.uint8 or not packed.is_contiguous():
         raise ValueError("packed must be a contiguous CUDA uint8 tensor")
     if packed.numel() != n_rows * qr_row_bytes(tid, n_per_row):
         raise ValueError("packed has the wrong size")
@@ -307,7 +330,9 @@ def imatrix_state(n_experts: int, n_cols: int, device):
             torch.zeros(n_experts, dtype=torch.int64, device=device))
 
 
-def _check_state(sums, counts, n_experts=None, n_cols=None):
+def _check_state(sums, counts, n_experts=None, n_cols=None, device=None):
+    _on(sums, "sums", device if device is not None else _cuda_device(sums, "sums"))
+    _on(counts, "counts", sums.device)
     if (not isinstance(sums, torch.Tensor) or not sums.is_cuda or sums.dtype != torch.float64
             or sums.dim() != 2 or not sums.is_contiguous()):
         raise ValueError("sums must be a contiguous CUDA float64 [n_experts, n_cols] tensor")
@@ -338,17 +363,20 @@ def qr_imatrix_accumulate(act: torch.Tensor, sums: torch.Tensor, counts: torch.T
         n_tokens, n_slots, n_cols = act.shape
     else:
         raise ValueError("act must be [n_tokens, n_cols] or [n_tokens, n_slots, n_cols]")
-    _check_state(sums, counts, n_cols=n_cols)
+    _check_state(sums, counts, n_cols=n_cols, device=act.device)
     n_experts = sums.shape[0]
     top_k = 0
     if ids is not None:
-        if (not ids.is_cuda or ids.dtype != torch.int32 or ids.dim() != 2
+        _on(ids, "ids", act.device)
+        if (ids.dtype != torch.int32 or ids.dim() != 2
                 or ids.shape[0] != n_tokens or not ids.is_contiguous()):
             raise ValueError("ids must be a contiguous CUDA int32 [n_tokens, top_k] tensor")
         top_k = ids.shape[1]
     need = qr_imatrix_workspace_bytes(n_tokens, top_k, n_experts, n_cols)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=act.device)
+    if workspace is not None:
+        _on(workspace, "workspace", act.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().qr_imatrix_accumulate(
         _src_dtype(act), _ptr(act), n_tokens, n_slots, n_cols, _ptr(ids), top_k,
@@ -360,7 +388,7 @@ def qr_imatrix_accumulate(act: torch.Tensor, sums: torch.Tensor, counts: torch.T
 def qr_imatrix_merge(sums, counts, src_sums, src_counts, stream=None):
     """(sums, counts) += (src_sums, src_counts), in place."""
     _check_state(sums, counts)
-    _check_state(src_sums, src_counts, sums.shape[0], sums.shape[1])
+    _check_state(src_sums, src_counts, sums.shape[0], sums.shape[1], device=sums.device)
     _check(load_library().qr_imatrix_merge(
         _ptr(sums), _ptr(counts), _ptr(src_sums), _ptr(src_counts),
         sums.shape[0], sums.shape[1], _stream(sums, stream)))
@@ -387,8 +415,8 @@ def qr_matmul_q8k(t, act, w: torch.Tensor, x: torch.Tensor, n_in: int, out=None,
     Q8_K format act (uint8 [n_tok, qr_row_bytes(act, n_in)]), both on the GPU."""
     tid, aid = _tid(t), _tid(act)
     for name, a in (("w", w), ("x", x)):
-        if (not isinstance(a, torch.Tensor) or not a.is_cuda or a.dtype != torch.uint8
-                or a.dim() != 2 or not a.is_contiguous()):
+        _on(a, name, _cuda_device(w, "w"))
+        if a.dtype != torch.uint8 or a.dim() != 2 or not a.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 2-D CUDA uint8 tensor")
     if w.shape[1] != qr_row_bytes(tid, n_in) or x.shape[1] != qr_row_bytes(aid, n_in):
         raise ValueError("packed row lengths do not match n_in")
@@ -405,8 +433,8 @@ def qr_matmul_q8k128(t, w: torch.Tensor, x: torch.Tensor, n_in: int, out=None, s
     (uint8 [n_tok, qr_row_bytes("q8_k128", n_in)]), both on the GPU."""
     tid = _tid(t)
     for name, a in (("w", w), ("x", x)):
-        if (not isinstance(a, torch.Tensor) or not a.is_cuda or a.dtype != torch.uint8
-                or a.dim() != 2 or not a.is_contiguous()):
+        _on(a, name, _cuda_device(w, "w"))
+        if a.dtype != torch.uint8 or a.dim() != 2 or not a.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 2-D CUDA uint8 tensor")
     if w.shape[1] != qr_row_bytes(tid, n_in) or x.shape[1] != qr_row_bytes(QR_Q8_K128, n_in):
         raise ValueError("packed row lengths do not match n_in")
@@ -420,7 +448,7 @@ def qr_matmul_q8k128(t, w: torch.Tensor, x: torch.Tensor, n_in: int, out=None, s
 # --------------------------------------------------------------------------
 # error statistics (include/qrow_stats.h)
 
-QR_STATS_BYTES = 48   # sizeof(qr_stats)
+QR_STATS_BYTES = 72   # sizeof(qr_stats)
 
 
 def qr_stats_workspace_bytes(n_rows: int, n_per_row: int) -> int:
@@ -430,22 +458,20 @@ def qr_stats_workspace_bytes(n_rows: int, n_per_row: int) -> int:
 def qr_quantize_stats(t, x: torch.Tensor, packed: torch.Tensor, imatrix=None, workspace=None,
                       stream=None) -> dict:
     """Error statistics of packed rows against x (see qr_stats); returns the
-    struct's fields plus rmse, rel_rmse and weighted_rel_rmse (this copies
-    the 48-byte result to the host, which waits for the stream)."""
+    struct's fields as a dict (this copies the 72-byte result to the host,
+    which waits for the stream)."""
     import numpy as np
     _dev2d(x, "x")
     tid = _tid(t)
     n_rows, n = x.shape
-    if (not packed.is_cuda or packed.dtype != torch.uint8 or not packed.is_contiguous()
+    _on(packed, "packed", x.device)
+    if (packed.dtype != torch.uint8 or not packed.is_contiguous()
             or packed.numel() != n_rows * qr_row_bytes(tid, n)):
         raise ValueError("packed must be a contiguous CUDA uint8 tensor of the rows' packed bytes")
-    q = None
-    if imatrix is not None:
-        if imatrix.dtype != torch.float32 or imatrix.numel() != n or not imatrix.is_cuda:
-            raise ValueError("imatrix must be a CUDA float32 tensor of n_per_row values")
-        q = imatrix.contiguous()
+    q = _imatrix(imatrix, n, x.device)
     if workspace is None:
         workspace = torch.empty(qr_stats_workspace_bytes(n_rows, n), dtype=torch.uint8, device=x.device)
+    _on(workspace, "workspace", x.device)
     out = torch.zeros(QR_STATS_BYTES, dtype=torch.uint8, device=x.device)
     _check(load_library().qr_quantize_stats(
         tid, _src_dtype(x), _ptr(x), _ptr(packed), _ptr(q), n_rows, n, _ptr(out),
@@ -453,10 +479,8 @@ def qr_quantize_stats(t, x: torch.Tensor, packed: torch.Tensor, imatrix=None, wo
     raw = out.cpu().numpy()
     sums = raw[:32].view(np.float64)
     mx, p95 = raw[32:40].view(np.float32)
-    res = {"sum_err2": float(sums[0]), "sum_x2": float(sums[1]), "sum_werr2": float(sums[2]),
-           "sum_wx2": float(sums[3]), "max_abs_err": float(mx), "p95_abs_err": float(p95),
-           "n": int(raw[40:48].view(np.int64)[0])}
-    res["rmse"] = (res["sum_err2"] / res["n"]) ** 0.5 if res["n"] else 0.0
-    res["rel_rmse"] = (res["sum_err2"] / res["sum_x2"]) ** 0.5 if res["sum_x2"] > 0 else 0.0
-    res["weighted_rel_rmse"] = (res["sum_werr2"] / res["sum_wx2"]) ** 0.5 if res["sum_wx2"] > 0 else 0.0
-    return res
+    ratios = raw[48:72].view(np.float64)
+    return {"sum_err2": float(sums[0]), "sum_x2": float(sums[1]), "sum_werr2": float(sums[2]),
+            "sum_wx2": float(sums[3]), "max_abs_err": float(mx), "p95_abs_err": float(p95),
+            "n": int(raw[40:48].view(np.int64)[0]), "rmse": float(ratios[0]),
+            "rel_rmse": float(ratios[1]), "weighted_rel_rmse": float(ratios[2])}

@@ -89,12 +89,104 @@ def test_argument_validation_without_a_gpu(lib):
     assert lib.qr_quantize_rows_grouped(0, 0, fake, None, 2 ** 40, 2 ** 40, 256,
                                         fake, None) == -4
     assert lib.qr_quantize_rows(0, 0, fake, None, 2 ** 33, 256, fake, None) == -4
+    # one workgroup per row: more rows than one launch holds are refused
+    # up front (64 threads per 2048-value row, 512 from 16384 values on)
+    assert lib.qr_quantize_rows(0, 0, fake, None, (2 ** 32 - 1) // 64 + 1, 2048, fake, None) == -2
+    assert b"launch" in lib.qr_last_error()
+    assert lib.qr_quantize_rows(0, 0, fake, None, (2 ** 32 - 1) // 512 + 1, 16384, fake, None) == -2
+    assert lib.qr_quantize_rows_grouped(4, 1, fake, None, 2 ** 13, 2 ** 10, 16384, fake, None) == -2
+    assert lib.qr_quantize_rows(0, 0, None, None, (2 ** 32 - 1) // 512, 16384, fake, None) == -3
 
 
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         qrow.qr_quantize_rows("q4_0", torch.zeros(4, 256), None)
+
+
+class _DeviceStandIn:
+    """Builds CPU tensors that report themselves as living on cuda:0, so the
+    binding's checks of the OTHER arguments can be driven without a GPU."""
+
+    @staticmethod
+    def make(t):
+        import torch
+
+        class FakeCuda(torch.Tensor):
+            __torch_function__ = torch._C._disabled_torch_function_impl
+
+            @property
+            def is_cuda(self):
+                return True
+
+            @property
+            def device(self):
+                return torch.device("cuda", 0)
+
+        return torch.Tensor._make_subclass(FakeCuda, t)
+
+
+class _NoCompute:
+    """Stands in for the loaded library: size queries pass through, every
+    call that would launch work fails the test."""
+
+    def __init__(self, real):
+        self._real = real
+
+    def __getattr__(self, name):
+        if name in ("qr_row_bytes", "qr_block_elems", "qr_last_error", "qr_solver_constants",
+                    "qr_imatrix_workspace_bytes", "qr_stats_workspace_bytes"):
+            return getattr(self._real, name)
+        raise AssertionError(f"{name} was called with a host buffer among its arguments")
+
+
+def test_binding_refuses_host_buffers_beside_a_device_input(lib, monkeypatch):
+    """A host out, imatrix, workspace, ids or state is refused with a
+    TypeError that names it, before any library call: its address would
+    otherwise reach a kernel as a device address."""
+    import torch
+    monkeypatch.setattr(qrow, "_lib", _NoCompute(lib))
+    dev = _DeviceStandIn.make
+    x = dev(torch.zeros((4, 256)))
+    rb = qrow.qr_row_bytes("q4_k", 256)
+    out_d = dev(torch.zeros((4, rb), dtype=torch.uint8))
+    host_q = torch.ones(256)
+    cases = [
+        ("out", lambda: qrow.qr_quantize_rows("q4_k", x, None, out=torch.zeros((4, rb), dtype=torch.uint8))),
+        ("imatrix", lambda: qrow.qr_quantize_rows("q4_k", x, host_q, out=out_d)),
+        ("imatrix", lambda: qrow.qr_quantize_rows_weighted("q4_k", x, host_q, "x2", out=out_d)),
+        ("imatrix", lambda: qrow.qr_quantize_rows_grouped("q4_k", x, torch.ones((2, 256)), 2, out=out_d)),
+        ("imatrix", lambda: qrow.qr_quantize_rows_ex("q4_k", x, torch.ones((2, 256)), out=out_d)),
+        ("out", lambda: qrow.qr_quantize_activations_q8k128(
+            x, out=torch.zeros((4, qrow.qr_row_bytes("q8_k128", 256)), dtype=torch.uint8))),
+        ("out", lambda: qrow.qr_quantize_activations_q8k(
+            "q8_k16", x, out=torch.zeros((4, qrow.qr_row_bytes("q8_k16", 256)), dtype=torch.uint8))),
+        ("out", lambda: qrow.qr_dequantize_rows("q4_k", out_d, 4, 256, out=torch.zeros((4, 256)))),
+        ("packed", lambda: qrow.qr_dequantize_rows("q4_k", torch.zeros((4, rb), dtype=torch.uint8), 4, 256)),
+        ("packed", lambda: qrow.qr_quantize_stats("q4_k", x, torch.zeros((4, rb), dtype=torch.uint8))),
+        ("imatrix", lambda: qrow.qr_quantize_stats("q4_k", x, out_d, host_q)),
+        ("workspace", lambda: qrow.qr_quantize_stats(
+            "q4_k", x, out_d, None, workspace=torch.zeros(qrow.qr_stats_workspace_bytes(4, 256), dtype=torch.uint8))),
+    ]
+    sums = dev(torch.zeros((2, 256), dtype=torch.float64))
+    counts = dev(torch.zeros(2, dtype=torch.int64))
+    ids = dev(torch.zeros((4, 1), dtype=torch.int32))
+    cases += [
+        ("sums", lambda: qrow.qr_imatrix_accumulate(x, torch.zeros((2, 256), dtype=torch.float64), counts, ids)),
+        ("counts", lambda: qrow.qr_imatrix_accumulate(x, sums, torch.zeros(2, dtype=torch.int64), ids)),
+        ("ids", lambda: qrow.qr_imatrix_accumulate(x, sums, counts, torch.zeros((4, 1), dtype=torch.int32))),
+        ("workspace", lambda: qrow.qr_imatrix_accumulate(
+            x, sums, counts, ids, workspace=torch.zeros(1 << 16, dtype=torch.uint8))),
+        ("sums", lambda: qrow.qr_imatrix_merge(sums, counts, torch.zeros((2, 256), dtype=torch.float64), counts)),
+        ("out", lambda: qrow.qr_imatrix_finalize(sums, counts, out=torch.zeros((2, 256)))),
+        ("x", lambda: qrow.qr_matmul_q8k128("q4_k", out_d, torch.zeros(
+            (1, qrow.qr_row_bytes("q8_k128", 256)), dtype=torch.uint8), 256)),
+        ("x", lambda: qrow.qr_matmul_q8k("q4_k", "q8_k16", out_d, torch.zeros(
+            (1, qrow.qr_row_bytes("q8_k16", 256)), dtype=torch.uint8), 256)),
+    ]
+    for name, call in cases:
+        with pytest.raises(TypeError, match=name):
+            call()
 
 
 def test_imatrix_workspace_sizes():

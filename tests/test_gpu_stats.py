@@ -50,6 +50,10 @@ def check(qr, t, x, packed, q, bf16):
     tol = 2.0 * o["n"] * 2.0 ** -53
     for key in ("sum_err2", "sum_x2", "sum_werr2", "sum_wx2"):
         assert abs(g[key] - o[key]) <= tol * o[key], key
+    # square roots of ratios of those sums: half the sums' relative spread,
+    # plus the rounding of the division and the root
+    for key in ("rmse", "rel_rmse", "weighted_rel_rmse"):
+        assert abs(g[key] - o[key]) <= (tol + 4 * 2.0 ** -53) * o[key], key
     return g
 
 

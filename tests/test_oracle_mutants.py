@@ -42,6 +42,8 @@ MUTANTS = [
     ("asym: levels from x instead of x - lo", "xs[i] = x[i] - lo;", "xs[i] = x[i];"),
     ("asym: flips start from Slx + m*Sl", "float A = fmaf(-mf, bSl, bSlx), B = bSll;", "float A = fmaf(mf, bSl, bSlx), B = bSll;"),
     ("asym: Q4_K offset may be positive", "if (k4 && mm > 0.0) {", "if (0 && k4 && mm > 0.0) {"),
+    ("asym: constant-code guard at D > 0", "if (D > Sw * Sll * 0x1p-16) {", "if (D > 0.0) {"),
+    ("asym: constant-code guard at 2^-6", "if (D > Sw * Sll * 0x1p-16) {", "if (D > Sw * Sll * 0x1p-6) {"),
     # Q4_K super-block
     ("q4k: sub-scale multiplied by d16", "rintf(a[j] / dA0)", "rintf(a[j] * dA0)"),
     ("q4k: re-round with +dm sign flipped", "rintf((x[32 * j + i] + dm) * id)", "rintf((x[32 * j + i] - dm) * id)"),
@@ -124,6 +126,9 @@ MUTANTS = [
     ("stats: percentile rank rounded down", "const int64_t k = (95 * n + 99) / 100;",
      "const int64_t k = (95 * n) / 100;"),
     ("stats: weighted error without q", "qe2 += qi * (ed * ed);", "qe2 += ed * ed;"),
+    ("stats: RMSE over the signal", "sums[4] = sqrt(e2 / (double)n);", "sums[4] = sqrt(e2 / x2);"),
+    ("stats: weighted relative RMSE without q", "sums[6] = qx2 > 0.0 ? sqrt(qe2 / qx2) : 0.0;",
+     "sums[6] = x2 > 0.0 ? sqrt(e2 / x2) : 0.0;"),
     ("stats: maximum of the signed error", "mx = fmaxf(mx, ae[i]);", "mx = fmaxf(mx, e);"),
     ("stats: imatrix by row", "const double qi = q ? (double)q[i % n_per_row] : 1.0;",
      "const double qi = q ? (double)q[i / n_per_row] : 1.0;"),

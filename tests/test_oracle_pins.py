@@ -439,6 +439,68 @@ def test_asym_brute_force_tiny_blocks(n, nmax):
             assert eo <= err_asym(x, w, l0, d0, m0) + tol
 
 
+def _two_level_block(eps):
+    """Element 0 at 0.25 with importance eps, 31 elements at 1.0 with
+    importance 1: every trial gives element 0 level 0 and the rest level 15,
+    so the codes' weighted spread, (Sw*Sll - Sl^2)/(Sw*Sll), is eps/(31+eps)."""
+    x = np.full(32, 1.0, F32)
+    x[0] = F32(0.25)
+    w = np.ones(32, F32)
+    w[0] = F32(eps)
+    return x, w
+
+
+def _exact_spread(w, l):
+    W = [Fraction(float(v)) for v in w]
+    L = [Fraction(int(v)) for v in l]
+    Sw, Sl, Sll = sum(W), sum(a * b for a, b in zip(W, L)), sum(a * b * b for a, b in zip(W, L))
+    return (Sw * Sll - Sl * Sl) / (Sw * Sll)
+
+
+def _exact_ls(x, w, l):
+    """Exact two-parameter weighted least squares (d, m) for codes l."""
+    X = [Fraction(float(v)) for v in x]
+    W = [Fraction(float(v)) for v in w]
+    L = [Fraction(int(v)) for v in l]
+    Sw, Sx = sum(W), sum(a * b for a, b in zip(W, X))
+    Sl, Sll = sum(a * b for a, b in zip(W, L)), sum(a * b * b for a, b in zip(W, L))
+    Slx = sum(a * b * c for a, b, c in zip(W, L, X))
+    D = Sw * Sll - Sl * Sl
+    return (Sw * Slx - Sl * Sx) / D, (Sll * Sx - Sl * Slx) / D
+
+
+def test_asym_codes_with_spread_above_the_guard_get_the_exact_two_parameter_fit():
+    """[WT 一] weighted least squares, with the constant-code reading (codes
+    whose weighted spread is below 2^-16 of sum w l^2 count as constant):
+    at twice that spread the fit must be the exact two-parameter least
+    squares of the codes. Here that fit is exact (two values, two levels)."""
+    for eps in (31 * 2.0 ** -15, 31 * 2.0 ** -14, 31 * 2.0 ** -10):
+        x, w = _two_level_block(eps)
+        l, d, m, _ = oracle.solve_asym(x, w, 15, F=0)
+        assert list(l) == [0] + [15] * 31
+        assert _exact_spread(w, l) > Fraction(2) ** -16
+        d_ls, m_ls = _exact_ls(x, w, l)
+        assert (d_ls, m_ls) == (Fraction(1, 20), Fraction(1, 4))
+        assert d == rn_f32(d_ls) and m == rn_f32(m_ls)
+        sxx = float(np.sum(np.float64(w) * np.float64(x) ** 2))
+        assert err_asym(x, w, l, d, m) <= 1e-12 * sxx
+
+
+def test_asym_codes_with_spread_below_the_guard_are_fit_as_constant():
+    """Below the guard (half of 2^-16 and less) the codes count as constant:
+    d = 0 and m the importance-weighted mean of the block (the least-squares
+    offset with d fixed at 0), one rounding from its exact value."""
+    for eps in (31 * 2.0 ** -17, 31 * 2.0 ** -20, 31 * 2.0 ** -26):
+        x, w = _two_level_block(eps)
+        l, d, m, _ = oracle.solve_asym(x, w, 15, F=0)
+        assert list(l) == [0] + [15] * 31
+        assert _exact_spread(w, l) < Fraction(2) ** -16
+        W = [Fraction(float(v)) for v in w]
+        mean = sum(a * Fraction(float(b)) for a, b in zip(W, x)) / sum(W)
+        assert d == 0
+        assert abs(Fraction(float(m)) - mean) <= abs(mean) * Fraction(2) ** -23
+
+
 def test_asym_power_of_two_scaling():
     rng = np.random.default_rng(17)
     for _ in range(200):

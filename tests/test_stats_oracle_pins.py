@@ -34,6 +34,12 @@ def test_against_numpy_on_the_decoded_rows(t):
     assert np.isclose(st["sum_werr2"], np.sum(q64 * e64 * e64), rtol=1e-12, atol=0)
     assert np.isclose(st["sum_wx2"], np.sum(q64 * x64 * x64), rtol=1e-12, atol=0)
     assert st["n"] == x.size
+    # [LR 3.2]: RMSE = sqrt(total error / number of samples); the relative
+    # forms against the signal
+    assert np.isclose(st["rmse"], np.sqrt(np.mean(e64 * e64)), rtol=1e-12, atol=0)
+    assert np.isclose(st["rel_rmse"], np.linalg.norm(e64) / np.linalg.norm(x64), rtol=1e-12, atol=0)
+    assert np.isclose(st["weighted_rel_rmse"],
+                      np.sqrt(np.sum(q64 * e64 * e64) / np.sum(q64 * x64 * x64)), rtol=1e-12, atol=0)
 
 
 def test_hand_built_block_with_known_errors():
@@ -77,3 +83,4 @@ def test_exact_lattice_has_no_error():
     packed = oracle.quantize_rows("q4_0", x, None)
     st = oracle.quantize_stats("q4_0", x, packed, None)
     assert st["sum_err2"] == 0.0 and st["max_abs_err"] == 0.0 and st["p95_abs_err"] == 0.0
+    assert st["rmse"] == 0.0 and st["rel_rmse"] == 0.0 and st["weighted_rel_rmse"] == 0.0
