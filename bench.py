@@ -7,6 +7,13 @@ importance LogNormal(0, 1.5); synthetic, seeded). One step = one call of
 qr_quantize_rows over the whole matrix: load, row statistic, importances,
 trial scales, least squares, flips, super-block scales, packing.
 
+The same run times all five workloads the method is measured on
+("configs": Q4_0 2048x2048 fp32; the headline; the 32-layer 7B-shaped bf16
+stack of 224 matrices, Q4_0 attention and Q5_1 FFN, one launch per matrix;
+Q8_K_128 activations 8192x7168 fp32; the 256-expert bf16 MoE stack in one
+grouped launch), each against the HBM roofline, and times the CPU oracle on
+a bounded sample of each (cpu_baseline), checking the GPU bytes against it.
+
 Protocol: W untimed warm-up steps, then K timed steps. Before every step a
 1 GiB buffer is read (outside the timed interval) so that neither L2 nor the
 256 MB Infinity Cache holds the input. It is read rather than written so
@@ -28,19 +35,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: VALU lane-operations per second
-# (packed fp32 instructions are not used, so one instruction = one op/lane)
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Operations of the method per Q4_K weight (3 trial scales, 1 flip pass),
-# counted from the oracle's loops: row statistic 2, importance + zero test 4,
-# range 2, w*x etc. 4, trials 24, block solves 2.5, winner codes 4, flip
-# setup 2, flip pass 19, refit sums 2, Q4_K re-round and scales 5.5.
-ALG_OPS_PER_WEIGHT_Q4K = 71.0
 # MI355X dense int8 matrix-core peak (no sparsity), Tera-ops per second
 INT8_PEAK_TOPS = 5000.0
 METRIC = "Gweights/s quantized (Q4_0, Q4_K) + achieved HBM GB/s fraction"
 COUNTERS = os.path.join(ROOT, "profiles", "q4_k_11008x4096_counters.json")
+VALU_COUNTERS = os.path.join(ROOT, "profiles", "q4_k_11008x4096_valu_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "post_weight_quantization_row_amd", "csrc", "qrow.hip")
+# Host threads for the oracle: the host share of one GPU's job (the box runs
+# one GPU's work on 16 cores, whatever the machine's total).
+HOST_SHARE = 16
 
 
 def measured_traffic():
@@ -57,6 +60,52 @@ def measured_traffic():
     if c.get("kernel_source_sha256") != h:
         return None
     return int(c["hbm_bytes_per_launch"])
+
+
+def measured_valu():
+    """Per-weight VALU figures of the Q4_K kernel (instruction counts by
+    class, dual issue, issue cycles) from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    import hashlib
+    try:
+        with open(VALU_COUNTERS) as f:
+            c = json.load(f)
+        with open(KERNEL_SRC, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != h:
+        return None
+    return c.get("summary")
+
+
+VALU_CLASSES = ("fma_f32", "add_f32", "xor_b32", "rndne_f32", "med3_f32", "cmp_cndmask",
+                "fma_rndne_mix", "fma_f64", "sqrt_f32", "fma_f32_one_chain")
+
+
+def valu_rates(waves_per_simd=8):
+    """SIMD cycles per wave64 instruction (at 2.4 GHz) of the instruction
+    classes of the row kernels, measured now by libqrow_probe.so (register-
+    only kernels, eight independent chains per lane unless named)."""
+    import ctypes as C
+    import torch
+    path = os.path.join(ROOT, "post_weight_quantization_row_amd", "libqrow_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = C.CDLL(path)
+    L.qrp_valu_rates.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
+    L.qrp_valu_classes.restype = C.c_int
+    n = L.qrp_valu_classes()
+    if n != len(VALU_CLASSES):
+        return None
+    n_simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    inp = torch.tensor([1.0000001, 1e-7], dtype=torch.float32, device="cuda")
+    sink = torch.empty(n_simds * waves_per_simd // 4, dtype=torch.float32, device="cuda")
+    out = (C.c_float * n)()
+    torch.cuda.synchronize()
+    if L.qrp_valu_rates(C.c_void_p(inp.data_ptr()), C.c_void_p(sink.data_ptr()), waves_per_simd, n_simds, out) != 0:
+        return None
+    return {k: round(float(v), 2) for k, v in zip(VALU_CLASSES, out)}
 
 
 def log(*a):
@@ -326,6 +375,74 @@ def weighting_ablation(x, q, flush):
     return rows
 
 
+def host_threads() -> int:
+    """Threads for the oracle: the visible CPUs, within OMP_NUM_THREADS when
+    set and within the host share of one GPU's job."""
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, HOST_SHARE))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def hbm_frac(nbytes, ms):
+    return round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+
+def timed_oracle(fn, min_wall):
+    """Runs fn() until at least min_wall seconds have passed (at least
+    once); returns (last result, passes, seconds)."""
+    passes, dt, out = 0, 0.0, None
+    while passes == 0 or dt < min_wall:
+        t = time.perf_counter()
+        out = fn()
+        dt += time.perf_counter() - t
+        passes += 1
+    return out, passes, dt
+
+
+def rows_differing(a, b) -> int:
+    """Rows (of packed bytes) that differ between two lists of 2-D arrays."""
+    import numpy as np
+    return int(sum((np.asarray(x) != np.asarray(y)).any(axis=1).sum() for x, y in zip(a, b)))
+
+
+def stack_step_times(mats, outs, steps, warmup, flush):
+    """The 224-launch stack: (end-to-end ms per step, sum of the launches'
+    own times per step). Two passes: one with events only around the whole
+    stack, one with events around every launch."""
+    import torch
+    from post_weight_quantization_row_amd import qrow
+
+    def launch_all():
+        for (t, x, q), o in zip(mats, outs):
+            qrow.qr_quantize_rows(t, x, q, out=o)
+    e2e, _, _ = timed_steps(launch_all, steps, warmup, flush)
+    sums = []
+    for _ in range(steps):
+        evict(flush)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in mats]
+        for ((t, x, q), o), (a, b) in zip(zip(mats, outs), ev):
+            a.record()
+            qrow.qr_quantize_rows(t, x, q, out=o)
+            b.record()
+        torch.cuda.synchronize()
+        sums.append(sum(a.elapsed_time(b) for a, b in ev))
+    return e2e, sum(sums) / len(sums)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,8 +457,8 @@ def main():
                          "print its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
-              "is not supported (rows and experts are independent: several GPUs "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
+              "supported (rows and experts are independent: several GPUs "
               "would each quantize their own share with the same kernel)",
               file=sys.stderr)
         sys.exit(2)
@@ -360,6 +477,11 @@ def main():
     if args.only:
         run_only(args, dev, flush)
         return
+    cpu = not args.no_cpu_baseline
+    if cpu:
+        import oracle
+        threads = host_threads()
+    host = {}   # per workload: (oracle timing function, GPU bytes, sample) for the CPU leg
 
     # ---- headline: Q4_K, 11008 x 4096 fp32
     n_rows, n = 11008, 4096
@@ -373,7 +495,6 @@ def main():
     alg_bytes = weights * 4 + n * 4 + n_rows * rb
     gws = weights / (ms * 1e-3) / 1e9
     gbs = alg_bytes / (ms * 1e-3) / 1e9
-    tops = ALG_OPS_PER_WEIGHT_Q4K * weights / (ms * 1e-3) / 1e12
     torch.cuda.synchronize()
     # back-to-back (input may stay in the Infinity Cache), for context only
     t = time.perf_counter()
@@ -399,73 +520,158 @@ def main():
                    "n_rows": n_rows, "n_per_row": n, "src": "f32",
                    "imatrix": "LogNormal(0,1.5) per column",
                    "cache_flush_between_steps": "1 GiB read"},
-        "roofline": {"bound": "alu", "achieved": round(tops, 3),
-                     "peak": round(VALU_PEAK_TOPS, 2), "unit": "Tops/s",
-                     "frac": round(tops / VALU_PEAK_TOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
                      "kernel": "k_quantize_rows<Q4_K,f32>",
-                     "alg_ops_per_weight": ALG_OPS_PER_WEIGHT_Q4K,
                      "alg_bytes_per_launch": alg_bytes},
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "hbm_GB/s": round(gbs, 1),
         "ms_per_step_min": round(ms_min, 5),
         "ms_per_step_back_to_back": round(ms_b2b, 5),
         "wall_s_timed_loop": round(wall, 4),
     }
+    # VALU figures beside the HBM roofline (secondary): issue cycles of the
+    # instruction classes, measured in this run, and the kernel's own
+    # instruction counts from the committed counters (if taken on this source)
+    valu = {"issue_cycles_per_wave64_instr_at_2.4GHz": valu_rates()}
+    counted = measured_valu()
+    if counted is not None:
+        valu.update(counted)
+    result["valu"] = valu
+    configs = {"q4_k_11008x4096": {"ms": round(ms, 5), "Gweights/s": round(gws, 3),
+                                   "alg_bytes": alg_bytes, "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    if cpu:
+        xh, qh, gh = x.cpu().numpy(), q.cpu().numpy(), out.cpu().numpy()
+        host["q4_k_11008x4096"] = (lambda: [oracle.quantize_rows("q4_k", xh, qh, threads=threads)], [gh],
+                                   weights, "the full 11008x4096 matrix")
+    del x, out
 
-    # ---- CPU baseline: the oracle on the same matrix (it also checks parity)
-    if not args.no_cpu_baseline:
-        import oracle
-        xh = x.cpu().numpy()
-        qh = q.cpu().numpy()
-        threads = min(16, os.cpu_count() or 1)
-        # whole passes over the full matrix until about 10 s of CPU work
-        # (wall time x threads), at least one and at most 32
-        log(f"cpu baseline: oracle on the full matrix, {threads} threads")
-        passes, dt = 0, 0.0
-        while passes < 32 and (passes == 0 or dt * threads < 10.0):
-            t = time.perf_counter()
-            ref = oracle.quantize_rows("q4_k", xh, qh, threads=threads)
-            dt += time.perf_counter() - t
-            passes += 1
-        same = np.array_equal(ref, out.cpu().numpy())
+    # ---- Q4_0, 2048 x 2048 fp32
+    x0, q0 = synth.q4_0_matrix()
+    x0d, q0d = torch.from_numpy(x0).to(dev), torch.from_numpy(q0).to(dev)
+    o0 = torch.empty((2048, qrow.qr_row_bytes("q4_0", 2048)), dtype=torch.uint8, device=dev)
+    log("q4_0 2048x2048")
+    m0, _, _ = timed_steps(lambda: qrow.qr_quantize_rows("q4_0", x0d, q0d, out=o0), args.steps, args.warmup, flush)
+    b0 = x0.nbytes + q0.nbytes + o0.numel()
+    configs["q4_0_2048x2048"] = {"ms": round(m0, 5), "Gweights/s": round(x0.size / m0 / 1e6, 3),
+                                 "alg_bytes": b0, "hbm_frac": hbm_frac(b0, m0)}
+    if cpu:
+        g0 = o0.cpu().numpy()
+        host["q4_0_2048x2048"] = (lambda: [oracle.quantize_rows("q4_0", x0, q0, threads=threads)], [g0], x0.size,
+                                  "the full 2048x2048 matrix")
+
+    # ---- Q8_K_128 activations, 8192 x 7168 fp32
+    xa, _ = synth.q8_k128_activations()
+    xad = torch.from_numpy(xa).to(dev)
+    oa = torch.empty((8192, qrow.qr_row_bytes("q8_k128", 7168)), dtype=torch.uint8, device=dev)
+    log("q8_k128 8192x7168")
+    ma, _, _ = timed_steps(lambda: qrow.qr_quantize_activations_q8k128(xad, out=oa), args.steps, args.warmup, flush)
+    ba = xa.nbytes + oa.numel()
+    configs["q8_k128_8192x7168"] = {"ms": round(ma, 5), "Gvalues/s": round(xa.size / ma / 1e6, 3),
+                                    "alg_bytes": ba, "hbm_frac": hbm_frac(ba, ma)}
+    if cpu:
+        ga = oa.cpu().numpy()
+        host["q8_k128_8192x7168"] = (lambda: [oracle.quantize_q8k128(xa, threads=threads)], [ga], xa.size,
+                                     "the full 8192x7168 matrix")
+    del xad, oa
+
+    # ---- the 7B-shaped stack: 32 layers x 7 bf16 matrices, 224 launches
+    log("stack_7b_32x7: drawing 224 bf16 matrices")
+    mats = [synth.torch_stack_matrix(layer, w, dev) for layer in range(32) for w in range(7)]
+    outs = [torch.empty((x.shape[0], qrow.qr_row_bytes(t, x.shape[1])), dtype=torch.uint8, device=dev)
+            for t, x, _ in mats]
+    st_steps = max(1, min(args.steps, 5))
+    log(f"stack_7b_32x7: warmup 1, steps {st_steps}")
+    e2e, ksum = stack_step_times(mats, outs, st_steps, 1, flush)
+    w_att = sum(x.numel() for t, x, _ in mats if t == "q4_0")
+    w_ffn = sum(x.numel() for t, x, _ in mats if t == "q5_1")
+    b_st = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
+    configs["stack_7b_32x7"] = {
+        "launches": len(mats), "ms_end_to_end": round(e2e, 4), "ms_kernel_sum": round(ksum, 4),
+        "Gweights/s": round((w_att + w_ffn) / e2e / 1e6, 3), "alg_bytes": b_st,
+        "hbm_frac": hbm_frac(b_st, e2e), "hbm_frac_kernel_sum": hbm_frac(b_st, ksum)}
+    # the attention (Q4_0) part alone, from one layer's launches
+    att = [(m, o) for m, o in zip(mats[:7], outs[:7]) if m[0] == "q4_0"]
+    ma0, _, _ = timed_steps(lambda: [qrow.qr_quantize_rows(t, x, q, out=o) for (t, x, q), o in att], 10, 2, flush)
+    b_a0 = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in att)
+    configs["stack_7b_32x7"]["q4_0_attention_layer"] = {"ms": round(ma0, 4), "hbm_frac": hbm_frac(b_a0, ma0)}
+    if cpu:
+        smp = [(t, x.float().cpu().numpy(), q.cpu().numpy(), o.cpu().numpy()) for (t, x, q), o in
+               zip(mats[:7], outs[:7])]
+
+        def stack_oracle(smp=smp):
+            return [oracle.quantize_rows(t, xs, qs, threads=threads) for t, xs, qs, _ in smp]
+        host["stack_7b_32x7"] = (stack_oracle, [g for *_, g in smp], sum(v[1].size for v in smp),
+                                 "layer 0 of the stack: its 7 matrices, every row")
+    del mats, outs
+    torch.cuda.empty_cache()
+
+    # ---- the 256-expert MoE stack, bf16, one grouped launch
+    log("moe_256x2048x7168: drawing the stack")
+    xm, qm = synth.torch_moe_stack(dev)
+    om = torch.empty((xm.shape[0], qrow.qr_row_bytes("q4_k", 7168)), dtype=torch.uint8, device=dev)
+    mo_steps = max(1, min(args.steps, 5))
+    log(f"moe_256x2048x7168: warmup 1, steps {mo_steps}")
+    mm, _, _ = timed_steps(lambda: qrow.qr_quantize_rows_grouped("q4_k", xm, qm, 2048, out=om), mo_steps, 1, flush)
+    bm = xm.numel() * 2 + qm.numel() * 4 + om.numel()
+    configs["moe_256x2048x7168"] = {"ms": round(mm, 4), "Gweights/s": round(xm.numel() / mm / 1e6, 3),
+                                    "alg_bytes": bm, "hbm_frac": hbm_frac(bm, mm)}
+    if cpu:
+        experts = [0, 37, 74, 111, 148, 185, 222, 255]
+        zero = synth.moe_zero_experts()
+        experts[1] = int(zero[0])                      # one expert with importances 1e-6
+        qmh = qm.cpu().numpy()
+        smp = [(e, xm[2048 * e:2048 * (e + 1)].float().cpu().numpy(),
+                om[2048 * e:2048 * (e + 1)].cpu().numpy()) for e in experts]
+
+        def moe_oracle(smp=smp):
+            return [oracle.quantize_rows("q4_k", xs, qmh[e], threads=threads) for e, xs, _ in smp]
+        host["moe_256x2048x7168"] = (moe_oracle, [g for _, _, g in smp], sum(v[1].size for v in smp),
+                                     f"experts {experts}, every row")
+    del xm, om
+    torch.cuda.empty_cache()
+    result["configs"] = configs
+
+    # ---- CPU baseline: the oracle on bounded samples of every workload, on
+    # the host share of cores; each sample's bytes are compared with the GPU's
+    if cpu:
+        log(f"cpu baseline: oracle on {threads} threads")
+        per = {}
+        for name, (fn, gpu_bytes, n_el, what) in host.items():
+            ref, passes, dt = timed_oracle(fn, 1.0 if name == "q4_k_11008x4096" else 0.5)
+            per[name] = {"G_elements_per_s": round(passes * n_el / dt / 1e9, 5), "seconds": round(dt, 3),
+                         "passes": passes, "sample": what,
+                         "rows_differing_from_gpu": rows_differing(ref, gpu_bytes)}
+        # one thread on the Q4_0 matrix
+        x1, q1 = synth.q4_0_matrix()
+        _, p1, d1 = timed_oracle(lambda: oracle.quantize_rows("q4_0", x1, q1, threads=1), 1.0)
+        head = per["q4_k_11008x4096"]
         result["cpu_baseline"] = {
-            "value": round(passes * weights / dt / 1e9, 5), "unit": "Gweights/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"the full 11008x4096 matrix, {passes} passes (about 10 s of CPU time)",
-            "seconds": round(dt, 3)}
-        result["parity_vs_oracle"] = "bit-identical" if same else "DIFFERS"
+            "value": head["G_elements_per_s"], "unit": "Gweights/s", "cores": threads, "kind": "oracle",
+            "sample": f"{head['sample']}, {head['passes']} passes",
+            "seconds": head["seconds"], "cpu_model": cpu_model(), "host_cpus_visible": os.cpu_count(),
+            "q4_0_2048x2048_one_thread_Gweights/s": round(p1 * x1.size / d1 / 1e9, 5),
+            "per_workload": per}
+        result["parity_vs_oracle"] = ("bit-identical" if all(v["rows_differing_from_gpu"] == 0 for v in per.values())
+                                      else "rows differ: see cpu_baseline.per_workload")
 
     # ---- secondary workloads (one line of numbers each)
     if not args.no_extra:
         extra = {}
-        x0, q0 = synth.q4_0_matrix()
-        x0d, q0d = torch.from_numpy(x0).to(dev), torch.from_numpy(q0).to(dev)
-        o0 = torch.empty((2048, qrow.qr_row_bytes("q4_0", 2048)), dtype=torch.uint8, device=dev)
-        m0, _, _ = timed_steps(lambda: qrow.qr_quantize_rows("q4_0", x0d, q0d, out=o0), 10, 2, flush)
-        b0 = 2048 * 2048 * 4 + 2048 * 4 + o0.numel()
-        extra["q4_0_2048x2048"] = {"ms": round(m0, 5), "Gweights/s": round(2048 * 2048 / m0 / 1e6, 3),
-                                   "hbm_frac": round(b0 / (m0 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        xa, _ = synth.q8_k128_activations()
-        xad = torch.from_numpy(xa).to(dev)
-        oa = torch.empty((8192, qrow.qr_row_bytes("q8_k128", 7168)), dtype=torch.uint8, device=dev)
-        ma, _, _ = timed_steps(lambda: qrow.qr_quantize_activations_q8k128(xad, out=oa), 10, 2, flush)
-        ba = xa.nbytes + oa.numel()
-        extra["q8_k128_8192x7168"] = {"ms": round(ma, 5), "Gvalues/s": round(xa.size / ma / 1e6, 3),
-                                      "hbm_frac": round(ba / (ma * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        x, q = synth.torch_q4_k_matrix(dev, n_rows, n)
+        out = qrow.qr_quantize_rows("q4_k", x, q)
         y = torch.empty((n_rows, n), dtype=torch.float32, device=dev)
         md, _, _ = timed_steps(lambda: qrow.qr_dequantize_rows("q4_k", out, n_rows, n, out=y), 10, 2, flush)
         bd = out.numel() + y.numel() * 4
-        extra["dequantize_q4_k_11008x4096"] = {"ms": round(md, 5),
-                                               "hbm_frac": round(bd / (md * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        extra["dequantize_q4_k_11008x4096"] = {"ms": round(md, 5), "hbm_frac": hbm_frac(bd, md)}
+        del y
         # importance-matrix accumulation (the step that produces the imatrix)
         # and the product with Q8_K_128 activations (the step that consumes both)
         for name in ("q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS:
             fn, nb, n_el = _setup(name, dev)
             mi, _, _ = timed_steps(fn, 10, 2, flush)
             extra[name] = {"ms": round(mi, 5), "alg_bytes": nb, "G_elements_per_s": round(n_el / mi / 1e6, 3),
-                           "GB/s": round(nb / (mi * 1e-3) / 1e9, 1),
-                           "hbm_frac": round(nb / (mi * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                           "GB/s": round(nb / (mi * 1e-3) / 1e9, 1), "hbm_frac": hbm_frac(nb, mi)}
             if name.startswith("mmq_"):
                 # integer multiply-adds against the dense int8 matrix-core peak
                 base = name
@@ -478,6 +684,8 @@ def main():
                 extra[name]["int8_mfma_frac"] = round(tops / INT8_PEAK_TOPS, 4)
         extra["weighting_ablation_q4_k_11008x4096"] = weighting_ablation(x, q, flush)
         extra["subscale_fit_q4_k_11008x4096"] = subscale_fit_comparison(x, q, flush)
+        del x, q, out
+        torch.cuda.empty_cache()
         extra["mix_q4_k_m_stack_7b"] = mix_stack_entry(dev, flush)
         extra["activation_block_ablation_calib_8192x7168"] = activation_block_ablation(dev, flush)
         result["extra"] = extra

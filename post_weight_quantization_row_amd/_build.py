@@ -10,6 +10,10 @@ SOURCES = [os.path.join(HERE, "csrc", "qrow.hip"),
            os.path.join(HERE, "csrc", "stats.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqrow.so")
+# measurement only: VALU issue rates of the instruction classes the kernels
+# use (loaded by bench.py; not part of the quantization path or its C-ABI)
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "valu_rates.hip")]
+PROBE_LIB = os.path.join(HERE, "libqrow_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -22,10 +26,10 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(sources, lib, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *SOURCES]
+    tmp = lib + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *sources]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so
     noise = "is not a recognized feature for this target"
@@ -34,8 +38,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _hipcc(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -283,33 +283,50 @@ def test_full_q8_k128_8192x7168(qr):
     assert bool(torch.isfinite(y).all())          # no fp16-style overflow
 
 
-def test_stack_7b_sampled_rows(qr):
-    rng = np.random.default_rng(1003)
-    for layer in (0, 31):
+# Oracle threads: the host share of one GPU's job.
+ORACLE_THREADS = 16
+
+
+@pytest.mark.parametrize("layers", [range(l0, l0 + 4) for l0 in range(0, 32, 4)],
+                         ids=[f"layers{l0}-{l0 + 3}" for l0 in range(0, 32, 4)])
+def test_stack_7b_every_row(qr, layers):
+    """The 7B-shaped stack as the benchmark quantizes it (bf16, drawn on the
+    GPU, one launch per matrix): every row of every matrix against the
+    oracle, four layers per test (all 32 layers x 7 matrices over the
+    eight tests)."""
+    for layer in layers:
         for which in range(7):
             typ, x, q = synth.torch_stack_matrix(layer, which, "cuda")
             say(f"case stack layer={layer} matrix={synth.STACK_LAYER[which][0]} {typ} {tuple(x.shape)}")
-            got = qr.qr_quantize_rows(typ, x, q)
-            rows = np.sort(rng.choice(x.shape[0], 24, replace=False))
-            xs = x[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+            got = qr.qr_quantize_rows(typ, x, q).cpu().numpy()
+            xh = x.float().cpu().numpy()
             qh = q.cpu().numpy()
-            ref = oracle.quantize_rows(typ, xs, qh, threads=8)
-            assert_rows_equal(typ, got[torch.from_numpy(rows).cuda()].cpu().numpy(), ref, xs, lambda r: qh)
-            del x, got
+            del x
+            ref = oracle.quantize_rows(typ, xh, qh, threads=ORACLE_THREADS)
+            assert_rows_equal(typ, got, ref, xh, lambda r: qh)
 
 
-def test_moe_256x2048x7168_grouped_sampled_rows(qr):
-    say("case moe_256x2048x7168 grouped")
+@pytest.fixture(scope="module")
+def moe_stack(qr):
+    """The 256-expert stack drawn on the GPU and quantized in one grouped
+    launch, as the benchmark does; shared by the tests below."""
+    say("case moe_256x2048x7168 grouped: draw and quantize")
     x, q = synth.torch_moe_stack("cuda")
     got = qr.qr_quantize_rows_grouped("q4_k", x, q, 2048)
-    zero = synth.moe_zero_experts()
-    rng = np.random.default_rng(1005)
-    experts = np.unique(np.concatenate([zero[:4], rng.choice(256, 12, replace=False), [255]]))
-    qh = q.cpu().numpy()
-    for e in experts:
-        rows = 2048 * e + np.sort(rng.choice(2048, 8, replace=False))
-        idx = torch.from_numpy(rows).cuda()
-        xs = x[idx].float().cpu().numpy()
-        ref = oracle.quantize_rows("q4_k", xs, qh[e])
-        assert_rows_equal("q4_k", got[idx].cpu().numpy(), ref, xs, lambda r: qh[e])
+    torch.cuda.synchronize()
+    yield x, q.cpu().numpy(), got
     del x, got
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("e0", range(0, 256, 32), ids=[f"experts{e}-{e + 31}" for e in range(0, 256, 32)])
+def test_moe_256x2048x7168_grouped_every_row(qr, moe_stack, e0):
+    """Every row of every expert (32 experts per test), including the 26
+    experts whose importances are all 1e-6."""
+    x, qh, got = moe_stack
+    for e in range(e0, e0 + 32):
+        say(f"case moe expert {e}")
+        xh = x[2048 * e:2048 * (e + 1)].float().cpu().numpy()
+        gh = got[2048 * e:2048 * (e + 1)].cpu().numpy()
+        ref = oracle.quantize_rows("q4_k", xh, qh[e], threads=ORACLE_THREADS)
+        assert_rows_equal("q4_k", gh, ref, xh, lambda r: qh[e])
