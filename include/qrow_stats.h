@@ -64,6 +64,29 @@ int qr_quantize_stats(int t, int src, const void *x, const void *packed,
                       qr_stats *out, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* Size of the device workspace that qr_quantize_stats_noalloc keeps in a
+ * static array, one per GPU (the same as qr_stats_workspace_bytes). */
+#define QR_STATS_STATIC_SCRATCH_BYTES 377088
+
+/*
+ * qr_quantize_stats_noalloc -- qr_quantize_stats for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments and results (bit for bit)
+ * as qr_quantize_stats, without the workspace: the library keeps it in a
+ * static device array of QR_STATS_STATIC_SCRATCH_BYTES per GPU, which
+ * covers every call that qr_quantize_stats accepts (n_rows * n_per_row
+ * below 2^32; larger calls return QR_EOVERFLOW before any launch). The
+ * array's device address is looked up once per device, on the first call
+ * whose stream belongs to it; nothing is allocated, then or later. Every
+ * call clears what must start at zero with a kernel (no memset). All calls
+ * on one GPU share that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from several host threads without ordering) race
+ * and give undefined results; order them on one stream.
+ */
+int qr_quantize_stats_noalloc(int t, int src, const void *x, const void *packed,
+                              const float *imatrix, int64_t n_rows,
+                              int64_t n_per_row, qr_stats *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

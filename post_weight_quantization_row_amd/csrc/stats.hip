@@ -25,6 +25,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qr_internal.h"
 #include "qrow.h"
 #include "qrow_stats.h"
@@ -392,6 +394,68 @@ int dispatch_stats(int t, const void* x, const uint8_t* packed, const float* q, 
 
 }  // namespace
 
+// The allocation-free entry point's workspace: one copy per GPU (each device
+// that loads the library holds it until the process ends). Host code never
+// uses this name as an address: it takes each device's address of the array
+// from hipGetSymbolAddress, with that device current, once per device.
+static_assert(WS_BYTES == QR_STATS_STATIC_SCRATCH_BYTES, "the header states the static workspace's size");
+static __device__ __align__(256) uint8_t scratch[WS_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[SCRATCH_MAX_DEVICES];   // device address of `scratch` on each device, once resolved
+
+// The device address of `scratch` on the device of `stream` (the current
+// device for the null stream), resolved on the first call for that device.
+int scratch_for(hipStream_t stream, uint8_t** ws) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return qr_fail(QR_EDEVICE, "hipGetDevice failed");
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipStreamGetDevice failed");
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return qr_fail(QR_EDEVICE, "device %d beyond the library's table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipSetDevice(%d) failed", dev);
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return qr_fail(QR_EDEVICE, "hipSetDevice(%d) failed", cur);
+    if (e != hipSuccess || !p) return qr_fail(QR_EDEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *ws = reinterpret_cast<uint8_t*>(g_scratch[dev]);
+  return QR_OK;
+}
+
+// Argument checks shared by both entry points; 1 means "nothing to do".
+int stats_check(int t, int src, const void* x, const void* packed, const float* imatrix, int64_t n_rows,
+                int64_t n_per_row, const qr_stats* out) {
+  if (t < QR_Q4_0 || t > QR_Q5_K) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
+  if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
+  const size_t rb = qr_row_bytes(t, n_per_row);
+  if (n_rows < 0 || n_per_row <= 0 || rb == 0 || n_per_row % 32 != 0)
+    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld is not a positive multiple of the block length and of 32",
+                   (long long)n_per_row);
+  if (n_rows == 0) return 1;
+  if (n_per_row > INT32_MAX || n_rows > (int64_t)UINT32_MAX / n_per_row)
+    return qr_fail(QR_EOVERFLOW, "n_rows * n_per_row must be below 2^32");
+  if (!x || !packed || !out) return qr_fail(QR_EINVAL_PTR, "x, packed and out must be non-NULL");
+  if (!qr_aligned(x, 16) || !qr_aligned(packed, 16) || (imatrix && !qr_aligned(imatrix, 16)) || !qr_aligned(out, 8))
+    return qr_fail(QR_EINVAL_PTR, "misaligned pointer (x, packed, imatrix: 16; out: 8)");
+  return QR_OK;
+}
+
+int stats_launch(int t, int src, const void* x, const void* packed, const float* imatrix, int64_t n_rows,
+                 int64_t n_per_row, qr_stats* out, uint8_t* ws, hipStream_t s) {
+  const int64_t rb = (int64_t)qr_row_bytes(t, n_per_row);
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(packed);
+  return src == QR_F32 ? dispatch_stats<false>(t, x, p, imatrix, n_rows, (int)n_per_row, rb, out, ws, s)
+                       : dispatch_stats<true>(t, x, p, imatrix, n_rows, (int)n_per_row, rb, out, ws, s);
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t qr_stats_workspace_bytes(int64_t n_rows, int64_t n_per_row) {
@@ -399,28 +463,28 @@ size_t qr_stats_workspace_bytes(int64_t n_rows, int64_t n_per_row) {
   return WS_BYTES;
 }
 
+int qr_quantize_stats_noalloc(int t, int src, const void* x, const void* packed, const float* imatrix,
+                              int64_t n_rows, int64_t n_per_row, qr_stats* out, void* stream) {
+  qr_clear_error();
+  const int rc = stats_check(t, src, x, packed, imatrix, n_rows, n_per_row, out);
+  if (rc != QR_OK) return rc < 0 ? rc : QR_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = nullptr;
+  const int rs = scratch_for(s, &ws);
+  if (rs != QR_OK) return rs;
+  return stats_launch(t, src, x, packed, imatrix, n_rows, n_per_row, out, ws, s);
+}
+
 int qr_quantize_stats(int t, int src, const void* x, const void* packed, const float* imatrix, int64_t n_rows,
                       int64_t n_per_row, qr_stats* out, void* workspace, size_t workspace_bytes, void* stream) {
   qr_clear_error();
-  if (t < QR_Q4_0 || t > QR_Q5_K) return qr_fail(QR_EINVAL_TYPE, "unknown type %d", t);
-  if (src != QR_F32 && src != QR_BF16) return qr_fail(QR_EINVAL_TYPE, "source dtype %d is not f32/bf16", src);
-  const size_t rb = qr_row_bytes(t, n_per_row);
-  if (n_rows < 0 || n_per_row <= 0 || rb == 0 || n_per_row % 32 != 0)
-    return qr_fail(QR_EINVAL_SHAPE, "n_per_row=%lld is not a positive multiple of the block length and of 32",
-                   (long long)n_per_row);
-  if (n_rows == 0) return QR_OK;
-  if (n_per_row > INT32_MAX || n_rows > (int64_t)UINT32_MAX / n_per_row)
-    return qr_fail(QR_EOVERFLOW, "n_rows * n_per_row must be below 2^32");
-  if (!x || !packed || !out || !workspace) return qr_fail(QR_EINVAL_PTR, "x, packed, out and workspace must be non-NULL");
-  if (!qr_aligned(x, 16) || !qr_aligned(packed, 16) || (imatrix && !qr_aligned(imatrix, 16)) ||
-      !qr_aligned(out, 8) || !qr_aligned(workspace, 256))
-    return qr_fail(QR_EINVAL_PTR, "misaligned pointer (x, packed, imatrix: 16; out: 8; workspace: 256)");
+  const int rc = stats_check(t, src, x, packed, imatrix, n_rows, n_per_row, out);
+  if (rc != QR_OK) return rc < 0 ? rc : QR_OK;
+  if (!workspace) return qr_fail(QR_EINVAL_PTR, "workspace must be non-NULL");
+  if (!qr_aligned(workspace, 256)) return qr_fail(QR_EINVAL_PTR, "misaligned workspace (256 bytes)");
   if (workspace_bytes < WS_BYTES) return qr_fail(QR_EINVAL_SHAPE, "workspace_bytes=%zu < %zu", workspace_bytes, WS_BYTES);
-  const uint8_t* p = reinterpret_cast<const uint8_t*>(packed);
-  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return src == QR_F32 ? dispatch_stats<false>(t, x, p, imatrix, n_rows, (int)n_per_row, (int64_t)rb, out, ws, s)
-                       : dispatch_stats<true>(t, x, p, imatrix, n_rows, (int)n_per_row, (int64_t)rb, out, ws, s);
+  return stats_launch(t, src, x, packed, imatrix, n_rows, n_per_row, out, reinterpret_cast<uint8_t*>(workspace),
+                      reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

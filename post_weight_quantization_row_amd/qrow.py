@@ -40,7 +40,7 @@ EXPORTS = ("qr_quantize_rows", "qr_quantize_rows_grouped",
            "qr_imatrix_finalize", "qr_matmul_q8k128",
            "qr_quantize_rows_weighted", "qr_stats_workspace_bytes",
            "qr_quantize_stats", "qr_quantize_activations_q8k", "qr_matmul_q8k",
-           "qr_quantize_rows_ex")
+           "qr_quantize_rows_ex", "qr_quantize_stats_noalloc")
 IMX_MAX_EXPERTS, IMX_MAX_TOP_K = 1024, 64
 
 
@@ -87,6 +87,7 @@ def load_library(path: str = LIB_PATH):
         L.qr_stats_workspace_bytes.argtypes = [i64, i64]
         L.qr_stats_workspace_bytes.restype = C.c_size_t
         L.qr_quantize_stats.argtypes = [i32, i32, vp, vp, vp, i64, i64, vp, vp, C.c_size_t, vp]
+        L.qr_quantize_stats_noalloc.argtypes = [i32, i32, vp, vp, vp, i64, i64, vp, vp]
         for name in (n for n in EXPORTS if n not in
                      ("qr_row_bytes", "qr_block_elems", "qr_last_error",
                       "qr_solver_constants", "qr_imatrix_workspace_bytes",
@@ -460,7 +461,6 @@ def qr_quantize_stats(t, x: torch.Tensor, packed: torch.Tensor, imatrix=None, wo
     """Error statistics of packed rows against x (see qr_stats); returns the
     struct's fields as a dict (this copies the 72-byte result to the host,
     which waits for the stream)."""
-    import numpy as np
     _dev2d(x, "x")
     tid = _tid(t)
     n_rows, n = x.shape
@@ -476,6 +476,13 @@ def qr_quantize_stats(t, x: torch.Tensor, packed: torch.Tensor, imatrix=None, wo
     _check(load_library().qr_quantize_stats(
         tid, _src_dtype(x), _ptr(x), _ptr(packed), _ptr(q), n_rows, n, _ptr(out),
         _ptr(workspace), workspace.numel(), _stream(x, stream)))
+    return stats_dict(out)
+
+
+def stats_dict(out: torch.Tensor) -> dict:
+    """The fields of a qr_stats struct held in a 72-byte device buffer (this
+    copies it to the host, which waits for its stream)."""
+    import numpy as np
     raw = out.cpu().numpy()
     sums = raw[:32].view(np.float64)
     mx, p95 = raw[32:40].view(np.float32)
@@ -484,3 +491,26 @@ def qr_quantize_stats(t, x: torch.Tensor, packed: torch.Tensor, imatrix=None, wo
             "sum_wx2": float(sums[3]), "max_abs_err": float(mx), "p95_abs_err": float(p95),
             "n": int(raw[40:48].view(np.int64)[0]), "rmse": float(ratios[0]),
             "rel_rmse": float(ratios[1]), "weighted_rel_rmse": float(ratios[2])}
+
+
+def qr_quantize_stats_noalloc(t, x: torch.Tensor, packed: torch.Tensor, out: torch.Tensor, imatrix=None,
+                              stream=None) -> torch.Tensor:
+    """qr_quantize_stats without a workspace and without allocating: the
+    caller passes `out`, a 72-byte uint8 CUDA buffer that receives the
+    qr_stats struct (read it with stats_dict). Returns out."""
+    _dev2d(x, "x")
+    tid = _tid(t)
+    n_rows, n = x.shape
+    _on(packed, "packed", x.device)
+    if (packed.dtype != torch.uint8 or not packed.is_contiguous()
+            or packed.numel() != n_rows * qr_row_bytes(tid, n)):
+        raise ValueError("packed must be a contiguous CUDA uint8 tensor of the rows' packed bytes")
+    if imatrix is not None and not imatrix.is_contiguous():
+        raise ValueError("imatrix must be contiguous (no copy is made here)")
+    q = _imatrix(imatrix, n, x.device)
+    _on(out, "out", x.device)
+    if out.dtype != torch.uint8 or out.numel() != QR_STATS_BYTES or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous uint8 tensor of {QR_STATS_BYTES} bytes")
+    _check(load_library().qr_quantize_stats_noalloc(
+        tid, _src_dtype(x), _ptr(x), _ptr(packed), _ptr(q), n_rows, n, _ptr(out), _stream(x, stream)))
+    return out

@@ -34,7 +34,7 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(HEADERS) == 4 and len(names) == 19
+    assert len(HEADERS) == 4 and len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(qrow.EXPORTS) == names
@@ -316,6 +316,18 @@ def test_stats_argument_validation_without_a_gpu(lib):
     assert st(0, 0, fake, fake, None, 4, 256, None, fake, ws, None) == -3
     assert st(0, 0, fake, fake, None, 4, 256, fake, C.c_void_p(0x10010), ws, None) == -3
     assert st(0, 0, fake, fake, None, 4, 256, fake, fake, ws - 1, None) == -2
+    # the allocation-free form: same checks, no workspace argument; its static
+    # workspace has the stated size
+    assert ws == 377088
+    na = lib.qr_quantize_stats_noalloc
+    assert na(11, 0, fake, fake, None, 4, 256, fake, None) == -1
+    assert na(8, 0, fake, fake, None, 4, 48, fake, None) == -2
+    assert na(0, 2, fake, fake, None, 4, 256, fake, None) == -1
+    assert na(0, 0, None, None, None, 0, 256, None, None) == 0             # no rows
+    assert na(0, 0, fake, fake, None, 2 ** 31, 4096, fake, None) == -4     # beyond 2^32 elements
+    assert "2^32" in qrow.qr_last_error()
+    assert na(0, 0, fake, fake, None, 4, 256, None, None) == -3
+    assert na(0, 0, fake, C.c_void_p(0x10008), None, 4, 256, fake, None) == -3
 
 
 def test_no_fallback_without_the_library_or_a_gpu():
