@@ -196,6 +196,17 @@ def _setup(name, dev):
                 qrow.qr_quantize_rows(t, x, q, out=o)
         nb = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
         return step, nb, sum(x.numel() for _, x, _ in mats)
+    if name == "stack_7b_32x7":
+        # the whole 32-layer stack: 224 launches per step
+        mats = [synth.torch_stack_matrix(layer, w, dev) for layer in range(32) for w in range(7)]
+        outs = [torch.empty((x.shape[0], qrow.qr_row_bytes(t, x.shape[1])), dtype=torch.uint8, device=dev)
+                for t, x, q in mats]
+
+        def step():
+            for (t, x, q), o in zip(mats, outs):
+                qrow.qr_quantize_rows(t, x, q, out=o)
+        nb = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
+        return step, nb, sum(x.numel() for _, x, _ in mats)
     if name == "moe_256x2048x7168":
         x, q = synth.torch_moe_stack(dev)
         out = torch.empty((x.shape[0], qrow.qr_row_bytes("q4_k", 7168)), dtype=torch.uint8, device=dev)
@@ -299,10 +310,16 @@ ACT_WORKLOADS = ("q8_k64_8192x7168", "q8_k16_8192x7168")
 STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "copy_1gib", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096", "q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
+                  "moe_256x2048x7168", "stack_7b_32x7", "copy_1gib", "valu_rates", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096", "q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
 
 
 def run_only(args, dev, flush):
+    if args.only == "valu_rates":
+        # issue cycles per wave64 instruction of each class at 1, 2, 4, 8
+        # waves per SIMD (the calibration of the VALU figures)
+        print(json.dumps({"workload": "valu_rates", "unit": "SIMD cycles per wave64 instruction at 2.4 GHz",
+                          "by_waves_per_simd": {w: valu_rates(w) for w in (1, 2, 4, 8)}}), flush=True)
+        return
     step, nbytes, n_el = _setup(args.only, dev)
     log(f"{args.only}: warmup {args.warmup}, steps {args.steps}")
     ms, ms_min, wall = timed_steps(step, args.steps, args.warmup, flush)

@@ -348,7 +348,7 @@ __device__ __forceinline__ void flip_passes(YW yw, const float (&w)[QK], float l
       const float e = fma_(y, B, -t);
       const float sg = __builtin_bit_cast(float, fbits(A) ^ fbits(e));   // sign: sign(A) * sign(e)
       const float s = __builtin_copysignf(1.0f, sg);    // +-1
-      const float s2 = __builtin_copysignf(2.0f, sg);   // +-2
+      const float s2 = s + s;                           // +-2, exactly
       const float lp = L[j] + s;
       const float A1 = fma_(s, wy, A);
       const float B1 = fma_(w[j], fma_(s2, L[j], 1.0f), B);
