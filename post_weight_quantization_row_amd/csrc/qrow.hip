@@ -1236,19 +1236,51 @@ size_t block_bytes(int t) {
 bool aligned16(const void* p) { return qr_aligned(p, 16); }
 
 
-// Waves of the workgroup that quantizes one row of n_per_row values.
-int row_waves(int n_per_row) {
-  const int waves = (n_per_row / QK + WAVE - 1) / WAVE;
-  return waves > MAX_ROW_WAVES ? MAX_ROW_WAVES : waves;
+// Bytes of LDS of the workgroup that quantizes one row: the staged row and
+// the cross-wave partial sums.
+size_t row_lds_bytes(int n_per_row, bool bf16, int waves) {
+  return (size_t)(n_per_row / QK) * (bf16 ? LDS_BF16_STRIDE * 2 : LDS_F32_STRIDE * 4) + 8 * (size_t)waves;
+}
+
+// Waves of the workgroup that quantizes one row of n_per_row values. Each
+// lane solves groups tid, tid + 64W, ..., so any W works; W is chosen for
+// the lanes kept busy and the waves a compute unit holds: at most 16 (four
+// per SIMD, the register budget of the row kernels) and as many workgroups
+// as its 160 KiB of LDS take. One wave per 64 groups, the plain choice,
+// wins ties; another W must do better by more than a tenth. (Rows of 11008
+// bf16 values, 344 groups: six waves give two workgroups, 12 waves, per CU;
+// three waves over two passes give five, 15 waves.)
+int row_waves(int n_per_row, bool bf16) {
+  const int groups = n_per_row / QK;
+  auto score = [&](int w) {
+    const int lanes = WAVE * w;
+    const int passes = (groups + lanes - 1) / lanes;
+    const double busy = (double)groups / ((double)passes * lanes);
+    int wgs = (int)(LDS_PER_WORKGROUP / row_lds_bytes(n_per_row, bf16, w));
+    if (wgs > 16 / w) wgs = 16 / w;
+    const int waves = wgs * w;
+    return busy * (waves < 16 ? waves : 16);
+  };
+  int plain = (groups + WAVE - 1) / WAVE;
+  if (plain > MAX_ROW_WAVES) plain = MAX_ROW_WAVES;
+  int best = plain;
+  double best_score = score(plain);
+  for (int w = 1; w <= MAX_ROW_WAVES; ++w) {
+    const double sc = score(w);
+    if (sc > 1.1 * best_score) {
+      best = w;
+      best_score = sc;
+    }
+  }
+  return best;
 }
 
 template <int TYPE, bool BF16, bool VAR>
 int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_row, int64_t rows_per_group,
                 void* out, size_t row_bytes, int weighting, int fit, hipStream_t stream) {
   auto kern = k_quantize_rows<TYPE, BF16, VAR>;
-  const int n_groups = n_per_row / QK;
-  const int waves = row_waves(n_per_row);
-  const size_t lds = (size_t)n_groups * (BF16 ? LDS_BF16_STRIDE * 2 : LDS_F32_STRIDE * 4) + 8 * (size_t)waves;
+  const int waves = row_waves(n_per_row, BF16);
+  const size_t lds = row_lds_bytes(n_per_row, BF16, waves);
   // Rows above 64 KB of LDS need the kernel's dynamic-LDS limit raised, once
   // per device. The attribute is set on the current device, so for a stream
   // of another device that device is made current for the call. The flags
@@ -1318,7 +1350,7 @@ int quantize_rows_common(int t, int src, const void* x, const float* imatrix, in
   if (n_rows == 0) return QR_OK;
   if (n_rows > (int64_t)UINT32_MAX) return qr_fail(QR_EOVERFLOW, "n_rows=%lld exceeds 2^32-1", (long long)n_rows);
   // one workgroup per row: the launch's work items must stay below 2^32
-  const int64_t row_threads = (int64_t)WAVE * row_waves((int)n_per_row);
+  const int64_t row_threads = (int64_t)WAVE * row_waves((int)n_per_row, src == QR_BF16);
   if (n_rows > (int64_t)UINT32_MAX / row_threads)
     return qr_fail(QR_EINVAL_SHAPE, "n_rows=%lld rows of %d threads exceed one launch (at most %lld rows)",
                    (long long)n_rows, (int)row_threads, (long long)((int64_t)UINT32_MAX / row_threads));
