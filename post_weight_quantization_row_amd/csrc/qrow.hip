@@ -189,6 +189,68 @@ __device__ __forceinline__ double stage_row(const void* __restrict__ xrow, int n
   return acc;
 }
 
+// The same staging in two steps, for the streaming kernel: stage_row_load
+// fetches this thread's vectors of the row into registers, and
+// stage_row_store writes them to LDS and returns the wave's sum of x^2, in the
+// order stage_row takes it. A row of at most 64 W groups gives each of the
+// 64 W threads at most 4 vectors (bf16) or 8 (fp32).
+template <bool BF16>
+struct RowRegs {
+  static constexpr int N = BF16 ? 4 : 8;
+  u32x4 v[N];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void stage_row_load(const void* __restrict__ xrow, int n, int tid, int nthreads,
+                                               RowRegs<BF16>& rr) {
+  const int nv = BF16 ? n >> 3 : n >> 2;
+  const u32x4* src = reinterpret_cast<const u32x4*>(xrow);
+#pragma unroll
+  for (int k = 0; k < RowRegs<BF16>::N; ++k) {
+    const int i = tid + k * nthreads;
+    rr.v[k] = u32x4{0u, 0u, 0u, 0u};
+    if (i < nv) rr.v[k] = __builtin_nontemporal_load(src + i);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ double stage_row_store(int n, void* lds, int tid, int nthreads, const RowRegs<BF16>& rr) {
+  double acc = 0.0;
+  const int nv = BF16 ? n >> 3 : n >> 2;
+#pragma unroll
+  for (int k = 0; k < RowRegs<BF16>::N; ++k) {
+    const int i = tid + k * nthreads;
+    if (i >= nv) continue;
+    const u32x4 v = rr.v[k];
+    if (!BF16) {
+      float* dst = reinterpret_cast<float*>(lds) + (i >> 3) * LDS_F32_STRIDE + (i & 7) * 4;
+      *reinterpret_cast<u32x4*>(dst) = v;
+      // the elements are copied out before the bit cast: this compiler's
+      // __builtin_bit_cast of a vector element (v.y) reads element 0
+      const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double a = (double)__builtin_bit_cast(float, p[e]);
+        acc = __builtin_fma(a, a, acc);
+      }
+    } else {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(lds) + (i >> 2) * LDS_BF16_STRIDE + (i & 3) * 8;
+      *reinterpret_cast<u32x4*>(dst) = v;
+      const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double a = (double)__builtin_bit_cast(float, p[e] << 16);
+        const double b = (double)__builtin_bit_cast(float, p[e] & 0xffff0000u);
+        acc = __builtin_fma(a, a, acc);
+        acc = __builtin_fma(b, b, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, WAVE);
+  return acc;
+}
+
 // Reads group g of the staged row. The empty asm is a compiler barrier: a
 // group is re-read from LDS when needed again instead of being kept live in
 // VGPRs.
@@ -705,6 +767,204 @@ static_assert((size_t)QR_MAX_ROW_F32 / QK * LDS_F32_STRIDE * 4 + 8 * MAX_ROW_WAV
 // the levels), which fits in 128 VGPRs without spills.
 __host__ __device__ constexpr int row_waves_per_eu(int) { return 4; }
 
+// Solves group g of a staged row (lds: the row's staged groups) with the
+// imatrix entries qg of its columns (nullptr: q = 1) and writes its packed
+// bytes into orow. For the K types lanes 8s .. 8s+7 must hold the eight
+// groups of one super-block, all active: they combine their scales.
+template <int TYPE, bool BF16, bool VAR>
+__device__ __forceinline__ void quantize_group(const void* lds, int g, const float* __restrict__ qg,
+                                               const RowImp& imp, uint8_t* __restrict__ orow, int fit) {
+  float L[QK];
+
+  if constexpr (TYPE == QR_Q6_K) {  // lanes 8s .. 8s+7: the eight 32-weight groups of a super-block
+    float x[QK], w[QK];
+    load_group<BF16>(lds, g, x);
+    group_importances<VAR>(x, qg, imp, w);
+    {  // a sub-block (16 weights) with no importance at all falls back to q = 1
+      uint32_t any0 = 0, any1 = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        any0 |= fbits(w[i]) & 0x7fffffffu;
+        any1 |= fbits(w[16 + i]) & 0x7fffffffu;
+      }
+      if (any0 == 0) unit_importances<VAR, 0, 16>(x, imp, w);
+      if (any1 == 0) unit_importances<VAR, 16, 16>(x, imp, w);
+    }
+    const float d0 = sym_fit_part<32, 0, 16>(x, w, L);    // sub-block 2j
+    const float d1 = sym_fit_part<32, 16, 16>(x, w, L);   // sub-block 2j+1
+    const float amx = oct_max(fmaxf(fabsf(d0), fabsf(d1)));   // over the super-block's 16 sub-blocks
+    const _Float16 d16 = (_Float16)(amx / 127.0f);
+    const float dA = (float)d16;
+    const float s0 = dA > 0.0f ? med3(rne(d0 / dA), -127.0f, 127.0f) : 0.0f;
+    const float s1 = dA > 0.0f ? med3(rne(d1 / dA), -127.0f, 127.0f) : 0.0f;
+    const float ds0 = dA * s0, ds1 = dA * s1;   // exact: 11-bit times 8-bit
+    const float id0 = ds0 == 0.0f ? 0.0f : 1.0f / ds0;
+    const float id1 = ds1 == 0.0f ? 0.0f : 1.0f / ds1;
+    uint32_t u[QK];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      u[i] = ds0 == 0.0f ? 32u : (uint32_t)(int32_t)(med3(rne(x[i] * id0), -32.0f, 31.0f) + 32.0f);
+      u[16 + i] = ds1 == 0.0f ? 32u : (uint32_t)(int32_t)(med3(rne(x[16 + i] * id1), -32.0f, 31.0f) + 32.0f);
+    }
+    uint32_t h0 = 0, h1 = 0;  // bits 4 and 5 of each code, two bits apiece
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      h0 |= ((u[i] >> 4) & 3u) << (2 * i);
+      h1 |= ((u[16 + i] >> 4) & 3u) << (2 * i);
+    }
+    const uint4 qs = pack_nibbles(u);
+    const int j = g & 7;
+    uint8_t* p = orow + (size_t)(g >> 3) * 212;
+    // sub-scales: lane j holds bytes 2j, 2j+1; even lanes write a word
+    const uint32_t v16 = ((uint32_t)(int32_t)s0 & 255u) | (((uint32_t)(int32_t)s1 & 255u) << 8);
+    const uint32_t pair = (uint32_t)dpp_i<DPP_QUAD_XOR1>((int)v16);
+    if ((j & 1) == 0) store_u32(p + 4 + 2 * j, v16 | (pair << 16));
+    if (j == 0) store_u32(p, (uint32_t)__builtin_bit_cast(uint16_t, d16));   // d16, then the zero pad
+    uint8_t* pq = p + 20 + 16 * j;
+    store_u32(pq, qs.x); store_u32(pq + 4, qs.y); store_u32(pq + 8, qs.z); store_u32(pq + 12, qs.w);
+    store_u32(p + 148 + 8 * j, h0);
+    store_u32(p + 152 + 8 * j, h1);
+  } else if constexpr (TYPE == QR_Q6_0) {
+    const float d = solve_sym<32, BF16, VAR>(lds, g, qg, imp, L);
+    uint32_t u[QK];
+#pragma unroll
+    for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + 32.0f);
+    uint32_t h0 = 0, h1 = 0;  // bits 4 and 5 of each code, two bits apiece
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      h0 |= ((u[i] >> 4) & 3u) << (2 * i);
+      h1 |= ((u[16 + i] >> 4) & 3u) << (2 * i);
+    }
+    const uint4 qs = pack_nibbles(u);
+    uint8_t* p = orow + (size_t)g * 28;
+    store_u32(p, fbits(d));
+    store_u32(p + 4, h0); store_u32(p + 8, h1);
+    store_u32(p + 12, qs.x); store_u32(p + 16, qs.y); store_u32(p + 20, qs.z); store_u32(p + 24, qs.w);
+  } else if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
+    constexpr int NMAX = TYPE == QR_Q4_0 ? 8 : 16;
+    const float d = solve_sym<NMAX, BF16, VAR>(lds, g, qg, imp, L);
+    if constexpr (TYPE == QR_Q4_0) {
+      float uf[QK];
+#pragma unroll
+      for (int i = 0; i < QK; ++i) uf[i] = L[i] + (float)NMAX;
+      const uint4 qs = pack_nibbles_f(uf);
+      uint8_t* p = orow + (size_t)g * 20;
+      store_u32(p, fbits(d));
+      store_u32(p + 4, qs.x); store_u32(p + 8, qs.y); store_u32(p + 12, qs.z); store_u32(p + 16, qs.w);
+    } else {
+      uint32_t u[QK];
+#pragma unroll
+      for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + (float)NMAX);
+      const uint4 qs = pack_nibbles(u);
+      uint8_t* p = orow + (size_t)g * 24;
+      store_u32(p, fbits(d));
+      store_u32(p + 4, pack_high_bits(u));
+      store_u32(p + 8, qs.x); store_u32(p + 12, qs.y); store_u32(p + 16, qs.z); store_u32(p + 20, qs.w);
+    }
+  } else if constexpr (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
+    constexpr int NMAX = TYPE == QR_Q4_1 ? 15 : 31;
+    float d, m;
+    float sw;
+    solve_asym<NMAX, false, BF16, VAR>(lds, g, qg, imp, L, d, m, sw);
+    if constexpr (TYPE == QR_Q4_1) {
+      const uint4 qs = pack_nibbles_f(L);
+      uint8_t* p = orow + (size_t)g * 24;
+      store_u32(p, fbits(d)); store_u32(p + 4, fbits(m));
+      store_u32(p + 8, qs.x); store_u32(p + 12, qs.y); store_u32(p + 16, qs.z); store_u32(p + 20, qs.w);
+    } else {
+      uint32_t u[QK];
+#pragma unroll
+      for (int i = 0; i < QK; ++i) u[i] = (uint32_t)L[i];
+      const uint4 qs = pack_nibbles(u);
+      uint8_t* p = orow + (size_t)g * 28;
+      store_u32(p, fbits(d)); store_u32(p + 4, fbits(m));
+      store_u32(p + 8, pack_high_bits(u));
+      store_u32(p + 12, qs.x); store_u32(p + 16, qs.y); store_u32(p + 20, qs.z); store_u32(p + 24, qs.w);
+    }
+  } else {  // QR_Q4_K, QR_Q5_K: lanes 8s .. 8s+7 hold the sub-blocks of one super-block [KQ 一]
+    constexpr int KMAX = TYPE == QR_Q5_K ? 31 : 15;    // levels 0..KMAX
+    constexpr int KBYTES = TYPE == QR_Q5_K ? 176 : 144;
+    float d, m, sw;
+    solve_asym<KMAX, true, BF16, VAR>(lds, g, qg, imp, L, d, m, sw);
+    const float a = d > 0.0f ? d : 0.0f;
+    const float b = -m > 0.0f ? -m : 0.0f;
+    const int j = g & 7;
+    _Float16 d16, m16;
+    float sc, mn;
+    if (VAR && fit == QR_FIT_WEIGHTED) {
+      // lanes 0-3 of the super-block fit the eight scales, lanes 4-7 the
+      // eight offsets (the same instructions on other data); lanes 0 and
+      // 4 then hand out their levels, four to a word, and their scales
+      const bool offs = (j & 4) != 0;
+      float vv[8], wv[8], lv[8], dv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float ak = __shfl(a, k, 8), bk = __shfl(b, k, 8);
+        vv[k] = offs ? bk : ak;
+        wv[k] = __shfl(sw, k, 8);
+      }
+      fit_levels_pos8(vv, wv, lv, dv);
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        w0 |= (uint32_t)lv[k] << (8 * k);
+        w1 |= (uint32_t)lv[4 + k] << (8 * k);
+      }
+      const uint32_t sw0 = __shfl(w0, 0, 8), sw1 = __shfl(w1, 0, 8);
+      const uint32_t mw0 = __shfl(w0, 4, 8), mw1 = __shfl(w1, 4, 8);
+      const float da = __shfl(dv, 0, 8), db = __shfl(dv, 4, 8);
+      d16 = (_Float16)da;
+      m16 = (_Float16)db;
+      sc = (float)(((j < 4 ? sw0 : sw1) >> (8 * (j & 3))) & 255u);
+      mn = (float)(((j < 4 ? mw0 : mw1) >> (8 * (j & 3))) & 255u);
+      if ((float)d16 == 0.0f) sc = 0.0f;
+      if ((float)m16 == 0.0f) mn = 0.0f;
+    } else {
+      const float A = oct_max(a), Bm = oct_max(b);   // the super-block's largest scale and offset
+      d16 = (_Float16)(A / 63.0f);
+      m16 = (_Float16)(Bm / 63.0f);
+      const float dA0 = (float)d16, dB0 = (float)m16;
+      sc = dA0 > 0.0f ? med3(rne(a / dA0), 0.0f, 63.0f) : 0.0f;
+      mn = dB0 > 0.0f ? med3(rne(b / dB0), 0.0f, 63.0f) : 0.0f;
+    }
+    const float dA = (float)d16, dB = (float)m16;
+    const float ds = dA * sc, dm = dB * mn;
+    float u[QK];
+    if (ds == 0.0f) {
+#pragma unroll
+      for (int i = 0; i < QK; ++i) u[i] = 0.0f;
+    } else {
+      const float id = 1.0f / ds;
+      load_group<BF16>(lds, g, u);
+#pragma unroll
+      for (int i = 0; i < QK; ++i) u[i] = med3(rne((u[i] + dm) * id), 0.0f, (float)KMAX);
+    }
+    uint8_t* p = orow + (size_t)(g >> 3) * KBYTES;
+    if constexpr (TYPE == QR_Q5_K) {   // fifth bits at 16 + 4j, low nibbles at 48 + 16j
+      uint32_t ui[QK];
+#pragma unroll
+      for (int i = 0; i < QK; ++i) ui[i] = (uint32_t)u[i];
+      store_u32(p + 16 + 4 * j, pack_high_bits(ui));
+      *reinterpret_cast<uint4*>(p + 48 + 16 * j) = pack_nibbles(ui);
+    } else {
+      *reinterpret_cast<uint4*>(p + 16 + 16 * j) = pack_nibbles_f(u);
+    }
+    // the eight 6-bit fields, merged over the super-block's lanes
+    const uint64_t scj = (uint64_t)(uint32_t)sc << (6 * j);
+    const uint64_t mnj = (uint64_t)(uint32_t)mn << (6 * j);
+    const uint64_t scb = (uint64_t)oct_or((uint32_t)scj) | ((uint64_t)oct_or((uint32_t)(scj >> 32)) << 32);
+    const uint64_t mnb = (uint64_t)oct_or((uint32_t)mnj) | ((uint64_t)oct_or((uint32_t)(mnj >> 32)) << 32);
+    if (j == 0) {
+      const uint32_t h0 = (uint32_t)__builtin_bit_cast(uint16_t, d16) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, m16) << 16);
+      const uint32_t h1 = (uint32_t)scb;
+      const uint32_t h2 = (uint32_t)(scb >> 32) | ((uint32_t)mnb << 16);
+      const uint32_t h3 = (uint32_t)(mnb >> 16);
+      *reinterpret_cast<uint4*>(p) = make_uint4(h0, h1, h2, h3);
+    }
+  }
+}
+
 template <int TYPE, bool BF16, bool VAR>
 __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(row_waves_per_eu(TYPE)))) void k_quantize_rows(const void* __restrict__ x,
                                                                         const float* __restrict__ imatrix,
@@ -741,196 +1001,86 @@ __global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_p
   for (int base = 0; base < n_groups; base += nthreads) {
     const int g = base + tid;
     if (g >= n_groups) continue;
-    const float* qg = q ? q + g * QK : nullptr;
-    float L[QK];
+    quantize_group<TYPE, BF16, VAR>(lds_raw, g, q ? q + g * QK : nullptr, imp, orow, fit);
+  }
+}
 
-    if constexpr (TYPE == QR_Q6_K) {  // lanes 8s .. 8s+7: the eight 32-weight groups of a super-block
-      float x[QK], w[QK];
-      load_group<BF16>(lds_raw, g, x);
-      group_importances<VAR>(x, qg, imp, w);
-      {  // a sub-block (16 weights) with no importance at all falls back to q = 1
-        uint32_t any0 = 0, any1 = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          any0 |= fbits(w[i]) & 0x7fffffffu;
-          any1 |= fbits(w[16 + i]) & 0x7fffffffu;
-        }
-        if (any0 == 0) unit_importances<VAR, 0, 16>(x, imp, w);
-        if (any1 == 0) unit_importances<VAR, 16, 16>(x, imp, w);
-      }
-      const float d0 = sym_fit_part<32, 0, 16>(x, w, L);    // sub-block 2j
-      const float d1 = sym_fit_part<32, 16, 16>(x, w, L);   // sub-block 2j+1
-      const float amx = oct_max(fmaxf(fabsf(d0), fabsf(d1)));   // over the super-block's 16 sub-blocks
-      const _Float16 d16 = (_Float16)(amx / 127.0f);
-      const float dA = (float)d16;
-      const float s0 = dA > 0.0f ? med3(rne(d0 / dA), -127.0f, 127.0f) : 0.0f;
-      const float s1 = dA > 0.0f ? med3(rne(d1 / dA), -127.0f, 127.0f) : 0.0f;
-      const float ds0 = dA * s0, ds1 = dA * s1;   // exact: 11-bit times 8-bit
-      const float id0 = ds0 == 0.0f ? 0.0f : 1.0f / ds0;
-      const float id1 = ds1 == 0.0f ? 0.0f : 1.0f / ds1;
-      uint32_t u[QK];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        u[i] = ds0 == 0.0f ? 32u : (uint32_t)(int32_t)(med3(rne(x[i] * id0), -32.0f, 31.0f) + 32.0f);
-        u[16 + i] = ds1 == 0.0f ? 32u : (uint32_t)(int32_t)(med3(rne(x[16 + i] * id1), -32.0f, 31.0f) + 32.0f);
-      }
-      uint32_t h0 = 0, h1 = 0;  // bits 4 and 5 of each code, two bits apiece
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        h0 |= ((u[i] >> 4) & 3u) << (2 * i);
-        h1 |= ((u[16 + i] >> 4) & 3u) << (2 * i);
-      }
-      const uint4 qs = pack_nibbles(u);
-      const int j = g & 7;
-      uint8_t* p = orow + (size_t)(g >> 3) * 212;
-      // sub-scales: lane j holds bytes 2j, 2j+1; even lanes write a word
-      const uint32_t v16 = ((uint32_t)(int32_t)s0 & 255u) | (((uint32_t)(int32_t)s1 & 255u) << 8);
-      const uint32_t pair = (uint32_t)dpp_i<DPP_QUAD_XOR1>((int)v16);
-      if ((j & 1) == 0) store_u32(p + 4 + 2 * j, v16 | (pair << 16));
-      if (j == 0) store_u32(p, (uint32_t)__builtin_bit_cast(uint16_t, d16));   // d16, then the zero pad
-      uint8_t* pq = p + 20 + 16 * j;
-      store_u32(pq, qs.x); store_u32(pq + 4, qs.y); store_u32(pq + 8, qs.z); store_u32(pq + 12, qs.w);
-      store_u32(p + 148 + 8 * j, h0);
-      store_u32(p + 152 + 8 * j, h1);
-    } else if constexpr (TYPE == QR_Q6_0) {
-      const float d = solve_sym<32, BF16, VAR>(lds_raw, g, qg, imp, L);
-      uint32_t u[QK];
-#pragma unroll
-      for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + 32.0f);
-      uint32_t h0 = 0, h1 = 0;  // bits 4 and 5 of each code, two bits apiece
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        h0 |= ((u[i] >> 4) & 3u) << (2 * i);
-        h1 |= ((u[16 + i] >> 4) & 3u) << (2 * i);
-      }
-      const uint4 qs = pack_nibbles(u);
-      uint8_t* p = orow + (size_t)g * 28;
-      store_u32(p, fbits(d));
-      store_u32(p + 4, h0); store_u32(p + 8, h1);
-      store_u32(p + 12, qs.x); store_u32(p + 16, qs.y); store_u32(p + 20, qs.z); store_u32(p + 24, qs.w);
-    } else if constexpr (TYPE == QR_Q4_0 || TYPE == QR_Q5_0) {
-      constexpr int NMAX = TYPE == QR_Q4_0 ? 8 : 16;
-      const float d = solve_sym<NMAX, BF16, VAR>(lds_raw, g, qg, imp, L);
-      if constexpr (TYPE == QR_Q4_0) {
-        float uf[QK];
-#pragma unroll
-        for (int i = 0; i < QK; ++i) uf[i] = L[i] + (float)NMAX;
-        const uint4 qs = pack_nibbles_f(uf);
-        uint8_t* p = orow + (size_t)g * 20;
-        store_u32(p, fbits(d));
-        store_u32(p + 4, qs.x); store_u32(p + 8, qs.y); store_u32(p + 12, qs.z); store_u32(p + 16, qs.w);
-      } else {
-        uint32_t u[QK];
-#pragma unroll
-        for (int i = 0; i < QK; ++i) u[i] = (uint32_t)(int32_t)(L[i] + (float)NMAX);
-        const uint4 qs = pack_nibbles(u);
-        uint8_t* p = orow + (size_t)g * 24;
-        store_u32(p, fbits(d));
-        store_u32(p + 4, pack_high_bits(u));
-        store_u32(p + 8, qs.x); store_u32(p + 12, qs.y); store_u32(p + 16, qs.z); store_u32(p + 20, qs.w);
-      }
-    } else if constexpr (TYPE == QR_Q4_1 || TYPE == QR_Q5_1) {
-      constexpr int NMAX = TYPE == QR_Q4_1 ? 15 : 31;
-      float d, m;
-      float sw;
-      solve_asym<NMAX, false, BF16, VAR>(lds_raw, g, qg, imp, L, d, m, sw);
-      if constexpr (TYPE == QR_Q4_1) {
-        const uint4 qs = pack_nibbles_f(L);
-        uint8_t* p = orow + (size_t)g * 24;
-        store_u32(p, fbits(d)); store_u32(p + 4, fbits(m));
-        store_u32(p + 8, qs.x); store_u32(p + 12, qs.y); store_u32(p + 16, qs.z); store_u32(p + 20, qs.w);
-      } else {
-        uint32_t u[QK];
-#pragma unroll
-        for (int i = 0; i < QK; ++i) u[i] = (uint32_t)L[i];
-        const uint4 qs = pack_nibbles(u);
-        uint8_t* p = orow + (size_t)g * 28;
-        store_u32(p, fbits(d)); store_u32(p + 4, fbits(m));
-        store_u32(p + 8, pack_high_bits(u));
-        store_u32(p + 12, qs.x); store_u32(p + 16, qs.y); store_u32(p + 20, qs.z); store_u32(p + 24, qs.w);
-      }
-    } else {  // QR_Q4_K, QR_Q5_K: lanes 8s .. 8s+7 hold the sub-blocks of one super-block [KQ 一]
-      constexpr int KMAX = TYPE == QR_Q5_K ? 31 : 15;    // levels 0..KMAX
-      constexpr int KBYTES = TYPE == QR_Q5_K ? 176 : 144;
-      float d, m, sw;
-      solve_asym<KMAX, true, BF16, VAR>(lds_raw, g, qg, imp, L, d, m, sw);
-      const float a = d > 0.0f ? d : 0.0f;
-      const float b = -m > 0.0f ? -m : 0.0f;
-      const int j = g & 7;
-      _Float16 d16, m16;
-      float sc, mn;
-      if (VAR && fit == QR_FIT_WEIGHTED) {
-        // lanes 0-3 of the super-block fit the eight scales, lanes 4-7 the
-        // eight offsets (the same instructions on other data); lanes 0 and
-        // 4 then hand out their levels, four to a word, and their scales
-        const bool offs = (j & 4) != 0;
-        float vv[8], wv[8], lv[8], dv;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float ak = __shfl(a, k, 8), bk = __shfl(b, k, 8);
-          vv[k] = offs ? bk : ak;
-          wv[k] = __shfl(sw, k, 8);
-        }
-        fit_levels_pos8(vv, wv, lv, dv);
-        uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          w0 |= (uint32_t)lv[k] << (8 * k);
-          w1 |= (uint32_t)lv[4 + k] << (8 * k);
-        }
-        const uint32_t sw0 = __shfl(w0, 0, 8), sw1 = __shfl(w1, 0, 8);
-        const uint32_t mw0 = __shfl(w0, 4, 8), mw1 = __shfl(w1, 4, 8);
-        const float da = __shfl(dv, 0, 8), db = __shfl(dv, 4, 8);
-        d16 = (_Float16)da;
-        m16 = (_Float16)db;
-        sc = (float)(((j < 4 ? sw0 : sw1) >> (8 * (j & 3))) & 255u);
-        mn = (float)(((j < 4 ? mw0 : mw1) >> (8 * (j & 3))) & 255u);
-        if ((float)d16 == 0.0f) sc = 0.0f;
-        if ((float)m16 == 0.0f) mn = 0.0f;
-      } else {
-        const float A = oct_max(a), Bm = oct_max(b);   // the super-block's largest scale and offset
-        d16 = (_Float16)(A / 63.0f);
-        m16 = (_Float16)(Bm / 63.0f);
-        const float dA0 = (float)d16, dB0 = (float)m16;
-        sc = dA0 > 0.0f ? med3(rne(a / dA0), 0.0f, 63.0f) : 0.0f;
-        mn = dB0 > 0.0f ? med3(rne(b / dB0), 0.0f, 63.0f) : 0.0f;
-      }
-      const float dA = (float)d16, dB = (float)m16;
-      const float ds = dA * sc, dm = dB * mn;
-      float u[QK];
-      if (ds == 0.0f) {
-#pragma unroll
-        for (int i = 0; i < QK; ++i) u[i] = 0.0f;
-      } else {
-        const float id = 1.0f / ds;
-        load_group<BF16>(lds_raw, g, u);
-#pragma unroll
-        for (int i = 0; i < QK; ++i) u[i] = med3(rne((u[i] + dm) * id), 0.0f, (float)KMAX);
-      }
-      uint8_t* p = orow + (size_t)(g >> 3) * KBYTES;
-      if constexpr (TYPE == QR_Q5_K) {   // fifth bits at 16 + 4j, low nibbles at 48 + 16j
-        uint32_t ui[QK];
-#pragma unroll
-        for (int i = 0; i < QK; ++i) ui[i] = (uint32_t)u[i];
-        store_u32(p + 16 + 4 * j, pack_high_bits(ui));
-        *reinterpret_cast<uint4*>(p + 48 + 16 * j) = pack_nibbles(ui);
-      } else {
-        *reinterpret_cast<uint4*>(p + 16 + 16 * j) = pack_nibbles_f(u);
-      }
-      // the eight 6-bit fields, merged over the super-block's lanes
-      const uint64_t scj = (uint64_t)(uint32_t)sc << (6 * j);
-      const uint64_t mnj = (uint64_t)(uint32_t)mn << (6 * j);
-      const uint64_t scb = (uint64_t)oct_or((uint32_t)scj) | ((uint64_t)oct_or((uint32_t)(scj >> 32)) << 32);
-      const uint64_t mnb = (uint64_t)oct_or((uint32_t)mnj) | ((uint64_t)oct_or((uint32_t)(mnj >> 32)) << 32);
-      if (j == 0) {
-        const uint32_t h0 = (uint32_t)__builtin_bit_cast(uint16_t, d16) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, m16) << 16);
-        const uint32_t h1 = (uint32_t)scb;
-        const uint32_t h2 = (uint32_t)(scb >> 32) | ((uint32_t)mnb << 16);
-        const uint32_t h3 = (uint32_t)(mnb >> 16);
-        *reinterpret_cast<uint4*>(p) = make_uint4(h0, h1, h2, h3);
-      }
+// Streaming weight-row kernel, for widths whose groups would leave lanes of
+// the last wave idle (7168 values: 224 groups on four waves, 32 of 256
+// lanes idle). The workgroup's L = 64 W lanes walk blocks of `block_rows`
+// consecutive rows as one sequence of groups: pass i gives lane t group
+// L i + t of the block, so every lane works (block_rows x groups is a
+// multiple of L). Two row slots in LDS hold the rows a pass touches (the
+// host checks that a pass spans at most two rows and that each pass needs
+// at most one row more than the one before); each row is staged, with its
+// statistic, when the first pass that needs it begins, into the slot of
+// the row two before it, which no later pass touches. Staging and the
+// statistic are those of k_quantize_rows with the same W, so the results
+// are the same bytes.
+template <int TYPE, bool BF16, bool VAR>
+__global__ __launch_bounds__(WAVE * MAX_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(row_waves_per_eu(TYPE)))) void k_quantize_rows_stream(
+    const void* __restrict__ x, const float* __restrict__ imatrix, int n_per_row, int64_t n_rows,
+    int64_t rows_per_group, uint8_t* __restrict__ out, int64_t row_bytes, int weighting, int fit, int block_rows) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  const int n_groups = n_per_row / QK;
+  const size_t elem = BF16 ? 2 : 4;
+  const size_t slot_bytes = (size_t)n_groups * (BF16 ? 2 * LDS_BF16_STRIDE : 4 * LDS_F32_STRIDE);
+  double* partial = reinterpret_cast<double*>(lds_raw + 2 * slot_bytes);
+  const int64_t row0 = (int64_t)blockIdx.x * block_rows;
+  const int rows = (int)(n_rows - row0 < block_rows ? n_rows - row0 : block_rows);
+  const int passes = (int)(((int64_t)rows * n_groups + nthreads - 1) / nthreads);
+  float sig0 = 0.0f, sig1 = 0.0f;   // the statistic of the row in each slot
+
+  // stages block row r into slot r & 1 and keeps its statistic; the row's
+  // loads are issued before the barrier, so they overlap the wait for the
+  // last waves of the pass before
+  auto stage = [&](int r) {
+    RowRegs<BF16> rr;
+    // the thread's addresses are recomputed here (a few integer
+    // instructions) rather than kept live through the passes
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const void* xrow = reinterpret_cast<const unsigned char*>(x) + (size_t)(row0 + r) * n_per_row * elem;
+    stage_row_load<BF16>(xrow, n_per_row, t, nthreads, rr);
+    __syncthreads();   // every lane is done with the row the slot held
+    const double ss_wave = stage_row_store<BF16>(n_per_row, lds_raw + (r & 1) * slot_bytes, t, nthreads, rr);
+    if ((t & (WAVE - 1)) == 0) partial[t / WAVE] = ss_wave;
+    __syncthreads();
+    double ss = 0.0;
+    for (int k = 0; k < nthreads / WAVE; ++k) ss += partial[k];
+    // the same value in every lane: kept in a scalar register
+    const float s2 = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, (float)(ss / (double)n_per_row))));
+    if (r & 1) sig1 = s2;
+    else sig0 = s2;
+  };
+  stage(0);
+  int staged = 0;   // the last block row staged
+  for (int p = 0; p < passes; ++p) {
+    // the last row this pass touches
+    int64_t last = ((int64_t)p * nthreads + nthreads - 1) / n_groups;
+    if (last > rows - 1) last = rows - 1;
+    if (last > staged) {
+      stage((int)last);
+      staged = (int)last;
     }
+    const int64_t gg = (int64_t)p * nthreads + tid;   // group in the block
+    const int r = (int)(gg / n_groups);
+    if (r >= rows) continue;
+    const int g = (int)(gg - (int64_t)r * n_groups);
+    const float sigma2 = (r & 1) ? sig1 : sig0;
+    const bool normal_range = sigma2 >= 0x1p-96f && sigma2 <= 3.0e38f;
+    RowImp imp;
+    imp.sigma2 = sigma2;
+    imp.normal = normal_range;
+    imp.mode = VAR ? weighting : QR_W_SQRT_SIGMA2_X2;
+    imp.sigma = VAR && weighting == QR_W_SIGMA_PLUS_ABS_X ? sqrt_cr(sigma2, normal_range) : 0.0f;
+    const int64_t row = row0 + r;
+    const float* q = imatrix ? imatrix + (row / rows_per_group) * (int64_t)n_per_row : nullptr;
+    quantize_group<TYPE, BF16, VAR>(lds_raw + (r & 1) * slot_bytes, g, q ? q + g * QK : nullptr, imp,
+                                    out + row * row_bytes, fit);
   }
 }
 
@@ -1275,33 +1425,89 @@ int row_waves(int n_per_row, bool bf16) {
   return best;
 }
 
+// Rows per block of the streaming row kernel for this width, or 0 when the
+// plain kernel is as good: the streaming layout must keep every lane busy
+// where the plain one does not (same W, one wave per 64 groups), hold as many
+// waves per compute unit with its two row slots of LDS, and meet the
+// kernel's conditions (a pass spans at most two rows; each pass needs at
+// most one row more than the one before).
+int stream_block_rows(int n_per_row, bool bf16) {
+  const int groups = n_per_row / QK;
+  int w = (groups + WAVE - 1) / WAVE;
+  if (w > MAX_ROW_WAVES) return 0;
+  const int lanes = WAVE * w;
+  if (groups % lanes == 0 || groups % 8 != 0) return 0;
+  int a = groups, b = lanes;   // gcd
+  while (b) { const int t = a % b; a = b; b = t; }
+  const int block_rows = lanes / a;
+  const int passes = block_rows * groups / lanes;
+  int64_t prev_last = 0;
+  for (int p = 0; p < passes; ++p) {
+    const int64_t first = (int64_t)p * lanes / groups;
+    const int64_t last = ((int64_t)p * lanes + lanes - 1) / groups;
+    if (last - first > 1 || last - prev_last > 1) return 0;
+    prev_last = last;
+  }
+  const size_t lds = 2 * (row_lds_bytes(n_per_row, bf16, w) - 8 * (size_t)w) + 8 * (size_t)w;
+  int wgs = (int)(LDS_PER_WORKGROUP / lds);
+  if (wgs > 16 / w) wgs = 16 / w;
+  const int waves = wgs * w < 16 ? wgs * w : 16;
+  // the plain kernel's best choice, scored the same way as row_waves does
+  const int pw = row_waves(n_per_row, bf16);
+  const int plane = WAVE * pw;
+  const int ppasses = (groups + plane - 1) / plane;
+  const double pbusy = (double)groups / ((double)ppasses * plane);
+  int pwgs = (int)(LDS_PER_WORKGROUP / row_lds_bytes(n_per_row, bf16, pw));
+  if (pwgs > 16 / pw) pwgs = 16 / pw;
+  const int pwaves = pwgs * pw < 16 ? pwgs * pw : 16;
+  return (double)waves > 1.05 * pbusy * pwaves ? block_rows : 0;
+}
+
+// Raises a row kernel's dynamic-LDS limit to the whole 160 KiB once per
+// device and kernel (each instantiation has its own flags), for workgroups
+// that need more than 64 KiB. The attribute is set on the current device, so
+// for a stream of another device that device is made current for the call.
+// The flags may be read and set by several host threads at once.
+template <int TYPE, bool BF16, bool VAR, bool STREAM>
+int raise_lds_limit(const void* kern, size_t lds, hipStream_t stream) {
+  constexpr int MAX_DEVICES = 64;
+  static std::atomic<bool> attr_set[MAX_DEVICES];
+  if (lds <= 65536) return QR_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipGetDevice failed");
+  int sdev = dev;
+  if (stream && hipStreamGetDevice(stream, &sdev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipStreamGetDevice failed");
+  if (sdev < 0 || sdev >= MAX_DEVICES || !attr_set[sdev].load(std::memory_order_acquire)) {
+    if (sdev != dev && hipSetDevice(sdev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipSetDevice failed");
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WORKGROUP);
+    if (sdev != dev && hipSetDevice(dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipSetDevice failed");
+    if (e != hipSuccess) return qr_fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    if (sdev >= 0 && sdev < MAX_DEVICES) attr_set[sdev].store(true, std::memory_order_release);
+  }
+  return QR_OK;
+}
+
 template <int TYPE, bool BF16, bool VAR>
 int launch_rows(const void* x, const float* imatrix, int64_t n_rows, int n_per_row, int64_t rows_per_group,
                 void* out, size_t row_bytes, int weighting, int fit, hipStream_t stream) {
+  const int block_rows = stream_block_rows(n_per_row, BF16);
+  if (block_rows > 0) {
+    auto kern = k_quantize_rows_stream<TYPE, BF16, VAR>;
+    const int waves = (n_per_row / QK + WAVE - 1) / WAVE;
+    const size_t lds = 2 * (row_lds_bytes(n_per_row, BF16, waves) - 8 * (size_t)waves) + 8 * (size_t)waves;
+    const int rc = raise_lds_limit<TYPE, BF16, VAR, true>(reinterpret_cast<const void*>(kern), lds, stream);
+    if (rc != QR_OK) return rc;
+    const int64_t blocks = (n_rows + block_rows - 1) / block_rows;
+    hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(WAVE * waves), lds, stream, x, imatrix, n_per_row, n_rows,
+                       rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes, weighting, fit,
+                       block_rows);
+    return qr_check_launch("k_quantize_rows_stream");
+  }
   auto kern = k_quantize_rows<TYPE, BF16, VAR>;
   const int waves = row_waves(n_per_row, BF16);
   const size_t lds = row_lds_bytes(n_per_row, BF16, waves);
-  // Rows above 64 KB of LDS need the kernel's dynamic-LDS limit raised, once
-  // per device. The attribute is set on the current device, so for a stream
-  // of another device that device is made current for the call. The flags
-  // may be read and set by several host threads at once.
-  constexpr int MAX_DEVICES = 64;
-  static std::atomic<bool> attr_set[MAX_DEVICES];
-  if (lds > 65536) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipGetDevice failed");
-    int sdev = dev;
-    if (stream && hipStreamGetDevice(stream, &sdev) != hipSuccess)
-      return qr_fail(QR_EDEVICE, "hipStreamGetDevice failed");
-    if (sdev < 0 || sdev >= MAX_DEVICES || !attr_set[sdev].load(std::memory_order_acquire)) {
-      if (sdev != dev && hipSetDevice(sdev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipSetDevice failed");
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_PER_WORKGROUP);
-      if (sdev != dev && hipSetDevice(dev) != hipSuccess) return qr_fail(QR_EDEVICE, "hipSetDevice failed");
-      if (e != hipSuccess) return qr_fail(QR_EDEVICE, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-      if (sdev >= 0 && sdev < MAX_DEVICES) attr_set[sdev].store(true, std::memory_order_release);
-    }
-  }
+  const int rc = raise_lds_limit<TYPE, BF16, VAR, false>(reinterpret_cast<const void*>(kern), lds, stream);
+  if (rc != QR_OK) return rc;
   hipLaunchKernelGGL(kern, dim3((uint32_t)n_rows), dim3(WAVE * waves), lds, stream, x, imatrix, n_per_row,
                      rows_per_group, reinterpret_cast<uint8_t*>(out), (int64_t)row_bytes, weighting, fit);
   return qr_check_launch("k_quantize_rows");

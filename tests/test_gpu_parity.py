@@ -125,6 +125,29 @@ def test_grouped_rows_with_odd_group_sizes(qr, t, bf16):
 
 @pytest.mark.parametrize("t", WEIGHT_TYPES)
 @pytest.mark.parametrize("bf16", [False, True])
+def test_rows_streamed_in_blocks(qr, t, bf16):
+    # bf16 widths whose groups do not fill whole waves go through blocks of
+    # consecutive rows (1024 values: 2 rows per block; 3072: 4; 5120: 6;
+    # 7168: 8; 9728: 20), here with partial last blocks, imatrix groups that
+    # split blocks and a group without importances; fp32 rows stream only at
+    # 1024 values (their larger LDS slots leave too few workgroups per CU at
+    # the other widths, which take the one-row kernel)
+    rng = np.random.default_rng(zlib.crc32(f"stream/{t}/{bf16}".encode()))
+    for n, rows_per_group, n_groups in ((1024, 3, 3), (3072, 5, 2), (5120, 7, 2), (7168, 11, 2), (9728, 9, 3)):
+        x = (0.02 * rng.standard_t(5, (n_groups * rows_per_group, n))).astype(F32)
+        x *= np.exp(0.5 * rng.standard_normal((x.shape[0], 1))).astype(F32)
+        q = np.exp(1.5 * rng.standard_normal((n_groups, n))).astype(F32)
+        q[-1, : n // 4] = 0.0
+        say(f"case {t} bf16={bf16} streamed shape={x.shape} rows_per_group={rows_per_group}")
+        got = qr.qr_quantize_rows_grouped(t, to_dev(x, bf16), torch.from_numpy(q).cuda(),
+                                          rows_per_group).cpu().numpy()
+        xh = host_values(x, bf16)
+        ref = oracle.quantize_rows_grouped(t, xh, q, rows_per_group, threads=8)
+        assert_rows_equal(t, got, ref, xh, lambda r: q[r // rows_per_group])
+
+
+@pytest.mark.parametrize("t", WEIGHT_TYPES)
+@pytest.mark.parametrize("bf16", [False, True])
 def test_longest_rows(qr, t, bf16):
     # rows of QR_MAX_ROW values: the whole row staged in LDS, eight waves
     # each solving several groups
