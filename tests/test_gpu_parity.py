@@ -133,7 +133,10 @@ def test_rows_streamed_in_blocks(qr, t, bf16):
     # 1024 values (their larger LDS slots leave too few workgroups per CU at
     # the other widths, which take the one-row kernel)
     rng = np.random.default_rng(zlib.crc32(f"stream/{t}/{bf16}".encode()))
-    for n, rows_per_group, n_groups in ((1024, 3, 3), (3072, 5, 2), (5120, 7, 2), (7168, 11, 2), (9728, 9, 3)):
+    # (7168, 1, 1) and (7168, 7, 1): one block, shorter than 8 rows;
+    # (1024, 1, 1): one row of a 2-row block
+    for n, rows_per_group, n_groups in ((1024, 3, 3), (3072, 5, 2), (5120, 7, 2), (7168, 11, 2), (9728, 9, 3),
+                                        (7168, 1, 1), (7168, 7, 1), (1024, 1, 1)):
         x = (0.02 * rng.standard_t(5, (n_groups * rows_per_group, n))).astype(F32)
         x *= np.exp(0.5 * rng.standard_normal((x.shape[0], 1))).astype(F32)
         q = np.exp(1.5 * rng.standard_normal((n_groups, n))).astype(F32)
