@@ -9,8 +9,9 @@ trial scales, least squares, flips, super-block scales, packing.
 
 The same run times all five workloads the method is measured on
 ("configs": Q4_0 2048x2048 fp32; the headline; the 32-layer 7B-shaped bf16
-stack of 224 matrices, Q4_0 attention and Q5_1 FFN, one launch per matrix;
-Q8_K_128 activations 8192x7168 fp32; the 256-expert bf16 MoE stack in one
+stack of 224 matrices, Q4_0 attention and Q5_1 FFN, one launch per matrix
+and, the same matrices in the same buffers, one grouped launch per group of
+same-shape matrices; Q8_K_128 activations 8192x7168 fp32; the 256-expert bf16 MoE stack in one
 grouped launch), each against the HBM roofline, and times the CPU oracle on
 a bounded sample of each (cpu_baseline), checking the GPU bytes against it.
 
@@ -196,15 +197,18 @@ def _setup(name, dev):
                 qrow.qr_quantize_rows(t, x, q, out=o)
         nb = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
         return step, nb, sum(x.numel() for _, x, _ in mats)
-    if name == "stack_7b_32x7":
-        # the whole 32-layer stack: 224 launches per step
-        mats = [synth.torch_stack_matrix(layer, w, dev) for layer in range(32) for w in range(7)]
-        outs = [torch.empty((x.shape[0], qrow.qr_row_bytes(t, x.shape[1])), dtype=torch.uint8, device=dev)
-                for t, x, q in mats]
-
-        def step():
-            for (t, x, q), o in zip(mats, outs):
-                qrow.qr_quantize_rows(t, x, q, out=o)
+    if name in ("stack_7b_32x7", "stack_7b_32x7_grouped"):
+        # the whole 32-layer stack: 224 launches per step, or one grouped
+        # launch per group of same-shape matrices (3 per step)
+        groups, outs_g, mats, outs = _stack(dev)
+        if name == "stack_7b_32x7":
+            def step():
+                for (t, x, q), o in zip(mats, outs):
+                    qrow.qr_quantize_rows(t, x, q, out=o)
+        else:
+            def step():
+                for (t, x, q, r), o in zip(groups, outs_g):
+                    qrow.qr_quantize_rows_grouped(t, x, q, r, out=o)
         nb = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
         return step, nb, sum(x.numel() for _, x, _ in mats)
     if name == "moe_256x2048x7168":
@@ -265,6 +269,25 @@ def _setup(name, dev):
     raise ValueError(name)
 
 
+def _stack(dev):
+    """The 32-layer stack, drawn on the GPU in its three same-shape groups:
+    (groups, their outputs, the 224 matrices as views, their outputs as
+    views of the same buffers)."""
+    import torch
+    from post_weight_quantization_row_amd import qrow, synth
+    groups, members = synth.torch_stack_grouped(dev)
+    outs_g = [torch.empty((x.shape[0], qrow.qr_row_bytes(t, x.shape[1])), dtype=torch.uint8, device=dev)
+              for t, x, _, _ in groups]
+    mats = synth.torch_stack_views(groups, members)
+    outs = []
+    for layer in range(32):
+        for which in range(7):
+            gi, i = members[(layer, which)]
+            r = groups[gi][3]
+            outs.append(outs_g[gi][i * r:(i + 1) * r])
+    return groups, outs_g, mats, outs
+
+
 def _mix_stack(dev):
     """The 32-layer 7B-shaped stack (bf16, resident) with its Q4_K_M-style
     plan: Q4_K everywhere, Q6_K for attn_v and ffn_down in the layers that
@@ -310,7 +333,7 @@ ACT_WORKLOADS = ("q8_k64_8192x7168", "q8_k16_8192x7168")
 STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "stack_7b_32x7", "copy_1gib", "valu_rates", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096", "q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
+                  "moe_256x2048x7168", "stack_7b_32x7", "stack_7b_32x7_grouped", "copy_1gib", "valu_rates", "q4_k_row_scan", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096", "q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -319,6 +342,23 @@ def run_only(args, dev, flush):
         # waves per SIMD (the calibration of the VALU figures)
         print(json.dumps({"workload": "valu_rates", "unit": "SIMD cycles per wave64 instruction at 2.4 GHz",
                           "by_waves_per_simd": {w: valu_rates(w) for w in (1, 2, 4, 8)}}), flush=True)
+        return
+    if args.only == "q4_k_row_scan":
+        # the Q4_K row kernel on 4096-value fp32 rows at several row counts:
+        # time against rows separates the per-row rate from the per-launch cost
+        import torch
+        from post_weight_quantization_row_amd import qrow
+        g = torch.Generator(device=dev).manual_seed(5)
+        q = torch.exp(1.5 * torch.randn(4096, generator=g, device=dev))
+        scan = {}
+        for rows in (1024, 2048, 4096, 6144, 8192, 10240, 11008, 12288, 16384, 20480):
+            x = 0.015 * torch.randn(rows, 4096, generator=g, device=dev)
+            out = torch.empty((rows, qrow.qr_row_bytes("q4_k", 4096)), dtype=torch.uint8, device=dev)
+            ms, _, _ = timed_steps(lambda: qrow.qr_quantize_rows("q4_k", x, q, out=out), args.steps,
+                                   args.warmup, flush)
+            scan[rows] = round(ms * 1e3, 2)
+            log(f"q4_k_row_scan: {rows} rows {ms * 1e3:.2f} us")
+        print(json.dumps({"workload": "q4_k_row_scan", "unit": "us per launch", "rows_of_4096": scan}), flush=True)
         return
     step, nbytes, n_el = _setup(args.only, dev)
     log(f"{args.only}: warmup {args.warmup}, steps {args.steps}")
@@ -592,21 +632,24 @@ def main():
                                      "the full 8192x7168 matrix")
     del xad, oa
 
-    # ---- the 7B-shaped stack: 32 layers x 7 bf16 matrices, 224 launches
-    log("stack_7b_32x7: drawing 224 bf16 matrices")
-    mats = [synth.torch_stack_matrix(layer, w, dev) for layer in range(32) for w in range(7)]
-    outs = [torch.empty((x.shape[0], qrow.qr_row_bytes(t, x.shape[1])), dtype=torch.uint8, device=dev)
-            for t, x, _ in mats]
+    # ---- the 7B-shaped stack: 32 layers x 7 bf16 matrices, one launch per
+    # matrix (224) and one grouped launch per group of same-shape matrices (3)
+    log("stack_7b_32x7: drawing 224 bf16 matrices in 3 same-shape groups")
+    groups, outs_g, mats, outs = _stack(dev)
     st_steps = max(1, min(args.steps, 5))
     log(f"stack_7b_32x7: warmup 1, steps {st_steps}")
     e2e, ksum = stack_step_times(mats, outs, st_steps, 1, flush)
+    mg, _, _ = timed_steps(lambda: [qrow.qr_quantize_rows_grouped(t, x, q, r, out=o)
+                                    for (t, x, q, r), o in zip(groups, outs_g)], st_steps, 1, flush)
     w_att = sum(x.numel() for t, x, _ in mats if t == "q4_0")
     w_ffn = sum(x.numel() for t, x, _ in mats if t == "q5_1")
     b_st = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
     configs["stack_7b_32x7"] = {
         "launches": len(mats), "ms_end_to_end": round(e2e, 4), "ms_kernel_sum": round(ksum, 4),
         "Gweights/s": round((w_att + w_ffn) / e2e / 1e6, 3), "alg_bytes": b_st,
-        "hbm_frac": hbm_frac(b_st, e2e), "hbm_frac_kernel_sum": hbm_frac(b_st, ksum)}
+        "hbm_frac": hbm_frac(b_st, e2e), "hbm_frac_kernel_sum": hbm_frac(b_st, ksum),
+        "grouped": {"launches": len(groups), "ms": round(mg, 4),
+                    "Gweights/s": round((w_att + w_ffn) / mg / 1e6, 3), "hbm_frac": hbm_frac(b_st, mg)}}
     # the attention (Q4_0) part alone, from one layer's launches
     att = [(m, o) for m, o in zip(mats[:7], outs[:7]) if m[0] == "q4_0"]
     ma0, _, _ = timed_steps(lambda: [qrow.qr_quantize_rows(t, x, q, out=o) for (t, x, q), o in att], 10, 2, flush)
@@ -620,7 +663,7 @@ def main():
             return [oracle.quantize_rows(t, xs, qs, threads=threads) for t, xs, qs, _ in smp]
         host["stack_7b_32x7"] = (stack_oracle, [g for *_, g in smp], sum(v[1].size for v in smp),
                                  "layer 0 of the stack: its 7 matrices, every row")
-    del mats, outs
+    del mats, outs, groups, outs_g
     torch.cuda.empty_cache()
 
     # ---- the 256-expert MoE stack, bf16, one grouped launch

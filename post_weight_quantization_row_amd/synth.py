@@ -269,6 +269,46 @@ def torch_stack_matrix(layer, which, device, seed=1003):
     return typ, x, q
 
 
+# The stack's matrices in three groups of one shape and type each: the four
+# attention matrices of every layer, the gate and up matrices, the down
+# matrices. Member i of a group is rows i*n_rows .. (i+1)*n_rows - 1 of one
+# contiguous tensor, so a group is quantized by one grouped launch.
+STACK_GROUPS = [(0, 1, 2, 3), (4, 5), (6,)]
+
+
+def torch_stack_grouped(device, seed=1003, n_layers=32):
+    """(groups, members) for the stack with the values of torch_stack_matrix.
+    groups: [(type, bf16 [n_members * n_rows, n], fp32 [n_members, n],
+    n_rows)]; members[(layer, which)] = (group index, member index)."""
+    import torch
+    groups, members = [], {}
+    for gi, whichs in enumerate(STACK_GROUPS):
+        _, typ, n_rows, n = STACK_LAYER[whichs[0]]
+        keys = [(layer, which) for layer in range(n_layers) for which in whichs]
+        x = torch.empty((len(keys) * n_rows, n), dtype=torch.bfloat16, device=device)
+        q = torch.empty((len(keys), n), dtype=torch.float32, device=device)
+        for i, (layer, which) in enumerate(keys):
+            _, xi, qi = torch_stack_matrix(layer, which, device, seed)
+            x[i * n_rows:(i + 1) * n_rows] = xi
+            q[i] = qi
+            members[(layer, which)] = (gi, i)
+            del xi
+        groups.append((typ, x, q, n_rows))
+    return groups, members
+
+
+def torch_stack_views(groups, members, n_layers=32):
+    """The stack as (type, x, q) per matrix, layer by layer, as views of the
+    grouped tensors."""
+    out = []
+    for layer in range(n_layers):
+        for which in range(len(STACK_LAYER)):
+            gi, i = members[(layer, which)]
+            typ, x, q, n_rows = groups[gi]
+            out.append((typ, x[i * n_rows:(i + 1) * n_rows], q[i]))
+    return out
+
+
 def torch_moe_stack(device, n_experts=256, n_rows=2048, n_per_row=7168,
                     seed=1005, n_zero=26):
     """bf16 [n_experts*n_rows, n_per_row] and fp32 [n_experts, n_per_row]."""

@@ -313,23 +313,49 @@ def test_full_q8_k128_8192x7168(qr):
 ORACLE_THREADS = 16
 
 
+@pytest.fixture(scope="module")
+def stack(qr):
+    """The 7B-shaped stack as the benchmark draws it (bf16 on the GPU, in
+    three groups of same-shape matrices) and quantizes it both ways it is
+    timed: one grouped launch per group, and one launch per matrix (on views
+    of the same inputs, into separate buffers)."""
+    groups, members = synth.torch_stack_grouped("cuda")
+    say("case stack: 3 grouped launches")
+    outs_g = [qr.qr_quantize_rows_grouped(t, x, q, r) for t, x, q, r in groups]
+    say("case stack: 224 launches, one per matrix")
+    same = {}
+    for (layer, which), (gi, i) in members.items():
+        t, x, q, r = groups[gi]
+        got = qr.qr_quantize_rows(t, x[i * r:(i + 1) * r], q[i])
+        same[(layer, which)] = bool(torch.equal(got, outs_g[gi][i * r:(i + 1) * r]))
+        del got
+    yield groups, members, outs_g, same
+    del groups, outs_g
+    torch.cuda.empty_cache()
+
+
+def test_stack_7b_launch_per_matrix_equals_grouped(stack):
+    _, _, _, same = stack
+    assert all(same.values()), [k for k, v in same.items() if not v]
+
+
 @pytest.mark.parametrize("layers", [range(l0, l0 + 4) for l0 in range(0, 32, 4)],
                          ids=[f"layers{l0}-{l0 + 3}" for l0 in range(0, 32, 4)])
-def test_stack_7b_every_row(qr, layers):
-    """The 7B-shaped stack as the benchmark quantizes it (bf16, drawn on the
-    GPU, one launch per matrix): every row of every matrix against the
-    oracle, four layers per test (all 32 layers x 7 matrices over the
-    eight tests)."""
+def test_stack_7b_every_row(qr, stack, layers):
+    """Every row of every matrix of the stack (grouped launches; the launch
+    per matrix gives the same bytes) against the oracle, four layers per
+    test (all 32 layers x 7 matrices over the eight tests)."""
+    groups, members, outs_g, _ = stack
     for layer in layers:
         for which in range(7):
-            typ, x, q = synth.torch_stack_matrix(layer, which, "cuda")
-            say(f"case stack layer={layer} matrix={synth.STACK_LAYER[which][0]} {typ} {tuple(x.shape)}")
-            got = qr.qr_quantize_rows(typ, x, q).cpu().numpy()
-            xh = x.float().cpu().numpy()
-            qh = q.cpu().numpy()
-            del x
+            gi, i = members[(layer, which)]
+            typ, x, q, r = groups[gi]
+            say(f"case stack layer={layer} matrix={synth.STACK_LAYER[which][0]} {typ} ({r}, {x.shape[1]})")
+            got = outs_g[gi][i * r:(i + 1) * r].cpu().numpy()
+            xh = x[i * r:(i + 1) * r].float().cpu().numpy()
+            qh = q[i].cpu().numpy()
             ref = oracle.quantize_rows(typ, xh, qh, threads=ORACLE_THREADS)
-            assert_rows_equal(typ, got, ref, xh, lambda r: qh)
+            assert_rows_equal(typ, got, ref, xh, lambda r_: qh)
 
 
 @pytest.fixture(scope="module")
