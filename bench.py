@@ -10,8 +10,9 @@ trial scales, least squares, flips, super-block scales, packing.
 The same run times all five workloads the method is measured on
 ("configs": Q4_0 2048x2048 fp32; the headline; the 32-layer 7B-shaped bf16
 stack of 224 matrices, Q4_0 attention and Q5_1 FFN, one launch per matrix
-and, the same matrices in the same buffers, one grouped launch per group of
-same-shape matrices; Q8_K_128 activations 8192x7168 fp32; the 256-expert bf16 MoE stack in one
+(on one stream, and spread over four) and, the same matrices in the same
+buffers, one grouped launch per group of same-shape matrices; Q8_K_128
+activations 8192x7168 fp32; the 256-expert bf16 MoE stack in one
 grouped launch), each against the HBM roofline, and times the CPU oracle on
 a bounded sample of each (cpu_baseline), checking the GPU bytes against it.
 
@@ -197,7 +198,7 @@ def _setup(name, dev):
                 qrow.qr_quantize_rows(t, x, q, out=o)
         nb = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
         return step, nb, sum(x.numel() for _, x, _ in mats)
-    if name in ("stack_7b_32x7", "stack_7b_32x7_grouped"):
+    if name in ("stack_7b_32x7", "stack_7b_32x7_grouped", "stack_7b_32x7_streams"):
         # the whole 32-layer stack: 224 launches per step, or one grouped
         # launch per group of same-shape matrices (3 per step)
         groups, outs_g, mats, outs = _stack(dev)
@@ -205,6 +206,22 @@ def _setup(name, dev):
             def step():
                 for (t, x, q), o in zip(mats, outs):
                     qrow.qr_quantize_rows(t, x, q, out=o)
+        elif name == "stack_7b_32x7_streams":
+            streams = [torch.cuda.Stream() for _ in range(4)]
+
+            def step():
+                main = torch.cuda.current_stream()
+                start = torch.cuda.Event()
+                start.record(main)
+                for st in streams:
+                    st.wait_event(start)
+                for k, ((t, x, q), o) in enumerate(zip(mats, outs)):
+                    with torch.cuda.stream(streams[k % 4]):
+                        qrow.qr_quantize_rows(t, x, q, out=o)
+                for st in streams:
+                    done = torch.cuda.Event()
+                    done.record(st)
+                    main.wait_event(done)
         else:
             def step():
                 for (t, x, q, r), o in zip(groups, outs_g):
@@ -333,7 +350,7 @@ ACT_WORKLOADS = ("q8_k64_8192x7168", "q8_k16_8192x7168")
 STATS_WORKLOADS = ("stats_q4_k_11008x4096",)
 ONLY_WORKLOADS = ("q4_k_11008x4096", "q4_0_2048x2048", "q8_k128_8192x7168",
                   "dequantize_q4_k_11008x4096", "stack_7b_layer0_bf16",
-                  "moe_256x2048x7168", "stack_7b_32x7", "stack_7b_32x7_grouped", "copy_1gib", "valu_rates", "q4_k_row_scan", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096", "q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
+                  "moe_256x2048x7168", "stack_7b_32x7", "stack_7b_32x7_grouped", "stack_7b_32x7_streams", "copy_1gib", "valu_rates", "q4_k_row_scan", "mix_q4_k_m_stack_7b", "q4_k_fit_11008x4096", "q6_k_11008x4096", "q5_k_11008x4096") + ACT_WORKLOADS + IMATRIX_WORKLOADS + MATMUL_WORKLOADS + STATS_WORKLOADS
 
 
 def run_only(args, dev, flush):
@@ -500,6 +517,32 @@ def stack_step_times(mats, outs, steps, warmup, flush):
     return e2e, sum(sums) / len(sums)
 
 
+def stack_streams_ms(mats, outs, n_streams, steps, warmup, flush):
+    """The 224 launches spread round-robin over n_streams streams (default
+    priority), so that one matrix's launch fills the chip while another's
+    drains: mean ms per step between events on the current stream, which
+    waits for every stream at the end of the step."""
+    import torch
+    from post_weight_quantization_row_amd import qrow
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+
+    def launch_all():
+        main = torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(main)
+        for st in streams:
+            st.wait_event(start)
+        for k, ((t, x, q), o) in enumerate(zip(mats, outs)):
+            with torch.cuda.stream(streams[k % n_streams]):
+                qrow.qr_quantize_rows(t, x, q, out=o)
+        for st in streams:
+            done = torch.cuda.Event()
+            done.record(st)
+            main.wait_event(done)
+    ms, _, _ = timed_steps(launch_all, steps, warmup, flush)
+    return ms
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -641,6 +684,7 @@ def main():
     e2e, ksum = stack_step_times(mats, outs, st_steps, 1, flush)
     mg, _, _ = timed_steps(lambda: [qrow.qr_quantize_rows_grouped(t, x, q, r, out=o)
                                     for (t, x, q, r), o in zip(groups, outs_g)], st_steps, 1, flush)
+    m4 = stack_streams_ms(mats, outs, 4, st_steps, 1, flush)
     w_att = sum(x.numel() for t, x, _ in mats if t == "q4_0")
     w_ffn = sum(x.numel() for t, x, _ in mats if t == "q5_1")
     b_st = sum(x.numel() * 2 + q.numel() * 4 + o.numel() for (t, x, q), o in zip(mats, outs))
@@ -649,7 +693,9 @@ def main():
         "Gweights/s": round((w_att + w_ffn) / e2e / 1e6, 3), "alg_bytes": b_st,
         "hbm_frac": hbm_frac(b_st, e2e), "hbm_frac_kernel_sum": hbm_frac(b_st, ksum),
         "grouped": {"launches": len(groups), "ms": round(mg, 4),
-                    "Gweights/s": round((w_att + w_ffn) / mg / 1e6, 3), "hbm_frac": hbm_frac(b_st, mg)}}
+                    "Gweights/s": round((w_att + w_ffn) / mg / 1e6, 3), "hbm_frac": hbm_frac(b_st, mg)},
+        "four_streams": {"launches": len(mats), "ms": round(m4, 4),
+                         "Gweights/s": round((w_att + w_ffn) / m4 / 1e6, 3), "hbm_frac": hbm_frac(b_st, m4)}}
     # the attention (Q4_0) part alone, from one layer's launches
     att = [(m, o) for m, o in zip(mats[:7], outs[:7]) if m[0] == "q4_0"]
     ma0, _, _ = timed_steps(lambda: [qrow.qr_quantize_rows(t, x, q, out=o) for (t, x, q), o in att], 10, 2, flush)
