@@ -688,21 +688,218 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     }
 }
 
+// Q4_K weights on the matrix cores with the sub-scales folded into the
+// integer products. A weight is d sc u - dmin mn (u, sc, mn integers), so one
+// activation block's share of an output is
+//   d * sum_k sc(k) u_k q_k  -  dmin * sum_k mn(k) q_k,
+// two integer dot products over the whole block instead of one per group.
+// The first needs sc u as int8: with sc = 8 sh + sl (sh, sl in 0..7) it is
+// 8 (sum sh u q) + (sum sl u q), whose operands sh u and sl u are at most
+// 105; the second takes mn (at most 63) repeated over the group's 32
+// values. So each activation block costs three chains of 16x16x64 products
+// (two groups per instruction) accumulated in int32 across its groups
+// (exact: |sum| < 2^24), then per output one conversion, one product with d
+// and one fused multiply-add with dmin: two roundings per block where the
+// per-group kernel has up to eight, and fewer vector instructions.
+struct MfStageK {
+  uint32_t aq[MF_TOK][MF_ROW_WORDS];    // activation codes
+  uint32_t wlo[MF_ROWS][MF_ROW_WORDS];  // code bytes times (sc & 7)
+  uint32_t whi[MF_ROWS][MF_ROW_WORDS];  // code bytes times (sc >> 3)
+  uint32_t wmn[4][MF_ROWS];             // the group's mn in each byte
+  float wd[MF_ROWS], wdm[MF_ROWS];      // d and dmin of the rows' super-block
+  float ad[2][MF_TOK];                  // activation scales (of each 64-value block for Q8_K64)
+};
+
+// codes u (bytes, at most 15) times s (at most 7): no byte carries
+__device__ __forceinline__ uint32_t bytes_times(uint32_t u, uint32_t s) { return u * s; }
+
+template <int ACT, int RT>
+__global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_matmul_mfma_q4k(
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ x, int64_t n_out, int64_t n_tok, int n_in,
+    int64_t w_row_bytes, float* __restrict__ y) {
+  constexpr int ROWS = 32 * RT;
+  constexpr int SB = mf_step_bytes(ACT);
+  constexpr int GPB = ACT == QR_Q8_K128 ? 4 : 2;   // groups per activation block
+  __shared__ __align__(16) MfStageK stage[2];      // double buffer: one barrier per K step
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t t0 = (int64_t)blockIdx.y * MF_TOK;
+  const int nsteps = n_in / 128;
+  const int64_t x_row_bytes = (int64_t)nsteps * SB;
+
+  // staging roles as in k_matmul_mfma: thread tid decodes group tid & 3 of
+  // row tid >> 2 and moves quarter tid & 3 of token tid >> 2's step (its 32
+  // code bytes, plus the block scale for the quarters that hold one)
+  const int srow = tid >> 2, sq = tid & 3;
+  const int64_t grow = r0 + srow < n_out ? r0 + srow : n_out - 1;   // rows past the end: unused
+  const uint8_t* wrow = w + grow * w_row_bytes;
+  const bool tok_ok = t0 + srow < n_tok;                            // tokens past the end: zeros
+  const uint8_t* xrow = x + (tok_ok ? t0 + srow : n_tok - 1) * x_row_bytes;
+  const int code_off = ACT == QR_Q8_K128 ? 4 + 32 * sq : 72 * (sq >> 1) + 4 + 32 * (sq & 1);
+  const bool is_scale = ACT == QR_Q8_K128 ? sq == 0 : (sq & 1) == 0;
+  const int scale_off = ACT == QR_Q8_K128 ? 0 : 72 * (sq >> 1);
+  RawGroup rg;
+  uint32_t av[9];
+  const bool wstage = srow < ROWS;   // uniform over each wave
+  auto load_step = [&](int s) {
+    if (wstage) rg = load_raw<QR_Q4_K>(wrow, 4 * s + sq);
+    const uint8_t* blk = xrow + (int64_t)s * SB;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) av[k] = ld32(blk + code_off + 4 * k);
+    av[8] = is_scale ? ld32(blk + scale_off) : 0u;
+  };
+  auto store_step = [&](int s, MfStageK& st) {
+    if (wstage) {
+      const int j = (4 * s + sq) & 7;   // the group inside its super-block
+      const uint64_t sc6 = (uint64_t)rg.v[1] | ((uint64_t)(rg.v[2] & 0xffffu) << 32);
+      const uint64_t mn6 = (uint64_t)(rg.v[2] >> 16) | ((uint64_t)rg.v[3] << 16);
+      const uint32_t sc = (uint32_t)(sc6 >> (6 * j)) & 63u;
+      const uint32_t mn = (uint32_t)(mn6 >> (6 * j)) & 63u;
+      const uint32_t sl = sc & 7u, sh = sc >> 3;
+      uint4 l0, l1, h0, h1;
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lo[k] = rg.v[4 + k] & 0x0f0f0f0fu;           // values 4k .. 4k+3 of the group
+        hi[k] = (rg.v[4 + k] >> 4) & 0x0f0f0f0fu;    // values 16 + 4k ..
+      }
+      l0 = make_uint4(bytes_times(lo[0], sl), bytes_times(lo[1], sl), bytes_times(lo[2], sl), bytes_times(lo[3], sl));
+      l1 = make_uint4(bytes_times(hi[0], sl), bytes_times(hi[1], sl), bytes_times(hi[2], sl), bytes_times(hi[3], sl));
+      h0 = make_uint4(bytes_times(lo[0], sh), bytes_times(lo[1], sh), bytes_times(lo[2], sh), bytes_times(lo[3], sh));
+      h1 = make_uint4(bytes_times(hi[0], sh), bytes_times(hi[1], sh), bytes_times(hi[2], sh), bytes_times(hi[3], sh));
+      *reinterpret_cast<uint4*>(&st.wlo[srow][8 * sq]) = l0;
+      *reinterpret_cast<uint4*>(&st.wlo[srow][8 * sq + 4]) = l1;
+      *reinterpret_cast<uint4*>(&st.whi[srow][8 * sq]) = h0;
+      *reinterpret_cast<uint4*>(&st.whi[srow][8 * sq + 4]) = h1;
+      st.wmn[sq][srow] = mn * 0x01010101u;
+      if (sq == 0) {
+        st.wd[srow] = half_bits(rg.v[0]);
+        st.wdm[srow] = half_bits(rg.v[0] >> 16);
+      }
+    }
+    uint4 a0, a1;
+    a0.x = tok_ok ? av[0] : 0u; a0.y = tok_ok ? av[1] : 0u; a0.z = tok_ok ? av[2] : 0u; a0.w = tok_ok ? av[3] : 0u;
+    a1.x = tok_ok ? av[4] : 0u; a1.y = tok_ok ? av[5] : 0u; a1.z = tok_ok ? av[6] : 0u; a1.w = tok_ok ? av[7] : 0u;
+    *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq]) = a0;
+    *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq + 4]) = a1;
+    if (is_scale) st.ad[sq >> 1][srow] = __builtin_bit_cast(float, tok_ok ? av[8] : 0u);
+  };
+
+  const int wt = (wave & 1) * 32, wr = (wave >> 1) * 16 * RT;   // this wave's tokens and rows in the tile
+  const int li = lane & 15, lk = lane >> 4;
+  double acc[2][RT][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < RT; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[a][b][v] = 0.0;
+
+  // one step's products from a staged tile: per pair of groups (64 values)
+  // one 16x16x64 product per chain and tile; lane l takes the 16 values
+  // 16 (l / 16) .. +15 of the pair from both operands, so any assignment of
+  // the pair's values to operand bytes that is the same for both sides gives
+  // the same sum
+  auto compute = [&](const MfStageK& st) {
+    i32x4 dl[2][RT], dh[2][RT], dm[2][RT];
+    float dw[RT], dmw[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      dw[rt] = st.wd[wr + 16 * rt + li];
+      dmw[rt] = st.wdm[wr + 16 * rt + li];
+    }
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      if ((2 * gp) % GPB == 0) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < RT; ++b) {
+            dl[a][b] = i32x4{0, 0, 0, 0};
+            dh[a][b] = i32x4{0, 0, 0, 0};
+            dm[a][b] = i32x4{0, 0, 0, 0};
+          }
+      }
+      i32x4 aop[2], blo[RT], bhi[RT], bmn[RT];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        aop[tt] = *reinterpret_cast<const i32x4*>(&st.aq[wt + 16 * tt + li][16 * gp + 4 * lk]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        blo[rt] = *reinterpret_cast<const i32x4*>(&st.wlo[wr + 16 * rt + li][16 * gp + 4 * lk]);
+        bhi[rt] = *reinterpret_cast<const i32x4*>(&st.whi[wr + 16 * rt + li][16 * gp + 4 * lk]);
+        const int m = (int)st.wmn[2 * gp + (lk >> 1)][wr + 16 * rt + li];   // lanes 32..63: the pair's second group
+        bmn[rt] = i32x4{m, m, m, m};
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          dl[tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], blo[rt], dl[tt][rt], 0, 0, 0);
+          dh[tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], bhi[rt], dh[tt][rt], 0, 0, 0);
+          dm[tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], bmn[rt], dm[tt][rt], 0, 0, 0);
+        }
+      if ((2 * gp + 1) % GPB == GPB - 1) {   // the block's share: d S - dmin O, then the activation scale
+        const int blk = (2 * gp + 1) / GPB;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const float4 d4 = *reinterpret_cast<const float4*>(&st.ad[blk][wt + 16 * tt + 4 * lk]);
+          const double dv[4] = {(double)d4.x, (double)d4.y, (double)d4.z, (double)d4.w};
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int S = dl[tt][rt][v] + 8 * dh[tt][rt][v];
+              const float yb = __builtin_fmaf(-dmw[rt], (float)dm[tt][rt][v], dw[rt] * (float)S);
+              acc[tt][rt][v] = __builtin_fma(dv[v], (double)yb, acc[tt][rt][v]);
+            }
+        }
+      }
+    }
+  };
+
+  load_step(0);
+  store_step(0, stage[0]);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) load_step(s + 1);   // in flight during this step's products
+    compute(stage[s & 1]);
+    if (s + 1 < nsteps) store_step(s + 1, stage[(s + 1) & 1]);
+    __syncthreads();   // the next step's tile is staged; this one is free again
+  }
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t tok = t0 + wt + 16 * tt + 4 * lk + v;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int64_t row = r0 + wr + 16 * rt + li;
+        if (tok < n_tok && row < n_out) y[tok * n_out + row] = (float)acc[tt][rt][v];
+      }
+    }
+}
+
 template <int TYPE, int ACT>
 int launch_mfma(const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok, int n_in, int64_t w_row_bytes,
                 float* y, hipStream_t s) {
   const int64_t tok_tiles = (n_tok + MF_TOK - 1) / MF_TOK;
   // 64-row tiles unless that leaves fewer than two workgroups per CU
   // (256 CUs): then 32-row tiles, twice as many
-  if (((n_out + 63) / 64) * tok_tiles >= 512) {
-    const dim3 grid((uint32_t)((n_out + 63) / 64), (uint32_t)tok_tiles);
-    hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 2>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
-                       w_row_bytes, y);
-  } else {
-    const dim3 grid((uint32_t)((n_out + 31) / 32), (uint32_t)tok_tiles);
-    hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
-                       w_row_bytes, y);
+  const bool tall = ((n_out + 63) / 64) * tok_tiles >= 512;
+  const dim3 grid((uint32_t)(tall ? (n_out + 63) / 64 : (n_out + 31) / 32), (uint32_t)tok_tiles);
+  if constexpr (TYPE == QR_Q4_K) {
+    if (tall) hipLaunchKernelGGL((k_matmul_mfma_q4k<ACT, 2>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
+                                 w_row_bytes, y);
+    else hipLaunchKernelGGL((k_matmul_mfma_q4k<ACT, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
+                            w_row_bytes, y);
+    return qr_check_launch("k_matmul_mfma_q4k");
   }
+  if (tall) hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 2>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
+                               w_row_bytes, y);
+  else hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
+                          w_row_bytes, y);
   return qr_check_launch("k_matmul_mfma");
 }
 

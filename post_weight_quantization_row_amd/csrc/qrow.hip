@@ -15,7 +15,9 @@
 //
 // Execution model (gfx950, wave64):
 //  * Weight rows: one workgroup per row, of one wave per 64 groups of 32
-//    weights (at most eight waves). The workgroup streams the row from HBM
+//    weights (at most eight waves; a width whose groups leave lanes of the
+//    last wave idle walks blocks of consecutive rows instead, see
+//    k_quantize_rows_stream). The workgroup streams the row from HBM
 //    once with coalesced 16-byte loads into LDS (32-element groups padded to
 //    a 16-byte multiple so that per-lane group reads are bank-conflict free)
 //    while accumulating sum x^2 in double; a workgroup reduction gives
