@@ -700,13 +700,16 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 // (two groups per instruction) accumulated in int32 across its groups
 // (exact: |sum| < 2^24), then per output one conversion, one product with d
 // and one fused multiply-add with dmin: two roundings per block where the
-// per-group kernel has up to eight, and fewer vector instructions.
+// per-group kernel has up to eight, and fewer vector instructions. The
+// weights are staged once as code bytes; each lane forms sl u and sh u from
+// them (two multiplies per word), which keeps a workgroup at 41 KB of LDS
+// and 164 VGPRs: three workgroups per CU.
+template <int ROWS>
 struct MfStageK {
   uint32_t aq[MF_TOK][MF_ROW_WORDS];    // activation codes
-  uint32_t wlo[MF_ROWS][MF_ROW_WORDS];  // code bytes times (sc & 7)
-  uint32_t whi[MF_ROWS][MF_ROW_WORDS];  // code bytes times (sc >> 3)
-  uint32_t wmn[4][MF_ROWS];             // the group's mn in each byte
-  float wd[MF_ROWS], wdm[MF_ROWS];      // d and dmin of the rows' super-block
+  uint32_t wu[ROWS][MF_ROW_WORDS];      // weight code bytes u
+  uint32_t wsc[4][ROWS];                // per group: sc & 7, sc >> 3, mn in bytes 0, 1, 2
+  float wd[ROWS], wdm[ROWS];            // d and dmin of the rows' super-block
   float ad[2][MF_TOK];                  // activation scales (of each 64-value block for Q8_K64)
 };
 
@@ -714,13 +717,13 @@ struct MfStageK {
 __device__ __forceinline__ uint32_t bytes_times(uint32_t u, uint32_t s) { return u * s; }
 
 template <int ACT, int RT>
-__global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k_matmul_mfma_q4k(
+__global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT == QR_Q8_K128 ? 3 : 2))) void k_matmul_mfma_q4k(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ x, int64_t n_out, int64_t n_tok, int n_in,
     int64_t w_row_bytes, float* __restrict__ y) {
   constexpr int ROWS = 32 * RT;
   constexpr int SB = mf_step_bytes(ACT);
   constexpr int GPB = ACT == QR_Q8_K128 ? 4 : 2;   // groups per activation block
-  __shared__ __align__(16) MfStageK stage[2];      // double buffer: one barrier per K step
+  __shared__ __align__(16) MfStageK<ROWS> stage[2];   // double buffer: one barrier per K step
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t r0 = (int64_t)blockIdx.x * ROWS;
@@ -749,30 +752,20 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     for (int k = 0; k < 8; ++k) av[k] = ld32(blk + code_off + 4 * k);
     av[8] = is_scale ? ld32(blk + scale_off) : 0u;
   };
-  auto store_step = [&](int s, MfStageK& st) {
+  auto store_step = [&](int s, MfStageK<ROWS>& st) {
     if (wstage) {
       const int j = (4 * s + sq) & 7;   // the group inside its super-block
       const uint64_t sc6 = (uint64_t)rg.v[1] | ((uint64_t)(rg.v[2] & 0xffffu) << 32);
       const uint64_t mn6 = (uint64_t)(rg.v[2] >> 16) | ((uint64_t)rg.v[3] << 16);
       const uint32_t sc = (uint32_t)(sc6 >> (6 * j)) & 63u;
       const uint32_t mn = (uint32_t)(mn6 >> (6 * j)) & 63u;
-      const uint32_t sl = sc & 7u, sh = sc >> 3;
-      uint4 l0, l1, h0, h1;
-      uint32_t lo[4], hi[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lo[k] = rg.v[4 + k] & 0x0f0f0f0fu;           // values 4k .. 4k+3 of the group
-        hi[k] = (rg.v[4 + k] >> 4) & 0x0f0f0f0fu;    // values 16 + 4k ..
-      }
-      l0 = make_uint4(bytes_times(lo[0], sl), bytes_times(lo[1], sl), bytes_times(lo[2], sl), bytes_times(lo[3], sl));
-      l1 = make_uint4(bytes_times(hi[0], sl), bytes_times(hi[1], sl), bytes_times(hi[2], sl), bytes_times(hi[3], sl));
-      h0 = make_uint4(bytes_times(lo[0], sh), bytes_times(lo[1], sh), bytes_times(lo[2], sh), bytes_times(lo[3], sh));
-      h1 = make_uint4(bytes_times(hi[0], sh), bytes_times(hi[1], sh), bytes_times(hi[2], sh), bytes_times(hi[3], sh));
-      *reinterpret_cast<uint4*>(&st.wlo[srow][8 * sq]) = l0;
-      *reinterpret_cast<uint4*>(&st.wlo[srow][8 * sq + 4]) = l1;
-      *reinterpret_cast<uint4*>(&st.whi[srow][8 * sq]) = h0;
-      *reinterpret_cast<uint4*>(&st.whi[srow][8 * sq + 4]) = h1;
-      st.wmn[sq][srow] = mn * 0x01010101u;
+      const uint4 l0 = make_uint4(rg.v[4] & 0x0f0f0f0fu, rg.v[5] & 0x0f0f0f0fu, rg.v[6] & 0x0f0f0f0fu,
+                                  rg.v[7] & 0x0f0f0f0fu);   // values 0 .. 15 of the group
+      const uint4 l1 = make_uint4((rg.v[4] >> 4) & 0x0f0f0f0fu, (rg.v[5] >> 4) & 0x0f0f0f0fu,
+                                  (rg.v[6] >> 4) & 0x0f0f0f0fu, (rg.v[7] >> 4) & 0x0f0f0f0fu);   // 16 .. 31
+      *reinterpret_cast<uint4*>(&st.wu[srow][8 * sq]) = l0;
+      *reinterpret_cast<uint4*>(&st.wu[srow][8 * sq + 4]) = l1;
+      st.wsc[sq][srow] = (sc & 7u) | ((sc >> 3) << 8) | (mn << 16);
       if (sq == 0) {
         st.wd[srow] = half_bits(rg.v[0]);
         st.wdm[srow] = half_bits(rg.v[0] >> 16);
@@ -801,7 +794,7 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
   // 16 (l / 16) .. +15 of the pair from both operands, so any assignment of
   // the pair's values to operand bytes that is the same for both sides gives
   // the same sum
-  auto compute = [&](const MfStageK& st) {
+  auto compute = [&](const MfStageK<ROWS>& st) {
     i32x4 dl[2][RT], dh[2][RT], dm[2][RT];
     float dw[RT], dmw[RT];
 #pragma unroll
@@ -827,9 +820,15 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
         aop[tt] = *reinterpret_cast<const i32x4*>(&st.aq[wt + 16 * tt + li][16 * gp + 4 * lk]);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        blo[rt] = *reinterpret_cast<const i32x4*>(&st.wlo[wr + 16 * rt + li][16 * gp + 4 * lk]);
-        bhi[rt] = *reinterpret_cast<const i32x4*>(&st.whi[wr + 16 * rt + li][16 * gp + 4 * lk]);
-        const int m = (int)st.wmn[2 * gp + (lk >> 1)][wr + 16 * rt + li];   // lanes 32..63: the pair's second group
+        const i32x4 u = *reinterpret_cast<const i32x4*>(&st.wu[wr + 16 * rt + li][16 * gp + 4 * lk]);
+        // lanes 32..63 hold the pair's second group
+        const uint32_t c = st.wsc[2 * gp + (lk >> 1)][wr + 16 * rt + li];
+        const uint32_t sl = c & 255u, sh = (c >> 8) & 255u;
+        const int m = (int)((c >> 16) * 0x01010101u);
+        blo[rt] = i32x4{(int)bytes_times((uint32_t)u[0], sl), (int)bytes_times((uint32_t)u[1], sl),
+                        (int)bytes_times((uint32_t)u[2], sl), (int)bytes_times((uint32_t)u[3], sl)};
+        bhi[rt] = i32x4{(int)bytes_times((uint32_t)u[0], sh), (int)bytes_times((uint32_t)u[1], sh),
+                        (int)bytes_times((uint32_t)u[2], sh), (int)bytes_times((uint32_t)u[3], sh)};
         bmn[rt] = i32x4{m, m, m, m};
       }
 #pragma unroll
