@@ -65,8 +65,10 @@ def assert_rows_equal(t, mode, gpu, ref, x, q):
 @pytest.mark.parametrize("t", TYPES)
 def test_weighting(qr, t, mode):
     rng = np.random.default_rng(zlib.crc32(f"{t}/{mode}".encode()))
+    # (2, 7168) bf16 and (5, 1024) fp32 go through the streaming row kernel
     for bf16, (n_rows, n), qkind in [(False, (5, 2304), "lognormal"), (True, (3, 4096), "none"),
-                                     (False, (33, 512), "zero-columns"), (True, (2, 7168), "lognormal")]:
+                                     (False, (33, 512), "zero-columns"), (True, (2, 7168), "lognormal"),
+                                     (False, (5, 1024), "zero-columns")]:
         if t in ("q4_k", "q5_k", "q6_k") and n % 256:
             n = n // 256 * 256
         x = (0.02 * rng.standard_t(5, (n_rows, n))).astype(F32)
