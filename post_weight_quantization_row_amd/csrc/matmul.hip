@@ -744,13 +744,26 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT 
   const int scale_off = ACT == QR_Q8_K128 ? 0 : 72 * (sq >> 1);
   RawGroup rg;
   uint32_t av[9];
-  const bool wstage = srow < ROWS;   // uniform over each wave
+  // uniform over each wave; always true for 64-row tiles. The loads are
+  // unconditional (rows past the tile load a valid row and are not staged),
+  // so that no register they write is touched before the step's products:
+  // a conditional load made the compiler wait for it at once.
+  const bool wstage = ROWS == MF_ROWS || srow < ROWS;
   auto load_step = [&](int s) {
-    if (wstage) rg = load_raw<QR_Q4_K>(wrow, 4 * s + sq);
+    // the super-block header as four words of their own (a four-word vector
+    // load had its registers split, and the split waited for the load), then
+    // the group's 16 code bytes
+    const int g = 4 * s + sq;
+    const uint8_t* sbk = wrow + (int64_t)(g >> 3) * 144;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rg.v[k] = ld32(sbk + 4 * k);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(sbk + 16 + 16 * (g & 7));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rg.v[4 + k] = c[k];
     const uint8_t* blk = xrow + (int64_t)s * SB;
 #pragma unroll
     for (int k = 0; k < 8; ++k) av[k] = ld32(blk + code_off + 4 * k);
-    av[8] = is_scale ? ld32(blk + scale_off) : 0u;
+    av[8] = ld32(blk + scale_off);   // the scale word, used by the quarters that hold one
   };
   auto store_step = [&](int s, MfStageK<ROWS>& st) {
     if (wstage) {
