@@ -543,9 +543,12 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
                                       : (sq == 0 ? 0 : sq == 1 ? 68 : sq == 2 ? 72 : 140);
   RawGroup rg;
   uint32_t av[9];
-  const bool wstage = srow < ROWS;   // uniform over each wave
+  // uniform over each wave; always true for 64-row tiles. The load itself is
+  // unconditional (rows past the tile load a valid row, not staged), so that
+  // the compiler does not wait for it before the step's products.
+  const bool wstage = ROWS == MF_ROWS || srow < ROWS;
   auto load_step = [&](int s) {
-    if (wstage) rg = load_raw<TYPE>(wrow, 4 * s + sq);
+    rg = load_raw<TYPE>(wrow, 4 * s + sq);
     const uint8_t* blk = xrow + (int64_t)s * SB;
 #pragma unroll
     for (int k = 0; k < 8; ++k) av[k] = ld32(blk + code_off + 4 * k);
@@ -907,12 +910,13 @@ int launch_mfma(const uint8_t* w, const uint8_t* x, int64_t n_out, int64_t n_tok
     else hipLaunchKernelGGL((k_matmul_mfma_q4k<ACT, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
                             w_row_bytes, y);
     return qr_check_launch("k_matmul_mfma_q4k");
+  } else {
+    if (tall) hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 2>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok,
+                                 n_in, w_row_bytes, y);
+    else hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
+                            w_row_bytes, y);
+    return qr_check_launch("k_matmul_mfma");
   }
-  if (tall) hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 2>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
-                               w_row_bytes, y);
-  else hipLaunchKernelGGL((k_matmul_mfma<TYPE, ACT, 1>), grid, dim3(MF_THREADS), 0, s, w, x, n_out, n_tok, n_in,
-                          w_row_bytes, y);
-  return qr_check_launch("k_matmul_mfma");
 }
 
 template <int ACT>
