@@ -41,3 +41,19 @@ def test_counters_are_used_only_for_the_source_they_were_taken_on(tmp_path):
     assert bench.measured_traffic() is None                      # taken on another source
     counters.write_text("not json")
     assert bench.measured_traffic() is None
+
+
+def test_stack_groups_hold_the_stack_matrices():
+    # the grouped layout the benchmark draws the stack in: every matrix is a
+    # contiguous slice of its group with the values torch_stack_matrix gives
+    torch = __import__("pytest").importorskip("torch")
+    sys.path.insert(0, ROOT)
+    from post_weight_quantization_row_amd import synth
+    groups, members = synth.torch_stack_grouped("cpu", n_layers=1)
+    assert [(t, tuple(x.shape), r) for t, x, _, r in groups] == [
+        ("q4_0", (4 * 4096, 4096), 4096), ("q5_1", (2 * 11008, 4096), 11008), ("q5_1", (4096, 11008), 4096)]
+    views = synth.torch_stack_views(groups, members, n_layers=1)
+    for which in (0, 3, 5, 6):   # first and last member of each group
+        t, x, q = views[which]
+        t2, x2, q2 = synth.torch_stack_matrix(0, which, "cpu")
+        assert t == t2 and x.is_contiguous() and torch.equal(x, x2) and torch.equal(q, q2)
