@@ -713,8 +713,15 @@ struct MfStageK {
   uint32_t wu[ROWS][MF_ROW_WORDS];      // weight code bytes u
   uint32_t wsc[4][ROWS];                // per group: sc & 7, sc >> 3, mn in bytes 0, 1, 2
   float wd[ROWS], wdm[ROWS];            // d and dmin of the rows' super-block
-  float ad[2][MF_TOK];                  // activation scales (of each 64-value block for Q8_K64)
+  double ad[2][MF_TOK];                 // activation scales (of each 64-value block for Q8_K64)
 };
+
+// the word that lane k of each group of four lanes holds (DPP quad_perm
+// [k, k, k, k])
+template <int K>
+__device__ __forceinline__ uint32_t quad_word(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, K * 0x55, 0xf, 0xf, false);
+}
 
 // codes u (bytes, at most 15) times s (at most 7): no byte carries
 __device__ __forceinline__ uint32_t bytes_times(uint32_t u, uint32_t s) { return u * s; }
@@ -740,12 +747,12 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT 
   const int srow = tid >> 2, sq = tid & 3;
   const int64_t grow = r0 + srow < n_out ? r0 + srow : n_out - 1;   // rows past the end: unused
   const uint8_t* wrow = w + grow * w_row_bytes;
-  const bool tok_ok = t0 + srow < n_tok;                            // tokens past the end: zeros
-  const uint8_t* xrow = x + (tok_ok ? t0 + srow : n_tok - 1) * x_row_bytes;
+  const uint8_t* xrow = x + (t0 + srow < n_tok ? t0 + srow : n_tok - 1) * x_row_bytes;
   const int code_off = ACT == QR_Q8_K128 ? 4 + 32 * sq : 72 * (sq >> 1) + 4 + 32 * (sq & 1);
   const bool is_scale = ACT == QR_Q8_K128 ? sq == 0 : (sq & 1) == 0;
   const int scale_off = ACT == QR_Q8_K128 ? 0 : 72 * (sq >> 1);
-  RawGroup rg;
+  uint32_t hdr;   // word sq of the super-block header
+  u32x4 codes;    // the group's 16 code bytes
   uint32_t av[9];
   // uniform over each wave; always true for 64-row tiles. The loads are
   // unconditional (rows past the tile load a valid row and are not staged),
@@ -753,124 +760,115 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT 
   // a conditional load made the compiler wait for it at once.
   const bool wstage = ROWS == MF_ROWS || srow < ROWS;
   auto load_step = [&](int s) {
-    // the super-block header as four words of their own (a four-word vector
-    // load had its registers split, and the split waited for the load), then
-    // the group's 16 code bytes
+    // each of a row's four threads loads one word of the super-block header
+    // (they are exchanged when staged: one register in flight instead of
+    // four, and no four-register tuple for the allocator to split, which
+    // made it wait for the load at once), then its group's 16 code bytes
     const int g = 4 * s + sq;
     const uint8_t* sbk = wrow + (int64_t)(g >> 3) * 144;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) rg.v[k] = ld32(sbk + 4 * k);
-    const u32x4 c = *reinterpret_cast<const u32x4*>(sbk + 16 + 16 * (g & 7));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) rg.v[4 + k] = c[k];
+    hdr = ld32(sbk + 4 * sq);
+    codes = *reinterpret_cast<const u32x4*>(sbk + 16 + 16 * (g & 7));
     const uint8_t* blk = xrow + (int64_t)s * SB;
 #pragma unroll
     for (int k = 0; k < 8; ++k) av[k] = ld32(blk + code_off + 4 * k);
     av[8] = ld32(blk + scale_off);   // the scale word, used by the quarters that hold one
   };
   auto store_step = [&](int s, MfStageK<ROWS>& st) {
+    const uint32_t h0 = quad_word<0>(hdr), h1 = quad_word<1>(hdr), h2 = quad_word<2>(hdr), h3 = quad_word<3>(hdr);
     if (wstage) {
       const int j = (4 * s + sq) & 7;   // the group inside its super-block
-      const uint64_t sc6 = (uint64_t)rg.v[1] | ((uint64_t)(rg.v[2] & 0xffffu) << 32);
-      const uint64_t mn6 = (uint64_t)(rg.v[2] >> 16) | ((uint64_t)rg.v[3] << 16);
+      const uint64_t sc6 = (uint64_t)h1 | ((uint64_t)(h2 & 0xffffu) << 32);
+      const uint64_t mn6 = (uint64_t)(h2 >> 16) | ((uint64_t)h3 << 16);
       const uint32_t sc = (uint32_t)(sc6 >> (6 * j)) & 63u;
       const uint32_t mn = (uint32_t)(mn6 >> (6 * j)) & 63u;
-      const uint4 l0 = make_uint4(rg.v[4] & 0x0f0f0f0fu, rg.v[5] & 0x0f0f0f0fu, rg.v[6] & 0x0f0f0f0fu,
-                                  rg.v[7] & 0x0f0f0f0fu);   // values 0 .. 15 of the group
-      const uint4 l1 = make_uint4((rg.v[4] >> 4) & 0x0f0f0f0fu, (rg.v[5] >> 4) & 0x0f0f0f0fu,
-                                  (rg.v[6] >> 4) & 0x0f0f0f0fu, (rg.v[7] >> 4) & 0x0f0f0f0fu);   // 16 .. 31
+      const uint32_t c0 = codes[0], c1 = codes[1], c2 = codes[2], c3 = codes[3];
+      const uint4 l0 = make_uint4(c0 & 0x0f0f0f0fu, c1 & 0x0f0f0f0fu, c2 & 0x0f0f0f0fu,
+                                  c3 & 0x0f0f0f0fu);   // values 0 .. 15 of the group
+      const uint4 l1 = make_uint4((c0 >> 4) & 0x0f0f0f0fu, (c1 >> 4) & 0x0f0f0f0fu,
+                                  (c2 >> 4) & 0x0f0f0f0fu, (c3 >> 4) & 0x0f0f0f0fu);   // 16 .. 31
       *reinterpret_cast<uint4*>(&st.wu[srow][8 * sq]) = l0;
       *reinterpret_cast<uint4*>(&st.wu[srow][8 * sq + 4]) = l1;
       st.wsc[sq][srow] = (sc & 7u) | ((sc >> 3) << 8) | (mn << 16);
       if (sq == 0) {
-        st.wd[srow] = half_bits(rg.v[0]);
-        st.wdm[srow] = half_bits(rg.v[0] >> 16);
+        st.wd[srow] = half_bits(h0);
+        st.wdm[srow] = half_bits(h0 >> 16);
       }
     }
-    uint4 a0, a1;
-    a0.x = tok_ok ? av[0] : 0u; a0.y = tok_ok ? av[1] : 0u; a0.z = tok_ok ? av[2] : 0u; a0.w = tok_ok ? av[3] : 0u;
-    a1.x = tok_ok ? av[4] : 0u; a1.y = tok_ok ? av[5] : 0u; a1.z = tok_ok ? av[6] : 0u; a1.w = tok_ok ? av[7] : 0u;
-    *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq]) = a0;
-    *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq + 4]) = a1;
-    if (is_scale) st.ad[sq >> 1][srow] = __builtin_bit_cast(float, tok_ok ? av[8] : 0u);
+    // tokens past the end hold the last token's block: each token is its
+    // own row of the products, so theirs are never mixed in or stored
+    *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq]) = make_uint4(av[0], av[1], av[2], av[3]);
+    *reinterpret_cast<uint4*>(&st.aq[srow][8 * sq + 4]) = make_uint4(av[4], av[5], av[6], av[7]);
+    if (is_scale) st.ad[sq >> 1][srow] = (double)__builtin_bit_cast(float, av[8]);
   };
 
-  const int wt = (wave & 1) * 32, wr = (wave >> 1) * 16 * RT;   // this wave's tokens and rows in the tile
+  // this wave's tokens and rows in the tile: 64 tokens x 16 rows (64-row
+  // tiles) or 32 x 16 (32-row tiles). One 16-row weight operand serves all
+  // of the wave's token tiles, so each (row, group) operand is formed by
+  // one wave only (64-row tiles) or two.
+  constexpr int TW = RT == 2 ? 4 : 2;   // 16-token tiles per wave
+  const int wt = RT == 2 ? 0 : (wave & 1) * 32, wr = RT == 2 ? 16 * wave : 16 * (wave >> 1);
   const int li = lane & 15, lk = lane >> 4;
-  double acc[2][RT][4];
+  double acc[TW][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TW; ++a)
 #pragma unroll
-    for (int b = 0; b < RT; ++b)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[a][b][v] = 0.0;
+    for (int v = 0; v < 4; ++v) acc[a][v] = 0.0;
 
   // one step's products from a staged tile: per pair of groups (64 values)
-  // one 16x16x64 product per chain and tile; lane l takes the 16 values
-  // 16 (l / 16) .. +15 of the pair from both operands, so any assignment of
-  // the pair's values to operand bytes that is the same for both sides gives
-  // the same sum
+  // one 16x16x64 product per chain and token tile; lane l takes the 16
+  // values 16 (l / 16) .. +15 of the pair from both operands, so any
+  // assignment of the pair's values to operand bytes that is the same for
+  // both sides gives the same sum
   auto compute = [&](const MfStageK<ROWS>& st) {
-    i32x4 dl[2][RT], dh[2][RT], dm[2][RT];
-    float dw[RT], dmw[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      dw[rt] = st.wd[wr + 16 * rt + li];
-      dmw[rt] = st.wdm[wr + 16 * rt + li];
-    }
+    i32x4 dl[TW], dh[TW], dm[TW];
+    const float dw = st.wd[wr + li], dmw = st.wdm[wr + li];
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
       if ((2 * gp) % GPB == 0) {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < RT; ++b) {
-            dl[a][b] = i32x4{0, 0, 0, 0};
-            dh[a][b] = i32x4{0, 0, 0, 0};
-            dm[a][b] = i32x4{0, 0, 0, 0};
-          }
-      }
-      i32x4 aop[2], blo[RT], bhi[RT], bmn[RT];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        aop[tt] = *reinterpret_cast<const i32x4*>(&st.aq[wt + 16 * tt + li][16 * gp + 4 * lk]);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const i32x4 u = *reinterpret_cast<const i32x4*>(&st.wu[wr + 16 * rt + li][16 * gp + 4 * lk]);
-        // lanes 32..63 hold the pair's second group
-        const uint32_t c = st.wsc[2 * gp + (lk >> 1)][wr + 16 * rt + li];
-        const uint32_t sl = c & 255u, sh = (c >> 8) & 255u;
-        const int m = (int)((c >> 16) * 0x01010101u);
-        blo[rt] = i32x4{(int)bytes_times((uint32_t)u[0], sl), (int)bytes_times((uint32_t)u[1], sl),
-                        (int)bytes_times((uint32_t)u[2], sl), (int)bytes_times((uint32_t)u[3], sl)};
-        bhi[rt] = i32x4{(int)bytes_times((uint32_t)u[0], sh), (int)bytes_times((uint32_t)u[1], sh),
-                        (int)bytes_times((uint32_t)u[2], sh), (int)bytes_times((uint32_t)u[3], sh)};
-        bmn[rt] = i32x4{m, m, m, m};
-      }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          dl[tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], blo[rt], dl[tt][rt], 0, 0, 0);
-          dh[tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], bhi[rt], dh[tt][rt], 0, 0, 0);
-          dm[tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], bmn[rt], dm[tt][rt], 0, 0, 0);
+        for (int a = 0; a < TW; ++a) {
+          dl[a] = i32x4{0, 0, 0, 0};
+          dh[a] = i32x4{0, 0, 0, 0};
+          dm[a] = i32x4{0, 0, 0, 0};
         }
+      }
+      i32x4 aop[TW];
+#pragma unroll
+      for (int tt = 0; tt < TW; ++tt)
+        aop[tt] = *reinterpret_cast<const i32x4*>(&st.aq[wt + 16 * tt + li][16 * gp + 4 * lk]);
+      const i32x4 u = *reinterpret_cast<const i32x4*>(&st.wu[wr + li][16 * gp + 4 * lk]);
+      // lanes 32..63 hold the pair's second group
+      const uint32_t c = st.wsc[2 * gp + (lk >> 1)][wr + li];
+      const uint32_t sl = c & 255u, sh = (c >> 8) & 255u;
+      const int m = (int)((c >> 16) * 0x01010101u);
+      // one weight operand at a time, each used by all token tiles
+      const i32x4 blo = i32x4{(int)bytes_times((uint32_t)u[0], sl), (int)bytes_times((uint32_t)u[1], sl),
+                              (int)bytes_times((uint32_t)u[2], sl), (int)bytes_times((uint32_t)u[3], sl)};
+#pragma unroll
+      for (int tt = 0; tt < TW; ++tt) dl[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], blo, dl[tt], 0, 0, 0);
+      const i32x4 bhi = i32x4{(int)bytes_times((uint32_t)u[0], sh), (int)bytes_times((uint32_t)u[1], sh),
+                              (int)bytes_times((uint32_t)u[2], sh), (int)bytes_times((uint32_t)u[3], sh)};
+#pragma unroll
+      for (int tt = 0; tt < TW; ++tt) dh[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], bhi, dh[tt], 0, 0, 0);
+      const i32x4 bmn = i32x4{m, m, m, m};
+#pragma unroll
+      for (int tt = 0; tt < TW; ++tt) dm[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[tt], bmn, dm[tt], 0, 0, 0);
       if ((2 * gp + 1) % GPB == GPB - 1) {   // the block's share: d S - dmin O, then the activation scale
         const int blk = (2 * gp + 1) / GPB;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const float4 d4 = *reinterpret_cast<const float4*>(&st.ad[blk][wt + 16 * tt + 4 * lk]);
-          const double dv[4] = {(double)d4.x, (double)d4.y, (double)d4.z, (double)d4.w};
+        for (int tt = 0; tt < TW; ++tt) {
+          const double* dv = &st.ad[blk][wt + 16 * tt + 4 * lk];
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int S = dl[tt][rt][v] + 8 * dh[tt][rt][v];
-              const float yb = __builtin_fmaf(-dmw[rt], (float)dm[tt][rt][v], dw[rt] * (float)S);
-              acc[tt][rt][v] = __builtin_fma(dv[v], (double)yb, acc[tt][rt][v]);
-            }
+          for (int v = 0; v < 4; ++v) {
+            const int S = dl[tt][v] + 8 * dh[tt][v];
+            const float yb = __builtin_fmaf(-dmw, (float)dm[tt][v], dw * (float)S);
+            acc[tt][v] = __builtin_fma(dv[v], (double)yb, acc[tt][v]);
+          }
         }
       }
+      // the next pair's operands are read after this pair's products, which
+      // keeps the live registers under the three-workgroup budget
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -883,16 +881,13 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT 
     if (s + 1 < nsteps) store_step(s + 1, stage[(s + 1) & 1]);
     __syncthreads();   // the next step's tile is staged; this one is free again
   }
+  const int64_t row = r0 + wr + li;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t tok = t0 + wt + 16 * tt + 4 * lk + v;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int64_t row = r0 + wr + 16 * rt + li;
-        if (tok < n_tok && row < n_out) y[tok * n_out + row] = (float)acc[tt][rt][v];
-      }
+      if (tok < n_tok && row < n_out) y[tok * n_out + row] = (float)acc[tt][v];
     }
 }
 
