@@ -723,6 +723,13 @@ __device__ __forceinline__ uint32_t quad_word(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, K * 0x55, 0xf, 0xf, false);
 }
 
+// An int32 sum that started from the bit pattern of 1.5 * 2^23 (0x4B400000)
+// and moved by n, |n| < 2^22, is the float 1.5 * 2^23 + n: the value n is then
+// one exact subtraction away, and no conversion instruction is needed.
+constexpr int MAGIC_I = 0x4B400000;
+constexpr float MAGIC_F = 12582912.0f;
+__device__ __forceinline__ float magic_value(int biased) { return __builtin_bit_cast(float, biased) - MAGIC_F; }
+
 // codes u (bytes, at most 15) times s (at most 7): no byte carries
 __device__ __forceinline__ uint32_t bytes_times(uint32_t u, uint32_t s) { return u * s; }
 
@@ -826,10 +833,10 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT 
     for (int gp = 0; gp < 2; ++gp) {
       if ((2 * gp) % GPB == 0) {
 #pragma unroll
-        for (int a = 0; a < TW; ++a) {
-          dl[a] = i32x4{0, 0, 0, 0};
-          dh[a] = i32x4{0, 0, 0, 0};
-          dm[a] = i32x4{0, 0, 0, 0};
+        for (int a = 0; a < TW; ++a) {   // each chain's sum is at most 127 * 105 * 128 < 2^21 in magnitude
+          dl[a] = i32x4{MAGIC_I, MAGIC_I, MAGIC_I, MAGIC_I};
+          dh[a] = i32x4{MAGIC_I, MAGIC_I, MAGIC_I, MAGIC_I};
+          dm[a] = i32x4{MAGIC_I, MAGIC_I, MAGIC_I, MAGIC_I};
         }
       }
       i32x4 aop[TW];
@@ -860,8 +867,9 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT 
           const double* dv = &st.ad[blk][wt + 16 * tt + 4 * lk];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int S = dl[tt][v] + 8 * dh[tt][v];
-            const float yb = __builtin_fmaf(-dmw, (float)dm[tt][v], dw * (float)S);
+            // S = 8 sum(sh u q) + sum(sl u q), |S| < 2^24: exact in fp32
+            const float S = __builtin_fmaf(8.0f, magic_value(dh[tt][v]), magic_value(dl[tt][v]));
+            const float yb = __builtin_fmaf(-dmw, magic_value(dm[tt][v]), dw * S);
             acc[tt][v] = __builtin_fma(dv[v], (double)yb, acc[tt][v]);
           }
         }
