@@ -711,7 +711,7 @@ template <int ROWS>
 struct MfStageK {
   uint32_t aq[MF_TOK][MF_ROW_WORDS];    // activation codes
   uint32_t wu[ROWS][MF_ROW_WORDS];      // weight code bytes u
-  uint32_t wsc[4][ROWS];                // per group: sc & 7, sc >> 3, mn in bytes 0, 1, 2
+  uint32_t wsc[ROWS][4];                // per row and group: sc & 7, sc >> 3, mn in bytes 0, 1, 2
   float wd[ROWS], wdm[ROWS];            // d and dmin of the rows' super-block
   double ad[2][MF_TOK];                 // activation scales (of each 64-value block for Q8_K64)
 };
@@ -795,7 +795,7 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT 
                                   (c2 >> 4) & 0x0f0f0f0fu, (c3 >> 4) & 0x0f0f0f0fu);   // 16 .. 31
       *reinterpret_cast<uint4*>(&st.wu[srow][8 * sq]) = l0;
       *reinterpret_cast<uint4*>(&st.wu[srow][8 * sq + 4]) = l1;
-      st.wsc[sq][srow] = (sc & 7u) | ((sc >> 3) << 8) | (mn << 16);
+      st.wsc[srow][sq] = (sc & 7u) | ((sc >> 3) << 8) | (mn << 16);
       if (sq == 0) {
         st.wd[srow] = half_bits(h0);
         st.wdm[srow] = half_bits(h0 >> 16);
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(ACT 
         aop[tt] = *reinterpret_cast<const i32x4*>(&st.aq[wt + 16 * tt + li][16 * gp + 4 * lk]);
       const i32x4 u = *reinterpret_cast<const i32x4*>(&st.wu[wr + li][16 * gp + 4 * lk]);
       // lanes 32..63 hold the pair's second group
-      const uint32_t c = st.wsc[2 * gp + (lk >> 1)][wr + li];
+      const uint32_t c = st.wsc[wr + li][2 * gp + (lk >> 1)];
       const uint32_t sl = c & 255u, sh = (c >> 8) & 255u;
       const int m = (int)((c >> 16) * 0x01010101u);
       // one weight operand at a time, each used by all token tiles
