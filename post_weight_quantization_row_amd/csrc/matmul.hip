@@ -701,12 +701,13 @@ __global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 // 105; the second takes mn (at most 63) repeated over the group's 32
 // values. So each activation block costs three chains of 16x16x64 products
 // (two groups per instruction) accumulated in int32 across its groups
-// (exact: |sum| < 2^24), then per output one conversion, one product with d
+// (exact: each chain's |sum| < 2^21, |8 sum(sh u q) + sum(sl u q)| < 2^24),
+// then per output the exact float values of the sums, one product with d
 // and one fused multiply-add with dmin: two roundings per block where the
 // per-group kernel has up to eight, and fewer vector instructions. The
 // weights are staged once as code bytes; each lane forms sl u and sh u from
-// them (two multiplies per word), which keeps a workgroup at 41 KB of LDS
-// and 164 VGPRs: three workgroups per CU.
+// them (two multiplies per word), which keeps a workgroup at 42 KB of LDS
+// and 168 VGPRs: three workgroups per CU.
 template <int ROWS>
 struct MfStageK {
   uint32_t aq[MF_TOK][MF_ROW_WORDS];    // activation codes
